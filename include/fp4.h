@@ -1,0 +1,160 @@
+/*
+ * fp4.h - block-scaled FP4 (E2M1) quantization for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libfp4.so.  Every tensor argument is a DEVICE pointer into memory
+ * the caller owns (allocates and frees); the library allocates nothing and
+ * keeps no mutable global state, so calls on different streams may run
+ * concurrently.  All work is enqueued asynchronously on `stream` (a
+ * hipStream_t passed as void*; NULL is the null stream).
+ *
+ * Formats (one definition each, as given on the pages cited):
+ *  - E2M1 element ("NVFP4 / MXFP4 format" page, charlestar.github.io, section
+ *    1): 4-bit code, bit 3 = sign, bits 0-2 index {0, .5, 1, 1.5, 2, 3, 4, 6};
+ *    rounding is to the nearest value with ties to the even code, magnitudes
+ *    saturate at 6 and the sign bit of the quotient is kept (so -0.0 -> 8).
+ *  - Packing (same page, section 1): byte j = code[2j] | code[2j+1] << 4.
+ *  - MXFP4 (same page, sections 2 and 5): 32-element blocks, one E8M0 scale
+ *    byte c meaning 2^(c-127); the block exponent follows the OCP floor rule
+ *    e = floor(log2 amax) - 2 (a zero block takes e = 0; e >= -127).
+ *  - NVFP4 (same page, section 3): 16-element blocks, an E4M3FN block scale
+ *    s_b = E4M3(A_g / (6 s_g)) (nearest, ties to even, saturating at 448) and
+ *    one fp32 tensor scale s_g = A / (6 * 448) (an all-zero tensor takes 1).
+ *    Elements are divided by alpha = RN32(s_g * s_b) with a correctly rounded
+ *    fp32 division, then rounded to E2M1.
+ *
+ * Layout: the input is row-major [rows, cols]; blocks run along the last
+ * dimension, so cols must be a multiple of the block.  Outputs:
+ *   codes  [rows, cols/2]      uint8, two codes per byte (even element low)
+ *   scales [rows, cols/block]  uint8, one scale byte per block, row-major
+ * Because every row holds whole blocks, the flat order of elements, codes and
+ * scales is the row-major order; the library treats the tensor as flat.
+ *
+ * Errors.  Argument errors are returned synchronously, before any HIP call
+ * (so they are testable without a GPU).  Data-dependent conditions are found
+ * on the device and OR-ed into *status (a device int32 the caller zeroes
+ * beforehand; may be NULL to ignore them) as FP4_FLAG_* bits; when a flag is
+ * set the outputs are unspecified.
+ */
+#ifndef FP4_H
+#define FP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FP4_OK = 0,
+    FP4_E_ARG = 1,       /* null pointer, wrong block size, bad candidate grid   */
+    FP4_E_SHAPE = 2,     /* rows < 1, cols < 1, or cols not a multiple of block   */
+    FP4_E_DTYPE = 3,     /* unknown fp4_dtype / fp4_format                        */
+    FP4_E_ALIGN = 4,     /* a pointer is not aligned as documented                */
+    FP4_E_WORKSPACE = 5, /* workspace missing or smaller than fp4_workspace_bytes */
+    FP4_E_HIP = 6        /* a HIP runtime call (e.g. a launch) failed             */
+} fp4_status;
+
+/* Device-side condition flags OR-ed into *status. */
+#define FP4_FLAG_NONFINITE 1       /* an input element is NaN or +-Inf          */
+#define FP4_FLAG_SCALE_UNDERFLOW 2 /* tensor scale, block scale or alpha is 0   */
+
+typedef enum { FP4_F32 = 0, FP4_BF16 = 1 } fp4_dtype;
+typedef enum { FP4_MXFP4 = 0, FP4_NVFP4 = 1 } fp4_format;
+
+/*
+ * MXFP4 quantize ("NVFP4 / MXFP4 format" page, sections 1, 2 and 5).
+ *   x       [rows, cols] fp32 or bf16, 16-byte aligned
+ *   block   must be 32
+ *   codes   [rows*cols/2] bytes, 16-byte aligned
+ *   scales  [rows*cols/32] E8M0 bytes
+ *   status  device int32 or NULL (FP4_FLAG_NONFINITE)
+ * One pass over x.  Deterministic.
+ */
+fp4_status fp4_quantize_mxfp4(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
+                              int32_t block, uint8_t *codes, uint8_t *scales,
+                              int32_t *status, void *stream);
+
+/*
+ * NVFP4 quantize ("NVFP4 / MXFP4 format" page, section 3, two-level scale
+ * and zero/tiny contract).
+ *   x, xt, rows, cols, codes as for MXFP4; block must be 16
+ *   scales        [rows*cols/16] E4M3FN bytes
+ *   global_scale  device float: receives s_g (dequantize direction, x ~ s_g*s_b*p)
+ *   workspace     device scratch of at least fp4_workspace_bytes(FP4_NVFP4, ...)
+ *                 bytes, 16-byte aligned; contents on entry are ignored
+ *   status        FP4_FLAG_NONFINITE, FP4_FLAG_SCALE_UNDERFLOW
+ * Two kernels: a tensor-amax pass, then the quantize pass (which reads the
+ * amax in stream order, without a host round trip).  Deterministic.
+ */
+fp4_status fp4_quantize_nvfp4(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
+                              int32_t block, uint8_t *codes, uint8_t *scales,
+                              float *global_scale, void *workspace, size_t workspace_bytes,
+                              int32_t *status, void *stream);
+
+/*
+ * Dequantize ("FP4 / NVFP4 math summary" page, section 10: x_hat = q * alpha).
+ *   fmt           FP4_MXFP4 (block 32) or FP4_NVFP4 (block 16)
+ *   codes, scales as produced by the quantizers (any byte values accepted)
+ *   global_scale  device float s_g for NVFP4, ignored (may be NULL) for MXFP4
+ *   y             [rows, cols] fp32 or bf16 output, 16-byte aligned
+ * MXFP4: y = E2M1(c) * 2^(s-127), exact in fp32 and bf16 for s <= 252.
+ * NVFP4: y = RN_out(RN32(E2M1(c) * RN32(s_g * E4M3(s)))).
+ * A NaN scale byte (E8M0 255, E4M3 0x7F / 0xFF) yields NaN outputs.
+ */
+fp4_status fp4_dequantize(fp4_format fmt, const uint8_t *codes, const uint8_t *scales,
+                          const float *global_scale, int64_t rows, int64_t cols,
+                          int32_t block, void *y, fp4_dtype yt, void *stream);
+
+/*
+ * MSE-optimal NVFP4 block-scale search ("FP4 / NVFP4 math summary" page,
+ * section 9: minimise sum (x - s * Round_FP4(x / s))^2; "NVFP4 / MXFP4 format"
+ * page, section 4: the encoded scale is what quantizes).
+ *   Candidate k of n: c_k = RN32(((n-1-k) c_lo + k c_hi) / (n-1)); its block
+ *   scale is E4M3(c_k * A_g / (6 s_g)) (exact real; code 0 skipped), and its
+ *   loss is evaluated in fp32: q = RN32(x/alpha), x_hat = RN32(E2M1(q)*alpha),
+ *   e = x - x_hat, sum of e*e as a balanced pairwise tree over the 16
+ *   elements in index order.  The smallest k with the least loss wins; the
+ *   block is then quantized with it.  s_g is the NVFP4 tensor scale.
+ *   Requirements: block 16, n_candidates >= 2, 0 < c_lo <= c_hi <= 4 and
+ *   (c_hi - c_lo) / (n_candidates - 1) <= c_lo / 24 (the candidate grid is
+ *   then finer than the E4M3 grid, whose rounding intervals are at least
+ *   1/15 of their value wide, so the distinct candidate scales of a block
+ *   are exactly the consecutive E4M3 codes between the two ends).
+ *   Other arguments as for fp4_quantize_nvfp4.  Deterministic.
+ */
+fp4_status fp4_scale_search(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
+                            int32_t block, int32_t n_candidates, float c_lo, float c_hi,
+                            uint8_t *codes, uint8_t *scales, float *global_scale,
+                            void *workspace, size_t workspace_bytes, int32_t *status,
+                            void *stream);
+
+/*
+ * MXFP4 x MXFP4 block-scaled GEMM ("FP4, FP8 and INT8/INT4" page,
+ * tom-jerr.github.io, section 5.1: C = sum_t sA sB sum_{k in t} qA qB with
+ * fp32 accumulation; "NVFP4 / MXFP4 format" page, section 6: scales come out
+ * only per K block, and storing the weight as N x K makes its last-dimension
+ * blocks the K blocks).
+ *   a_codes   [M, K/2], a_scales  [M, K/32]   (A quantized along K)
+ *   bt_codes  [N, K/2], bt_scales [N, K/32]   (B stored transposed as Bt [N, K])
+ *   c         [M, N] fp32 or bf16 (bf16 = RNE of the fp32 result)
+ * K must be a multiple of 32; codes 16-byte aligned with K/2 a multiple of 16
+ * (K % 32 == 0 suffices), c 4-byte aligned.  The summation order is fixed, so
+ * results are deterministic.
+ */
+fp4_status fp4_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales,
+                          const uint8_t *bt_codes, const uint8_t *bt_scales, int64_t M,
+                          int64_t N, int64_t K, void *c, fp4_dtype ct, void *stream);
+
+/* Bytes of device workspace fp4_quantize_nvfp4 / fp4_scale_search need for a
+ * [rows, cols] input (0 for MXFP4). */
+size_t fp4_workspace_bytes(fp4_format fmt, int64_t rows, int64_t cols);
+
+/* Static English text for a status code. */
+const char *fp4_status_str(fp4_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4_H */

@@ -1,0 +1,210 @@
+"""Block-scaled FP4 (MXFP4 / NVFP4) quantization for AMD MI355X (gfx950).
+
+Thin Python binding over ``libfp4.so`` (C ABI in ``include/fp4.h``): argument
+marshalling only.  Every step of the method runs in the library's HIP
+kernels; PyTorch provides device memory and the current stream.  If the
+library is not built, every call raises; there is no fallback.
+
+Functions mirror the C entry points:
+
+    quantize_mxfp4(x)                       -> (codes, scales)
+    quantize_nvfp4(x)                       -> (codes, scales, global_scale)
+    dequantize(fmt, codes, scales, s_g, out_dtype)
+    scale_search(x, n_candidates, c_lo, c_hi) -> (codes, scales, global_scale)
+    gemm_mxfp4(a_codes, a_scales, bt_codes, bt_scales, out_dtype)
+
+Inputs are contiguous CUDA (HIP) tensors of dtype float32 or bfloat16 whose
+last dimension is a multiple of the block (32 for MXFP4, 16 for NVFP4).
+codes have shape [..., K/2] (uint8, two E2M1 codes per byte, even element in
+the low nibble); scales [..., K/block] (uint8: E8M0 for MXFP4, E4M3FN for
+NVFP4); global_scale is a 1-element float32 tensor (NVFP4 s_g).
+
+With ``check=True`` (the default) a call synchronises the stream, reads the
+device status word and raises ValueError for non-finite input or a scale
+that underflows, as the format page's reference contract does.  Pass
+``check=False`` to keep calls asynchronous (benchmarks).
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp4.so")
+
+MXFP4 = 0
+NVFP4 = 1
+F32 = 0
+BF16 = 1
+FLAG_NONFINITE = 1
+FLAG_SCALE_UNDERFLOW = 2
+
+EXPORTS = ("fp4_quantize_mxfp4", "fp4_quantize_nvfp4", "fp4_dequantize", "fp4_scale_search",
+           "fp4_gemm_mxfp4", "fp4_workspace_bytes", "fp4_status_str")
+
+_lib = None
+
+
+class Fp4Error(RuntimeError):
+    """A libfp4 entry point returned a non-OK status."""
+
+
+def lib() -> ctypes.CDLL:
+    """Load the in-tree libfp4.so (built by ``mxfp4_block_amax_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise Fp4Error(f"{LIB_PATH} is not built; run python -m mxfp4_block_amax_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, F, S = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float,
+                         ctypes.c_size_t)
+    I = ctypes.c_int
+    L.fp4_quantize_mxfp4.argtypes = [P, I, I64, I64, I32, P, P, P, P]
+    L.fp4_quantize_nvfp4.argtypes = [P, I, I64, I64, I32, P, P, P, P, S, P, P]
+    L.fp4_dequantize.argtypes = [I, P, P, P, I64, I64, I32, P, I, P]
+    L.fp4_scale_search.argtypes = [P, I, I64, I64, I32, I32, F, F, P, P, P, P, S, P, P]
+    L.fp4_gemm_mxfp4.argtypes = [P, P, P, P, I64, I64, I64, P, I, P]
+    L.fp4_workspace_bytes.argtypes = [I, I64, I64]
+    L.fp4_workspace_bytes.restype = S
+    L.fp4_status_str.argtypes = [I]
+    L.fp4_status_str.restype = ctypes.c_char_p
+    for name in ("fp4_quantize_mxfp4", "fp4_quantize_nvfp4", "fp4_dequantize",
+                 "fp4_scale_search", "fp4_gemm_mxfp4"):
+        getattr(L, name).restype = I
+    _lib = L
+    return L
+
+
+def status_str(code: int) -> str:
+    return lib().fp4_status_str(int(code)).decode()
+
+
+def _ok(code: int):
+    if code != 0:
+        raise Fp4Error(f"libfp4 status {code}: {status_str(code)}")
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _dtype_code(dt) -> int:
+    if dt == torch.float32:
+        return F32
+    if dt == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {dt}; use torch.float32 or torch.bfloat16")
+
+
+def _rows_cols(x: torch.Tensor):
+    if not x.is_cuda:
+        raise TypeError("expected a device tensor")
+    if not x.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    if x.dim() < 1 or x.numel() == 0:
+        raise ValueError("expected a non-empty tensor")
+    cols = x.shape[-1]
+    return x.numel() // cols, cols
+
+
+def _raise_flags(flags: int):
+    if flags & FLAG_NONFINITE:
+        raise ValueError("finite input required (NaN or Inf found)")
+    if flags & FLAG_SCALE_UNDERFLOW:
+        raise ValueError("a nonzero scale rounded to zero (tensor, block scale or alpha underflow)")
+
+
+def _finish(status: torch.Tensor, check: bool):
+    if check:
+        _raise_flags(int(status.item()))
+
+
+def workspace_bytes(fmt: int, rows: int, cols: int) -> int:
+    return int(lib().fp4_workspace_bytes(int(fmt), int(rows), int(cols)))
+
+
+def quantize_mxfp4(x: torch.Tensor, check: bool = True, out=None, status=None):
+    rows, cols = _rows_cols(x)
+    if out is None:
+        codes = torch.empty(*x.shape[:-1], cols // 2, dtype=torch.uint8, device=x.device)
+        scales = torch.empty(*x.shape[:-1], max(cols // 32, 1), dtype=torch.uint8, device=x.device)
+    else:
+        codes, scales = out
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _ok(lib().fp4_quantize_mxfp4(_ptr(x), _dtype_code(x.dtype), rows, cols, 32, _ptr(codes),
+                                 _ptr(scales), _ptr(status), _stream(x)))
+    _finish(status, check)
+    return codes, scales
+
+
+def quantize_nvfp4(x: torch.Tensor, check: bool = True, out=None, status=None, workspace=None):
+    rows, cols = _rows_cols(x)
+    if out is None:
+        codes = torch.empty(*x.shape[:-1], cols // 2, dtype=torch.uint8, device=x.device)
+        scales = torch.empty(*x.shape[:-1], max(cols // 16, 1), dtype=torch.uint8, device=x.device)
+        s_g = torch.empty(1, dtype=torch.float32, device=x.device)
+    else:
+        codes, scales, s_g = out
+    ws_bytes = workspace_bytes(NVFP4, rows, cols)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _ok(lib().fp4_quantize_nvfp4(_ptr(x), _dtype_code(x.dtype), rows, cols, 16, _ptr(codes),
+                                 _ptr(scales), _ptr(s_g), _ptr(workspace), workspace.numel(),
+                                 _ptr(status), _stream(x)))
+    _finish(status, check)
+    return codes, scales, s_g
+
+
+def dequantize(fmt: int, codes: torch.Tensor, scales: torch.Tensor, global_scale=None,
+               out_dtype=torch.bfloat16, out=None):
+    rows, half = _rows_cols(codes)
+    cols = half * 2
+    block = 32 if fmt == MXFP4 else 16
+    y = out if out is not None else torch.empty(*codes.shape[:-1], cols, dtype=out_dtype,
+                                                device=codes.device)
+    _ok(lib().fp4_dequantize(int(fmt), _ptr(codes), _ptr(scales), _ptr(global_scale), rows, cols,
+                             block, _ptr(y), _dtype_code(y.dtype), _stream(codes)))
+    return y
+
+
+def scale_search(x: torch.Tensor, n_candidates: int = 64, c_lo: float = 0.5, c_hi: float = 1.0,
+                 check: bool = True, out=None, status=None, workspace=None):
+    rows, cols = _rows_cols(x)
+    if out is None:
+        codes = torch.empty(*x.shape[:-1], cols // 2, dtype=torch.uint8, device=x.device)
+        scales = torch.empty(*x.shape[:-1], max(cols // 16, 1), dtype=torch.uint8, device=x.device)
+        s_g = torch.empty(1, dtype=torch.float32, device=x.device)
+    else:
+        codes, scales, s_g = out
+    ws_bytes = workspace_bytes(NVFP4, rows, cols)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _ok(lib().fp4_scale_search(_ptr(x), _dtype_code(x.dtype), rows, cols, 16, int(n_candidates),
+                               float(c_lo), float(c_hi), _ptr(codes), _ptr(scales), _ptr(s_g),
+                               _ptr(workspace), workspace.numel(), _ptr(status), _stream(x)))
+    _finish(status, check)
+    return codes, scales, s_g
+
+
+def gemm_mxfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, bt_codes: torch.Tensor,
+               bt_scales: torch.Tensor, out_dtype=torch.bfloat16, out=None):
+    """C [M, N] = A [M, K] @ B [K, N] with A and Bt = B^T [N, K] in MXFP4."""
+    M, kh = _rows_cols(a_codes)
+    N, kh2 = _rows_cols(bt_codes)
+    if kh != kh2:
+        raise ValueError("A and Bt must share K")
+    K = 2 * kh
+    c = out if out is not None else torch.empty(M, N, dtype=out_dtype, device=a_codes.device)
+    _ok(lib().fp4_gemm_mxfp4(_ptr(a_codes), _ptr(a_scales), _ptr(bt_codes), _ptr(bt_scales), M, N,
+                             K, _ptr(c), _dtype_code(c.dtype), _stream(a_codes)))
+    return c

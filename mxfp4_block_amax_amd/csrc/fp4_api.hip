@@ -1,0 +1,137 @@
+// fp4_api.hip - the extern "C" entry points of libfp4.so (declared in
+// include/fp4.h): argument validation on the host, then kernel launches on
+// the caller's stream.  Every argument error is returned before any HIP call.
+#include <stdint.h>
+
+#include "../../include/fp4.h"
+#include "fp4_kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool valid_dtype(fp4_dtype t) { return t == FP4_F32 || t == FP4_BF16; }
+
+fp4_status check_shape(int64_t rows, int64_t cols, int32_t block) {
+    if (rows < 1 || cols < 1) return FP4_E_SHAPE;
+    if (cols % block) return FP4_E_SHAPE;          // incomplete block / odd length
+    if (rows > kMaxElems / cols) return FP4_E_SHAPE;
+    return FP4_OK;
+}
+
+fp4_status from_hip(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_E_HIP; }
+
+// The NVFP4 and scale-search tensor-amax pass needs this many bytes.
+size_t nv_workspace() { return fp4dev::kNvWorkspaceBytes; }
+
+}  // namespace
+
+extern "C" {
+
+fp4_status fp4_quantize_mxfp4(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
+                              int32_t block, uint8_t *codes, uint8_t *scales,
+                              int32_t *status, void *stream) {
+    if (!x || !codes || !scales) return FP4_E_ARG;
+    if (block != 32) return FP4_E_ARG;
+    if (!valid_dtype(xt)) return FP4_E_DTYPE;
+    fp4_status st = check_shape(rows, cols, block);
+    if (st != FP4_OK) return st;
+    if (!aligned(x, 16) || !aligned(codes, 4) || !aligned(status, 4)) return FP4_E_ALIGN;
+    return from_hip(fp4dev::launch_mx_quantize(x, xt == FP4_BF16, rows * cols, codes, scales,
+                                               status, (hipStream_t)stream));
+}
+
+fp4_status fp4_quantize_nvfp4(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
+                              int32_t block, uint8_t *codes, uint8_t *scales,
+                              float *global_scale, void *workspace, size_t workspace_bytes,
+                              int32_t *status, void *stream) {
+    if (!x || !codes || !scales || !global_scale) return FP4_E_ARG;
+    if (block != 16) return FP4_E_ARG;
+    if (!valid_dtype(xt)) return FP4_E_DTYPE;
+    fp4_status st = check_shape(rows, cols, block);
+    if (st != FP4_OK) return st;
+    if (!workspace || workspace_bytes < nv_workspace()) return FP4_E_WORKSPACE;
+    if (!aligned(x, 16) || !aligned(codes, 4) || !aligned(global_scale, 4) ||
+        !aligned(workspace, 16) || !aligned(status, 4))
+        return FP4_E_ALIGN;
+    return from_hip(fp4dev::launch_nv_quantize(x, xt == FP4_BF16, rows * cols, codes, scales,
+                                               global_scale, workspace, status,
+                                               (hipStream_t)stream));
+}
+
+fp4_status fp4_dequantize(fp4_format fmt, const uint8_t *codes, const uint8_t *scales,
+                          const float *global_scale, int64_t rows, int64_t cols,
+                          int32_t block, void *y, fp4_dtype yt, void *stream) {
+    if (fmt != FP4_MXFP4 && fmt != FP4_NVFP4) return FP4_E_DTYPE;
+    if (!valid_dtype(yt)) return FP4_E_DTYPE;
+    if (!codes || !scales || !y) return FP4_E_ARG;
+    if (fmt == FP4_NVFP4 && !global_scale) return FP4_E_ARG;
+    if (block != (fmt == FP4_MXFP4 ? 32 : 16)) return FP4_E_ARG;
+    fp4_status st = check_shape(rows, cols, block);
+    if (st != FP4_OK) return st;
+    if (!aligned(codes, 4) || !aligned(y, 16) || !aligned(global_scale, 4)) return FP4_E_ALIGN;
+    return from_hip(fp4dev::launch_dequantize((int)fmt, codes, scales, global_scale,
+                                              rows * cols, y, yt == FP4_BF16,
+                                              (hipStream_t)stream));
+}
+
+fp4_status fp4_scale_search(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
+                            int32_t block, int32_t n_candidates, float c_lo, float c_hi,
+                            uint8_t *codes, uint8_t *scales, float *global_scale,
+                            void *workspace, size_t workspace_bytes, int32_t *status,
+                            void *stream) {
+    if (!x || !codes || !scales || !global_scale) return FP4_E_ARG;
+    if (block != 16) return FP4_E_ARG;
+    // candidate grid: c_k = linspace(c_lo, c_hi, n); it must be finer than the
+    // E4M3 grid so that the distinct encoded candidates are consecutive codes
+    if (n_candidates < 2) return FP4_E_ARG;
+    if (!(c_lo > 0.0f) || !(c_hi >= c_lo) || !(c_hi <= 4.0f)) return FP4_E_ARG;
+    // an E4M3 rounding interval is at least 1/15 of its code's value wide, so a
+    // candidate step below c_lo / 24 of the block's t cannot jump over a code
+    if ((double)(c_hi - c_lo) / (double)(n_candidates - 1) > (double)c_lo / 24.0) return FP4_E_ARG;
+    if (!valid_dtype(xt)) return FP4_E_DTYPE;
+    fp4_status st = check_shape(rows, cols, block);
+    if (st != FP4_OK) return st;
+    if (!workspace || workspace_bytes < nv_workspace()) return FP4_E_WORKSPACE;
+    if (!aligned(x, 16) || !aligned(codes, 4) || !aligned(global_scale, 4) ||
+        !aligned(workspace, 16) || !aligned(status, 4))
+        return FP4_E_ALIGN;
+    return from_hip(fp4dev::launch_scale_search(x, xt == FP4_BF16, rows * cols, c_lo, c_hi,
+                                                codes, scales, global_scale, workspace,
+                                                status, (hipStream_t)stream));
+}
+
+fp4_status fp4_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales,
+                          const uint8_t *bt_codes, const uint8_t *bt_scales, int64_t M,
+                          int64_t N, int64_t K, void *c, fp4_dtype ct, void *stream) {
+    if (!a_codes || !a_scales || !bt_codes || !bt_scales || !c) return FP4_E_ARG;
+    if (!valid_dtype(ct)) return FP4_E_DTYPE;
+    if (M < 1 || N < 1 || K < 32 || K % 32) return FP4_E_SHAPE;
+    if (M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return FP4_E_SHAPE;
+    if (!aligned(a_codes, 16) || !aligned(bt_codes, 16) || !aligned(c, 4)) return FP4_E_ALIGN;
+    return from_hip(fp4dev::launch_gemm_mxfp4(a_codes, a_scales, bt_codes, bt_scales, M, N, K,
+                                              c, ct == FP4_BF16, (hipStream_t)stream));
+}
+
+size_t fp4_workspace_bytes(fp4_format fmt, int64_t rows, int64_t cols) {
+    (void)rows;
+    (void)cols;
+    return fmt == FP4_NVFP4 ? nv_workspace() : 0;
+}
+
+const char *fp4_status_str(fp4_status s) {
+    switch (s) {
+        case FP4_OK: return "ok";
+        case FP4_E_ARG: return "invalid argument (null pointer, block size or candidate grid)";
+        case FP4_E_SHAPE: return "invalid shape (rows/cols < 1 or cols not a multiple of the block)";
+        case FP4_E_DTYPE: return "invalid dtype or format";
+        case FP4_E_ALIGN: return "misaligned pointer";
+        case FP4_E_WORKSPACE: return "workspace missing or too small";
+        case FP4_E_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

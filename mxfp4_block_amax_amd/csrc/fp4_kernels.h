@@ -1,0 +1,32 @@
+// fp4_kernels.h - launchers shared by the C ABI (fp4_api.hip) and the kernel
+// translation units.  Internal to libfp4.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4dev {
+
+// Largest grid of the streaming kernels (workgroups of 256 threads); waves
+// loop over tiles beyond it.
+constexpr int kMaxGrid = 4096;
+// Workgroups (hence partial maxima) of the tensor-amax pass.
+constexpr int kAmaxPartials = 1024;
+constexpr size_t kNvWorkspaceBytes = kAmaxPartials * sizeof(uint32_t);
+
+hipError_t launch_mx_quantize(const void *x, bool bf16, int64_t n, uint8_t *codes,
+                              uint8_t *scales, int32_t *status, hipStream_t s);
+hipError_t launch_nv_quantize(const void *x, bool bf16, int64_t n, uint8_t *codes,
+                              uint8_t *scales, float *global_scale, void *workspace,
+                              int32_t *status, hipStream_t s);
+hipError_t launch_scale_search(const void *x, bool bf16, int64_t n, float c_lo, float c_hi,
+                               uint8_t *codes, uint8_t *scales, float *global_scale,
+                               void *workspace, int32_t *status, hipStream_t s);
+hipError_t launch_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales,
+                             const float *global_scale, int64_t n, void *y, bool out_bf16,
+                             hipStream_t s);
+hipError_t launch_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales,
+                             const uint8_t *bt_codes, const uint8_t *bt_scales, int64_t M,
+                             int64_t N, int64_t K, void *c, bool out_bf16, hipStream_t s);
+
+}  // namespace fp4dev

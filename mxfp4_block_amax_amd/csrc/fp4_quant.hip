@@ -1,0 +1,552 @@
+// fp4_quant.hip - MXFP4 / NVFP4 quantize, dequantize and MSE scale search
+// kernels for gfx950.
+//
+// Data layout.  The input is treated as a flat sequence of E elements (every
+// row holds whole blocks), cut into 16-byte "chunks" of 8 elements for bf16
+// input (32 bytes for fp32).  Lane l of a wave owns chunk  tile*64*U + r*64 + l
+// for r < U, so every load instruction of a wave reads 1 KiB of consecutive
+// bf16 bytes and every code store writes 256 consecutive bytes.  Blocks are
+// consecutive lanes: an NVFP4 block (16 elements) is a lane pair, an MXFP4
+// block (32) a lane quad, and the block amax is finished with DPP quad
+// permutes.  Scales are stored by one lane per block.
+//
+// Method ("NVFP4 / MXFP4 format" page, charlestar.github.io):
+//   MXFP4 (sections 2 and 5): E8M0 exponent by the OCP floor rule,
+//     e = floor(log2 amax) - 2, elements divided by 2^e and rounded to E2M1.
+//   NVFP4 (section 3): s_g = A / 2688, s_b = E4M3(A_g / (6 s_g)) encoded before
+//     it quantizes, alpha = RN32(s_g * s_b), q = RN32(x / alpha) -> E2M1.
+//   Zero/tiny contract (section 3): an all-zero tensor takes s_g = 1, a zero
+//     block takes s_b = 1 (0x38); a nonzero block whose s_b or alpha is 0, or
+//     an s_g that underflows, raises FP4_FLAG_SCALE_UNDERFLOW.
+// Scale search ("FP4 / NVFP4 math summary" page, devpress.csdn.net, section 9):
+//   per block, the candidate E4M3 scale with the least fp32 squared error.
+#include "fp4_device.h"
+#include "fp4_kernels.h"
+
+namespace fp4dev {
+
+constexpr int WG = 256;
+constexpr int WAVES_PER_WG = WG / WAVE;
+
+// ---------------------------------------------------------------------------
+// chunk loads
+// ---------------------------------------------------------------------------
+template <bool BF16>
+struct Chunk {
+    uint4 lo, hi;  // hi used only for fp32 input
+};
+
+template <bool BF16>
+__device__ __forceinline__ Chunk<BF16> load_chunk(const uint4 *__restrict__ x, int64_t c, bool ok) {
+    Chunk<BF16> k;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    if (BF16) {
+        k.lo = ok ? ld_stream(x + c) : z;
+        k.hi = z;
+    } else {
+        k.lo = ok ? ld_stream(x + 2 * c) : z;
+        k.hi = ok ? ld_stream(x + 2 * c + 1) : z;
+    }
+    return k;
+}
+
+template <bool BF16>
+__device__ __forceinline__ uint32_t chunk_amax(const Chunk<BF16> &k) {
+    return BF16 ? amax_bf16x8(k.lo) : amax_f32x8(k.lo, k.hi);
+}
+
+// fp32 bit pattern of a chunk-amax pattern
+template <bool BF16>
+__device__ __forceinline__ uint32_t amax_as_f32_bits(uint32_t m) {
+    return BF16 ? (m << 16) : m;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void chunk_values(const Chunk<BF16> &k, float (&v)[8]) {
+    if (BF16) widen_bf16x8(k.lo, v);
+    else widen_f32x8(k.lo, k.hi, v);
+}
+
+// ---------------------------------------------------------------------------
+// MXFP4 quantize: one pass.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(WG) void mx_quantize_kernel(const uint4 *__restrict__ x,
+                                                         int64_t nchunks,
+                                                         uint32_t *__restrict__ codes,
+                                                         uint8_t *__restrict__ scales,
+                                                         int32_t *status) {
+    constexpr int U = 4;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int64_t wave = (int64_t)blockIdx.x * WAVES_PER_WG + (threadIdx.x / WAVE);
+    const int64_t nwaves = (int64_t)gridDim.x * WAVES_PER_WG;
+    const int64_t ntiles = (nchunks + WAVE * U - 1) / (WAVE * U);
+    uint32_t flags = 0;
+    for (int64_t t = wave; t < ntiles; t += nwaves) {
+        Chunk<BF16> k[U];
+#pragma unroll
+        for (int r = 0; r < U; ++r) {
+            int64_t c = t * (WAVE * U) + r * WAVE + lane;
+            k[r] = load_chunk<BF16>(x, c, c < nchunks);
+        }
+#pragma unroll
+        for (int r = 0; r < U; ++r) {
+            int64_t c = t * (WAVE * U) + r * WAVE + lane;
+            uint32_t m = chunk_amax<BF16>(k[r]);
+            m = max(m, dpp<QP_XOR1>(m));
+            m = max(m, dpp<QP_XOR2>(m));
+            const int sh = BF16 ? 7 : 23;
+            if ((m >> sh) >= 0xFFu) flags |= FLAG_NONFINITE;
+            uint32_t sb = mx_scale_byte(m, sh);
+            float so = e8m0_operand(sb);
+            uint32_t q;
+            if (BF16) {
+                q = cvt_fp4x8_bf16(k[r].lo, so);
+            } else {
+                float v[8];
+                chunk_values<BF16>(k[r], v);
+                q = cvt_fp4x8_f32(v, so);
+            }
+            if (c < nchunks) {
+                codes[c] = q;
+                if ((lane & 3) == 0) scales[c >> 2] = (uint8_t)sb;
+            }
+        }
+    }
+    report_flags(status, flags);
+}
+
+// ---------------------------------------------------------------------------
+// Tensor amax (NVFP4 and scale search, pass 1): one partial max of the
+// sign-cleared bit patterns per workgroup.  No atomics, no initialisation.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(WG) void tensor_amax_kernel(const uint4 *__restrict__ x,
+                                                         int64_t nchunks,
+                                                         uint32_t *__restrict__ partials) {
+    constexpr int U = 4;
+    __shared__ uint32_t red[WAVES_PER_WG];
+    uint32_t m = 0;
+    const int64_t stride = (int64_t)gridDim.x * WG;
+    for (int64_t c0 = (int64_t)blockIdx.x * WG + threadIdx.x; c0 < nchunks; c0 += stride * U) {
+        Chunk<BF16> k[U];
+#pragma unroll
+        for (int r = 0; r < U; ++r) {
+            int64_t c = c0 + r * stride;
+            k[r] = load_chunk<BF16>(x, c, c < nchunks);
+        }
+#pragma unroll
+        for (int r = 0; r < U; ++r) m = max(m, chunk_amax<BF16>(k[r]));
+    }
+    m = wave_max_u32(m);
+    if ((threadIdx.x & (WAVE - 1)) == 0) red[threadIdx.x / WAVE] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = red[0];
+        for (int i = 1; i < WAVES_PER_WG; ++i) r = max(r, red[i]);
+        partials[blockIdx.x] = r;
+    }
+}
+
+// Reduce the pass-1 partials (every workgroup does it; the array is tiny and
+// L2-resident) and derive the tensor scale s_g = RN32(A / 2688), 1 for an
+// all-zero tensor ("NVFP4 / MXFP4 format" page, section 3).
+struct TensorScale {
+    float s_g;
+    uint32_t flags;
+};
+
+template <bool BF16>
+__device__ TensorScale tensor_scale(const uint32_t *__restrict__ partials, int npart) {
+    __shared__ uint32_t red[WAVES_PER_WG];
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < npart; i += WG) m = max(m, partials[i]);
+    m = wave_max_u32(m);
+    if ((threadIdx.x & (WAVE - 1)) == 0) red[threadIdx.x / WAVE] = m;
+    __syncthreads();
+    m = red[0];
+    for (int i = 1; i < WAVES_PER_WG; ++i) m = max(m, red[i]);
+    uint32_t A = amax_as_f32_bits<BF16>(m);
+    TensorScale ts;
+    ts.flags = 0;
+    if (A >= 0x7F800000u) {
+        ts.flags = FLAG_NONFINITE;
+        ts.s_g = 1.0f;
+        return ts;
+    }
+    ts.s_g = (A == 0) ? 1.0f : u2f(A) / 2688.0f;  // correctly rounded fp32 divide
+    if (ts.s_g == 0.0f) ts.flags = FLAG_SCALE_UNDERFLOW;
+    return ts;
+}
+
+// Per-block NVFP4 scale: E4M3 code, alpha and its reciprocal.
+struct BlockScale {
+    float alpha, y;
+    uint32_t code;
+    bool fast;  // alpha and 1/alpha normal: the reciprocal-correction divide is exact
+};
+
+__device__ __forceinline__ BlockScale nv_block_scale(uint32_t ag_bits, float s_g, double sg64,
+                                                     double inv6sg, uint32_t &flags) {
+    BlockScale b;
+    b.code = (ag_bits == 0) ? 0x38u : e4m3_code_exact((double)u2f(ag_bits), sg64, inv6sg);
+    b.alpha = s_g * e4m3_pos_value(b.code);
+    if ((ag_bits != 0 && b.code == 0) || b.alpha == 0.0f) flags |= FLAG_SCALE_UNDERFLOW;
+    b.fast = b.alpha >= 0x1p-126f;
+    b.y = 1.0f / (b.fast ? b.alpha : 1.0f);
+    return b;
+}
+
+// E2M1 codes of 8 values divided by alpha (fp32 correctly rounded divide).
+__device__ __forceinline__ uint32_t nv_quant8(const float (&v)[8], float alpha, float y, bool fast) {
+    float q[8];
+    if (fast) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = div_rn(v[i], alpha, y);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = v[i] / alpha;
+    }
+    return cvt_fp4x8_f32(q, e8m0_operand(E8M0_ONE));
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 quantize, pass 2.  Each wave tile is two chunk-rows; a lane pair holds
+// one block of each row.  The even lane derives row 0's block scale and the
+// odd lane row 1's, and they swap results, so no block scale is computed
+// twice.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(WG) void nv_quantize_kernel(const uint4 *__restrict__ x,
+                                                         int64_t nchunks,
+                                                         const uint32_t *__restrict__ partials,
+                                                         int npart, uint32_t *__restrict__ codes,
+                                                         uint8_t *__restrict__ scales,
+                                                         float *__restrict__ global_scale,
+                                                         int32_t *status) {
+    constexpr int U = 2;
+    TensorScale ts = tensor_scale<BF16>(partials, npart);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *global_scale = ts.s_g;
+    if (ts.flags) {  // uniform over the grid: outputs unspecified
+        if (blockIdx.x == 0 && threadIdx.x == 0 && status) atomicOr(status, (int32_t)ts.flags);
+        return;
+    }
+    const float s_g = ts.s_g;
+    const double sg64 = (double)s_g;
+    const double inv6sg = 1.0 / (6.0 * sg64);
+    const int lane = threadIdx.x & (WAVE - 1);
+    const bool odd = lane & 1;
+    const int64_t wave = (int64_t)blockIdx.x * WAVES_PER_WG + (threadIdx.x / WAVE);
+    const int64_t nwaves = (int64_t)gridDim.x * WAVES_PER_WG;
+    const int64_t ntiles = (nchunks + WAVE * U - 1) / (WAVE * U);
+    uint32_t flags = 0;
+    for (int64_t t = wave; t < ntiles; t += nwaves) {
+        const int64_t c0 = t * (WAVE * U) + lane, c1 = c0 + WAVE;
+        Chunk<BF16> k0 = load_chunk<BF16>(x, c0, c0 < nchunks);
+        Chunk<BF16> k1 = load_chunk<BF16>(x, c1, c1 < nchunks);
+        uint32_t m0 = chunk_amax<BF16>(k0), m1 = chunk_amax<BF16>(k1);
+        m0 = max(m0, dpp<QP_XOR1>(m0));
+        m1 = max(m1, dpp<QP_XOR1>(m1));
+        BlockScale mine = nv_block_scale(amax_as_f32_bits<BF16>(odd ? m1 : m0), s_g, sg64,
+                                         inv6sg, flags);
+        float pa = dppf<QP_XOR1>(mine.alpha), py = dppf<QP_XOR1>(mine.y);
+        bool pf = dpp<QP_XOR1>((uint32_t)mine.fast) != 0;
+        // row 0 uses the even lane's scale, row 1 the odd lane's
+        const float a0 = odd ? pa : mine.alpha, y0 = odd ? py : mine.y;
+        const float a1 = odd ? mine.alpha : pa, y1 = odd ? mine.y : py;
+        const bool f0 = odd ? pf : mine.fast, f1 = odd ? mine.fast : pf;
+        float v[8];
+        chunk_values<BF16>(k0, v);
+        uint32_t q0 = nv_quant8(v, a0, y0, f0);
+        chunk_values<BF16>(k1, v);
+        uint32_t q1 = nv_quant8(v, a1, y1, f1);
+        if (c0 < nchunks) codes[c0] = q0;
+        if (c1 < nchunks) codes[c1] = q1;
+        const int64_t cs = odd ? c1 : c0;  // chunk whose block this lane's scale belongs to
+        if (cs < nchunks) scales[cs >> 1] = (uint8_t)mine.code;
+    }
+    report_flags(status, flags);
+}
+
+// ---------------------------------------------------------------------------
+// Dequantize.  Lane = one chunk of 8 codes (one dword) -> 8 outputs.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float e4m3_any_value(uint32_t s) {
+    uint32_t mag = s & 0x7Fu;
+    if (mag == 0x7Fu) return __builtin_nanf("");
+    float v = e4m3_pos_value(mag);
+    return (s & 0x80u) ? -v : v;
+}
+
+// nearest-even fp32 -> bf16 (NaN kept quiet)
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    uint32_t b = f2u(f);
+    if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (b >> 16) | 0x40u;
+    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+template <int FMT, bool OUT_BF16>
+__global__ __launch_bounds__(WG) void dequant_kernel(const uint32_t *__restrict__ codes,
+                                                     const uint8_t *__restrict__ scales,
+                                                     const float *__restrict__ global_scale,
+                                                     int64_t nchunks, uint4 *__restrict__ y) {
+    const int64_t stride = (int64_t)gridDim.x * WG;
+    float s_g = 1.0f;
+    if (FMT == 1) s_g = *global_scale;
+    for (int64_t c = (int64_t)blockIdx.x * WG + threadIdx.x; c < nchunks; c += stride) {
+        uint32_t q = __builtin_nontemporal_load(codes + c);
+        float v[8];
+        if (FMT == 0) {
+            uint32_t sb = scales[c >> 2];
+            float so = e8m0_operand(sb);
+            if (OUT_BF16) {
+                uint32_t o[4];
+                o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, so, 0));
+                o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, so, 1));
+                o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, so, 2));
+                o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, so, 3));
+                if (sb == 0xFFu) o[0] = o[1] = o[2] = o[3] = 0x7FC07FC0u;
+                st_stream(y + c, make_uint4(o[0], o[1], o[2], o[3]));
+                continue;
+            }
+            f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, so, 0);
+            f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, so, 1);
+            f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, so, 2);
+            f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, so, 3);
+            v[0] = p0.x; v[1] = p0.y; v[2] = p1.x; v[3] = p1.y;
+            v[4] = p2.x; v[5] = p2.y; v[6] = p3.x; v[7] = p3.y;
+            if (sb == 0xFFu) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = __builtin_nanf("");
+            }
+        } else {
+            float alpha = s_g * e4m3_any_value(scales[c >> 1]);
+            const float one = e8m0_operand(E8M0_ONE);
+            f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, one, 0);
+            f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, one, 1);
+            f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, one, 2);
+            f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, one, 3);
+            v[0] = p0.x * alpha; v[1] = p0.y * alpha; v[2] = p1.x * alpha; v[3] = p1.y * alpha;
+            v[4] = p2.x * alpha; v[5] = p2.y * alpha; v[6] = p3.x * alpha; v[7] = p3.y * alpha;
+        }
+        if (OUT_BF16) {
+            uint4 o;
+            o.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
+            o.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+            o.z = bf16_rne(v[4]) | (bf16_rne(v[5]) << 16);
+            o.w = bf16_rne(v[6]) | (bf16_rne(v[7]) << 16);
+            st_stream(y + c, o);
+        } else {
+            st_stream(y + 2 * c, make_uint4(f2u(v[0]), f2u(v[1]), f2u(v[2]), f2u(v[3])));
+            st_stream(y + 2 * c + 1, make_uint4(f2u(v[4]), f2u(v[5]), f2u(v[6]), f2u(v[7])));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// MSE-optimal NVFP4 scale search.  A lane pair holds one block (8 elements
+// each).  The distinct encoded candidates of a block are the consecutive
+// E4M3 codes from E4M3(c_lo t) to E4M3(c_hi t), t = A_g / (6 s_g) (the host
+// checks the candidate grid is fine enough for that), visited in increasing
+// order, which is increasing candidate index; a strictly smaller loss
+// replaces the incumbent, so the smallest index wins ties.
+// Loss: each lane sums its 8 squared errors as ((t0+t1)+(t2+t3))+((t4+t5)+
+// (t6+t7)) and the pair adds the two halves: the balanced pairwise tree over
+// the 16 elements in index order.  |x| and |x_hat| give the same squared
+// error as the signed values.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float half_block_loss(const float (&a)[8], float alpha, float y,
+                                                 bool fast) {
+    float q[8];
+    if (fast) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = div_rn(a[i], alpha, y);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = a[i] / alpha;
+    }
+    const float one = e8m0_operand(E8M0_ONE);
+    uint32_t code = cvt_fp4x8_f32(q, one);
+    float t[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f32x2_t p;
+        switch (j) {  // the byte selector must be a constant
+            case 0: p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, one, 0); break;
+            case 1: p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, one, 1); break;
+            case 2: p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, one, 2); break;
+            default: p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, one, 3); break;
+        }
+        float e0 = a[2 * j] - p.x * alpha;
+        float e1 = a[2 * j + 1] - p.y * alpha;
+        t[2 * j] = e0 * e0;
+        t[2 * j + 1] = e1 * e1;
+    }
+    return ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(WG) void scale_search_kernel(
+    const uint4 *__restrict__ x, int64_t nchunks, const uint32_t *__restrict__ partials,
+    int npart, float c_lo, float c_hi, uint32_t *__restrict__ codes,
+    uint8_t *__restrict__ scales, float *__restrict__ global_scale, int32_t *status) {
+    TensorScale ts = tensor_scale<BF16>(partials, npart);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *global_scale = ts.s_g;
+    if (ts.flags) {
+        if (blockIdx.x == 0 && threadIdx.x == 0 && status) atomicOr(status, (int32_t)ts.flags);
+        return;
+    }
+    const float s_g = ts.s_g;
+    const double sg64 = (double)s_g;
+    const double inv6sg = 1.0 / (6.0 * sg64);
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int64_t wave = (int64_t)blockIdx.x * WAVES_PER_WG + (threadIdx.x / WAVE);
+    const int64_t nwaves = (int64_t)gridDim.x * WAVES_PER_WG;
+    const int64_t ntiles = (nchunks + WAVE - 1) / WAVE;
+    uint32_t flags = 0;
+    for (int64_t t = wave; t < ntiles; t += nwaves) {
+        const int64_t c = t * WAVE + lane;
+        Chunk<BF16> k = load_chunk<BF16>(x, c, c < nchunks);
+        uint32_t m = chunk_amax<BF16>(k);
+        m = max(m, dpp<QP_XOR1>(m));
+        const uint32_t ag_bits = amax_as_f32_bits<BF16>(m);
+        float a[8];
+        chunk_values<BF16>(k, a);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] = __builtin_fabsf(a[i]);
+        uint32_t best = 0x38u;
+        if (ag_bits != 0) {
+            const double ag = (double)u2f(ag_bits);
+            uint32_t lo = e4m3_code_exact((double)c_lo * ag, sg64, inv6sg);
+            uint32_t hi = e4m3_code_exact((double)c_hi * ag, sg64, inv6sg);
+            lo = lo < 1u ? 1u : lo;
+            float bestL = 0.0f;
+            bool have = false;
+            for (uint32_t code = lo; code <= hi; ++code) {
+                float alpha = s_g * e4m3_pos_value(code);
+                if (alpha == 0.0f) continue;
+                bool fast = alpha >= 0x1p-126f;
+                float y = 1.0f / (fast ? alpha : 1.0f);
+                float part = half_block_loss(a, alpha, y, fast);
+                float L = part + dppf<QP_XOR1>(part);
+                if (!have || L < bestL) {
+                    best = code;
+                    bestL = L;
+                    have = true;
+                }
+            }
+            if (!have) {
+                flags |= FLAG_SCALE_UNDERFLOW;
+                best = 0;
+            }
+        }
+        float alpha = s_g * e4m3_pos_value(best);
+        bool fast = alpha >= 0x1p-126f;
+        float y = 1.0f / (fast ? alpha : 1.0f);
+        chunk_values<BF16>(k, a);
+        uint32_t q = nv_quant8(a, alpha, y, fast);
+        if (c < nchunks) {
+            codes[c] = q;
+            if ((lane & 1) == 0) scales[c >> 1] = (uint8_t)best;
+        }
+    }
+    report_flags(status, flags);
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+static inline int grid_for(int64_t waves_needed, int max_wg) {
+    int64_t g = (waves_needed + WAVES_PER_WG - 1) / WAVES_PER_WG;
+    if (g > max_wg) g = max_wg;
+    return (int)(g < 1 ? 1 : g);
+}
+
+hipError_t launch_mx_quantize(const void *x, bool bf16, int64_t n, uint8_t *codes,
+                              uint8_t *scales, int32_t *status, hipStream_t s) {
+    const int64_t nchunks = n / 8;
+    const int g = grid_for((nchunks + WAVE * 4 - 1) / (WAVE * 4), kMaxGrid);
+    if (bf16)
+        hipLaunchKernelGGL(mx_quantize_kernel<true>, dim3(g), dim3(WG), 0, s, (const uint4 *)x,
+                           nchunks, (uint32_t *)codes, scales, status);
+    else
+        hipLaunchKernelGGL(mx_quantize_kernel<false>, dim3(g), dim3(WG), 0, s, (const uint4 *)x,
+                           nchunks, (uint32_t *)codes, scales, status);
+    return hipGetLastError();
+}
+
+static int amax_grid(int64_t nchunks) {
+    int64_t g = (nchunks + WG * 4 - 1) / (WG * 4);
+    if (g > kAmaxPartials) g = kAmaxPartials;
+    return (int)(g < 1 ? 1 : g);
+}
+
+static hipError_t launch_amax(const void *x, bool bf16, int64_t nchunks, uint32_t *partials,
+                              int g, hipStream_t s) {
+    if (bf16)
+        hipLaunchKernelGGL(tensor_amax_kernel<true>, dim3(g), dim3(WG), 0, s, (const uint4 *)x,
+                           nchunks, partials);
+    else
+        hipLaunchKernelGGL(tensor_amax_kernel<false>, dim3(g), dim3(WG), 0, s, (const uint4 *)x,
+                           nchunks, partials);
+    return hipGetLastError();
+}
+
+hipError_t launch_nv_quantize(const void *x, bool bf16, int64_t n, uint8_t *codes,
+                              uint8_t *scales, float *global_scale, void *workspace,
+                              int32_t *status, hipStream_t s) {
+    const int64_t nchunks = n / 8;
+    uint32_t *partials = (uint32_t *)workspace;
+    const int g1 = amax_grid(nchunks);
+    hipError_t e = launch_amax(x, bf16, nchunks, partials, g1, s);
+    if (e != hipSuccess) return e;
+    const int g = grid_for((nchunks + WAVE * 2 - 1) / (WAVE * 2), kMaxGrid);
+    if (bf16)
+        hipLaunchKernelGGL(nv_quantize_kernel<true>, dim3(g), dim3(WG), 0, s, (const uint4 *)x,
+                           nchunks, partials, g1, (uint32_t *)codes, scales, global_scale, status);
+    else
+        hipLaunchKernelGGL(nv_quantize_kernel<false>, dim3(g), dim3(WG), 0, s, (const uint4 *)x,
+                           nchunks, partials, g1, (uint32_t *)codes, scales, global_scale, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_scale_search(const void *x, bool bf16, int64_t n, float c_lo, float c_hi,
+                               uint8_t *codes, uint8_t *scales, float *global_scale,
+                               void *workspace, int32_t *status, hipStream_t s) {
+    const int64_t nchunks = n / 8;
+    uint32_t *partials = (uint32_t *)workspace;
+    const int g1 = amax_grid(nchunks);
+    hipError_t e = launch_amax(x, bf16, nchunks, partials, g1, s);
+    if (e != hipSuccess) return e;
+    const int g = grid_for((nchunks + WAVE - 1) / WAVE, kMaxGrid);
+    if (bf16)
+        hipLaunchKernelGGL(scale_search_kernel<true>, dim3(g), dim3(WG), 0, s, (const uint4 *)x,
+                           nchunks, partials, g1, c_lo, c_hi, (uint32_t *)codes, scales,
+                           global_scale, status);
+    else
+        hipLaunchKernelGGL(scale_search_kernel<false>, dim3(g), dim3(WG), 0, s, (const uint4 *)x,
+                           nchunks, partials, g1, c_lo, c_hi, (uint32_t *)codes, scales,
+                           global_scale, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales,
+                             const float *global_scale, int64_t n, void *y, bool out_bf16,
+                             hipStream_t s) {
+    const int64_t nchunks = n / 8;
+    const int g = grid_for((nchunks + WAVE - 1) / WAVE, kMaxGrid);
+#define FP4_DQ(F, B)                                                                          \
+    hipLaunchKernelGGL((dequant_kernel<F, B>), dim3(g), dim3(WG), 0, s, (const uint32_t *)codes, \
+                       scales, global_scale, nchunks, (uint4 *)y)
+    if (fmt == 0) {
+        if (out_bf16) FP4_DQ(0, true);
+        else FP4_DQ(0, false);
+    } else {
+        if (out_bf16) FP4_DQ(1, true);
+        else FP4_DQ(1, false);
+    }
+#undef FP4_DQ
+    return hipGetLastError();
+}
+
+}  // namespace fp4dev

@@ -1,0 +1,113 @@
+"""Host-side tests of the C ABI: the library loads, exports every entry point
+include/fp4.h declares, and rejects invalid arguments synchronously, before
+any HIP call (so no GPU is needed).  No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp4_block_amax_amd as fp4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4.h")
+
+OK, E_ARG, E_SHAPE, E_DTYPE, E_ALIGN, E_WORKSPACE = 0, 1, 2, 3, 4, 5
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fp4.LIB_PATH), reason="libfp4.so not built")
+
+# fake, never-dereferenced device addresses: validation must fail before use
+A16 = ctypes.c_void_p(0x10000)
+A1 = ctypes.c_void_p(0x10001)
+NULL = None
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(fp4_[a-z_0-9]+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(fp4.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = fp4.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    for code in range(7):
+        assert fp4.status_str(code)
+    assert fp4.status_str(0) == "ok"
+
+
+def test_workspace_bytes():
+    assert fp4.workspace_bytes(fp4.MXFP4, 8192, 8192) == 0
+    assert fp4.workspace_bytes(fp4.NVFP4, 8192, 8192) >= 1024 * 4
+
+
+def mx(x=A16, dt=fp4.BF16, rows=4, cols=64, block=32, codes=A16, scales=A16, status=NULL):
+    return fp4.lib().fp4_quantize_mxfp4(x, dt, rows, cols, block, codes, scales, status, NULL)
+
+
+def nv(x=A16, dt=fp4.BF16, rows=4, cols=64, block=16, codes=A16, scales=A16, sg=A16, ws=A16,
+       wsb=1 << 20, status=NULL):
+    return fp4.lib().fp4_quantize_nvfp4(x, dt, rows, cols, block, codes, scales, sg, ws, wsb,
+                                        status, NULL)
+
+
+def test_mx_validation():
+    assert mx(x=NULL) == E_ARG
+    assert mx(codes=NULL) == E_ARG
+    assert mx(block=16) == E_ARG
+    assert mx(dt=7) == E_DTYPE
+    assert mx(cols=48) == E_SHAPE        # incomplete 32-block
+    assert mx(rows=0) == E_SHAPE
+    assert mx(cols=0) == E_SHAPE
+    assert mx(x=A1) == E_ALIGN
+
+
+def test_nv_validation():
+    assert nv(sg=NULL) == E_ARG
+    assert nv(block=32) == E_ARG
+    assert nv(cols=17) == E_SHAPE         # the page's 17-element case
+    assert nv(ws=NULL) == E_WORKSPACE
+    assert nv(wsb=16) == E_WORKSPACE
+    assert nv(x=A1) == E_ALIGN
+
+
+def test_dequant_validation():
+    L = fp4.lib()
+    assert L.fp4_dequantize(5, A16, A16, A16, 4, 64, 32, A16, fp4.BF16, NULL) == E_DTYPE
+    assert L.fp4_dequantize(fp4.NVFP4, A16, A16, NULL, 4, 64, 16, A16, fp4.BF16, NULL) == E_ARG
+    assert L.fp4_dequantize(fp4.MXFP4, A16, A16, NULL, 4, 64, 16, A16, fp4.BF16, NULL) == E_ARG
+    assert L.fp4_dequantize(fp4.MXFP4, A16, A16, NULL, 4, 40, 32, A16, fp4.BF16, NULL) == E_SHAPE
+    assert L.fp4_dequantize(fp4.MXFP4, A16, A16, NULL, 4, 64, 32, A1, fp4.BF16, NULL) == E_ALIGN
+
+
+def test_search_validation():
+    L = fp4.lib()
+
+    def s(n=64, lo=0.5, hi=1.0, block=16, cols=64):
+        return L.fp4_scale_search(A16, fp4.BF16, 4, cols, block, n, lo, hi, A16, A16, A16, A16,
+                                  1 << 20, NULL, NULL)
+    assert s(n=1) == E_ARG
+    assert s(lo=0.0) == E_ARG
+    assert s(lo=1.0, hi=0.5) == E_ARG
+    assert s(n=4) == E_ARG                # grid coarser than the E4M3 grid
+    assert s(hi=5.0, n=4096) == E_ARG
+    assert s(block=32) == E_ARG
+    assert s(cols=24) == E_SHAPE
+
+
+def test_gemm_validation():
+    L = fp4.lib()
+
+    def g(M=128, N=256, K=256, a=A16, c=A16):
+        return L.fp4_gemm_mxfp4(a, A16, A16, A16, M, N, K, c, fp4.BF16, NULL)
+    assert g(a=NULL) == E_ARG
+    assert g(K=48) == E_SHAPE
+    assert g(M=0) == E_SHAPE
+    assert g(a=A1) == E_ALIGN

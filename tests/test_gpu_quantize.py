@@ -1,0 +1,204 @@
+"""GPU parity: MXFP4 and NVFP4 quantization, bit-exact against the oracle on
+codes, scale bytes and the tensor scale, on the five workloads' inputs and on
+adversarial tensors (ties, signed zero, subnormals, saturation, zero blocks,
+extreme tensor scales) and ragged sizes."""
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_block_amax_amd as fp4
+import oracle
+import workloads
+from tests._gpu import announce, assert_bytes_equal, dev, f32_bits, host_u8, oracle_view
+
+pytestmark = pytest.mark.gpu
+
+
+def check_mx(x: torch.Tensor, what: str):
+    announce(f"mxfp4 quantize {what} {tuple(x.shape)} {x.dtype}")
+    codes, scales = fp4.quantize_mxfp4(dev(x))
+    torch.cuda.synchronize()
+    p, s, flags = oracle.mx_quantize(oracle_view(x))
+    assert flags == 0
+    assert_bytes_equal(host_u8(scales), s, f"{what}: MX scales")
+    assert_bytes_equal(host_u8(codes), p, f"{what}: MX codes")
+
+
+def check_nv(x: torch.Tensor, what: str):
+    announce(f"nvfp4 quantize {what} {tuple(x.shape)} {x.dtype}")
+    codes, scales, s_g = fp4.quantize_nvfp4(dev(x))
+    torch.cuda.synchronize()
+    p, s, sg, flags = oracle.nv_quantize(oracle_view(x))
+    assert flags == 0
+    assert f32_bits(s_g.cpu().numpy())[0] == f32_bits([sg])[0], f"{what}: s_g"
+    assert_bytes_equal(host_u8(scales), s, f"{what}: NV scales")
+    assert_bytes_equal(host_u8(codes), p, f"{what}: NV codes")
+
+
+# ---- the workloads' inputs -------------------------------------------------
+
+def test_tiny_roundtrip_input_both_formats():
+    x = workloads.tiny_roundtrip()
+    check_mx(x, "tiny 4096 fp32")
+    check_nv(x, "tiny 4096 fp32")
+
+
+def test_nvfp4_weight_8192_full():
+    x = workloads.nvfp4_weight()
+    check_nv(x, "weight 8192x8192 bf16")
+    check_mx(x, "weight 8192x8192 bf16")
+
+
+def test_mxfp4_activation_16384x7168_full():
+    check_mx(workloads.mxfp4_activation(), "activation 16384x7168 bf16")
+
+
+# ---- exhaustive conversion sweep --------------------------------------------
+
+def _mx_sweep_tensor() -> torch.Tensor:
+    """bf16 values at every E8M0 exponent: for each block exponent e, blocks
+    hold an anchor just below 2^(e+3) (so the exponent is e) and 31 other
+    values, both signs: every bf16 pattern in the seven binades that can
+    round to a nonzero code (all patterns for e <= -120, where subnormal
+    quotients occur), and a sample of the smaller ones."""
+    allbits = np.arange(0, 0x7F80, dtype=np.uint32)  # finite non-negative bf16
+    blocks = []
+    for byte in range(0, 253):
+        e = byte - 127
+        if e == -127:
+            anchor_bits = (2 << 7) | 0x7F   # just below 2^-124: floor(log2) = -125
+        else:
+            anchor_bits = ((e + 2 + 127) << 7) | 0x7F
+        vals = allbits[allbits <= anchor_bits]
+        lo = ((e - 4 + 127) << 7) if e > -120 else 0
+        vals = np.concatenate([vals[vals >= lo], vals[vals < lo][::97]])
+        vals = vals | np.where(np.arange(vals.size) % 2 == 1, 0x8000, 0).astype(np.uint32)
+        vals = np.concatenate([vals, np.zeros((-vals.size) % 31, np.uint32)]).reshape(-1, 31)
+        anchor = np.full((vals.shape[0], 1), anchor_bits, np.uint32)
+        blocks.append(np.concatenate([anchor, vals], axis=1))
+    b = np.concatenate(blocks).astype(np.uint16)
+    b = np.concatenate([b, np.zeros(((-b.shape[0]) % 16, 32), np.uint16)])
+    return torch.from_numpy(b.reshape(-1, 512).view(np.int16)).view(torch.bfloat16)
+
+
+def test_mx_every_bf16_value_at_every_exponent():
+    check_mx(_mx_sweep_tensor(), "exhaustive bf16 x E8M0 sweep")
+
+
+def test_mx_fp32_every_midpoint_and_subnormal():
+    # fp32 values on and one ulp around every E2M1 decision point, at several
+    # block exponents, plus signed zeros and subnormals
+    pts = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.0, 0.5, 1.0, 4.0], np.float32)
+    rows = []
+    for e in (-127, -126, -100, -3, 0, 5, 60, 125):
+        s = np.float32(2.0 ** e)
+        anchor = np.float32(np.nextafter(np.float32(8.0), np.float32(0)) * s) if e > -127 else np.float32(2.0 ** -125)
+        vals = []
+        for p in pts:
+            v = np.float32(p * s)
+            vals += [np.nextafter(v, np.float32(0)), v, np.nextafter(v, np.float32(np.inf))]
+        vals = np.array(vals, np.float32)
+        vals = np.concatenate([vals, -vals, [0.0, -0.0, 1e-45, -1e-45, 1e-40]]).astype(np.float32)
+        vals = np.concatenate([vals, np.zeros((-vals.size) % 31, np.float32)]).reshape(-1, 31)
+        rows.append(np.concatenate([np.full((vals.shape[0], 1), anchor, np.float32), vals], 1))
+    x = torch.from_numpy(np.concatenate(rows).reshape(-1))
+    x = x[: (x.numel() // 32) * 32].reshape(-1, 32)
+    check_mx(x, "fp32 midpoints")
+
+
+# ---- adversarial NVFP4 ------------------------------------------------------
+
+def test_nv_ties_signed_zero_and_zero_blocks():
+    # a 2688 block fixes s_g = 1; a block with amax 6 has s_b = 1 (0x38), so
+    # alpha = 1 and the elements below sit exactly on E2M1 midpoints
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, -0.25, -0.75, -5.0, -0.0, 0.0, 1e-30,
+            -1e-30, 2.0]
+    x = np.concatenate([np.full(16, 2688.0), mids, np.zeros(16), [-0.0] * 16,
+                        [0.3, 0.6, 0.9, 1.2, 1.8, 2.4, 3.6, 0.0] * 2, [0.4] * 15 + [3.6]])
+    check_nv(torch.tensor(x, dtype=torch.float32).reshape(1, -1), "ties/zeros fp32")
+    check_nv(torch.tensor(x, dtype=torch.float32).to(torch.bfloat16).reshape(1, -1), "ties/zeros bf16")
+
+
+def test_nv_block_scale_ties():
+    # block amaxes placed exactly on E4M3 midpoints times 6 s_g (s_g = 1)
+    rng = np.random.default_rng(0)
+    blocks = [np.full(16, 2688.0, np.float32)]
+    e4 = [oracle.e4m3_value(c) for c in range(127)]
+    for c in range(1, 126):   # the 0|1 tie rounds to code 0: an underflow, tested below
+        m = (e4[c] + e4[c + 1]) / 2 * 6.0
+        b = rng.uniform(-m, m, 16).astype(np.float32)
+        b[3] = np.float32(m)
+        blocks.append(b)
+    x = torch.from_numpy(np.concatenate(blocks)).reshape(1, -1)
+    check_nv(x, "E4M3 midpoint amaxes")
+    # amax 6 * 2^-10 sits halfway between codes 0 and 1: even code 0, so the
+    # nonzero block's scale underflows, on both sides
+    tie0 = np.concatenate([np.full(16, 2688.0, np.float32), np.full(16, 6 * 2.0 ** -10, np.float32)])
+    assert oracle.nv_quantize(tie0)[3] & oracle.FLAG_SCALE_UNDERFLOW
+    announce("nvfp4 quantize E4M3 0|1 tie underflow")
+    with pytest.raises(ValueError):
+        fp4.quantize_nvfp4(dev(torch.from_numpy(tie0).reshape(1, -1)))
+
+
+@pytest.mark.parametrize("scale_exp", [-140, -130, -126, -120, -100, -64, -20, 0, 20, 64, 100, 110])
+def test_nv_extreme_tensor_scales(scale_exp):
+    # tensors at every magnitude, including subnormal s_g and subnormal alpha
+    g = torch.Generator().manual_seed(scale_exp + 1000)
+    x = torch.randn(64, 256, generator=g) * torch.rand(64, 256, generator=g) ** 4
+    x = (x * 2.0 ** scale_exp).to(torch.float32)
+    p, s, sg, flags = oracle.nv_quantize(x.numpy().reshape(-1))
+    if flags:
+        pytest.skip("oracle reports underflow for this magnitude (covered by the status test)")
+    check_nv(x, f"magnitude 2^{scale_exp}")
+
+
+def test_nv_bf16_subnormals_and_ragged_sizes():
+    g = torch.Generator().manual_seed(5)
+    for rows, cols in [(1, 16), (3, 48), (5, 1040), (7, 4112), (129, 80)]:
+        x = torch.randn(rows, cols, generator=g) * 0.02
+        x[0, : min(cols, 8)] = torch.tensor([1e-39, -1e-39, 3e-40, 0.0, -0.0, 1e-38, 2e-38, -5e-39][: min(cols, 8)])
+        check_nv(x.to(torch.bfloat16), f"ragged {rows}x{cols}")
+        if cols % 32 == 0:
+            check_mx(x.to(torch.bfloat16), f"ragged {rows}x{cols}")
+
+
+def test_mx_ragged_fp32_and_bf16():
+    g = torch.Generator().manual_seed(6)
+    for rows, cols in [(1, 32), (3, 96), (11, 4128), (257, 160)]:
+        x = torch.randn(rows, cols, generator=g) * torch.rand(rows, cols, generator=g) * 100
+        check_mx(x, f"ragged fp32 {rows}x{cols}")
+        check_mx(x.to(torch.bfloat16), f"ragged bf16 {rows}x{cols}")
+
+
+# ---- status flags -------------------------------------------------------------
+
+def test_status_flags_match_the_contract():
+    announce("status flags")
+    x = torch.zeros(2, 64, dtype=torch.float32)
+    x[1, 5] = float("nan")
+    with pytest.raises(ValueError):
+        fp4.quantize_mxfp4(dev(x))
+    with pytest.raises(ValueError):
+        fp4.quantize_nvfp4(dev(x))
+    tiny = torch.full((1, 16), 1e-42, dtype=torch.float32)       # s_g underflows
+    with pytest.raises(ValueError):
+        fp4.quantize_nvfp4(dev(tiny))
+    blk = torch.tensor([2688.0] * 16 + [1e-10] * 16).reshape(1, 32)  # block scale underflows
+    with pytest.raises(ValueError):
+        fp4.quantize_nvfp4(dev(blk))
+    z = torch.zeros(4, 64, dtype=torch.bfloat16)                  # all-zero tensor is fine
+    codes, scales, sg = fp4.quantize_nvfp4(dev(z))
+    assert float(sg.item()) == 1.0 and bool((scales == 0x38).all()) and bool((codes == 0).all())
+
+
+def test_deterministic_repeat():
+    x = dev(workloads.nvfp4_weight(1024, 4096, seed=3))
+    announce("determinism nvfp4/mxfp4 1024x4096")
+    a = fp4.quantize_nvfp4(x)
+    b = fp4.quantize_nvfp4(x)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+    c = fp4.quantize_mxfp4(x)
+    d = fp4.quantize_mxfp4(x)
+    for u, v in zip(c, d):
+        assert torch.equal(u, v)

@@ -89,11 +89,16 @@ def test_distinct_candidate_codes_form_a_contiguous_range():
     rng = np.random.default_rng(31)
     s_g = np.float32(1.0)
     amaxes = np.concatenate([rng.uniform(1e-4, 2688, 300), 2.0 ** rng.uniform(-12, 12, 300)])
-    for amax in amaxes.astype(np.float32):
-        codes = {oracle.e4m3_nearest(float(oracle.candidate_c(k)) * float(amax), 6.0) for k in range(64)}
-        lo = oracle.e4m3_nearest(0.5 * float(amax), 6.0)
-        hi = oracle.e4m3_nearest(float(amax), 6.0)
-        assert codes == set(range(lo, hi + 1)), amax
+    # the grids the library accepts: step (c_hi - c_lo)/(n - 1) <= c_lo/24
+    grids = [(64, 0.5, 1.0), (64, 0.5, 1.5), (33, 0.75, 1.25), (13, 0.5, 0.75)]
+    for n, c_lo, c_hi in grids:
+        assert (c_hi - c_lo) / (n - 1) <= c_lo / 24
+        for amax in amaxes.astype(np.float32):
+            cs = [float(oracle.candidate_c(k, n, c_lo, c_hi)) for k in range(n)]
+            codes = {oracle.e4m3_nearest(c * float(amax), 6.0) for c in cs}
+            lo = oracle.e4m3_nearest(cs[0] * float(amax), 6.0)
+            hi = oracle.e4m3_nearest(cs[-1] * float(amax), 6.0)
+            assert codes == set(range(lo, hi + 1)), (n, c_lo, c_hi, amax)
 
 
 def test_zero_block_and_underflow():
