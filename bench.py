@@ -1,0 +1,342 @@
+"""Benchmark of the block-scaled FP4 hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--no-extra] [--calibrate-copy]
+
+A step is one pass of the whole quantize/dequantize path over the
+8192 x 8192 bf16 tensor ~ N(0, 0.02^2) (seed 0):
+    NVFP4 quantize (tensor-amax kernel + quantize kernel),
+    NVFP4 dequantize -> bf16,
+    MXFP4 quantize, MXFP4 dequantize -> bf16.
+The step is captured once as a HIP graph and replayed K times between two
+HIP events (the timed region).  NVFP4 works on one copy of the input and
+MXFP4 on another, so between two reads of the same input ~500 MB of other
+traffic passes through the 256 MB MALL; nothing is flushed.  Inputs are
+resident in HBM before timing.
+
+Per-op rows (`breakdown`) time each entry point over a graph of 24
+back-to-back launches cycling through three buffer sets (each set is evicted
+from the MALL before it is reused), so they match the profiler's kernel
+durations.
+
+value = algorithmic bytes of the four ops per step / step time (GB/s).
+Algorithmic bytes count every input byte once and every output byte once:
+  quantize: 2 B per bf16 element in, 1/2 B codes + 1 B per block scale out
+            (+ 4 B tensor scale for NVFP4); dequantize: the mirror.
+The NVFP4 tensor-amax pass re-reads the input; that is implementation cost,
+not algorithmic bytes.
+
+One JSON line on stdout.  `roofline` is for the op with the largest launch
+time in the breakdown, timed with HIP events on the stream it runs on (for
+NVFP4 quantize that launch is the entry point's two kernels).
+`cpu_baseline` is the CPU oracle (single thread) on one full step of the same
+input.  `extra` reports the other workloads measured in the same run: MXFP4
+quantize of the 16384 x 7168 activation, the 4096 x 14336 NVFP4 scale
+search, and the 128 x 8192 x 8192 MXFP4 GEMM.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import mxfp4_block_amax_amd as fp4  # noqa: E402
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP4_DENSE_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 MFMA, published
+METRIC = "quantize GB/s (bytes in+out) and % of HBM peak; Gelem/s, NVFP4 & MXFP4"
+
+
+# ---------------------------------------------------------------------------
+# algorithmic byte accounting ("NVFP4 / MXFP4 format" page, section 8: T/2
+# payload bytes, one byte per block, 4 bytes of tensor scale for NVFP4)
+# ---------------------------------------------------------------------------
+def fp4_bytes(elements: int, block: int, global_bytes: int) -> int:
+    return elements // 2 + elements // block + global_bytes
+
+
+def quantize_bytes(elements: int, in_bytes_per_elem: int, fmt: str) -> int:
+    block, gb = (32, 0) if fmt == "mx" else (16, 4)
+    return elements * in_bytes_per_elem + fp4_bytes(elements, block, gb)
+
+
+def gemm_bytes(M: int, N: int, K: int, out_bytes: int = 2) -> int:
+    return fp4_bytes(M * K, 32, 0) + fp4_bytes(N * K, 32, 0) + M * N * out_bytes
+
+
+def gemm_flops(M: int, N: int, K: int) -> int:
+    return 2 * M * N * K
+
+
+# ---------------------------------------------------------------------------
+# timing helpers
+# ---------------------------------------------------------------------------
+def capture(fn) -> "torch.cuda.CUDAGraph":
+    """A HIP graph of fn()'s launches (the library's kernels record no memset
+    nodes; every buffer is preallocated)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, reps: int) -> float:
+    """Mean milliseconds per replay, HIP events on the replay stream."""
+    g.replay()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def time_rotating(fns, launches: int = 24, reps: int = 5) -> float:
+    """Mean milliseconds per launch of an op over `launches` back-to-back
+    launches that cycle through the given buffer sets (each fn is the op on
+    one set; enough sets that a set is evicted from the 256 MB MALL before it
+    is used again), captured in one graph."""
+    def run():
+        for i in range(launches):
+            fns[i % len(fns)]()
+    return time_graph(capture(run), reps) / launches
+
+
+# ---------------------------------------------------------------------------
+# the step
+# ---------------------------------------------------------------------------
+NSETS = 3  # buffer sets rotated by the per-op timing
+
+
+class RoundTrip:
+    """Buffers for NVFP4 + MXFP4 quantize/dequantize of one [R, C] tensor,
+    NSETS copies of everything."""
+
+    def __init__(self, x_cpu: torch.Tensor):
+        R, C = x_cpu.shape
+        dev = torch.device("cuda")
+        self.shape = (R, C)
+        self.sets = []
+        for _ in range(NSETS):
+            b = {
+                "x": x_cpu.to(dev),
+                "nv": (torch.empty(R, C // 2, dtype=torch.uint8, device=dev),
+                       torch.empty(R, C // 16, dtype=torch.uint8, device=dev),
+                       torch.empty(1, dtype=torch.float32, device=dev)),
+                "mx": (torch.empty(R, C // 2, dtype=torch.uint8, device=dev),
+                       torch.empty(R, C // 32, dtype=torch.uint8, device=dev)),
+                "y_nv": torch.empty(R, C, dtype=torch.bfloat16, device=dev),
+                "y_mx": torch.empty(R, C, dtype=torch.bfloat16, device=dev),
+                "ws": torch.empty(fp4.workspace_bytes(fp4.NVFP4, R, C), dtype=torch.uint8, device=dev),
+                "status": torch.zeros(1, dtype=torch.int32, device=dev),
+            }
+            self.sets.append(b)
+        n = R * C
+        self.elements = n
+        self.bytes = {
+            "nvfp4_quantize": quantize_bytes(n, 2, "nv"),
+            "nvfp4_dequantize": quantize_bytes(n, 2, "nv"),
+            "mxfp4_quantize": quantize_bytes(n, 2, "mx"),
+            "mxfp4_dequantize": quantize_bytes(n, 2, "mx"),
+        }
+
+    def op(self, tag, i):
+        b = self.sets[i]
+        if tag == "nvfp4_quantize":
+            return lambda: fp4.quantize_nvfp4(b["x"], check=False, out=b["nv"], status=b["status"],
+                                              workspace=b["ws"])
+        if tag == "nvfp4_dequantize":
+            return lambda: fp4.dequantize(fp4.NVFP4, b["nv"][0], b["nv"][1], b["nv"][2], out=b["y_nv"])
+        if tag == "mxfp4_quantize":
+            return lambda: fp4.quantize_mxfp4(b["x"], check=False, out=b["mx"], status=b["status"])
+        if tag == "mxfp4_dequantize":
+            return lambda: fp4.dequantize(fp4.MXFP4, b["mx"][0], b["mx"][1], None, out=b["y_mx"])
+        raise KeyError(tag)
+
+    def step(self):
+        # NVFP4 on set 0's input, MXFP4 on set 1's: between two reads of the
+        # same input ~500 MB of other traffic passes through the MALL
+        self.op("nvfp4_quantize", 0)()
+        self.op("nvfp4_dequantize", 0)()
+        self.op("mxfp4_quantize", 1)()
+        self.op("mxfp4_dequantize", 1)()
+
+
+def cpu_baseline(x_cpu: torch.Tensor, step_bytes: int):
+    """The oracle (plain C, one thread) on one full step of the same input."""
+    import oracle
+    xo = workloads.bf16_bits(x_cpu).reshape(-1)
+    t0 = time.perf_counter()
+    p, s, sg, f = oracle.nv_quantize(xo)
+    oracle.dequantize(oracle.NV, p, s, sg, out_bf16=True)
+    p, s, f = oracle.mx_quantize(xo)
+    oracle.dequantize(oracle.MX, p, s, out_bf16=True)
+    dt = time.perf_counter() - t0
+    return {"value": round(step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"one full step (NVFP4 + MXFP4 quantize and dequantize) of the "
+                      f"{x_cpu.shape[0]}x{x_cpu.shape[1]} bf16 input; {dt:.2f} s wall"}
+
+
+def _rate(b: int, ms: float, elements: int = None):
+    d = {"us": round(ms * 1e3, 2), "GB/s": round(b / ms / 1e6, 1),
+         "pct_hbm_peak": round(100 * b / ms / 1e6 / HBM_PEAK_GBS, 1)}
+    if elements:
+        d["Gelem/s"] = round(elements / ms / 1e6, 1)
+    return d
+
+
+def extra_workloads():
+    out = {}
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    # MXFP4 activation quantize, 16384 x 7168 bf16: two 235 MB input copies
+    xa_cpu = workloads.mxfp4_activation()
+    xs = [xa_cpu.cuda() for _ in range(2)]
+    outs = [fp4.quantize_mxfp4(x) for x in xs]
+    ms = time_rotating([lambda x=x, o=o: fp4.quantize_mxfp4(x, check=False, out=o, status=st)
+                        for x, o in zip(xs, outs)])
+    out["mxfp4_activation_quantize_16384x7168_bf16"] = _rate(quantize_bytes(xa_cpu.numel(), 2, "mx"),
+                                                             ms, xa_cpu.numel())
+    del xs, outs
+    # NVFP4 MSE scale search, 4096 x 14336 bf16 ~ Laplace(0, 0.01), 64 candidates
+    xs_cpu = workloads.scale_search_input()
+    xs = [xs_cpu.cuda() for _ in range(3)]
+    res = [fp4.scale_search(x) for x in xs]
+    ws = torch.empty(fp4.workspace_bytes(fp4.NVFP4, *xs_cpu.shape), dtype=torch.uint8, device="cuda")
+    ms = time_rotating([lambda x=x, r=r: fp4.scale_search(x, check=False, out=r, status=st, workspace=ws)
+                        for x, r in zip(xs, res)], launches=6)
+    d = _rate(quantize_bytes(xs_cpu.numel(), 2, "nv"), ms, xs_cpu.numel())
+    d["candidate_element_evals_per_s"] = f"{xs_cpu.numel() * 64 / ms / 1e-3:.3e}"
+    out["nvfp4_scale_search_4096x14336_bf16"] = d
+    del xs, res
+    # MXFP4 GEMM 128 x 8192 x 8192: operands quantized on the GPU; eight
+    # copies of B (36 MB each) rotate so B comes from HBM
+    M, N, K = 128, 8192, 8192
+    a, bt = workloads.gemm_operands(M, N, K)
+    ac, asc = fp4.quantize_mxfp4(a.cuda())
+    bq = [fp4.quantize_mxfp4(bt.cuda()) for _ in range(8)]
+    c = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    ms = time_rotating([lambda b=b: fp4.gemm_mxfp4(ac, asc, b[0], b[1], out=c) for b in bq])
+    d = _rate(gemm_bytes(M, N, K), ms)
+    tf = gemm_flops(M, N, K) / ms / 1e9
+    d.update({"TFLOP/s": round(tf, 1), "pct_fp4_mfma_peak": round(100 * tf / FP4_DENSE_PEAK_TFLOPS, 2)})
+    out["mxfp4_gemm_128x8192x8192_bf16out"] = d
+    return out
+
+
+def calibrate_copy(iters: int = 5):
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(iters):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"bytes_read": n, "bytes_written": n, "iters": iters}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the quantize path runs on one device and this "
+              "build launches no multi-GPU work; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+
+    x_cpu = workloads.nvfp4_weight()
+    rt = RoundTrip(x_cpu)
+    step_bytes = sum(rt.bytes.values())
+
+    # correctness gate on the benchmark's own buffers before timing
+    for i in range(NSETS):
+        b = rt.sets[i]
+        fp4.quantize_nvfp4(b["x"], out=b["nv"], workspace=b["ws"])
+        fp4.quantize_mxfp4(b["x"], out=b["mx"])
+
+    # the timed region: K replays of the graph-captured step
+    step_graph = capture(rt.step)
+    for _ in range(args.warmup):
+        step_graph.replay()
+    torch.cuda.synchronize()
+    s_ev = torch.cuda.Event(enable_timing=True)
+    e_ev = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    s_ev.record()
+    for _ in range(args.steps):
+        step_graph.replay()
+    e_ev.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    ms_per_step = max(wall_s * 1e3, s_ev.elapsed_time(e_ev)) / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # per-op launch durations: back-to-back launches rotating NSETS buffer sets
+    breakdown = {}
+    for tag in rt.bytes:
+        ms = time_rotating([rt.op(tag, i) for i in range(NSETS)])
+        breakdown[tag] = _rate(rt.bytes[tag], ms, rt.elements)
+        breakdown[tag]["bytes"] = rt.bytes[tag]
+
+    dom = max(breakdown, key=lambda t: breakdown[t]["us"])
+    kernel_names = {"nvfp4_quantize": "fp4_quantize_nvfp4 = tensor_amax_kernel + nv_quantize_kernel",
+                    "nvfp4_dequantize": "dequant_kernel<1, bf16 out>",
+                    "mxfp4_quantize": "mx_quantize_kernel<bf16 in>",
+                    "mxfp4_dequantize": "dequant_kernel<0, bf16 out>"}
+    roofline = {"bound": "hbm", "kernel": kernel_names[dom],
+                "achieved": breakdown[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(breakdown[dom]["GB/s"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes_per_launch": rt.bytes[dom],
+                "avg_launch_us": breakdown[dom]["us"]}
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "nvfp4_mxfp4_roundtrip_8192x8192_bf16",
+                   "shape": [8192, 8192], "input": "bf16 N(0, 0.02^2), seed 0",
+                   "ops": list(rt.bytes), "step_bytes": step_bytes,
+                   "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
+                   "Gelem/s_per_op": round(4 * rt.elements / (ms_per_step * 1e-3) / 1e9, 1),
+                   "timing": "HIP graph of one step replayed K times; per-op rows from graphs "
+                             "of back-to-back launches over 3 rotating buffer sets"},
+        "breakdown": breakdown,
+        "roofline": roofline,
+    }
+    if not args.no_extra:
+        line["extra"] = extra_workloads()
+    if args.calibrate_copy:
+        line["copy_calibration"] = calibrate_copy()
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(x_cpu, step_bytes)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -106,10 +106,157 @@ __global__ __launch_bounds__(GEMM_WG) void mxfp4_gemm_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Fast path (K a multiple of 2048; code rows 16-byte and scale rows 8-byte
+// aligned).  A workgroup still owns a 128 x 32 tile of C, but its four waves
+// split K into quarters instead of splitting M: each wave runs all four
+// 32-row slices of A against the one 32-column slice of B over its quarter,
+// so every A and B byte the workgroup needs is loaded exactly once, by one
+// lane.  Loads are unpredicated (rows past M / columns past N are clamped to
+// the last valid one and their results discarded) and software-pipelined
+// two groups of four K steps deep in registers.  The four partial tiles are
+// summed through LDS in a fixed order (wave 0 + 1 + 2 + 3), so results are
+// deterministic.
+// ---------------------------------------------------------------------------
+constexpr int GF_G = 4;  // K steps per load group
+
+struct GemmGroup {
+    uint4 a[GF_G][4];  // [step][32-row slice]
+    uint4 b[GF_G];
+    uint2 sa[4];       // 8 scale bytes = 4 steps x 2 K-halves, per row slice
+    uint2 sb;
+};
+
+__device__ __forceinline__ void gemm_load_group(GemmGroup &g, const uint4 *const (&pa)[4],
+                                                const uint4 *pb, const uint2 *const (&psa)[4],
+                                                const uint2 *psb, int s, int rot, int steps_w) {
+    // visit this wave's K range starting at a workgroup-dependent offset
+    s += rot;
+    if (s >= steps_w) s -= steps_w;
+    // step s (a multiple of GF_G): lane reads block 2s' + kh of its rows
+#pragma unroll
+    for (int p = 0; p < GF_G; ++p) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) g.a[p][mi] = pa[mi][2 * (s + p)];
+        g.b[p] = ld_stream(pb + 2 * (s + p));
+    }
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) g.sa[mi] = psa[mi][s / GF_G];
+    g.sb = psb[s / GF_G];
+}
+
+__device__ __forceinline__ uint32_t scale_byte(uint2 w, int p, int kh) {
+    // byte 2p + kh of the 8-byte group; the MFMA reads the low byte
+    const int i = 2 * p + kh;
+    return (i < 4 ? w.x : w.y) >> (8 * (i & 3));
+}
+
+__device__ __forceinline__ void gemm_mma_group(f32x16_t (&acc)[4], const GemmGroup &g, int kh) {
+#pragma unroll
+    for (int p = 0; p < GF_G; ++p) {
+        const int sb = (int)scale_byte(g.sb, p, kh);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+            acc[mi] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                as_operand(g.a[p][mi]), as_operand(g.b[p]), acc[mi], 4, 4, 0,
+                (int)scale_byte(g.sa[mi], p, kh), 0, sb);
+    }
+}
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(GEMM_WG) void mxfp4_gemm_fast_kernel(
+    const uint4 *__restrict__ A, const uint8_t *__restrict__ As, const uint4 *__restrict__ Bt,
+    const uint8_t *__restrict__ Bs, int M, int N, int K, void *__restrict__ C) {
+    __shared__ float part[4][4][16][64];  // [wave][row slice][acc element][lane]
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int r32 = lane & 31;
+    const int kh = lane >> 5;
+    const int nblk = K / 32;
+    const int steps_w = K / 64 / 4;  // K steps per wave (a multiple of 2 * GF_G)
+    const int s0 = w * steps_w;
+    const int bn = min((int)blockIdx.x * GEMM_TN + r32, N - 1);
+
+    const uint4 *pa[4];
+    const uint2 *psa[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        const int am = min((int)blockIdx.y * GEMM_TM + 32 * mi + r32, M - 1);
+        pa[mi] = A + (int64_t)am * nblk + 2 * s0 + kh;
+        psa[mi] = (const uint2 *)(As + (int64_t)am * nblk + 2 * s0);
+    }
+    const uint4 *pb = Bt + (int64_t)bn * nblk + 2 * s0 + kh;
+    const uint2 *psb = (const uint2 *)(Bs + (int64_t)bn * nblk + 2 * s0);
+
+    // Workgroups start their K walk at different groups so that they do not
+    // all read the same lines of A (L2-resident, shared by every workgroup)
+    // at the same time.  The order is a fixed function of the tile.
+    const int ngroups2 = steps_w / (2 * GF_G);
+    const int rot = (int)((blockIdx.x + 3u * blockIdx.y) % (unsigned)ngroups2) * (2 * GF_G);
+
+    f32x16_t acc[4] = {};
+    GemmGroup g0, g1;
+    gemm_load_group(g0, pa, pb, psa, psb, 0, rot, steps_w);
+    for (int s = 0; s < steps_w; s += 2 * GF_G) {
+        gemm_load_group(g1, pa, pb, psa, psb, s + GF_G, rot, steps_w);
+        // keep each group's loads ahead of the MFMAs that do not need them:
+        // without the fence the scheduler sinks them next to their uses
+        __builtin_amdgcn_sched_barrier(0);
+        gemm_mma_group(acc, g0, kh);
+        // unconditional prefetch (the last round re-reads group 0, in bounds),
+        // so no branch splits the load counting of the pipeline
+        const int sn = (s + 2 * GF_G < steps_w) ? s + 2 * GF_G : 0;
+        gemm_load_group(g0, pa, pb, psa, psb, sn, rot, steps_w);
+        __builtin_amdgcn_sched_barrier(0);
+        gemm_mma_group(acc, g1, kh);
+    }
+
+    // fixed-order reduction of the four K-quarter partials
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) part[w][mi][j][lane] = acc[mi][j];
+    __syncthreads();
+    const int mi = w;  // wave w finishes row slice w
+    const int col = blockIdx.x * GEMM_TN + r32;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        float v = part[0][mi][j][lane];
+        v = v + part[1][mi][j][lane];
+        v = v + part[2][mi][j][lane];
+        v = v + part[3][mi][j][lane];
+        const int row = blockIdx.y * GEMM_TM + 32 * mi + 8 * (j / 4) + 4 * kh + (j % 4);
+        if (row < M && col < N) {
+            if (OUT_BF16)
+                ((uint16_t *)C)[(int64_t)row * N + col] = (uint16_t)bf16_rne_bits(v);
+            else
+                ((float *)C)[(int64_t)row * N + col] = v;
+        }
+    }
+}
+
+static bool gemm_fast_ok(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *bt_codes,
+                         const uint8_t *bt_scales, int64_t K) {
+    auto al = [](const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; };
+    return K % 2048 == 0 && al(a_codes, 16) && al(bt_codes, 16) && al(a_scales, 8) &&
+           al(bt_scales, 8);
+}
+
 hipError_t launch_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales,
                              const uint8_t *bt_codes, const uint8_t *bt_scales, int64_t M,
                              int64_t N, int64_t K, void *c, bool out_bf16, hipStream_t s) {
     dim3 grid((unsigned)((N + GEMM_TN - 1) / GEMM_TN), (unsigned)((M + GEMM_TM - 1) / GEMM_TM));
+    if (gemm_fast_ok(a_codes, a_scales, bt_codes, bt_scales, K)) {
+        if (out_bf16)
+            hipLaunchKernelGGL(mxfp4_gemm_fast_kernel<true>, grid, dim3(GEMM_WG), 0, s,
+                               (const uint4 *)a_codes, a_scales, (const uint4 *)bt_codes,
+                               bt_scales, (int)M, (int)N, (int)K, c);
+        else
+            hipLaunchKernelGGL(mxfp4_gemm_fast_kernel<false>, grid, dim3(GEMM_WG), 0, s,
+                               (const uint4 *)a_codes, a_scales, (const uint4 *)bt_codes,
+                               bt_scales, (int)M, (int)N, (int)K, c);
+        return hipGetLastError();
+    }
     if (out_bf16)
         hipLaunchKernelGGL(mxfp4_gemm_kernel<true>, grid, dim3(GEMM_WG), 0, s,
                            (const uint4 *)a_codes, a_scales, (const uint4 *)bt_codes, bt_scales,

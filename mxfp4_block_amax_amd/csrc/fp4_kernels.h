@@ -11,7 +11,7 @@ namespace fp4dev {
 // loop over tiles beyond it.
 constexpr int kMaxGrid = 4096;
 // Workgroups (hence partial maxima) of the tensor-amax pass.
-constexpr int kAmaxPartials = 1024;
+constexpr int kAmaxPartials = 2048;
 constexpr size_t kNvWorkspaceBytes = kAmaxPartials * sizeof(uint32_t);
 
 hipError_t launch_mx_quantize(const void *x, bool bf16, int64_t n, uint8_t *codes,

@@ -36,16 +36,18 @@ struct Chunk {
     uint4 lo, hi;  // hi used only for fp32 input
 };
 
-template <bool BF16>
+// STREAM: data read once (non-temporal); otherwise ordinary loads that may
+// allocate in the caches, for data a second pass reads again.
+template <bool BF16, bool STREAM = true>
 __device__ __forceinline__ Chunk<BF16> load_chunk(const uint4 *__restrict__ x, int64_t c, bool ok) {
     Chunk<BF16> k;
     const uint4 z = make_uint4(0, 0, 0, 0);
     if (BF16) {
-        k.lo = ok ? ld_stream(x + c) : z;
+        k.lo = ok ? (STREAM ? ld_stream(x + c) : x[c]) : z;
         k.hi = z;
     } else {
-        k.lo = ok ? ld_stream(x + 2 * c) : z;
-        k.hi = ok ? ld_stream(x + 2 * c + 1) : z;
+        k.lo = ok ? (STREAM ? ld_stream(x + 2 * c) : x[2 * c]) : z;
+        k.hi = ok ? (STREAM ? ld_stream(x + 2 * c + 1) : x[2 * c + 1]) : z;
     }
     return k;
 }
@@ -285,60 +287,83 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
     return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
 }
 
+// Decode one chunk (8 codes in a dword) to 8 outputs, written with streaming
+// (non-temporal) stores: measured faster here than ordinary stores for this
+// write-heavy kernel.
+template <int FMT, bool OUT_BF16>
+__device__ __forceinline__ void dequant_chunk(uint32_t q, uint32_t sb, float s_g, uint4 *y, int64_t c) {
+    float v[8];
+    if (FMT == 0) {
+        const float so = e8m0_operand(sb);
+        if (OUT_BF16) {
+            uint32_t o[4];
+            o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, so, 0));
+            o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, so, 1));
+            o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, so, 2));
+            o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, so, 3));
+            if (sb == 0xFFu) o[0] = o[1] = o[2] = o[3] = 0x7FC07FC0u;
+            st_stream(y + c, make_uint4(o[0], o[1], o[2], o[3]));
+            return;
+        }
+        f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, so, 0);
+        f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, so, 1);
+        f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, so, 2);
+        f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, so, 3);
+        v[0] = p0.x; v[1] = p0.y; v[2] = p1.x; v[3] = p1.y;
+        v[4] = p2.x; v[5] = p2.y; v[6] = p3.x; v[7] = p3.y;
+        if (sb == 0xFFu) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = __builtin_nanf("");
+        }
+    } else {
+        const float alpha = s_g * e4m3_any_value(sb);
+        const float one = e8m0_operand(E8M0_ONE);
+        f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, one, 0);
+        f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, one, 1);
+        f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, one, 2);
+        f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, one, 3);
+        v[0] = p0.x * alpha; v[1] = p0.y * alpha; v[2] = p1.x * alpha; v[3] = p1.y * alpha;
+        v[4] = p2.x * alpha; v[5] = p2.y * alpha; v[6] = p3.x * alpha; v[7] = p3.y * alpha;
+    }
+    if (OUT_BF16) {
+        uint4 o;
+        o.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
+        o.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+        o.z = bf16_rne(v[4]) | (bf16_rne(v[5]) << 16);
+        o.w = bf16_rne(v[6]) | (bf16_rne(v[7]) << 16);
+        st_stream(y + c, o);
+    } else {
+        st_stream(y + 2 * c, make_uint4(f2u(v[0]), f2u(v[1]), f2u(v[2]), f2u(v[3])));
+        st_stream(y + 2 * c + 1, make_uint4(f2u(v[4]), f2u(v[5]), f2u(v[6]), f2u(v[7])));
+    }
+}
+
+// Lane l of a wave tile decodes chunks tile*64*U + r*64 + l, r < U: every
+// code load and output store of the wave is contiguous.
 template <int FMT, bool OUT_BF16>
 __global__ __launch_bounds__(WG) void dequant_kernel(const uint32_t *__restrict__ codes,
                                                      const uint8_t *__restrict__ scales,
                                                      const float *__restrict__ global_scale,
                                                      int64_t nchunks, uint4 *__restrict__ y) {
-    const int64_t stride = (int64_t)gridDim.x * WG;
-    float s_g = 1.0f;
-    if (FMT == 1) s_g = *global_scale;
-    for (int64_t c = (int64_t)blockIdx.x * WG + threadIdx.x; c < nchunks; c += stride) {
-        uint32_t q = __builtin_nontemporal_load(codes + c);
-        float v[8];
-        if (FMT == 0) {
-            uint32_t sb = scales[c >> 2];
-            float so = e8m0_operand(sb);
-            if (OUT_BF16) {
-                uint32_t o[4];
-                o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, so, 0));
-                o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, so, 1));
-                o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, so, 2));
-                o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, so, 3));
-                if (sb == 0xFFu) o[0] = o[1] = o[2] = o[3] = 0x7FC07FC0u;
-                st_stream(y + c, make_uint4(o[0], o[1], o[2], o[3]));
-                continue;
-            }
-            f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, so, 0);
-            f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, so, 1);
-            f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, so, 2);
-            f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, so, 3);
-            v[0] = p0.x; v[1] = p0.y; v[2] = p1.x; v[3] = p1.y;
-            v[4] = p2.x; v[5] = p2.y; v[6] = p3.x; v[7] = p3.y;
-            if (sb == 0xFFu) {
+    constexpr int U = 4;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int64_t wave = (int64_t)blockIdx.x * WAVES_PER_WG + (threadIdx.x / WAVE);
+    const int64_t nwaves = (int64_t)gridDim.x * WAVES_PER_WG;
+    const int64_t ntiles = (nchunks + WAVE * U - 1) / (WAVE * U);
+    const float s_g = (FMT == 1) ? *global_scale : 1.0f;
+    for (int64_t t = wave; t < ntiles; t += nwaves) {
+        uint32_t q[U], sb[U];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) v[i] = __builtin_nanf("");
-            }
-        } else {
-            float alpha = s_g * e4m3_any_value(scales[c >> 1]);
-            const float one = e8m0_operand(E8M0_ONE);
-            f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, one, 0);
-            f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, one, 1);
-            f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, one, 2);
-            f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, one, 3);
-            v[0] = p0.x * alpha; v[1] = p0.y * alpha; v[2] = p1.x * alpha; v[3] = p1.y * alpha;
-            v[4] = p2.x * alpha; v[5] = p2.y * alpha; v[6] = p3.x * alpha; v[7] = p3.y * alpha;
+        for (int r = 0; r < U; ++r) {
+            const int64_t c = t * (WAVE * U) + r * WAVE + lane;
+            const bool ok = c < nchunks;
+            q[r] = ok ? __builtin_nontemporal_load(codes + c) : 0u;
+            sb[r] = ok ? (uint32_t)scales[FMT == 0 ? (c >> 2) : (c >> 1)] : 0u;
         }
-        if (OUT_BF16) {
-            uint4 o;
-            o.x = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
-            o.y = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
-            o.z = bf16_rne(v[4]) | (bf16_rne(v[5]) << 16);
-            o.w = bf16_rne(v[6]) | (bf16_rne(v[7]) << 16);
-            st_stream(y + c, o);
-        } else {
-            st_stream(y + 2 * c, make_uint4(f2u(v[0]), f2u(v[1]), f2u(v[2]), f2u(v[3])));
-            st_stream(y + 2 * c + 1, make_uint4(f2u(v[4]), f2u(v[5]), f2u(v[6]), f2u(v[7])));
+#pragma unroll
+        for (int r = 0; r < U; ++r) {
+            const int64_t c = t * (WAVE * U) + r * WAVE + lane;
+            if (c < nchunks) dequant_chunk<FMT, OUT_BF16>(q[r], sb[r], s_g, y, c);
         }
     }
 }
@@ -534,7 +559,7 @@ hipError_t launch_dequantize(int fmt, const uint8_t *codes, const uint8_t *scale
                              const float *global_scale, int64_t n, void *y, bool out_bf16,
                              hipStream_t s) {
     const int64_t nchunks = n / 8;
-    const int g = grid_for((nchunks + WAVE - 1) / WAVE, kMaxGrid);
+    const int g = grid_for((nchunks + WAVE * 4 - 1) / (WAVE * 4), kMaxGrid);
 #define FP4_DQ(F, B)                                                                          \
     hipLaunchKernelGGL((dequant_kernel<F, B>), dim3(g), dim3(WG), 0, s, (const uint32_t *)codes, \
                        scales, global_scale, nchunks, (uint4 *)y)
