@@ -35,6 +35,8 @@ quantize of the 16384 x 7168 activation, the 4096 x 14336 NVFP4 scale
 search, and the 128 x 8192 x 8192 MXFP4 GEMM.
 """
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -73,6 +75,35 @@ def gemm_bytes(M: int, N: int, K: int, out_bytes: int = 2) -> int:
 
 def gemm_flops(M: int, N: int, K: int) -> int:
     return 2 * M * N * K
+
+
+# ---------------------------------------------------------------------------
+# measured HBM traffic (rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated against a
+# device copy of known size), valid only for the kernel sources it was taken on
+# ---------------------------------------------------------------------------
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "roundtrip_8192x8192_bf16_hbm_traffic.md")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "mxfp4_block_amax_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """Per-launch HBM bytes by entry point, or None if the kernels changed."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            for line in f:
+                if line.startswith("traffic_record:"):
+                    rec = json.loads(line.split(":", 1)[1])
+                    if rec.get("source_sha256_16") == kernel_source_hash():
+                        return rec["per_launch_bytes"]
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
 
 
 # ---------------------------------------------------------------------------
@@ -144,7 +175,7 @@ class RoundTrip:
                        torch.empty(R, C // 32, dtype=torch.uint8, device=dev)),
                 "y_nv": torch.empty(R, C, dtype=torch.bfloat16, device=dev),
                 "y_mx": torch.empty(R, C, dtype=torch.bfloat16, device=dev),
-                "ws": torch.empty(fp4.workspace_bytes(fp4.NVFP4, R, C), dtype=torch.uint8, device=dev),
+                "ws": fp4.new_workspace(R, C, dev),
                 "status": torch.zeros(1, dtype=torch.int32, device=dev),
             }
             self.sets.append(b)
@@ -218,7 +249,7 @@ def extra_workloads():
     xs_cpu = workloads.scale_search_input()
     xs = [xs_cpu.cuda() for _ in range(3)]
     res = [fp4.scale_search(x) for x in xs]
-    ws = torch.empty(fp4.workspace_bytes(fp4.NVFP4, *xs_cpu.shape), dtype=torch.uint8, device="cuda")
+    ws = fp4.new_workspace(*xs_cpu.shape, "cuda")
     ms = time_rotating([lambda x=x, r=r: fp4.scale_search(x, check=False, out=r, status=st, workspace=ws)
                         for x, r in zip(xs, res)], launches=6)
     d = _rate(quantize_bytes(xs_cpu.numel(), 2, "nv"), ms, xs_cpu.numel())
@@ -308,11 +339,15 @@ def main():
                     "nvfp4_dequantize": "dequant_kernel<1, bf16 out>",
                     "mxfp4_quantize": "mx_quantize_kernel<bf16 in>",
                     "mxfp4_dequantize": "dequant_kernel<0, bf16 out>"}
+    traffic = measured_traffic()
     roofline = {"bound": "hbm", "kernel": kernel_names[dom],
                 "achieved": breakdown[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(breakdown[dom]["GB/s"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(breakdown[dom]["GB/s"] / HBM_PEAK_GBS, 4),
+                "traffic": traffic[dom] if traffic else None,
                 "algorithmic_bytes_per_launch": rt.bytes[dom],
                 "avg_launch_us": breakdown[dom]["us"]}
+    if traffic:
+        roofline["traffic_GB/s"] = round(traffic[dom] / (breakdown[dom]["us"] * 1e3), 1)
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,

@@ -119,6 +119,7 @@ def _raise_flags(flags: int):
         raise ValueError("a nonzero scale rounded to zero (tensor, block scale or alpha underflow)")
 
 
+
 def _finish(status: torch.Tensor, check: bool):
     if check:
         _raise_flags(int(status.item()))
@@ -126,6 +127,11 @@ def _finish(status: torch.Tensor, check: bool):
 
 def workspace_bytes(fmt: int, rows: int, cols: int) -> int:
     return int(lib().fp4_workspace_bytes(int(fmt), int(rows), int(cols)))
+
+
+def new_workspace(rows: int, cols: int, device) -> torch.Tensor:
+    """An NVFP4 / scale-search workspace (its contents on entry are ignored)."""
+    return torch.zeros(max(workspace_bytes(NVFP4, rows, cols), 16), dtype=torch.uint8, device=device)
 
 
 def quantize_mxfp4(x: torch.Tensor, check: bool = True, out=None, status=None):
@@ -151,9 +157,8 @@ def quantize_nvfp4(x: torch.Tensor, check: bool = True, out=None, status=None, w
         s_g = torch.empty(1, dtype=torch.float32, device=x.device)
     else:
         codes, scales, s_g = out
-    ws_bytes = workspace_bytes(NVFP4, rows, cols)
     if workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+        workspace = new_workspace(rows, cols, x.device)
     if status is None:
         status = torch.zeros(1, dtype=torch.int32, device=x.device)
     _ok(lib().fp4_quantize_nvfp4(_ptr(x), _dtype_code(x.dtype), rows, cols, 16, _ptr(codes),
@@ -184,9 +189,8 @@ def scale_search(x: torch.Tensor, n_candidates: int = 64, c_lo: float = 0.5, c_h
         s_g = torch.empty(1, dtype=torch.float32, device=x.device)
     else:
         codes, scales, s_g = out
-    ws_bytes = workspace_bytes(NVFP4, rows, cols)
     if workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+        workspace = new_workspace(rows, cols, x.device)
     if status is None:
         status = torch.zeros(1, dtype=torch.int32, device=x.device)
     _ok(lib().fp4_scale_search(_ptr(x), _dtype_code(x.dtype), rows, cols, 16, int(n_candidates),

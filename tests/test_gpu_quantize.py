@@ -202,3 +202,4 @@ def test_deterministic_repeat():
     d = fp4.quantize_mxfp4(x)
     for u, v in zip(c, d):
         assert torch.equal(u, v)
+
