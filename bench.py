@@ -268,6 +268,8 @@ def extra_workloads():
     tf = gemm_flops(M, N, K) / ms / 1e9
     d.update({"TFLOP/s": round(tf, 1), "pct_fp4_mfma_peak": round(100 * tf / FP4_DENSE_PEAK_TFLOPS, 2)})
     out["mxfp4_gemm_128x8192x8192_bf16out"] = d
+    if int(st.item()) != 0:
+        raise RuntimeError(f"a timed call raised status flags {int(st.item())}")
     return out
 
 
@@ -334,8 +336,13 @@ def main():
         breakdown[tag] = _rate(rt.bytes[tag], ms, rt.elements)
         breakdown[tag]["bytes"] = rt.bytes[tag]
 
+    # every call of the timed region reported its conditions here
+    for b in rt.sets:
+        if int(b["status"].item()) != 0:
+            raise RuntimeError(f"a timed call raised status flags {int(b['status'].item())}")
+
     dom = max(breakdown, key=lambda t: breakdown[t]["us"])
-    kernel_names = {"nvfp4_quantize": "fp4_quantize_nvfp4 = tensor_amax_kernel + nv_quantize_kernel",
+    kernel_names = {"nvfp4_quantize": "nv_resident_kernel (one pass, tensor held on chip)",
                     "nvfp4_dequantize": "dequant_kernel<1, bf16 out>",
                     "mxfp4_quantize": "mx_quantize_kernel<bf16 in>",
                     "mxfp4_dequantize": "dequant_kernel<0, bf16 out>"}

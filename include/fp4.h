@@ -2,10 +2,12 @@
  * fp4.h - block-scaled FP4 (E2M1) quantization for AMD Instinct MI355X (gfx950).
  *
  * C ABI of libfp4.so.  Every tensor argument is a DEVICE pointer into memory
- * the caller owns (allocates and frees); the library allocates nothing and
- * keeps no mutable global state, so calls on different streams may run
- * concurrently.  All work is enqueued asynchronously on `stream` (a
- * hipStream_t passed as void*; NULL is the null stream).
+ * the caller owns (allocates and frees); the library allocates nothing.  Its
+ * only global state is a per-device record, filled once, of whether the
+ * one-pass NVFP4 kernel fits (CU count and occupancy).  Calls on different
+ * streams may run concurrently unless they share a workspace.  All work is
+ * enqueued asynchronously on `stream` (a hipStream_t passed as void*; NULL is
+ * the null stream).
  *
  * Formats (one definition each, as given on the pages cited):
  *  - E2M1 element ("NVFP4 / MXFP4 format" page, charlestar.github.io, section
@@ -58,6 +60,7 @@ typedef enum {
 /* Device-side condition flags OR-ed into *status. */
 #define FP4_FLAG_NONFINITE 1       /* an input element is NaN or +-Inf          */
 #define FP4_FLAG_SCALE_UNDERFLOW 2 /* tensor scale, block scale or alpha is 0   */
+#define FP4_FLAG_BARRIER_TIMEOUT 4 /* one-pass NVFP4: the grid barrier gave up   */
 
 typedef enum { FP4_F32 = 0, FP4_BF16 = 1 } fp4_dtype;
 typedef enum { FP4_MXFP4 = 0, FP4_NVFP4 = 1 } fp4_format;
@@ -81,11 +84,20 @@ fp4_status fp4_quantize_mxfp4(const void *x, fp4_dtype xt, int64_t rows, int64_t
  *   x, xt, rows, cols, codes as for MXFP4; block must be 16
  *   scales        [rows*cols/16] E4M3FN bytes
  *   global_scale  device float: receives s_g (dequantize direction, x ~ s_g*s_b*p)
- *   workspace     device scratch of at least fp4_workspace_bytes(FP4_NVFP4, ...)
- *                 bytes, 16-byte aligned; contents on entry are ignored
- *   status        FP4_FLAG_NONFINITE, FP4_FLAG_SCALE_UNDERFLOW
- * Two kernels: a tensor-amax pass, then the quantize pass (which reads the
- * amax in stream order, without a host round trip).  Deterministic.
+ *   workspace     device memory of at least fp4_workspace_bytes(FP4_NVFP4, ...)
+ *                 bytes, 16-byte aligned, ZERO-FILLED before its first use and
+ *                 then left to the library: it keeps a barrier epoch there
+ *                 between calls.  Calls that share a workspace must be ordered
+ *                 (one stream, or synchronised); the same workspace may serve
+ *                 fp4_scale_search too.
+ *   status        FP4_FLAG_NONFINITE, FP4_FLAG_SCALE_UNDERFLOW,
+ *                 FP4_FLAG_BARRIER_TIMEOUT (then zero the workspace again)
+ * s_g needs the amax of the whole tensor.  A bf16 tensor that fits on chip
+ * (one 512 KiB slice per CU: 8192 x 8192 on 256 CUs) is read from HBM once
+ * by a single kernel whose workgroups, one per CU, meet at a grid barrier
+ * after the amax; other inputs take two kernels, a tensor-amax pass and a
+ * quantize pass (which reads the amax in stream order, without a host round
+ * trip).  Results are identical either way.  Deterministic.
  */
 fp4_status fp4_quantize_nvfp4(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
                               int32_t block, uint8_t *codes, uint8_t *scales,
@@ -121,7 +133,8 @@ fp4_status fp4_dequantize(fp4_format fmt, const uint8_t *codes, const uint8_t *s
  *   then finer than the E4M3 grid, whose rounding intervals are at least
  *   1/15 of their value wide, so the distinct candidate scales of a block
  *   are exactly the consecutive E4M3 codes between the two ends).
- *   Other arguments as for fp4_quantize_nvfp4.  Deterministic.
+ *   Other arguments as for fp4_quantize_nvfp4 (two kernels: tensor amax, then
+ *   search and quantize).  Deterministic.
  */
 fp4_status fp4_scale_search(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
                             int32_t block, int32_t n_candidates, float c_lo, float c_hi,

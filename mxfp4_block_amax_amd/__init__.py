@@ -38,6 +38,7 @@ F32 = 0
 BF16 = 1
 FLAG_NONFINITE = 1
 FLAG_SCALE_UNDERFLOW = 2
+FLAG_BARRIER_TIMEOUT = 4
 
 EXPORTS = ("fp4_quantize_mxfp4", "fp4_quantize_nvfp4", "fp4_dequantize", "fp4_scale_search",
            "fp4_gemm_mxfp4", "fp4_workspace_bytes", "fp4_status_str")
@@ -117,7 +118,8 @@ def _raise_flags(flags: int):
         raise ValueError("finite input required (NaN or Inf found)")
     if flags & FLAG_SCALE_UNDERFLOW:
         raise ValueError("a nonzero scale rounded to zero (tensor, block scale or alpha underflow)")
-
+    if flags & FLAG_BARRIER_TIMEOUT:
+        raise Fp4Error("the one-pass NVFP4 grid barrier timed out; re-zero the workspace")
 
 
 def _finish(status: torch.Tensor, check: bool):
@@ -130,7 +132,9 @@ def workspace_bytes(fmt: int, rows: int, cols: int) -> int:
 
 
 def new_workspace(rows: int, cols: int, device) -> torch.Tensor:
-    """An NVFP4 / scale-search workspace (its contents on entry are ignored)."""
+    """A zero-filled NVFP4 / scale-search workspace.  Reuse it across calls
+    (the library keeps a barrier epoch in it); calls sharing one must be
+    stream-ordered."""
     return torch.zeros(max(workspace_bytes(NVFP4, rows, cols), 16), dtype=torch.uint8, device=device)
 
 

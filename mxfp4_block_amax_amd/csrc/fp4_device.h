@@ -24,6 +24,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int WAVE = 64;
 constexpr uint32_t FLAG_NONFINITE = 1;
 constexpr uint32_t FLAG_SCALE_UNDERFLOW = 2;
+constexpr uint32_t FLAG_BARRIER_TIMEOUT = 4;
 
 __device__ __forceinline__ float u2f(uint32_t u) { return __uint_as_float(u); }
 __device__ __forceinline__ uint32_t f2u(float f) { return __float_as_uint(f); }
@@ -142,38 +143,184 @@ __device__ __forceinline__ float e4m3_mid6(uint32_t c) {
     return (float)(3u * (17u + 2u * (c & 7u))) * p2;
 }
 
-// Nearest code to a finite t >= 0 (ties to even, saturating); used only as a
-// first guess that an exact comparison then corrects.
-__device__ __forceinline__ uint32_t e4m3_code_guess(float t) {
-    if (!(t < 448.0f)) return 126u;
-    if (t < 0x1p-6f) return (uint32_t)__builtin_rintf(t * 512.0f);
-    uint32_t b = f2u(t);
-    b += 0x7FFFFu + ((b >> 20) & 1u);
-    uint32_t c = (((b >> 23) - 120u) << 3) | ((b >> 20) & 7u);
-    return c > 126u ? 126u : c;
+// ---- per-tensor E4M3 block-scale table ------------------------------------
+// Once s_g is known the NVFP4 block scale is a function of the block amax
+// alone and takes one of 127 values, so a workgroup tabulates per call:
+//   lo[k]  the smallest fp32 amax whose code is >= k (lo[0] = 0, lo[127] =
+//          +inf), from the exact threshold 6 * midpoint(k-1, k) * s_g (at most
+//          31 significant bits, so exact in binary64); at an exact tie the
+//          amax goes to the even code;
+//   th[k]  that threshold itself, for amax multiples that are not fp32;
+//   q[c]   {alpha_c, alpha'_c, +-1/alpha'_c, sc_c}: alpha_c = RN32(s_g E4M3(c));
+//          the divide x / alpha_c is done as (x sc) / alpha'_c with
+//          alpha'_c = alpha_c sc, where sc = 2^64 when alpha_c < 2^-90 (else
+//          1): scaling both operands by a power of two leaves the quotient
+//          unchanged and keeps the reciprocal-correction divide away from
+//          underflow.  The reciprocal is 0 when alpha_c = 0 (a scale
+//          underflow; outputs are then unspecified).  Its sign bit marks
+//          codes whose one-multiply quotient may differ (see below).
+//
+// One-multiply quotient for bf16 input.  With y = RN32(1/a), q0 = RN32(x y)
+// is within 2^-23 (relative) of x/a, and RN32(x/a) within 2^-24, so their
+// E2M1 codes can differ only if x/a lies within 2^-22 of a decision point m
+// (0.25, 0.75, ..., 5).  A bf16 value (scaled by sc or not) has at most 8
+// significant bits; if no such value lies that close to m a, for every m,
+// the product alone decides every bf16 element of a block with this scale.
+constexpr float kDivScale = 0x1p64f;
+constexpr float kDivScaleBelow = 0x1p-90f;
+
+struct NvScaleTable {
+    float lo[128];
+    float4 q[127];
+    double th[128];
+};
+
+// Whether some value with at most 8 significant bits lies within 2^-22 of
+// m a for an E2M1 decision point m (a normal, a >= 2^-90).  m a is exact in
+// binary64; its distance to the nearest 8-significant-bit value is the
+// smaller of the 45 discarded mantissa bits and their complement, counted
+// in units of 2^(e-52) for m a in [2^e, 2^(e+1)), and m a 2^-22 < 2^(e-21)
+// is 2^31 such units (so the test below flags a superset).
+__device__ __forceinline__ bool near_bf16_midpoint(float a) {
+    const double mids[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
+    bool near = false;
+#pragma unroll
+    for (int i = 0; i < 7; ++i) {
+        const uint64_t b = (uint64_t)__double_as_longlong(mids[i] * (double)a);
+        const uint64_t low = b & ((1ull << 45) - 1ull);
+        const uint64_t dist = low < (1ull << 44) ? low : (1ull << 45) - low;
+        near = near || dist <= (1ull << 31);
+    }
+    return near;
 }
 
-// E4M3 code nearest to the exact real num / (6 * sg), ties to the even code,
-// saturating at 448 (code 126).  num >= 0 is exact in binary64 (an fp32
-// value or the product of two); inv6sg = RN64(1 / (6 sg)).
-// The guess from an approximate quotient can only be wrong when the exact
-// quotient sits within ~2^-50 (relative) of the midpoint nearest the guess,
-// so one exact comparison with that midpoint settles it: the sign of
-// num - 6m * sg from a binary64 fma is exact (a single rounding of the exact
-// difference; the operands are far above the binary64 underflow range).
-__device__ __forceinline__ uint32_t e4m3_code_exact(double num, double sg, double inv6sg) {
-    float t = (float)(num * inv6sg);
-    uint32_t c = e4m3_code_guess(t);
-    if (t >= e4m3_pos_value(c)) {
-        if (c < 126u) {
-            double d = __builtin_fma(-(double)e4m3_mid6(c), sg, num);
-            if (d > 0.0 || (d == 0.0 && (c & 1u))) c += 1u;
-        }
-    } else {
-        double d = __builtin_fma(-(double)e4m3_mid6(c - 1u), sg, num);
-        if (d < 0.0 || (d == 0.0 && (c & 1u))) c -= 1u;
+// Exact threshold between codes k-1 and k (k in 1..126), times 6 s_g.
+__device__ __forceinline__ double nv_threshold(int k, float s_g) {
+    return (double)e4m3_mid6((uint32_t)k - 1u) * (double)s_g;  // exact
+}
+
+// lo[k]: the smallest fp32 amax whose code is >= k.
+__device__ __forceinline__ float nv_lo(int k, float s_g) {
+    if (k == 0) return 0.0f;
+    if (k == 127) return __builtin_inff();
+    const double th = nv_threshold(k, s_g);
+    const float f = (float)th;
+    const double fd = (double)f;
+    // f if it is the first fp32 value reaching code k, else its successor
+    return (fd > th || (fd == th && (k & 1) == 0)) ? f : u2f(f2u(f) + 1u);
+}
+
+// {alpha_c, alpha'_c, +-1/alpha'_c, sc_c} of code c in 0..126.
+__device__ __forceinline__ float4 nv_divisor(int c, float s_g) {
+    const float a = s_g * e4m3_pos_value((uint32_t)c);
+    const float sc = a < kDivScaleBelow ? kDivScale : 1.0f;
+    const float ad = a * sc;  // exact
+    float y = a > 0.0f ? 1.0f / ad : 0.0f;
+    if (a > 0.0f && near_bf16_midpoint(ad)) y = -y;
+    return make_float4(a, ad, y, sc);
+}
+
+__device__ __forceinline__ void nv_table_build(NvScaleTable &T, float s_g) {
+    for (int k = threadIdx.x; k < 128; k += blockDim.x) {
+        T.lo[k] = nv_lo(k, s_g);
+        T.th[k] = k == 0 ? -1.0 : (k == 127 ? __builtin_inf() : nv_threshold(k, s_g));
+        if (k < 127) T.q[k] = nv_divisor(k, s_g);
     }
-    return c;
+}
+
+// Compact table for the one-pass bf16 kernel, indexed by the first-guess code
+// g, so that one LDS round trip settles a block scale:
+//   e[g]  = {lo[g], lo[g+1], ys[g-1], ys[g]},  e1[g] = ys[g+1]
+//   d[g]  = {alpha'[g-1], alpha'[g], alpha'[g+1]} for the full divide
+//   ys[c] = the reciprocal of alpha'_c, negated when code c needs the full
+//           divide (marked, or operands scaled by sc != 1); 0 for alpha_c = 0
+//   sa[c] = {alpha'_c, sc_c}.
+struct NvGuessTable {
+    float4 e[127];
+    float4 d[127];
+    float e1[127];
+    float2 sa[127];
+};
+
+__device__ __forceinline__ float nv_signed_recip(int c, float s_g) {
+    const float4 q = nv_divisor(c, s_g);
+    return q.w != 1.0f ? -__builtin_fabsf(q.z) : q.z;
+}
+
+// Builds the table; returns (to every thread) how many codes are marked and
+// whether any needs operand scaling, as marked + 1024 * scaled.
+__device__ __forceinline__ int nv_guess_table_build(NvGuessTable &R, float s_g) {
+    int marked = 0, scaled = 0;
+    for (int g = threadIdx.x; g < 127; g += blockDim.x) {
+        const float4 q = nv_divisor(g, s_g);
+        const float4 qm = g > 0 ? nv_divisor(g - 1, s_g) : make_float4(0, 0, 0, 1);
+        const float4 qp = g < 126 ? nv_divisor(g + 1, s_g) : make_float4(0, 0, 0, 1);
+        auto ys = [](const float4 &v) { return v.w != 1.0f ? -__builtin_fabsf(v.z) : v.z; };
+        R.e[g] = make_float4(nv_lo(g, s_g), nv_lo(g + 1, s_g), ys(qm), ys(q));
+        R.e1[g] = ys(qp);
+        R.d[g] = make_float4(qm.y, q.y, qp.y, 0.0f);
+        R.sa[g] = make_float2(q.y, q.w);
+        marked += ys(q) < 0.0f;
+        scaled += q.w != 1.0f;
+    }
+    return __syncthreads_count(marked) + 1024 * __syncthreads_count(scaled);
+}
+
+// Truncated E4M3 code of an approximate quotient t >= 0 (saturating);
+// branch-free: the subnormal-range form reads t clamped below 2^-6.
+__device__ __forceinline__ uint32_t e4m3_trunc_code(float t) {
+    const uint32_t sub = (uint32_t)(__builtin_fminf(t, 0x1p-6f) * 512.0f);
+    const uint32_t nrm = min((f2u(t) >> 20) - 960u, 126u);  // wraps to 126 below 2^-6
+    return t < 0x1p-6f ? sub : nrm;
+}
+
+// First guess of a block's E4M3 code in fp32: t = amax * r approximates
+// amax / (6 s_g) * 2^-k (relative error ~2^-23, or an absolute error far
+// below the subnormal code step), with k = 64 when s_g < 2^-120 so that r
+// stays a normal number; the truncated code of t 2^k is read off t's bits
+// with the shift folded into the constants.
+struct CodeGuess {
+    float r;         // RN32(2^-k / (6 s_g))
+    float sub_lim;   // 2^(-6-k): below it the code is floor(t 2^(9+k))
+    float sub_mul;   // 2^(9+k)
+    uint32_t bias;   // 960 - 8k: exponent-and-mantissa bits of t minus this is the code
+};
+
+__device__ __forceinline__ CodeGuess make_code_guess(float s_g) {
+    const bool tiny = s_g < 0x1p-120f;
+    CodeGuess G;
+    G.r = (float)((tiny ? 0x1p-64 : 1.0) / (6.0 * (double)s_g));
+    G.sub_lim = tiny ? 0x1p-70f : 0x1p-6f;
+    G.sub_mul = tiny ? 0x1p73f : 0x1p9f;
+    G.bias = tiny ? 960u - 512u : 960u;
+    return G;
+}
+
+// E4M3 code of a nonzero finite block amax ag: nearest to the exact
+// ag / (6 s_g), ties to the even code, saturating at 448.  The truncated code
+// of the approximate quotient is within one code of the answer; the two exact
+// thresholds around it settle it.  A zero amax gives code 0.
+__device__ __forceinline__ uint32_t code_guess(float ag, const CodeGuess &G) {
+    const float t = ag * G.r;
+    const uint32_t sub = (uint32_t)(__builtin_fminf(t, G.sub_lim) * G.sub_mul);
+    const uint32_t nrm = min((f2u(t) >> 20) - G.bias, 126u);
+    return t < G.sub_lim ? sub : nrm;
+}
+
+__device__ __forceinline__ uint32_t nv_code(const NvScaleTable &T, float ag, const CodeGuess &G) {
+    const uint32_t g = code_guess(ag, G);
+    const float l0 = T.lo[g], l1 = T.lo[g + 1];
+    return g + (uint32_t)(ag >= l1) - (uint32_t)(ag < l0);
+}
+
+// The same for a real z >= 0 exact in binary64 but not necessarily in fp32
+// (a candidate multiple c * amax), against the exact binary64 thresholds.
+__device__ __forceinline__ uint32_t nv_code_real(const NvScaleTable &T, double z, double inv6sg) {
+    const uint32_t g = e4m3_trunc_code((float)(z * inv6sg));
+    const double t0 = T.th[g], t1 = T.th[g + 1];
+    if (z > t1 || (z == t1 && ((g + 1u) & 1u) == 0)) return g + 1u;
+    if (z < t0 || (z == t0 && (g & 1u))) return g - 1u;
+    return g;
 }
 
 // ---- the NV element divide ------------------------------------------------
@@ -197,12 +344,12 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // OR the calling wave's condition flags into *status with one atomic.  Safe
 // in divergent code (ballot counts active lanes only).
 __device__ __forceinline__ void report_flags(int32_t *status, uint32_t flags) {
-    uint64_t n = __ballot((flags & FLAG_NONFINITE) != 0);
-    uint64_t u = __ballot((flags & FLAG_SCALE_UNDERFLOW) != 0);
-    if ((n | u) == 0 || status == nullptr) return;
+    uint32_t any = 0;
+    for (uint32_t bit = 1; bit <= FLAG_BARRIER_TIMEOUT; bit <<= 1)
+        if (__ballot((flags & bit) != 0)) any |= bit;
+    if (any == 0 || status == nullptr) return;
     uint64_t active = __ballot(1);
-    if (__lane_id() == (uint32_t)__builtin_ctzll(active))
-        atomicOr(status, (int32_t)((n ? FLAG_NONFINITE : 0u) | (u ? FLAG_SCALE_UNDERFLOW : 0u)));
+    if (__lane_id() == (uint32_t)__builtin_ctzll(active)) atomicOr(status, (int32_t)any);
 }
 
 }  // namespace fp4dev

@@ -12,7 +12,17 @@ namespace fp4dev {
 constexpr int kMaxGrid = 4096;
 // Workgroups (hence partial maxima) of the tensor-amax pass.
 constexpr int kAmaxPartials = 2048;
-constexpr size_t kNvWorkspaceBytes = kAmaxPartials * sizeof(uint32_t);
+// Workspace of the NVFP4 / scale-search calls: the pass-1 partial maxima,
+// then (one-pass NVFP4 path) an epoch word and one 64-bit barrier slot per
+// workgroup.  The epoch and slots must start zeroed and are kept between
+// calls.
+constexpr size_t kResidentEpochOffset = kAmaxPartials * sizeof(uint32_t);
+constexpr size_t kResidentSlotsOffset = kResidentEpochOffset + 256;
+constexpr int kResidentSlots = 1024;
+constexpr size_t kNvWorkspaceBytes = kResidentSlotsOffset + kResidentSlots * sizeof(uint64_t);
+// Polls of the one-pass grid barrier before it gives up (about a second).
+constexpr uint32_t kResidentSpinLimit = 1u << 19;
+constexpr int kMaxDevices = 64;
 
 hipError_t launch_mx_quantize(const void *x, bool bf16, int64_t n, uint8_t *codes,
                               uint8_t *scales, int32_t *status, hipStream_t s);

@@ -20,6 +20,8 @@
 //     an s_g that underflows, raises FP4_FLAG_SCALE_UNDERFLOW.
 // Scale search ("FP4 / NVFP4 math summary" page, devpress.csdn.net, section 9):
 //   per block, the candidate E4M3 scale with the least fp32 squared error.
+#include <mutex>
+
 #include "fp4_device.h"
 #include "fp4_kernels.h"
 
@@ -158,17 +160,8 @@ struct TensorScale {
     uint32_t flags;
 };
 
-template <bool BF16>
-__device__ TensorScale tensor_scale(const uint32_t *__restrict__ partials, int npart) {
-    __shared__ uint32_t red[WAVES_PER_WG];
-    uint32_t m = 0;
-    for (int i = threadIdx.x; i < npart; i += WG) m = max(m, partials[i]);
-    m = wave_max_u32(m);
-    if ((threadIdx.x & (WAVE - 1)) == 0) red[threadIdx.x / WAVE] = m;
-    __syncthreads();
-    m = red[0];
-    for (int i = 1; i < WAVES_PER_WG; ++i) m = max(m, red[i]);
-    uint32_t A = amax_as_f32_bits<BF16>(m);
+// s_g from the fp32 bit pattern of the tensor amax.
+__device__ __forceinline__ TensorScale scale_from_amax(uint32_t A) {
     TensorScale ts;
     ts.flags = 0;
     if (A >= 0x7F800000u) {
@@ -181,33 +174,67 @@ __device__ TensorScale tensor_scale(const uint32_t *__restrict__ partials, int n
     return ts;
 }
 
-// Per-block NVFP4 scale: E4M3 code, alpha and its reciprocal.
+template <bool BF16>
+__device__ TensorScale tensor_scale(const uint32_t *__restrict__ partials, int npart) {
+    __shared__ uint32_t red[WAVES_PER_WG];
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < npart; i += WG) m = max(m, partials[i]);
+    m = wave_max_u32(m);
+    if ((threadIdx.x & (WAVE - 1)) == 0) red[threadIdx.x / WAVE] = m;
+    __syncthreads();
+    m = red[0];
+    for (int i = 1; i < WAVES_PER_WG; ++i) m = max(m, red[i]);
+    return scale_from_amax(amax_as_f32_bits<BF16>(m));
+}
+
+// Per-block NVFP4 scale from the workgroup's table: the E4M3 code and the
+// divide operands alpha', +-1/alpha', sc (x / alpha is done as
+// (x sc) / alpha'; a negative reciprocal marks a scale whose one-multiply
+// quotient may differ for some bf16 input).  A zero block takes scale 1
+// (code 0x38).
 struct BlockScale {
-    float alpha, y;
+    float ad, y, sc;
     uint32_t code;
-    bool fast;  // alpha and 1/alpha normal: the reciprocal-correction divide is exact
 };
 
-__device__ __forceinline__ BlockScale nv_block_scale(uint32_t ag_bits, float s_g, double sg64,
-                                                     double inv6sg, uint32_t &flags) {
+__device__ __forceinline__ BlockScale nv_block_scale(const NvScaleTable &T, uint32_t ag_bits,
+                                                     const CodeGuess &G, uint32_t &flags) {
     BlockScale b;
-    b.code = (ag_bits == 0) ? 0x38u : e4m3_code_exact((double)u2f(ag_bits), sg64, inv6sg);
-    b.alpha = s_g * e4m3_pos_value(b.code);
-    if ((ag_bits != 0 && b.code == 0) || b.alpha == 0.0f) flags |= FLAG_SCALE_UNDERFLOW;
-    b.fast = b.alpha >= 0x1p-126f;
-    b.y = 1.0f / (b.fast ? b.alpha : 1.0f);
+    const uint32_t c = nv_code(T, u2f(ag_bits), G);  // 0 for a zero amax
+    b.code = ag_bits == 0 ? 0x38u : c;
+    const float4 q = T.q[b.code];
+    b.ad = q.y;
+    b.y = q.z;
+    b.sc = q.w;
+    const bool under = (ag_bits != 0 && c == 0) || q.z == 0.0f;
+    flags |= under ? FLAG_SCALE_UNDERFLOW : 0u;
     return b;
 }
 
-// E2M1 codes of 8 values divided by alpha (fp32 correctly rounded divide).
-__device__ __forceinline__ uint32_t nv_quant8(const float (&v)[8], float alpha, float y, bool fast) {
-    float q[8];
-    if (fast) {
+// x scaled by sc in place; sc is 1 except in tensors whose s_g is tiny, so the
+// multiply sits behind a wave-uniform branch.
+__device__ __forceinline__ void scale_values(float (&v)[8], float sc) {
+    if (__ballot(sc != 1.0f)) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = div_rn(v[i], alpha, y);
+        for (int i = 0; i < 8; ++i) v[i] *= sc;
+    }
+}
+
+// E2M1 codes of 8 values divided by alpha, the fp32 correctly rounded
+// quotient, given alpha' = alpha sc, ys = +-RN32(1 / alpha') and sc.  BF16:
+// the inputs have at most 8 significant bits, so unless some lane's scale is
+// marked (ys < 0) the product with the reciprocal decides the same codes.
+template <bool BF16>
+__device__ __forceinline__ uint32_t nv_quant8(float (&v)[8], float ad, float ys, float sc) {
+    scale_values(v, sc);
+    const float y = __builtin_fabsf(ys);
+    float q[8];
+    if (BF16 && !__ballot(ys < 0.0f)) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = v[i] * y;
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = v[i] / alpha;
+        for (int i = 0; i < 8; ++i) q[i] = div_rn(v[i], ad, y);
     }
     return cvt_fp4x8_f32(q, e8m0_operand(E8M0_ONE));
 }
@@ -227,15 +254,16 @@ __global__ __launch_bounds__(WG) void nv_quantize_kernel(const uint4 *__restrict
                                                          float *__restrict__ global_scale,
                                                          int32_t *status) {
     constexpr int U = 2;
+    __shared__ NvScaleTable T;
     TensorScale ts = tensor_scale<BF16>(partials, npart);
     if (blockIdx.x == 0 && threadIdx.x == 0) *global_scale = ts.s_g;
     if (ts.flags) {  // uniform over the grid: outputs unspecified
         if (blockIdx.x == 0 && threadIdx.x == 0 && status) atomicOr(status, (int32_t)ts.flags);
         return;
     }
-    const float s_g = ts.s_g;
-    const double sg64 = (double)s_g;
-    const double inv6sg = 1.0 / (6.0 * sg64);
+    nv_table_build(T, ts.s_g);
+    __syncthreads();
+    const CodeGuess G = make_code_guess(ts.s_g);
     const int lane = threadIdx.x & (WAVE - 1);
     const bool odd = lane & 1;
     const int64_t wave = (int64_t)blockIdx.x * WAVES_PER_WG + (threadIdx.x / WAVE);
@@ -249,23 +277,322 @@ __global__ __launch_bounds__(WG) void nv_quantize_kernel(const uint4 *__restrict
         uint32_t m0 = chunk_amax<BF16>(k0), m1 = chunk_amax<BF16>(k1);
         m0 = max(m0, dpp<QP_XOR1>(m0));
         m1 = max(m1, dpp<QP_XOR1>(m1));
-        BlockScale mine = nv_block_scale(amax_as_f32_bits<BF16>(odd ? m1 : m0), s_g, sg64,
-                                         inv6sg, flags);
-        float pa = dppf<QP_XOR1>(mine.alpha), py = dppf<QP_XOR1>(mine.y);
-        bool pf = dpp<QP_XOR1>((uint32_t)mine.fast) != 0;
+        BlockScale mine = nv_block_scale(T, amax_as_f32_bits<BF16>(odd ? m1 : m0), G, flags);
+        const float pa = dppf<QP_XOR1>(mine.ad), py = dppf<QP_XOR1>(mine.y),
+                    ps = dppf<QP_XOR1>(mine.sc);
         // row 0 uses the even lane's scale, row 1 the odd lane's
-        const float a0 = odd ? pa : mine.alpha, y0 = odd ? py : mine.y;
-        const float a1 = odd ? mine.alpha : pa, y1 = odd ? mine.y : py;
-        const bool f0 = odd ? pf : mine.fast, f1 = odd ? mine.fast : pf;
+        const float a0 = odd ? pa : mine.ad, y0 = odd ? py : mine.y, s0 = odd ? ps : mine.sc;
+        const float a1 = odd ? mine.ad : pa, y1 = odd ? mine.y : py, s1 = odd ? mine.sc : ps;
         float v[8];
         chunk_values<BF16>(k0, v);
-        uint32_t q0 = nv_quant8(v, a0, y0, f0);
+        uint32_t q0 = nv_quant8<BF16>(v, a0, y0, s0);
         chunk_values<BF16>(k1, v);
-        uint32_t q1 = nv_quant8(v, a1, y1, f1);
+        uint32_t q1 = nv_quant8<BF16>(v, a1, y1, s1);
         if (c0 < nchunks) codes[c0] = q0;
         if (c1 < nchunks) codes[c1] = q1;
         const int64_t cs = odd ? c1 : c0;  // chunk whose block this lane's scale belongs to
         if (cs < nchunks) scales[cs >> 1] = (uint8_t)mine.code;
+    }
+    report_flags(status, flags);
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 quantize of a bf16 tensor in one pass, the tensor held on chip.
+//
+// s_g needs the amax of the whole tensor before any block can be quantized,
+// so the two-pass path reads the input from HBM twice.  Here one workgroup
+// per CU (8 waves, two per SIMD) loads its slice once: up to 64 chunks of 16
+// bytes per lane, the first RES_LDS_CHUNKS of them straight into LDS (the
+// global->LDS load path; 152 KiB per workgroup) and the rest into VGPRs (180
+// registers).  It takes its partial amax, meets the other workgroups at a
+// grid barrier and quantizes from registers and LDS.  256 CUs hold 128 MiB of
+// bf16 this way, an 8192 x 8192 tensor.
+//
+// Chunk j of lane t in workgroup w is  w*cpl*512 + j*512 + t  (cpl chunks per
+// lane, even), so each wave load reads 1 KiB of consecutive bytes, a lane
+// pair holds one 16-element block, and rows j and j+1 pair up as in the
+// two-pass kernel (even lane: row j's block scale, odd lane: row j+1's).
+// Loads past the end of the tensor re-read its last chunk (a duplicate
+// cannot change the amax); stores past it are skipped.
+//
+// Grid barrier.  Each workgroup publishes (tag << 32 | partial amax) in its
+// own 64-bit slot with one device-coherent store, then polls every slot with
+// device-coherent loads until all carry the tag.  The tag is one more than
+// the epoch word in the workspace; every workgroup reads the epoch before it
+// publishes, and workgroup 0 advances it only after the barrier, so the next
+// call (stream-ordered) uses a new tag and stale slots never match.  The
+// launcher starts this kernel only when one workgroup per CU fits and the
+// grid is at most the CU count, so all workgroups are resident together; the
+// wait is still bounded: past spin_limit polls a workgroup raises
+// FLAG_BARRIER_TIMEOUT and goes on.
+// ---------------------------------------------------------------------------
+// Block scales of a tile of four chunk rows (rows 0..3 of a lane pair): the
+// even lane derives rows 0 and 2, the odd lane rows 1 and 3 -- two
+// independent chains per lane, one table read each -- and they swap the
+// signed reciprocals (and, for the full divide, the divisors alpha').
+// marked: one of this lane's two scales needs the full divide.
+struct TileScales {
+    uint32_t cA, cB;  // this lane's two E4M3 codes
+    float ys[4];      // signed reciprocal of each row's alpha'
+    float ad[4];      // each row's alpha' (WITH_DIVISOR only)
+    bool marked;
+};
+
+template <bool WITH_DIVISOR>
+__device__ __forceinline__ TileScales tile_scales(const uint4 (&w)[4], const NvGuessTable &R,
+                                                  const CodeGuess &G, float y38, float a38,
+                                                  bool odd, uint32_t &flags) {
+    uint32_t m[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        m[k] = amax_bf16x8(w[k]);
+        m[k] = max(m[k], dpp<QP_XOR1>(m[k]));
+    }
+    const uint32_t agA = (odd ? m[1] : m[0]) << 16, agB = (odd ? m[3] : m[2]) << 16;
+    const uint32_t gA = code_guess(u2f(agA), G), gB = code_guess(u2f(agB), G);
+    const float4 eA = R.e[gA], eB = R.e[gB];
+    const float fA = R.e1[gA], fB = R.e1[gB];
+    const uint32_t upA = u2f(agA) >= eA.y, dnA = u2f(agA) < eA.x;
+    const uint32_t upB = u2f(agB) >= eB.y, dnB = u2f(agB) < eB.x;
+    const float yA0 = upA ? fA : (dnA ? eA.z : eA.w), yB0 = upB ? fB : (dnB ? eB.z : eB.w);
+    TileScales t;
+    // a zero block takes scale 1 (code 0x38)
+    t.cA = agA == 0 ? 0x38u : gA + upA - dnA;
+    t.cB = agB == 0 ? 0x38u : gB + upB - dnB;
+    const float yA = agA == 0 ? y38 : yA0, yB = agB == 0 ? y38 : yB0;
+    flags |= (yA == 0.0f) | (yB == 0.0f) ? FLAG_SCALE_UNDERFLOW : 0u;
+    const float pyA = dppf<QP_XOR1>(yA), pyB = dppf<QP_XOR1>(yB);
+    t.ys[0] = odd ? pyA : yA;
+    t.ys[1] = odd ? yA : pyA;
+    t.ys[2] = odd ? pyB : yB;
+    t.ys[3] = odd ? yB : pyB;
+    t.marked = (yA < 0.0f) | (yB < 0.0f);
+    if (WITH_DIVISOR) {
+        const float4 dA = R.d[gA], dB = R.d[gB];
+        const float aA0 = upA ? dA.z : (dnA ? dA.x : dA.y), aB0 = upB ? dB.z : (dnB ? dB.x : dB.y);
+        const float aA = agA == 0 ? a38 : aA0, aB = agB == 0 ? a38 : aB0;
+        const float paA = dppf<QP_XOR1>(aA), paB = dppf<QP_XOR1>(aB);
+        t.ad[0] = odd ? paA : aA;
+        t.ad[1] = odd ? aA : paA;
+        t.ad[2] = odd ? paB : aB;
+        t.ad[3] = odd ? aB : paB;
+    }
+    return t;
+}
+
+constexpr int RES_WG = 512;
+// Above this many marked codes the one-pass kernel divides in full throughout.
+constexpr int kMaxMarkedCodes = 4;
+constexpr int RES_WAVES = RES_WG / WAVE;
+constexpr int RES_LDS_CHUNKS = 19;
+constexpr int RES_MAX_CHUNKS = 64;
+
+typedef __attribute__((address_space(1))) const void *global_cptr;
+typedef __attribute__((address_space(3))) void *lds_ptr;
+
+template <int CPL>
+__global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
+    const uint4 *__restrict__ x, int nchunks, uint32_t *__restrict__ codes,
+    uint8_t *__restrict__ scales, float *__restrict__ global_scale, uint64_t *slots,
+    uint32_t *epoch, uint32_t spin_limit, int32_t *status) {
+    constexpr int LC = CPL < RES_LDS_CHUNKS ? CPL : RES_LDS_CHUNKS;  // chunks per lane in LDS
+    constexpr int RC = CPL - LC;                                     // ... and in VGPRs
+    __shared__ uint4 lds[LC * RES_WG];
+    __shared__ NvGuessTable R;
+    __shared__ uint32_t red[RES_WAVES];
+    __shared__ uint32_t tensor_amax;
+
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), wv = tid / WAVE;
+    const int stride = gridDim.x * RES_WG;       // chunks covered by one step j of the grid
+    const int c00 = blockIdx.x * RES_WG + tid;   // this lane's chunk at step 0
+    const int last = nchunks - 1;
+
+    // ---- phase 1: load the slice once, partial amax ----------------------
+    // step j reads x[j*stride + c00]: a uniform base plus this lane's offset,
+    // clamped to the last chunk
+#pragma unroll
+    for (int j = 0; j < LC; ++j) {
+        const uint4 *xj = x + j * stride;
+        __builtin_amdgcn_global_load_lds((global_cptr)(xj + min(c00, last - j * stride)),
+                                         (lds_ptr)&lds[j * RES_WG + wv * WAVE], 16, 0, 0);
+    }
+    uint4 v[RC > 0 ? RC : 1];
+#pragma unroll
+    for (int r = 0; r < RC; ++r) {
+        const int j = LC + r;
+        v[r] = ld_stream(x + j * stride + min(c00, last - j * stride));
+    }
+    uint32_t tag = 0;
+    if (wv == 0) {
+        const uint32_t e = __hip_atomic_load(epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        tag = e + 1u == 0u ? 1u : e + 1u;
+    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int r = 0; r < RC; ++r) m = max(m, amax_bf16x8(v[r]));
+    __builtin_amdgcn_s_waitcnt(0);  // the global->LDS loads of this wave have landed
+#pragma unroll
+    for (int j = 0; j < LC; ++j) m = max(m, amax_bf16x8(lds[j * RES_WG + tid]));
+    m = wave_max_u32(m);
+    if (lane == 0) red[wv] = m;
+    __syncthreads();
+
+    // ---- grid barrier: wave 0 publishes and polls -----------------------
+    uint32_t flags = 0;
+    if (wv == 0) {
+        uint32_t wm = lane < RES_WAVES ? red[lane] : 0u;
+        wm = wave_max_u32(wm);
+        if (lane == 0)
+            __hip_atomic_store(&slots[blockIdx.x], ((uint64_t)tag << 32) | wm, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        const int G = gridDim.x;
+        uint32_t A = 0;
+        for (uint32_t it = 0;; ++it) {
+            bool ok = true;
+            uint32_t mm = 0;
+            for (int i = lane; i < G; i += WAVE) {
+                const uint64_t sl =
+                    __hip_atomic_load(&slots[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ok = ok && (uint32_t)(sl >> 32) == tag;
+                mm = max(mm, (uint32_t)sl);
+            }
+            const bool all = __ballot(!ok) == 0;
+            if (all || it >= spin_limit) {
+                if (!all) flags |= FLAG_BARRIER_TIMEOUT;
+                A = wave_max_u32(mm);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        if (lane == 0) {
+            tensor_amax = A;
+            if (blockIdx.x == 0)
+                __hip_atomic_store(epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    __syncthreads();
+    const TensorScale ts = scale_from_amax(tensor_amax << 16);
+    if (blockIdx.x == 0 && tid == 0) *global_scale = ts.s_g;
+    if (ts.flags) {  // uniform over the grid: outputs unspecified
+        if (blockIdx.x == 0 && tid == 0 && status) atomicOr(status, (int32_t)ts.flags);
+        report_flags(status, flags);
+        return;
+    }
+    const int table_info = nv_guess_table_build(R, ts.s_g);  // ends with a barrier
+
+    // ---- phase 2: quantize from LDS and registers -----------------------
+    // Four chunk rows per iteration: the even lane of a pair derives the block
+    // scales of rows 0 and 2, the odd lane those of rows 1 and 3 (two
+    // independent chains per lane), and they swap them.
+    // Opaque to the optimiser: phase 1's per-chunk results are not kept alive
+    // across the barrier for reuse (there are no registers for them).
+#pragma unroll
+    for (int r = 0; r < RC; ++r) asm volatile("" : "+v"(v[r].x), "+v"(v[r].y), "+v"(v[r].z), "+v"(v[r].w));
+    const CodeGuess G = make_code_guess(ts.s_g);
+    const float4 q38 = nv_divisor(0x38, ts.s_g);  // zero blocks: scale 1
+    const float y38 = q38.w != 1.0f ? -__builtin_fabsf(q38.z) : q38.z, a38 = q38.y;
+    const bool odd = lane & 1;
+    const uint32_t c00u = (uint32_t)c00;
+    const int cs = odd ? c00 + stride : c00;  // this lane's scale chunk, relative to rows 0 / 2
+    static_assert(CPL % 4 == 0 && CPL / 4 <= 32, "four chunk rows per iteration");
+    // Three forms of the loop below, chosen once per call (uniformly: the
+    // table depends on s_g alone); only the chosen one is ever fetched, which
+    // matters because the unrolled loop's size is what limits it.
+    //  - few marked codes: the one-multiply quotient, marked tiles left to a
+    //    compact pass that re-reads them from HBM;
+    //  - many marked codes (an s_g with few significant bits makes every
+    //    alpha short, so exact ties x = m alpha are everywhere): the full
+    //    divide in the unrolled loop;
+    //  - some code needs operand scaling (tensors below ~1e-21): every tile
+    //    goes through the compact pass.
+    const int n_marked = table_info & 1023, any_scaled = table_info >> 10;
+    uint32_t full_divide = 0;  // bit i: tile i still to do with the full divide (uniform)
+    if (any_scaled) {
+        full_divide = CPL / 4 == 32 ? 0xFFFFFFFFu : (1u << (CPL / 4)) - 1u;
+    } else if (n_marked > kMaxMarkedCodes) {
+#pragma unroll
+        for (int j0 = 0; j0 < CPL; j0 += 4) {
+            __builtin_amdgcn_sched_barrier(0);  // keep iterations apart: registers are scarce
+            uint4 w[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int j = j0 + k;
+                w[k] = j < LC ? lds[j * RES_WG + tid] : v[j - LC];
+            }
+            const TileScales t = tile_scales<true>(w, R, G, y38, a38, odd, flags);
+            const int b0 = j0 * stride, b2 = (j0 + 2) * stride;
+            if (cs <= last - b0) (scales + (b0 >> 1))[(uint32_t)cs >> 1] = (uint8_t)t.cA;
+            if (cs <= last - b2) (scales + (b2 >> 1))[(uint32_t)cs >> 1] = (uint8_t)t.cB;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                float f[8];
+                widen_bf16x8(w[k], f);
+                const float y = __builtin_fabsf(t.ys[k]);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) f[i] = div_rn(f[i], t.ad[k], y);
+                const uint32_t q = cvt_fp4x8_f32(f, e8m0_operand(E8M0_ONE));
+                const int bk = (j0 + k) * stride;  // uniform
+                if (c00 <= last - bk) (codes + bk)[c00u] = q;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j0 = 0; j0 < CPL; j0 += 4) {
+            __builtin_amdgcn_sched_barrier(0);
+            uint4 w[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int j = j0 + k;
+                w[k] = j < LC ? lds[j * RES_WG + tid] : v[j - LC];
+            }
+            const TileScales t = tile_scales<false>(w, R, G, y38, a38, odd, flags);
+            const int b0 = j0 * stride, b2 = (j0 + 2) * stride;
+            if (cs <= last - b0) (scales + (b0 >> 1))[(uint32_t)cs >> 1] = (uint8_t)t.cA;
+            if (cs <= last - b2) (scales + (b2 >> 1))[(uint32_t)cs >> 1] = (uint8_t)t.cB;
+            if (__ballot(t.marked)) {  // left to the compact pass
+                full_divide |= 1u << (j0 / 4);
+                continue;
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                float f[8];
+                widen_bf16x8(w[k], f);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) f[i] *= t.ys[k];
+                const uint32_t q = cvt_fp4x8_f32(f, e8m0_operand(E8M0_ONE));
+                const int bk = (j0 + k) * stride;  // uniform
+                if (c00 <= last - bk) (codes + bk)[c00u] = q;
+            }
+        }
+    }
+    // ---- the compact pass: tiles re-read from HBM, full divide -----------
+    while (full_divide) {
+        const int j0 = 4 * __builtin_ctz(full_divide);
+        full_divide &= full_divide - 1u;
+        uint4 w[4];
+        for (int k = 0; k < 4; ++k) {
+            const int bk = (j0 + k) * stride;
+            w[k] = ld_stream(x + bk + min(c00, last - bk));
+        }
+        const TileScales t = tile_scales<false>(w, R, G, y38, a38, odd, flags);
+        const int b0 = j0 * stride, b2 = (j0 + 2) * stride;
+        if (cs <= last - b0) (scales + (b0 >> 1))[(uint32_t)cs >> 1] = (uint8_t)t.cA;
+        if (cs <= last - b2) (scales + (b2 >> 1))[(uint32_t)cs >> 1] = (uint8_t)t.cB;
+        const float2 sA = R.sa[t.cA], sB = R.sa[t.cB];
+        const float pAa = dppf<QP_XOR1>(sA.x), pAs = dppf<QP_XOR1>(sA.y);
+        const float pBa = dppf<QP_XOR1>(sB.x), pBs = dppf<QP_XOR1>(sB.y);
+        const float ad[4] = {odd ? pAa : sA.x, odd ? sA.x : pAa, odd ? pBa : sB.x, odd ? sB.x : pBa};
+        const float sc[4] = {odd ? pAs : sA.y, odd ? sA.y : pAs, odd ? pBs : sB.y, odd ? sB.y : pBs};
+        for (int k = 0; k < 4; ++k) {
+            float f[8];
+            widen_bf16x8(w[k], f);
+            const float y = __builtin_fabsf(t.ys[k]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) f[i] = div_rn(f[i] * sc[k], ad[k], y);
+            const uint32_t q = cvt_fp4x8_f32(f, e8m0_operand(E8M0_ONE));
+            const int bk = (j0 + k) * stride;
+            if (c00 <= last - bk) (codes + bk)[c00u] = q;
+        }
     }
     report_flags(status, flags);
 }
@@ -380,15 +707,23 @@ __global__ __launch_bounds__(WG) void dequant_kernel(const uint32_t *__restrict_
 // the 16 elements in index order.  |x| and |x_hat| give the same squared
 // error as the signed values.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float half_block_loss(const float (&a)[8], float alpha, float y,
-                                                 bool fast) {
-    float q[8];
-    if (fast) {
+template <bool BF16>
+__device__ __forceinline__ float half_block_loss(const float (&a)[8], float4 sq) {
+    // sq = {alpha, alpha', +-1/alpha', sc}: divide as (a sc) / alpha' (one
+    // multiply for bf16 input when no lane's scale is marked), rebuild with alpha
+    const float alpha = sq.x;
+    float xs[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = div_rn(a[i], alpha, y);
+    for (int i = 0; i < 8; ++i) xs[i] = a[i];
+    scale_values(xs, sq.w);
+    const float y = __builtin_fabsf(sq.z);
+    float q[8];
+    if (BF16 && !__ballot(sq.z < 0.0f)) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = xs[i] * y;
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = a[i] / alpha;
+        for (int i = 0; i < 8; ++i) q[i] = div_rn(xs[i], sq.y, y);
     }
     const float one = e8m0_operand(E8M0_ONE);
     uint32_t code = cvt_fp4x8_f32(q, one);
@@ -415,15 +750,16 @@ __global__ __launch_bounds__(WG) void scale_search_kernel(
     const uint4 *__restrict__ x, int64_t nchunks, const uint32_t *__restrict__ partials,
     int npart, float c_lo, float c_hi, uint32_t *__restrict__ codes,
     uint8_t *__restrict__ scales, float *__restrict__ global_scale, int32_t *status) {
+    __shared__ NvScaleTable T;
     TensorScale ts = tensor_scale<BF16>(partials, npart);
     if (blockIdx.x == 0 && threadIdx.x == 0) *global_scale = ts.s_g;
     if (ts.flags) {
         if (blockIdx.x == 0 && threadIdx.x == 0 && status) atomicOr(status, (int32_t)ts.flags);
         return;
     }
-    const float s_g = ts.s_g;
-    const double sg64 = (double)s_g;
-    const double inv6sg = 1.0 / (6.0 * sg64);
+    nv_table_build(T, ts.s_g);
+    __syncthreads();
+    const double inv6sg = 1.0 / (6.0 * (double)ts.s_g);
     const int lane = threadIdx.x & (WAVE - 1);
     const int64_t wave = (int64_t)blockIdx.x * WAVES_PER_WG + (threadIdx.x / WAVE);
     const int64_t nwaves = (int64_t)gridDim.x * WAVES_PER_WG;
@@ -442,17 +778,15 @@ __global__ __launch_bounds__(WG) void scale_search_kernel(
         uint32_t best = 0x38u;
         if (ag_bits != 0) {
             const double ag = (double)u2f(ag_bits);
-            uint32_t lo = e4m3_code_exact((double)c_lo * ag, sg64, inv6sg);
-            uint32_t hi = e4m3_code_exact((double)c_hi * ag, sg64, inv6sg);
+            uint32_t lo = nv_code_real(T, (double)c_lo * ag, inv6sg);
+            uint32_t hi = nv_code_real(T, (double)c_hi * ag, inv6sg);
             lo = lo < 1u ? 1u : lo;
             float bestL = 0.0f;
             bool have = false;
             for (uint32_t code = lo; code <= hi; ++code) {
-                float alpha = s_g * e4m3_pos_value(code);
-                if (alpha == 0.0f) continue;
-                bool fast = alpha >= 0x1p-126f;
-                float y = 1.0f / (fast ? alpha : 1.0f);
-                float part = half_block_loss(a, alpha, y, fast);
+                const float4 sq = T.q[code];
+                if (sq.x == 0.0f) continue;
+                float part = half_block_loss<BF16>(a, sq);
                 float L = part + dppf<QP_XOR1>(part);
                 if (!have || L < bestL) {
                     best = code;
@@ -465,11 +799,9 @@ __global__ __launch_bounds__(WG) void scale_search_kernel(
                 best = 0;
             }
         }
-        float alpha = s_g * e4m3_pos_value(best);
-        bool fast = alpha >= 0x1p-126f;
-        float y = 1.0f / (fast ? alpha : 1.0f);
+        const float4 sq = T.q[best];
         chunk_values<BF16>(k, a);
-        uint32_t q = nv_quant8(a, alpha, y, fast);
+        uint32_t q = nv_quant8<BF16>(a, sq.y, sq.z, sq.w);
         if (c < nchunks) {
             codes[c] = q;
             if ((lane & 1) == 0) scales[c >> 1] = (uint8_t)best;
@@ -517,10 +849,64 @@ static hipError_t launch_amax(const void *x, bool bf16, int64_t nchunks, uint32_
     return hipGetLastError();
 }
 
+// Whether the one-pass resident kernel can run on the current device, and on
+// how many CUs: one workgroup per CU must fit (so the whole grid is resident
+// at once).  Probed once per device.
+struct ResidentInfo {
+    int cus;  // 0: not available
+};
+
+static ResidentInfo resident_info() {
+    static ResidentInfo info[kMaxDevices];
+    static std::once_flag once[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ResidentInfo{0};
+    std::call_once(once[dev], [dev] {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 0;
+        // the largest instance bounds the resources of all of them
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, nv_resident_kernel<RES_MAX_CHUNKS>,
+                                                         RES_WG, 0) != hipSuccess ||
+            per_cu < 1)
+            cus = 0;
+        info[dev].cus = cus > kResidentSlots ? 0 : cus;
+    });
+    return info[dev];
+}
+
+template <int CPL>
+static void launch_resident(int g, const void *x, int64_t nchunks, uint8_t *codes,
+                            uint8_t *scales, float *global_scale, uint8_t *ws, int32_t *status,
+                            hipStream_t s) {
+    hipLaunchKernelGGL(nv_resident_kernel<CPL>, dim3(g), dim3(RES_WG), 0, s, (const uint4 *)x,
+                       (int)nchunks, (uint32_t *)codes, scales, global_scale,
+                       (uint64_t *)(ws + kResidentSlotsOffset),
+                       (uint32_t *)(ws + kResidentEpochOffset), kResidentSpinLimit, status);
+}
+
 hipError_t launch_nv_quantize(const void *x, bool bf16, int64_t n, uint8_t *codes,
                               uint8_t *scales, float *global_scale, void *workspace,
                               int32_t *status, hipStream_t s) {
     const int64_t nchunks = n / 8;
+    if (bf16) {
+        const ResidentInfo ri = resident_info();
+        const int64_t per_step = (int64_t)ri.cus * RES_WG;  // chunks one step of a full grid covers
+        if (ri.cus > 0 && nchunks <= per_step * RES_MAX_CHUNKS) {
+            // fewest chunks per lane (a row pair at least) that fit on the CUs
+            int cpl = 8;
+            while ((int64_t)cpl * per_step < nchunks) cpl *= 2;
+            const int g = (int)((nchunks + (int64_t)cpl * RES_WG - 1) / ((int64_t)cpl * RES_WG));
+            uint8_t *ws = (uint8_t *)workspace;
+            switch (cpl) {
+                case 8: launch_resident<8>(g, x, nchunks, codes, scales, global_scale, ws, status, s); break;
+                case 16: launch_resident<16>(g, x, nchunks, codes, scales, global_scale, ws, status, s); break;
+                case 32: launch_resident<32>(g, x, nchunks, codes, scales, global_scale, ws, status, s); break;
+                default: launch_resident<64>(g, x, nchunks, codes, scales, global_scale, ws, status, s); break;
+            }
+            return hipGetLastError();
+        }
+    }
     uint32_t *partials = (uint32_t *)workspace;
     const int g1 = amax_grid(nchunks);
     hipError_t e = launch_amax(x, bf16, nchunks, partials, g1, s);

@@ -203,3 +203,118 @@ def test_deterministic_repeat():
     for u, v in zip(c, d):
         assert torch.equal(u, v)
 
+
+
+# ---- one-pass (tensor on chip) and two-pass NVFP4 paths ------------------------
+
+def test_nv_bf16_beyond_on_chip_capacity_takes_two_passes():
+    # 10240 x 8192 bf16 (168 MB) exceeds what the CUs hold at once, so this
+    # runs the tensor-amax + quantize kernels; 8192 x 8192 above runs the
+    # one-pass kernel
+    x = workloads.nvfp4_weight(10240, 8192, seed=7)
+    check_nv(x, "weight 10240x8192 bf16")
+
+
+def test_nv_workspace_reused_across_sizes_and_graph_replays():
+    # the barrier epoch lives in the workspace: reuse it across calls of
+    # different grid sizes (stale slots from larger grids must never match)
+    # and across replays of a captured graph, with eager work in between
+    ws = fp4.new_workspace(8192, 8192, "cuda")
+    shapes = [(8192, 8192), (64, 1024), (4096, 8192), (3, 48), (8192, 8192), (1024, 4096)]
+    for i, (r, c) in enumerate(shapes):
+        x = workloads.nvfp4_weight(r, c, seed=20 + i)
+        announce(f"nvfp4 quantize shared workspace call {i} {r}x{c}")
+        codes, scales, s_g = fp4.quantize_nvfp4(dev(x), workspace=ws)
+        torch.cuda.synchronize()
+        p, s, sg, flags = oracle.nv_quantize(oracle_view(x))
+        assert flags == 0
+        assert f32_bits(s_g.cpu().numpy())[0] == f32_bits([sg])[0]
+        assert_bytes_equal(host_u8(scales), s, f"call {i}: NV scales")
+        assert_bytes_equal(host_u8(codes), p, f"call {i}: NV codes")
+
+    x = dev(workloads.nvfp4_weight(2048, 4096, seed=31))
+    p, s, sg, flags = oracle.nv_quantize(oracle_view(x))
+    codes = torch.empty(2048, 2048, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(2048, 256, dtype=torch.uint8, device="cuda")
+    s_g = torch.empty(1, dtype=torch.float32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    announce("nvfp4 quantize graph capture 2048x4096")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up outside the graph
+        fp4.quantize_nvfp4(x, check=False, out=(codes, scales, s_g), status=status, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fp4.quantize_nvfp4(x, check=False, out=(codes, scales, s_g), status=status, workspace=ws)
+    for rep in range(4):
+        codes.zero_()
+        scales.zero_()
+        y = fp4.quantize_nvfp4(x, workspace=ws)      # eager call on the same workspace
+        torch.cuda.synchronize()
+        announce(f"nvfp4 graph replay {rep}")
+        graph.replay()
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        assert_bytes_equal(host_u8(scales), s, f"replay {rep}: NV scales")
+        assert_bytes_equal(host_u8(codes), p, f"replay {rep}: NV codes")
+        assert torch.equal(y[0], codes) and torch.equal(y[1], scales)
+
+
+# ---- the one-multiply quotient and its guard ------------------------------------
+
+def _bf16(v) -> np.ndarray:
+    """Round float64 values to bf16 (nearest even) and return them as float32."""
+    f = np.asarray(v, np.float32).view(np.uint32).astype(np.uint64)
+    r = ((f + 0x7FFF + ((f >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
+def _product_errs_cases(max_cases=6):
+    """bf16 tensors (one row: [tensor-amax block | test block]) in which the
+    plain product x * RN32(1/alpha) would give a wrong E2M1 code for some
+    element of the test block: found by search over tensor amaxes A (which
+    fix s_g) and block codes c (alpha = RN32(s_g E4M3(c)))."""
+    from tests.test_fast_quotient_rule import all_bf16_finite, codes_both_ways
+    xs = all_bf16_finite()
+    xs = xs[xs > 0]
+    cases = []
+    rng = np.random.default_rng(21)
+    e4 = np.array([oracle.e4m3_value(c) for c in range(127)], np.float64)
+    for A in _bf16(rng.uniform(1.0, 4096.0, 4000)):
+        s_g = np.float32(np.float64(A) / 2688.0)
+        for c in range(96, 127):
+            alpha = np.float32(s_g * np.float32(e4[c]))
+            x = xs[(xs >= 0.2 * alpha) & (xs <= 5.5 * alpha)]
+            cd, cm = codes_both_ways(x, alpha)
+            bad = x[cd != cm]
+            if bad.size == 0:
+                continue
+            ag = _bf16([6.0 * np.float64(s_g) * e4[c]])[0]
+            if not (ag > bad.max()) or ag >= A:
+                continue
+            block = np.concatenate([[ag], bad[:15]]).astype(np.float32)
+            block = np.concatenate([block, np.zeros(16 - block.size, np.float32)])
+            row = np.concatenate([[A], np.zeros(15, np.float32), block]).astype(np.float32)
+            t = torch.from_numpy(row).reshape(1, 32).to(torch.bfloat16)
+            p, s, sg, flags = oracle.nv_quantize(oracle_view(t))
+            if flags or s[1] != c:
+                continue
+            cases.append((t, c, bad[:15]))
+            break
+        if len(cases) >= max_cases:
+            break
+    return cases
+
+
+def test_nv_one_multiply_quotient_guard():
+    from tests.test_fast_quotient_rule import codes_both_ways
+    cases = _product_errs_cases()
+    assert len(cases) >= 3, "search found too few sensitive tensors"
+    for i, (t, c, bad) in enumerate(cases):
+        # sensitivity: the unguarded product disagrees with the oracle here
+        p, s, sg, flags = oracle.nv_quantize(oracle_view(t))
+        alpha = np.float32(np.float32(sg) * np.float32(oracle.e4m3_value(c)))
+        cd, cm = codes_both_ways(bad, alpha)
+        assert (cd != cm).any()
+        check_nv(t, f"one-multiply guard case {i} (code {c})")
