@@ -213,7 +213,7 @@ __device__ __forceinline__ float nv_lo(int k, float s_g) {
 // {alpha_c, alpha'_c, +-1/alpha'_c, sc_c} of code c in 0..126.
 __device__ __forceinline__ float4 nv_divisor(int c, float s_g) {
     const float a = s_g * e4m3_pos_value((uint32_t)c);
-    const float sc = a < kDivScaleBelow ? kDivScale : 1.0f;
+    const float sc = a > 0.0f && a < kDivScaleBelow ? kDivScale : 1.0f;  // code 0: alpha = 0
     const float ad = a * sc;  // exact
     float y = a > 0.0f ? 1.0f / ad : 0.0f;
     if (a > 0.0f && near_bf16_midpoint(ad)) y = -y;
@@ -230,38 +230,78 @@ __device__ __forceinline__ void nv_table_build(NvScaleTable &T, float s_g) {
 
 // Compact table for the one-pass bf16 kernel, indexed by the first-guess code
 // g, so that one LDS round trip settles a block scale:
-//   e[g]  = {lo[g], lo[g+1], ys[g-1], ys[g]},  e1[g] = ys[g+1]
-//   d[g]  = {alpha'[g-1], alpha'[g], alpha'[g+1]} for the full divide
-//   ys[c] = the reciprocal of alpha'_c, negated when code c needs the full
-//           divide (marked, or operands scaled by sc != 1); 0 for alpha_c = 0
-//   sa[c] = {alpha'_c, sc_c}.
+//   e[g]  = {lo[g], lo[g+1], Y[g-1], Y[g]},  e1[g] = Y[g+1]
+//   d[g]  = {D[g-1], D[g], D[g+1]}
+// where, for code c,
+//   in general        Y = +-RN32(1/alpha'_c) (negated when the code needs the
+//                     full divide: marked, or operands scaled by sc != 1; 0
+//                     for alpha_c = 0) and D = alpha'_c;
+//   for a short s_g   Y = RD32(1/alpha_c) and D = RN32(1/alpha_c - Y) >= 0, a
+//   (<= 12 bits)      two-float reciprocal for the two-operation divide;
+//   sa[c] = {alpha'_c, sc_c}, always, for the compact full-divide pass.
 struct NvGuessTable {
     float4 e[127];
     float4 d[127];
     float e1[127];
+    float dd[127];  // D per code, assembled into d
     float2 sa[127];
 };
+
+// An s_g with at most 12 significant bits: every alpha_c = s_g E4M3(c) then
+// has at most 16, which the two-operation divide needs.
+__device__ __forceinline__ bool short_tensor_scale(float s_g) {
+    return s_g >= 0x1p-126f && (f2u(s_g) & 0xFFFu) == 0;
+}
 
 __device__ __forceinline__ float nv_signed_recip(int c, float s_g) {
     const float4 q = nv_divisor(c, s_g);
     return q.w != 1.0f ? -__builtin_fabsf(q.z) : q.z;
 }
 
-// Builds the table; returns (to every thread) how many codes are marked and
-// whether any needs operand scaling, as marked + 1024 * scaled.
+// Builds the table in two steps over the workgroup (per code, then per
+// guess); returns to every thread how many codes are marked and whether any
+// needs operand scaling, as marked + 1024 * scaled.  Ends with a barrier.
 __device__ __forceinline__ int nv_guess_table_build(NvGuessTable &R, float s_g) {
     int marked = 0, scaled = 0;
-    for (int g = threadIdx.x; g < 127; g += blockDim.x) {
-        const float4 q = nv_divisor(g, s_g);
-        const float4 qm = g > 0 ? nv_divisor(g - 1, s_g) : make_float4(0, 0, 0, 1);
-        const float4 qp = g < 126 ? nv_divisor(g + 1, s_g) : make_float4(0, 0, 0, 1);
-        auto ys = [](const float4 &v) { return v.w != 1.0f ? -__builtin_fabsf(v.z) : v.z; };
-        R.e[g] = make_float4(nv_lo(g, s_g), nv_lo(g + 1, s_g), ys(qm), ys(q));
-        R.e1[g] = ys(qp);
-        R.d[g] = make_float4(qm.y, q.y, qp.y, 0.0f);
-        R.sa[g] = make_float2(q.y, q.w);
-        marked += ys(q) < 0.0f;
-        scaled += q.w != 1.0f;
+    const int t = threadIdx.x;
+    const bool shrt = short_tensor_scale(s_g);
+    // step 1: per code c, sa[c], Y into e1[c] and D into dd[c]; lo[k] into e[k].x
+    if (t < 127) {
+        const float4 q = nv_divisor(t, s_g);
+        const float ys = q.w != 1.0f ? -__builtin_fabsf(q.z) : q.z;
+        float Y = ys, D = q.y;
+        if (shrt && q.x > 0.0f) {
+            // RD32 and the (non-negative) remainder of 1 / alpha
+            const double r = 1.0 / (double)q.x;
+            float yh = (float)r;
+            if ((double)yh > r) yh = u2f(f2u(yh) - 1u);
+            Y = yh;
+            D = (float)(r - (double)yh);
+        }
+        R.sa[t] = make_float2(q.y, q.w);
+        R.e1[t] = Y;
+        R.dd[t] = D;
+        marked = ys < 0.0f;
+        scaled = q.w != 1.0f;
+    } else if (t >= 128 && t < 128 + 127) {
+        R.e[t - 128].x = nv_lo(t - 128, s_g);
+    }
+    __syncthreads();
+    // step 2: assemble per guess g (reads step 1's values, then rewrites e1)
+    float4 e = make_float4(0, 0, 0, 0), d = e;
+    float e1 = 0.0f;
+    if (t < 127) {
+        const int g = t;
+        e = make_float4(R.e[g].x, g < 126 ? R.e[g + 1].x : __builtin_inff(),
+                        g > 0 ? R.e1[g - 1] : 0.0f, R.e1[g]);
+        e1 = g < 126 ? R.e1[g + 1] : 0.0f;
+        d = make_float4(g > 0 ? R.dd[g - 1] : 0.0f, R.dd[g], g < 126 ? R.dd[g + 1] : 0.0f, 0.0f);
+    }
+    __syncthreads();
+    if (t < 127) {
+        R.e[t] = e;
+        R.e1[t] = e1;
+        R.d[t] = d;
     }
     return __syncthreads_count(marked) + 1024 * __syncthreads_count(scaled);
 }

@@ -21,6 +21,7 @@
 // Scale search ("FP4 / NVFP4 math summary" page, devpress.csdn.net, section 9):
 //   per block, the candidate E4M3 scale with the least fp32 squared error.
 #include <mutex>
+#include <type_traits>
 
 #include "fp4_device.h"
 #include "fp4_kernels.h"
@@ -380,6 +381,39 @@ __device__ __forceinline__ TileScales tile_scales(const uint4 (&w)[4], const NvG
     return t;
 }
 
+// The same for a tile of two chunk rows: the even lane derives row 0's scale,
+// the odd lane row 1's, and they swap reciprocal and divisor.
+struct PairScales {
+    uint32_t c;     // this lane's E4M3 code
+    float ys[2];    // signed reciprocal of each row's alpha'
+    float ad[2];    // each row's alpha'
+};
+
+__device__ __forceinline__ PairScales pair_scales(uint4 w0, uint4 w1, const NvGuessTable &R,
+                                                  const CodeGuess &G, float y38, float a38,
+                                                  bool odd, uint32_t &flags) {
+    uint32_t m0 = amax_bf16x8(w0), m1 = amax_bf16x8(w1);
+    m0 = max(m0, dpp<QP_XOR1>(m0));
+    m1 = max(m1, dpp<QP_XOR1>(m1));
+    const uint32_t ag = (odd ? m1 : m0) << 16;
+    const uint32_t g = code_guess(u2f(ag), G);
+    const float4 e = R.e[g];
+    const float f1 = R.e1[g];
+    const float4 d = R.d[g];
+    const uint32_t up = u2f(ag) >= e.y, dn = u2f(ag) < e.x;
+    PairScales p;
+    p.c = ag == 0 ? 0x38u : g + up - dn;
+    const float y = ag == 0 ? y38 : (up ? f1 : (dn ? e.z : e.w));
+    const float a = ag == 0 ? a38 : (up ? d.z : (dn ? d.x : d.y));
+    flags |= y == 0.0f ? FLAG_SCALE_UNDERFLOW : 0u;
+    // row 0 takes the even lane's values, row 1 the odd lane's
+    p.ys[0] = dppf<0xA0>(y);  // quad_perm [0,0,2,2]
+    p.ys[1] = dppf<0xF5>(y);  // quad_perm [1,1,3,3]
+    p.ad[0] = dppf<0xA0>(a);
+    p.ad[1] = dppf<0xF5>(a);
+    return p;
+}
+
 constexpr int RES_WG = 512;
 // Above this many marked codes the one-pass kernel divides in full throughout.
 constexpr int kMaxMarkedCodes = 4;
@@ -390,7 +424,9 @@ constexpr int RES_MAX_CHUNKS = 64;
 typedef __attribute__((address_space(1))) const void *global_cptr;
 typedef __attribute__((address_space(3))) void *lds_ptr;
 
-template <int CPL>
+// EXACT: the grid covers the tensor exactly (nchunks = gridDim.x * 512 * CPL),
+// so no load is clamped and no store predicated.
+template <int CPL, bool EXACT>
 __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
     const uint4 *__restrict__ x, int nchunks, uint32_t *__restrict__ codes,
     uint8_t *__restrict__ scales, float *__restrict__ global_scale, uint64_t *slots,
@@ -413,14 +449,14 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
 #pragma unroll
     for (int j = 0; j < LC; ++j) {
         const uint4 *xj = x + j * stride;
-        __builtin_amdgcn_global_load_lds((global_cptr)(xj + min(c00, last - j * stride)),
+        __builtin_amdgcn_global_load_lds((global_cptr)(xj + (EXACT ? c00 : min(c00, last - j * stride))),
                                          (lds_ptr)&lds[j * RES_WG + wv * WAVE], 16, 0, 0);
     }
     uint4 v[RC > 0 ? RC : 1];
 #pragma unroll
     for (int r = 0; r < RC; ++r) {
         const int j = LC + r;
-        v[r] = ld_stream(x + j * stride + min(c00, last - j * stride));
+        v[r] = ld_stream(x + j * stride + (EXACT ? c00 : min(c00, last - j * stride)));
     }
     uint32_t tag = 0;
     if (wv == 0) {
@@ -507,34 +543,40 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
     //    goes through the compact pass.
     const int n_marked = table_info & 1023, any_scaled = table_info >> 10;
     uint32_t full_divide = 0;  // bit i: tile i still to do with the full divide (uniform)
-    if (any_scaled) {
-        full_divide = CPL / 4 == 32 ? 0xFFFFFFFFu : (1u << (CPL / 4)) - 1u;
-    } else if (n_marked > kMaxMarkedCodes) {
+    // Full divide of every tile in the unrolled loop, two chunk rows per
+    // iteration: SHORT, the two-operation form (short s_g); else the
+    // reciprocal-correction divide.
+    auto full_loop = [&](auto short_tag) {
+        constexpr bool SHORT = decltype(short_tag)::value;
 #pragma unroll
-        for (int j0 = 0; j0 < CPL; j0 += 4) {
+        for (int j0 = 0; j0 < CPL; j0 += 2) {
             __builtin_amdgcn_sched_barrier(0);  // keep iterations apart: registers are scarce
-            uint4 w[4];
+            const int j1 = j0 + 1;
+            const uint4 w0 = j0 < LC ? lds[j0 * RES_WG + tid] : v[j0 - LC];
+            const uint4 w1 = j1 < LC ? lds[j1 * RES_WG + tid] : v[j1 - LC];
+            const PairScales t = pair_scales(w0, w1, R, G, y38, a38, odd, flags);
+            const int b0 = j0 * stride;
+            if (EXACT || cs <= last - b0) (scales + (b0 >> 1))[(uint32_t)cs >> 1] = (uint8_t)t.c;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int j = j0 + k;
-                w[k] = j < LC ? lds[j * RES_WG + tid] : v[j - LC];
-            }
-            const TileScales t = tile_scales<true>(w, R, G, y38, a38, odd, flags);
-            const int b0 = j0 * stride, b2 = (j0 + 2) * stride;
-            if (cs <= last - b0) (scales + (b0 >> 1))[(uint32_t)cs >> 1] = (uint8_t)t.cA;
-            if (cs <= last - b2) (scales + (b2 >> 1))[(uint32_t)cs >> 1] = (uint8_t)t.cB;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
+            for (int k = 0; k < 2; ++k) {
                 float f[8];
-                widen_bf16x8(w[k], f);
+                widen_bf16x8(k ? w1 : w0, f);
                 const float y = __builtin_fabsf(t.ys[k]);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) f[i] = div_rn(f[i], t.ad[k], y);
+                for (int i = 0; i < 8; ++i)
+                    f[i] = SHORT ? __builtin_fmaf(f[i], y, f[i] * t.ad[k]) : div_rn(f[i], t.ad[k], y);
                 const uint32_t q = cvt_fp4x8_f32(f, e8m0_operand(E8M0_ONE));
                 const int bk = (j0 + k) * stride;  // uniform
-                if (c00 <= last - bk) (codes + bk)[c00u] = q;
+                if (EXACT || c00 <= last - bk) (codes + bk)[c00u] = q;
             }
         }
+    };
+    if (any_scaled) {
+        full_divide = CPL / 4 == 32 ? 0xFFFFFFFFu : (1u << (CPL / 4)) - 1u;
+    } else if (short_tensor_scale(ts.s_g)) {
+        full_loop(std::true_type{});
+    } else if (n_marked > kMaxMarkedCodes) {
+        full_loop(std::false_type{});
     } else {
 #pragma unroll
         for (int j0 = 0; j0 < CPL; j0 += 4) {
@@ -547,8 +589,8 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
             }
             const TileScales t = tile_scales<false>(w, R, G, y38, a38, odd, flags);
             const int b0 = j0 * stride, b2 = (j0 + 2) * stride;
-            if (cs <= last - b0) (scales + (b0 >> 1))[(uint32_t)cs >> 1] = (uint8_t)t.cA;
-            if (cs <= last - b2) (scales + (b2 >> 1))[(uint32_t)cs >> 1] = (uint8_t)t.cB;
+            if (EXACT || cs <= last - b0) (scales + (b0 >> 1))[(uint32_t)cs >> 1] = (uint8_t)t.cA;
+            if (EXACT || cs <= last - b2) (scales + (b2 >> 1))[(uint32_t)cs >> 1] = (uint8_t)t.cB;
             if (__ballot(t.marked)) {  // left to the compact pass
                 full_divide |= 1u << (j0 / 4);
                 continue;
@@ -561,7 +603,7 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
                 for (int i = 0; i < 8; ++i) f[i] *= t.ys[k];
                 const uint32_t q = cvt_fp4x8_f32(f, e8m0_operand(E8M0_ONE));
                 const int bk = (j0 + k) * stride;  // uniform
-                if (c00 <= last - bk) (codes + bk)[c00u] = q;
+                if (EXACT || c00 <= last - bk) (codes + bk)[c00u] = q;
             }
         }
     }
@@ -866,7 +908,8 @@ static ResidentInfo resident_info() {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             cus = 0;
         // the largest instance bounds the resources of all of them
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, nv_resident_kernel<RES_MAX_CHUNKS>,
+        auto largest = nv_resident_kernel<RES_MAX_CHUNKS, false>;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, largest,
                                                          RES_WG, 0) != hipSuccess ||
             per_cu < 1)
             cus = 0;
@@ -879,7 +922,9 @@ template <int CPL>
 static void launch_resident(int g, const void *x, int64_t nchunks, uint8_t *codes,
                             uint8_t *scales, float *global_scale, uint8_t *ws, int32_t *status,
                             hipStream_t s) {
-    hipLaunchKernelGGL(nv_resident_kernel<CPL>, dim3(g), dim3(RES_WG), 0, s, (const uint4 *)x,
+    const bool exact = nchunks == (int64_t)g * CPL * RES_WG;
+    auto kernel = exact ? nv_resident_kernel<CPL, true> : nv_resident_kernel<CPL, false>;
+    hipLaunchKernelGGL(kernel, dim3(g), dim3(RES_WG), 0, s, (const uint4 *)x,
                        (int)nchunks, (uint32_t *)codes, scales, global_scale,
                        (uint64_t *)(ws + kResidentSlotsOffset),
                        (uint32_t *)(ws + kResidentEpochOffset), kResidentSpinLimit, status);
