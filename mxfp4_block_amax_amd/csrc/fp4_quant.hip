@@ -327,62 +327,9 @@ __global__ __launch_bounds__(WG) void nv_quantize_kernel(const uint4 *__restrict
 // wait is still bounded: past spin_limit polls a workgroup raises
 // FLAG_BARRIER_TIMEOUT and goes on.
 // ---------------------------------------------------------------------------
-// Block scales of a tile of four chunk rows (rows 0..3 of a lane pair): the
-// even lane derives rows 0 and 2, the odd lane rows 1 and 3 -- two
-// independent chains per lane, one table read each -- and they swap the
-// signed reciprocals (and, for the full divide, the divisors alpha').
-// marked: one of this lane's two scales needs the full divide.
-struct TileScales {
-    uint32_t cA, cB;  // this lane's two E4M3 codes
-    float ys[4];      // signed reciprocal of each row's alpha'
-    float ad[4];      // each row's alpha' (WITH_DIVISOR only)
-    bool marked;
-};
-
-template <bool WITH_DIVISOR>
-__device__ __forceinline__ TileScales tile_scales(const uint4 (&w)[4], const NvGuessTable &R,
-                                                  const CodeGuess &G, float y38, float a38,
-                                                  bool odd, uint32_t &flags) {
-    uint32_t m[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        m[k] = amax_bf16x8(w[k]);
-        m[k] = max(m[k], dpp<QP_XOR1>(m[k]));
-    }
-    const uint32_t agA = (odd ? m[1] : m[0]) << 16, agB = (odd ? m[3] : m[2]) << 16;
-    const uint32_t gA = code_guess(u2f(agA), G), gB = code_guess(u2f(agB), G);
-    const float4 eA = R.e[gA], eB = R.e[gB];
-    const float fA = R.e1[gA], fB = R.e1[gB];
-    const uint32_t upA = u2f(agA) >= eA.y, dnA = u2f(agA) < eA.x;
-    const uint32_t upB = u2f(agB) >= eB.y, dnB = u2f(agB) < eB.x;
-    const float yA0 = upA ? fA : (dnA ? eA.z : eA.w), yB0 = upB ? fB : (dnB ? eB.z : eB.w);
-    TileScales t;
-    // a zero block takes scale 1 (code 0x38)
-    t.cA = agA == 0 ? 0x38u : gA + upA - dnA;
-    t.cB = agB == 0 ? 0x38u : gB + upB - dnB;
-    const float yA = agA == 0 ? y38 : yA0, yB = agB == 0 ? y38 : yB0;
-    flags |= (yA == 0.0f) | (yB == 0.0f) ? FLAG_SCALE_UNDERFLOW : 0u;
-    const float pyA = dppf<QP_XOR1>(yA), pyB = dppf<QP_XOR1>(yB);
-    t.ys[0] = odd ? pyA : yA;
-    t.ys[1] = odd ? yA : pyA;
-    t.ys[2] = odd ? pyB : yB;
-    t.ys[3] = odd ? yB : pyB;
-    t.marked = (yA < 0.0f) | (yB < 0.0f);
-    if (WITH_DIVISOR) {
-        const float4 dA = R.d[gA], dB = R.d[gB];
-        const float aA0 = upA ? dA.z : (dnA ? dA.x : dA.y), aB0 = upB ? dB.z : (dnB ? dB.x : dB.y);
-        const float aA = agA == 0 ? a38 : aA0, aB = agB == 0 ? a38 : aB0;
-        const float paA = dppf<QP_XOR1>(aA), paB = dppf<QP_XOR1>(aB);
-        t.ad[0] = odd ? paA : aA;
-        t.ad[1] = odd ? aA : paA;
-        t.ad[2] = odd ? paB : aB;
-        t.ad[3] = odd ? aB : paB;
-    }
-    return t;
-}
-
-// The same for a tile of two chunk rows: the even lane derives row 0's scale,
-// the odd lane row 1's, and they swap reciprocal and divisor.
+// Block scales of a tile of two chunk rows held by a lane pair: the even
+// lane derives row 0's scale, the odd lane row 1's (one table read each),
+// and they swap the table's reciprocal term Y and divisor term D.
 struct PairScales {
     uint32_t c;     // this lane's E4M3 code
     float ys[2];    // signed reciprocal of each row's alpha'
@@ -415,8 +362,6 @@ __device__ __forceinline__ PairScales pair_scales(uint4 w0, uint4 w1, const NvGu
 }
 
 constexpr int RES_WG = 512;
-// Above this many marked codes the one-pass kernel divides in full throughout.
-constexpr int kMaxMarkedCodes = 4;
 constexpr int RES_WAVES = RES_WG / WAVE;
 constexpr int RES_LDS_CHUNKS = 19;
 constexpr int RES_MAX_CHUNKS = 64;
@@ -526,26 +471,30 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
     for (int r = 0; r < RC; ++r) asm volatile("" : "+v"(v[r].x), "+v"(v[r].y), "+v"(v[r].z), "+v"(v[r].w));
     const CodeGuess G = make_code_guess(ts.s_g);
     const float4 q38 = nv_divisor(0x38, ts.s_g);  // zero blocks: scale 1
-    const float y38 = q38.w != 1.0f ? -__builtin_fabsf(q38.z) : q38.z, a38 = q38.y;
+    const bool shrt = short_tensor_scale(ts.s_g);
+    float y38 = q38.z, a38 = q38.y;
+    if (shrt) {  // the two-float reciprocal, as the table holds it
+        const double r = 1.0 / (double)q38.x;
+        y38 = (float)r;
+        if ((double)y38 > r) y38 = u2f(f2u(y38) - 1u);
+        a38 = (float)(r - (double)y38);
+    }
     const bool odd = lane & 1;
     const uint32_t c00u = (uint32_t)c00;
-    const int cs = odd ? c00 + stride : c00;  // this lane's scale chunk, relative to rows 0 / 2
-    static_assert(CPL % 4 == 0 && CPL / 4 <= 32, "four chunk rows per iteration");
-    // Three forms of the loop below, chosen once per call (uniformly: the
-    // table depends on s_g alone); only the chosen one is ever fetched, which
-    // matters because the unrolled loop's size is what limits it.
-    //  - few marked codes: the one-multiply quotient, marked tiles left to a
-    //    compact pass that re-reads them from HBM;
-    //  - many marked codes (an s_g with few significant bits makes every
-    //    alpha short, so exact ties x = m alpha are everywhere): the full
-    //    divide in the unrolled loop;
+    const int cs = odd ? c00 + stride : c00;  // this lane's scale chunk, relative to row 0
+    // The quotient x / alpha, chosen once per call (uniformly: it depends on
+    // s_g alone):
+    //  - s_g with at most 12 significant bits: fma(x, Y, x D), the two-float
+    //    reciprocal, exact there;
+    //  - otherwise the reciprocal-correction divide.  (For bf16 the plain
+    //    product x / alpha ~ x * RN(1/alpha) is wrong too often to pay: s_g is
+    //    a bf16 amax over 2688 = 21 * 2^7, whose period-6 binary expansion puts
+    //    m alpha within 2^-24 of a bf16 value for many codes.)
     //  - some code needs operand scaling (tensors below ~1e-21): every tile
-    //    goes through the compact pass.
-    const int n_marked = table_info & 1023, any_scaled = table_info >> 10;
-    uint32_t full_divide = 0;  // bit i: tile i still to do with the full divide (uniform)
-    // Full divide of every tile in the unrolled loop, two chunk rows per
-    // iteration: SHORT, the two-operation form (short s_g); else the
-    // reciprocal-correction divide.
+    //    goes through a compact loop that re-reads it from HBM.
+    // Only the chosen loop is ever fetched: the unrolled loop's size, not its
+    // arithmetic, is what limits it otherwise.
+    const bool any_scaled = (table_info >> 10) != 0;
     auto full_loop = [&](auto short_tag) {
         constexpr bool SHORT = decltype(short_tag)::value;
 #pragma unroll
@@ -571,69 +520,33 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
             }
         }
     };
-    if (any_scaled) {
-        full_divide = CPL / 4 == 32 ? 0xFFFFFFFFu : (1u << (CPL / 4)) - 1u;
-    } else if (short_tensor_scale(ts.s_g)) {
-        full_loop(std::true_type{});
-    } else if (n_marked > kMaxMarkedCodes) {
-        full_loop(std::false_type{});
+    if (!any_scaled) {
+        if (shrt) full_loop(std::true_type{});
+        else full_loop(std::false_type{});
     } else {
-#pragma unroll
-        for (int j0 = 0; j0 < CPL; j0 += 4) {
-            __builtin_amdgcn_sched_barrier(0);
-            uint4 w[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int j = j0 + k;
-                w[k] = j < LC ? lds[j * RES_WG + tid] : v[j - LC];
+        // the compact loop: (x sc) / alpha' with alpha' = alpha sc from sa
+        for (int j0 = 0; j0 < CPL; j0 += 2) {
+            uint4 w[2];
+            for (int k = 0; k < 2; ++k) {
+                const int bk = (j0 + k) * stride;
+                w[k] = ld_stream(x + bk + (EXACT ? c00 : min(c00, last - bk)));
             }
-            const TileScales t = tile_scales<false>(w, R, G, y38, a38, odd, flags);
-            const int b0 = j0 * stride, b2 = (j0 + 2) * stride;
-            if (EXACT || cs <= last - b0) (scales + (b0 >> 1))[(uint32_t)cs >> 1] = (uint8_t)t.cA;
-            if (EXACT || cs <= last - b2) (scales + (b2 >> 1))[(uint32_t)cs >> 1] = (uint8_t)t.cB;
-            if (__ballot(t.marked)) {  // left to the compact pass
-                full_divide |= 1u << (j0 / 4);
-                continue;
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
+            const PairScales t = pair_scales(w[0], w[1], R, G, y38, a38, odd, flags);
+            const int b0 = j0 * stride;
+            if (EXACT || cs <= last - b0) (scales + (b0 >> 1))[(uint32_t)cs >> 1] = (uint8_t)t.c;
+            const float2 sa = R.sa[t.c];
+            const float ad[2] = {dppf<0xA0>(sa.x), dppf<0xF5>(sa.x)};  // rows 0, 1
+            const float sc[2] = {dppf<0xA0>(sa.y), dppf<0xF5>(sa.y)};
+            for (int k = 0; k < 2; ++k) {
                 float f[8];
                 widen_bf16x8(w[k], f);
+                const float y = ad[k] > 0.0f ? 1.0f / ad[k] : 0.0f;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) f[i] *= t.ys[k];
+                for (int i = 0; i < 8; ++i) f[i] = div_rn(f[i] * sc[k], ad[k], y);
                 const uint32_t q = cvt_fp4x8_f32(f, e8m0_operand(E8M0_ONE));
-                const int bk = (j0 + k) * stride;  // uniform
+                const int bk = (j0 + k) * stride;
                 if (EXACT || c00 <= last - bk) (codes + bk)[c00u] = q;
             }
-        }
-    }
-    // ---- the compact pass: tiles re-read from HBM, full divide -----------
-    while (full_divide) {
-        const int j0 = 4 * __builtin_ctz(full_divide);
-        full_divide &= full_divide - 1u;
-        uint4 w[4];
-        for (int k = 0; k < 4; ++k) {
-            const int bk = (j0 + k) * stride;
-            w[k] = ld_stream(x + bk + min(c00, last - bk));
-        }
-        const TileScales t = tile_scales<false>(w, R, G, y38, a38, odd, flags);
-        const int b0 = j0 * stride, b2 = (j0 + 2) * stride;
-        if (cs <= last - b0) (scales + (b0 >> 1))[(uint32_t)cs >> 1] = (uint8_t)t.cA;
-        if (cs <= last - b2) (scales + (b2 >> 1))[(uint32_t)cs >> 1] = (uint8_t)t.cB;
-        const float2 sA = R.sa[t.cA], sB = R.sa[t.cB];
-        const float pAa = dppf<QP_XOR1>(sA.x), pAs = dppf<QP_XOR1>(sA.y);
-        const float pBa = dppf<QP_XOR1>(sB.x), pBs = dppf<QP_XOR1>(sB.y);
-        const float ad[4] = {odd ? pAa : sA.x, odd ? sA.x : pAa, odd ? pBa : sB.x, odd ? sB.x : pBa};
-        const float sc[4] = {odd ? pAs : sA.y, odd ? sA.y : pAs, odd ? pBs : sB.y, odd ? sB.y : pBs};
-        for (int k = 0; k < 4; ++k) {
-            float f[8];
-            widen_bf16x8(w[k], f);
-            const float y = __builtin_fabsf(t.ys[k]);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) f[i] = div_rn(f[i] * sc[k], ad[k], y);
-            const uint32_t q = cvt_fp4x8_f32(f, e8m0_operand(E8M0_ONE));
-            const int bk = (j0 + k) * stride;
-            if (c00 <= last - bk) (codes + bk)[c00u] = q;
         }
     }
     report_flags(status, flags);

@@ -318,3 +318,34 @@ def test_nv_one_multiply_quotient_guard():
         cd, cm = codes_both_ways(bad, alpha)
         assert (cd != cm).any()
         check_nv(t, f"one-multiply guard case {i} (code {c})")
+
+
+# ---- every form of the one-pass kernel's quantize loop ---------------------------
+
+def _one_pass_form(A: float) -> str:
+    """Which loop the one-pass kernel runs for a bf16 tensor of amax A (the
+    kernel decides from s_g alone): restated from the rules it follows."""
+    sg = np.float32(np.float64(A) / 2688.0)
+    alphas = [np.float32(sg * np.float32(oracle.e4m3_value(c))) for c in range(1, 127)]
+    if any(0 < a < 2.0 ** -90 for a in alphas):
+        return "compact"
+    if sg >= 2.0 ** -126 and (sg.view(np.uint32) & 0xFFF) == 0:
+        return "short"
+    return "full"
+
+
+@pytest.mark.parametrize("M,exp,form", [(168, -4, "short"), (231, 20, "short"), (129, -4, "full"),
+                                        (131, -4, "full"), (131, -90, "compact"),
+                                        (168, -100, "compact")])
+def test_nv_one_pass_forms(M, exp, form):
+    # amax significand M: 168 = 21 * 8 and 231 = 21 * 11 make s_g short;
+    # 129 = 3 * 43 and the prime 131 make it a repeating fraction; the tiny
+    # amaxes need operand scaling for the smallest codes
+    A = float(M) * 2.0 ** exp
+    assert _one_pass_form(A) == form
+    g = torch.Generator().manual_seed(M + exp)
+    for rows, cols in [(2048, 4096), (1000, 4112)]:   # exact cover, and ragged
+        x = torch.randn(rows, cols, generator=g) * (A / 8)
+        x = x.clamp(-A, A)
+        x[rows // 2, cols // 3] = -A
+        check_nv(x.to(torch.bfloat16), f"one-pass form {form} amax {A!r} {rows}x{cols}")
