@@ -236,6 +236,19 @@ def _rate(b: int, ms: float, elements: int = None):
 def extra_workloads():
     out = {}
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    # NVFP4 quantize of the same-shape weight with seed 1: amax 235 * 2^-11,
+    # a generic tensor scale, so the one-pass kernel takes the
+    # reciprocal-correction divide (seed 0's amax is 21 * 11 * 2^-11)
+    xw_cpu = workloads.nvfp4_weight(8192, 8192, seed=1)
+    xs = [xw_cpu.cuda() for _ in range(3)]
+    outs = [fp4.quantize_nvfp4(x) for x in xs]
+    wss = [fp4.new_workspace(8192, 8192, "cuda") for _ in range(3)]
+    ms = time_rotating([lambda x=x, o=o, w=w: fp4.quantize_nvfp4(x, check=False, out=o, status=st,
+                                                                 workspace=w)
+                        for x, o, w in zip(xs, outs, wss)])
+    out["nvfp4_quantize_8192x8192_bf16_seed1"] = _rate(quantize_bytes(xw_cpu.numel(), 2, "nv"), ms,
+                                                      xw_cpu.numel())
+    del xs, outs, wss
     # MXFP4 activation quantize, 16384 x 7168 bf16: two 235 MB input copies
     xa_cpu = workloads.mxfp4_activation()
     xs = [xa_cpu.cuda() for _ in range(2)]
@@ -342,7 +355,8 @@ def main():
             raise RuntimeError(f"a timed call raised status flags {int(b['status'].item())}")
 
     dom = max(breakdown, key=lambda t: breakdown[t]["us"])
-    kernel_names = {"nvfp4_quantize": "nv_resident_kernel (one pass, tensor held on chip)",
+    kernel_names = {"nvfp4_quantize": "nv_resident_kernel<64, exact> (one pass, tensor held on chip; "
+                                      "this tensor's s_g = 11 * 2^-18 takes the two-operation divide)",
                     "nvfp4_dequantize": "dequant_kernel<1, bf16 out>",
                     "mxfp4_quantize": "mx_quantize_kernel<bf16 in>",
                     "mxfp4_dequantize": "dequant_kernel<0, bf16 out>"}
