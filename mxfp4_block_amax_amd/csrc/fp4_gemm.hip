@@ -19,6 +19,8 @@
 // of K; wave w owns rows 32w..32w+31.  B (N x K, the large operand at M=128)
 // is read from HBM once in total; A is re-read by every workgroup from L2.
 // The K loop is unrolled with a register prefetch of the next steps' codes.
+#include <type_traits>
+
 #include "fp4_device.h"
 #include "fp4_kernels.h"
 
@@ -235,6 +237,195 @@ __global__ __launch_bounds__(GEMM_WG) void mxfp4_gemm_fast_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// LDS-staged kernel (K a multiple of 256; code rows 16-byte and scale rows
+// 8-byte aligned).  The operand layout of the scaled MFMA wants, per load
+// instruction, 32 rows x 32 bytes at the row stride, which keeps the address
+// unit busy most of the time.  Here every load instruction instead reads
+// eight full 128-byte row segments, straight into LDS (global->LDS loads, no
+// registers), and the MFMA operands are read back from LDS.
+//
+// Tile: a workgroup (4 waves) owns 128 x 32 of C; wave w owns rows
+// 32w..32w+31 and walks all of K in order (deterministic).  K is cut into
+// stages of 4 MFMA steps (256 K values, 128 bytes of codes per row): per
+// stage the workgroup stages A 128 x 128 B and B 32 x 128 B, GEMM_S stages in
+// flight.  Each wave loads its own 32 rows of A and 8 of the 32 rows of B;
+// a barrier per stage makes the shared B rows visible.  Within a row the
+// 16-byte chunk c of a stage sits at chunk c ^ (row & 7) of the LDS row, so
+// the MFMA-layout reads (32 rows, one chunk each) hit distinct banks.
+// Scale bytes go to registers: one 8-byte load per operand row per stage.
+// ---------------------------------------------------------------------------
+constexpr int GEMM_S = 5;                   // stages in flight
+constexpr int GEMM_STAGE_K = 256;           // K values per stage (4 MFMA steps)
+constexpr int GEMM_A_CHUNKS = GEMM_TM * 8;  // 16-byte chunks of A codes per stage
+constexpr int GEMM_B_CHUNKS = GEMM_TN * 8;
+constexpr int GEMM_STAGE_CHUNKS = GEMM_A_CHUNKS + GEMM_B_CHUNKS;
+constexpr int GEMM_LOADS = 5;               // code loads per wave per stage
+constexpr int GEMM_MAX_K = 8192;            // scales of the whole K range held in LDS
+constexpr int GEMM_SCALE_COLS = GEMM_MAX_K / 32 / 16;  // 16-byte scale chunks per row
+
+typedef __attribute__((address_space(1))) const void *gemm_gptr;
+typedef __attribute__((address_space(3))) void *gemm_lptr;
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(GEMM_WG) void mxfp4_gemm_lds_kernel(
+    const uint4 *__restrict__ A, const uint8_t *__restrict__ As, const uint4 *__restrict__ Bt,
+    const uint8_t *__restrict__ Bs, int M, int N, int K, void *__restrict__ C) {
+    // ring of code stages: A [128 rows][8 chunks], B [32][8];
+    // the scales of all K, transposed: A [16-byte chunk][128 rows], B [chunk][32 rows]
+    __shared__ uint4 ring[GEMM_S][GEMM_STAGE_CHUNKS];
+    __shared__ uint4 a_scales[GEMM_SCALE_COLS][GEMM_TM];
+    __shared__ uint4 b_scales[GEMM_SCALE_COLS][GEMM_TN];
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int r32 = lane & 31;
+    const int kh = lane >> 5;
+    const int nblk = K / 32;
+    const int nst = K / GEMM_STAGE_K;
+    const int ncols = nblk / 16;  // 16-byte scale chunks per row (2 stages each)
+    const int m0 = blockIdx.y * GEMM_TM, n0 = blockIdx.x * GEMM_TN;
+
+    // ---- the scales, once: lane l of a load moves 16 bytes (2 stages) of one
+    // row; A: chunk column c, rows 64h + l; B: columns 2j + l / 32, rows l % 32
+    for (int i = w; i < 2 * ncols; i += 4) {
+        const int c = i >> 1, row = 64 * (i & 1) + lane;
+        const uint8_t *src = As + (int64_t)min(m0 + row, M - 1) * nblk + 16 * c;
+        __builtin_amdgcn_global_load_lds((gemm_gptr)src, (gemm_lptr)&a_scales[c][64 * (i & 1)], 16, 0, 0);
+    }
+    for (int j = w; 2 * j < ncols; j += 4) {
+        const int c = 2 * j + kh;
+        const uint8_t *src = Bs + (int64_t)min(n0 + r32, N - 1) * nblk + 16 * min(c, ncols - 1);
+        __builtin_amdgcn_global_load_lds((gemm_gptr)src, (gemm_lptr)&b_scales[2 * j][0], 16, 0, 0);
+    }
+
+    // code loads: lane l of a load covers row (8i + l / 8) of its group and
+    // LDS chunk l % 8, which holds the row's chunk (l % 8) ^ (row & 7)
+    const int lrow = lane >> 3, lpc = lane & 7;
+    const uint4 *ga[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 32 * w + 8 * i + lrow;  // row within the A tile
+        const int am = min(m0 + row, M - 1);
+        ga[i] = A + (int64_t)am * nblk + (lpc ^ (row & 7));
+    }
+    const int brow = 8 * w + lrow;
+    const uint4 *gb = Bt + (int64_t)min(n0 + brow, N - 1) * nblk + (lpc ^ (brow & 7));
+
+    // Five code loads per wave per stage: its 32 rows of A and 8 of the 32
+    // rows of B, global -> LDS.  Stages past the end re-read the last one
+    // (cache hits) into a slot that is never read, so every iteration issues
+    // the same loads and the wait below is one constant.
+    auto issue = [&](int st, uint32_t slot) {
+        st = min(st, nst - 1);
+        uint4 *sb = &ring[0][0] + slot * GEMM_STAGE_CHUNKS;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_global_load_lds((gemm_gptr)(ga[i] + st * 8),
+                                             (gemm_lptr)&sb[(32 * w + 8 * i) * 8], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gemm_gptr)(gb + st * 8),
+                                         (gemm_lptr)&sb[GEMM_A_CHUNKS + 8 * w * 8], 16, 0, 0);
+    };
+
+    // two accumulators (alternate MFMA steps) so that consecutive MFMAs do
+    // not wait for each other; summed once at the end, in a fixed order
+    f32x16_t acc0 = {}, acc1 = {};
+    const int arow = 32 * w + r32;  // this lane's A operand row in the tile
+    const int sw = r32 & 7;         // its swizzle (same for the B row r32)
+    // LDS byte addresses of this lane's operands in slot 0: chunk
+    // (2 s4 + kh) ^ swizzle of its A row and of its B row for steps s4 = 0..3
+    uint32_t la[4], lb[4];
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(gemm_lptr)&ring[0][0];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+        const uint32_t c = (uint32_t)((2 * s4 + kh) ^ sw);
+        la[s4] = lds0 + (uint32_t)(arow * 8 + c) * 16u;
+        lb[s4] = lds0 + (uint32_t)(GEMM_A_CHUNKS + r32 * 8 + c) * 16u;
+    }
+    // this lane's scale rows: stage st's 8 bytes are half (st & 1) of chunk st / 2
+    const uint32_t lsa = (uint32_t)(uintptr_t)(gemm_lptr)&a_scales[0][arow];
+    const uint32_t lsb = (uint32_t)(uintptr_t)(gemm_lptr)&b_scales[0][r32];
+    constexpr uint32_t kSlotBytes = GEMM_STAGE_CHUNKS * 16u;
+
+#pragma unroll
+    for (int st = 0; st < GEMM_S - 1; ++st) issue(st, (uint32_t)st);
+    uint32_t slot = 0, fill = GEMM_S - 1;  // slot of stage st, and of stage st + S - 1
+    for (int st = 0; st < nst; ++st) {
+        // stage st landed once only the later S - 2 stages' loads are in
+        // flight (the scale loads, issued first, have landed by then too)
+        constexpr int kLater = GEMM_LOADS * (GEMM_S - 2);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (kLater & 15) | ((kLater >> 4) << 14));
+        __builtin_amdgcn_s_barrier();  // every wave's part visible; slot `fill` is free
+        issue(st + GEMM_S - 1, fill);
+        // One asm block reads the stage's operands and waits for them: the
+        // compiler cannot tell which LDS the global->LDS loads of later
+        // stages write, and would otherwise wait for all of them here.
+        const uint32_t off = slot * kSlotBytes;
+        const uint32_t soff = (uint32_t)(st >> 1) * 16u * GEMM_TM + (uint32_t)(st & 1) * 8u;
+        const uint32_t soffb = (uint32_t)(st >> 1) * 16u * GEMM_TN + (uint32_t)(st & 1) * 8u;
+        u32x4_t a0, a1, a2, a3, b0, b1, b2, b3;
+        uint2 sa, sb;
+        asm volatile(
+            "ds_read_b128 %0, %10\n\t"
+            "ds_read_b128 %4, %14\n\t"
+            "ds_read_b128 %1, %11\n\t"
+            "ds_read_b128 %5, %15\n\t"
+            "ds_read_b128 %2, %12\n\t"
+            "ds_read_b128 %6, %16\n\t"
+            "ds_read_b128 %3, %13\n\t"
+            "ds_read_b128 %7, %17\n\t"
+            "ds_read_b64 %8, %18\n\t"
+            "ds_read_b64 %9, %19\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(b0), "=&v"(b1), "=&v"(b2),
+              "=&v"(b3), "=&v"(sa), "=&v"(sb)
+            : "v"(la[0] + off), "v"(la[1] + off), "v"(la[2] + off), "v"(la[3] + off),
+              "v"(lb[0] + off), "v"(lb[1] + off), "v"(lb[2] + off), "v"(lb[3] + off),
+              "v"(lsa + soff), "v"(lsb + soffb)
+            : "memory");
+        slot = slot + 1 == GEMM_S ? 0 : slot + 1;
+        fill = fill + 1 == GEMM_S ? 0 : fill + 1;
+        const u32x4_t av[4] = {a0, a1, a2, a3}, bv[4] = {b0, b1, b2, b3};
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            const int i = 2 * s4 + kh;  // scale byte of this step and half
+            const uint32_t ea = (i < 4 ? sa.x : sa.y) >> (8 * (i & 3));
+            const uint32_t eb = (i < 4 ? sb.x : sb.y) >> (8 * (i & 3));
+            const i32x8_t ao = {(int)av[s4].x, (int)av[s4].y, (int)av[s4].z, (int)av[s4].w, 0, 0, 0, 0};
+            const i32x8_t bo = {(int)bv[s4].x, (int)bv[s4].y, (int)bv[s4].z, (int)bv[s4].w, 0, 0, 0, 0};
+            if (s4 & 1)
+                acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ao, bo, acc1, 4, 4, 0, (int)ea,
+                                                                      0, (int)eb);
+            else
+                acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ao, bo, acc0, 4, 4, 0, (int)ea,
+                                                                      0, (int)eb);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // the trailing re-reads land before the workgroup ends
+    const f32x16_t acc = acc0 + acc1;
+
+    // accumulator layout of the 32x32 MFMA: lane l holds column l % 32 and
+    // rows 8 (j / 4) + 4 (l / 32) + (j % 4), j = 0..15
+    const int col = n0 + r32;
+    if (col >= N) return;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int row = m0 + 32 * w + 8 * (j / 4) + 4 * kh + (j % 4);
+        if (row < M) {
+            if (OUT_BF16)
+                ((uint16_t *)C)[(int64_t)row * N + col] = (uint16_t)bf16_rne_bits(acc[j]);
+            else
+                ((float *)C)[(int64_t)row * N + col] = acc[j];
+        }
+    }
+}
+
+static bool gemm_lds_ok(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *bt_codes,
+                        const uint8_t *bt_scales, int64_t K) {
+    auto al = [](const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; };
+    return K % (2 * GEMM_STAGE_K) == 0 && K <= GEMM_MAX_K && al(a_codes, 16) && al(bt_codes, 16) &&
+           al(a_scales, 16) && al(bt_scales, 16);
+}
+
 static bool gemm_fast_ok(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *bt_codes,
                          const uint8_t *bt_scales, int64_t K) {
     auto al = [](const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; };
@@ -246,6 +437,17 @@ hipError_t launch_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales,
                              const uint8_t *bt_codes, const uint8_t *bt_scales, int64_t M,
                              int64_t N, int64_t K, void *c, bool out_bf16, hipStream_t s) {
     dim3 grid((unsigned)((N + GEMM_TN - 1) / GEMM_TN), (unsigned)((M + GEMM_TM - 1) / GEMM_TM));
+    if (gemm_lds_ok(a_codes, a_scales, bt_codes, bt_scales, K)) {
+        if (out_bf16)
+            hipLaunchKernelGGL(mxfp4_gemm_lds_kernel<true>, grid, dim3(GEMM_WG), 0, s,
+                               (const uint4 *)a_codes, a_scales, (const uint4 *)bt_codes,
+                               bt_scales, (int)M, (int)N, (int)K, c);
+        else
+            hipLaunchKernelGGL(mxfp4_gemm_lds_kernel<false>, grid, dim3(GEMM_WG), 0, s,
+                               (const uint4 *)a_codes, a_scales, (const uint4 *)bt_codes,
+                               bt_scales, (int)M, (int)N, (int)K, c);
+        return hipGetLastError();
+    }
     if (gemm_fast_ok(a_codes, a_scales, bt_codes, bt_scales, K)) {
         if (out_bf16)
             hipLaunchKernelGGL(mxfp4_gemm_fast_kernel<true>, grid, dim3(GEMM_WG), 0, s,

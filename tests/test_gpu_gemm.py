@@ -55,7 +55,8 @@ def _check(M, N, K, seed=0):
 
 
 @pytest.mark.parametrize("M,N,K", [(128, 256, 512), (32, 32, 64), (70, 50, 96), (128, 96, 32),
-                                   (256, 64, 8192), (1, 33, 4128)])
+                                   (256, 64, 8192), (1, 33, 4128), (200, 72, 1536), (130, 96, 768),
+                                   (96, 40, 8704)])
 def test_gemm_small_and_ragged(M, N, K):
     _check(M, N, K)
 
