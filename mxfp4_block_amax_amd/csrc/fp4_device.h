@@ -44,13 +44,19 @@ __device__ __forceinline__ void st_stream(uint4 *p, uint4 v) {
     __builtin_nontemporal_store(w, (u32x4_t *)p);
 }
 
+// Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format,
+// no swizzle): the form untyped buffer loads and stores take.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
 // ---- DPP lane exchange inside quads -------------------------------------
 constexpr int QP_XOR1 = 0xB1;  // quad_perm [1,0,3,2]
 constexpr int QP_XOR2 = 0x4E;  // quad_perm [2,3,0,1]
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+    // full row and bank masks: every lane is written, so no old value (and
+    // bound_ctrl changes nothing for in-quad permutes)
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
 }
 template <int CTRL>
 __device__ __forceinline__ float dppf(float v) {
@@ -97,7 +103,9 @@ __device__ __forceinline__ uint32_t cvt_fp4x8_bf16(uint4 w, float scale) {
 }
 
 __device__ __forceinline__ uint32_t cvt_fp4x8_f32(const float (&q)[8], float scale) {
-    uint32_t r = 0;
+    // the four converts write all four bytes: the start value (here the
+    // first input's bits, which need no register of their own) is never read
+    uint32_t r = __builtin_bit_cast(uint32_t, q[0]);
     r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, q[0], q[1], scale, 0);
     r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, q[2], q[3], scale, 1);
     r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, q[4], q[5], scale, 2);
@@ -228,10 +236,15 @@ __device__ __forceinline__ void nv_table_build(NvScaleTable &T, float s_g) {
     }
 }
 
-// Compact table for the one-pass bf16 kernel, indexed by the first-guess code
-// g, so that one LDS round trip settles a block scale:
-//   e[g]  = {lo[g], lo[g+1], Y[g-1], Y[g]},  e1[g] = Y[g+1]
-//   d[g]  = {D[g-1], D[g], D[g+1]}
+// Compact table for the one-pass bf16 kernel.  A block scale takes two
+// dependent LDS reads: the guess g's thresholds, then the final code's entry:
+//   lohi[g]  = {lo[g], lo[g+1]} as fp32 bit patterns (integer order equals
+//              value order for these non-negative numbers), except that
+//              lo[0] is 1: a zero amax then resolves to "code" -1; and
+//              lohi[127] = {~0, ~0}, which resolves the converter's NaN code
+//              (a guess past 448) to 126;
+//   ent[c+1] = {Y_c, D_c, c, 0} for codes c = 0..126, and ent[0] = the
+//              entry of code 0x38 (scale 1), which a zero block takes;
 // where, for code c,
 //   in general        Y = +-RN32(1/alpha'_c) (negated when the code needs the
 //                     full divide: marked, or operands scaled by sc != 1; 0
@@ -239,12 +252,12 @@ __device__ __forceinline__ void nv_table_build(NvScaleTable &T, float s_g) {
 //   for a short s_g   Y = RD32(1/alpha_c) and D = RN32(1/alpha_c - Y) >= 0, a
 //   (<= 12 bits)      two-float reciprocal for the two-operation divide;
 //   sa[c] = {alpha'_c, sc_c}, always, for the compact full-divide pass.
+// lo is staged in the last array.
 struct NvGuessTable {
-    float4 e[127];
-    float4 d[127];
-    float e1[127];
-    float dd[127];  // D per code, assembled into d
+    uint2 lohi[128];
+    float4 ent[128];
     float2 sa[127];
+    float lo[127];
 };
 
 // An s_g with at most 12 significant bits: every alpha_c = s_g E4M3(c) then
@@ -265,7 +278,7 @@ __device__ __forceinline__ int nv_guess_table_build(NvGuessTable &R, float s_g) 
     int marked = 0, scaled = 0;
     const int t = threadIdx.x;
     const bool shrt = short_tensor_scale(s_g);
-    // step 1: per code c, sa[c], Y into e1[c] and D into dd[c]; lo[k] into e[k].x
+    // step 1: per code c, sa[c] and ent[c + 1]; lo[k]
     if (t < 127) {
         const float4 q = nv_divisor(t, s_g);
         const float ys = q.w != 1.0f ? -__builtin_fabsf(q.z) : q.z;
@@ -279,30 +292,19 @@ __device__ __forceinline__ int nv_guess_table_build(NvGuessTable &R, float s_g) 
             D = (float)(r - (double)yh);
         }
         R.sa[t] = make_float2(q.y, q.w);
-        R.e1[t] = Y;
-        R.dd[t] = D;
+        R.ent[t + 1] = make_float4(Y, D, u2f((uint32_t)t), 0.0f);
+        if (t == 0x38) R.ent[0] = make_float4(Y, D, u2f(0x38u), 0.0f);
         marked = ys < 0.0f;
         scaled = q.w != 1.0f;
     } else if (t >= 128 && t < 128 + 127) {
-        R.e[t - 128].x = nv_lo(t - 128, s_g);
+        R.lo[t - 128] = nv_lo(t - 128, s_g);
     }
     __syncthreads();
-    // step 2: assemble per guess g (reads step 1's values, then rewrites e1)
-    float4 e = make_float4(0, 0, 0, 0), d = e;
-    float e1 = 0.0f;
-    if (t < 127) {
-        const int g = t;
-        e = make_float4(R.e[g].x, g < 126 ? R.e[g + 1].x : __builtin_inff(),
-                        g > 0 ? R.e1[g - 1] : 0.0f, R.e1[g]);
-        e1 = g < 126 ? R.e1[g + 1] : 0.0f;
-        d = make_float4(g > 0 ? R.dd[g - 1] : 0.0f, R.dd[g], g < 126 ? R.dd[g + 1] : 0.0f, 0.0f);
-    }
-    __syncthreads();
-    if (t < 127) {
-        R.e[t] = e;
-        R.e1[t] = e1;
-        R.d[t] = d;
-    }
+    // step 2: threshold pairs per guess g
+    if (t < 127)
+        R.lohi[t] = make_uint2(t == 0 ? 1u : f2u(R.lo[t]), t < 126 ? f2u(R.lo[t + 1]) : 0x7F800000u);
+    else if (t == 127)
+        R.lohi[t] = make_uint2(~0u, ~0u);
     return __syncthreads_count(marked) + 1024 * __syncthreads_count(scaled);
 }
 
@@ -324,6 +326,7 @@ struct CodeGuess {
     float sub_lim;   // 2^(-6-k): below it the code is floor(t 2^(9+k))
     float sub_mul;   // 2^(9+k)
     uint32_t bias;   // 960 - 8k: exponent-and-mantissa bits of t minus this is the code
+    float cs;        // 2^-k: the FP8 converter divides by its scale's power of two
 };
 
 __device__ __forceinline__ CodeGuess make_code_guess(float s_g) {
@@ -333,7 +336,21 @@ __device__ __forceinline__ CodeGuess make_code_guess(float s_g) {
     G.sub_lim = tiny ? 0x1p-70f : 0x1p-6f;
     G.sub_mul = tiny ? 0x1p73f : 0x1p9f;
     G.bias = tiny ? 960u - 512u : 960u;
+    G.cs = tiny ? 0x1p-64f : 1.0f;
     return G;
+}
+
+// The same guess from the FP8 converter: the E4M3 code of t 2^k rounded to
+// nearest even (it divides t by its scale's power of two and keeps
+// subnormals; past 464 it gives the NaN code 127, which a table must map to
+// 126).  Within one code of the exact one, like the truncated guess.  The
+// converter writes the low two bytes (t's code, then 0.0's) over t's own bits.
+__device__ __forceinline__ uint32_t code_guess_cvt(float ag, const CodeGuess &G) {
+    typedef short v2i16 __attribute__((ext_vector_type(2)));
+    const float t = ag * G.r;
+    const v2i16 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(v2i16, t), t, 0.0f,
+                                                             G.cs, false);
+    return __builtin_bit_cast(uint32_t, r) & 0xFFu;
 }
 
 // E4M3 code of a nonzero finite block amax ag: nearest to the exact

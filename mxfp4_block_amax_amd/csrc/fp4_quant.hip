@@ -336,28 +336,53 @@ struct PairScales {
     float ad[2];    // each row's alpha'
 };
 
-__device__ __forceinline__ PairScales pair_scales(uint4 w0, uint4 w1, const NvGuessTable &R,
-                                                  const CodeGuess &G, float y38, float a38,
-                                                  bool odd, uint32_t &flags) {
-    uint32_t m0 = amax_bf16x8(w0), m1 = amax_bf16x8(w1);
-    m0 = max(m0, dpp<QP_XOR1>(m0));
-    m1 = max(m1, dpp<QP_XOR1>(m1));
-    const uint32_t ag = (odd ? m1 : m0) << 16;
-    const uint32_t g = code_guess(u2f(ag), G);
-    const float4 e = R.e[g];
-    const float f1 = R.e1[g];
-    const float4 d = R.d[g];
-    const uint32_t up = u2f(ag) >= e.y, dn = u2f(ag) < e.x;
+// Largest magnitude of 8 finite fp32 values (three-input max with |.|
+// operand modifiers; finite inputs need no NaN handling).
+__device__ __forceinline__ float absmax8(const float (&f)[8]) {
+    float a, b, c;
+    asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(a) : "v"(f[0]), "v"(f[1]), "v"(f[2]));
+    asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(b) : "v"(f[3]), "v"(f[4]), "v"(f[5]));
+    asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(c) : "v"(a), "v"(f[6]), "v"(f[7]));
+    asm("v_max_f32 %0, %1, %2" : "=v"(a) : "v"(b), "v"(c));
+    return a;
+}
+
+// Amax bits (bf16 magnitude) of the block this lane derives the scale of,
+// given its chunk amaxes m0 (row 0) and m1 (row 1): the even lane takes row
+// 0's block and the odd lane row 1's; each lane also hands its partner its
+// share of the partner's block.
+__device__ __forceinline__ uint32_t pair_amax(uint32_t m0, uint32_t m1, bool odd) {
+    const uint32_t own = odd ? m1 : m0, other = odd ? m0 : m1;
+    return max(own, dpp<QP_XOR1>(other));
+}
+
+// The block scales of a chunk pair from this lane's block amax (fp32 bit
+// pattern): the code byte for this lane's row, and both rows' divide
+// operands.  A zero block resolves to the table's first entry (code 0x38,
+// scale 1).  ymin collects min |Y|: 0 marks a scale that underflowed.
+__device__ __forceinline__ PairScales pair_scales(uint32_t ag, const NvGuessTable &R,
+                                                  const CodeGuess &G, float &ymin) {
+    const uint32_t g = code_guess_cvt(u2f(ag), G);
+    const uint2 e = R.lohi[g];
+    // c = g + [ag >= lo[g+1]] - [ag < lo[g]] with carry arithmetic; -1 for a
+    // zero block
+    int c;
+    asm("v_cmp_le_u32 vcc, %3, %1\n\t"
+        "v_addc_co_u32 %0, vcc, %2, 0, vcc\n\t"
+        "v_cmp_gt_u32 vcc, %4, %1\n\t"
+        "v_subb_co_u32 %0, vcc, %0, 0, vcc"
+        : "=&v"(c)
+        : "v"(ag), "v"(g), "v"(e.y), "v"(e.x)
+        : "vcc");
+    const float4 en = R.ent[c + 1];
     PairScales p;
-    p.c = ag == 0 ? 0x38u : g + up - dn;
-    const float y = ag == 0 ? y38 : (up ? f1 : (dn ? e.z : e.w));
-    const float a = ag == 0 ? a38 : (up ? d.z : (dn ? d.x : d.y));
-    flags |= y == 0.0f ? FLAG_SCALE_UNDERFLOW : 0u;
+    p.c = f2u(en.z);
+    asm("v_min_f32 %0, %1, |%2|" : "=v"(ymin) : "v"(ymin), "v"(en.x));
     // row 0 takes the even lane's values, row 1 the odd lane's
-    p.ys[0] = dppf<0xA0>(y);  // quad_perm [0,0,2,2]
-    p.ys[1] = dppf<0xF5>(y);  // quad_perm [1,1,3,3]
-    p.ad[0] = dppf<0xA0>(a);
-    p.ad[1] = dppf<0xF5>(a);
+    p.ys[0] = dppf<0xA0>(en.x);  // quad_perm [0,0,2,2]
+    p.ys[1] = dppf<0xF5>(en.x);  // quad_perm [1,1,3,3]
+    p.ad[0] = dppf<0xA0>(en.y);
+    p.ad[1] = dppf<0xF5>(en.y);
     return p;
 }
 
@@ -378,10 +403,19 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
     uint32_t *epoch, uint32_t spin_limit, int32_t *status) {
     constexpr int LC = CPL < RES_LDS_CHUNKS ? CPL : RES_LDS_CHUNKS;  // chunks per lane in LDS
     constexpr int RC = CPL - LC;                                     // ... and in VGPRs
-    __shared__ uint4 lds[LC * RES_WG];
-    __shared__ NvGuessTable R;
-    __shared__ uint32_t red[RES_WAVES];
-    __shared__ uint32_t tensor_amax;
+    // one LDS block, table first: its addresses then fit the 16-bit
+    // immediate offset of an LDS read, so no base is rebuilt per lookup
+    struct Shared {
+        NvGuessTable R;
+        uint32_t red[RES_WAVES];
+        uint32_t tensor_amax;
+        uint4 data[LC * RES_WG];
+    };
+    __shared__ Shared sh;
+    NvGuessTable &R = sh.R;
+    uint32_t(&red)[RES_WAVES] = sh.red;
+    uint32_t &tensor_amax = sh.tensor_amax;
+    uint4(&lds)[LC * RES_WG] = sh.data;
 
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), wv = tid / WAVE;
     const int stride = gridDim.x * RES_WG;       // chunks covered by one step j of the grid
@@ -470,17 +504,14 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
 #pragma unroll
     for (int r = 0; r < RC; ++r) asm volatile("" : "+v"(v[r].x), "+v"(v[r].y), "+v"(v[r].z), "+v"(v[r].w));
     const CodeGuess G = make_code_guess(ts.s_g);
-    const float4 q38 = nv_divisor(0x38, ts.s_g);  // zero blocks: scale 1
     const bool shrt = short_tensor_scale(ts.s_g);
-    float y38 = q38.z, a38 = q38.y;
-    if (shrt) {  // the two-float reciprocal, as the table holds it
-        const double r = 1.0 / (double)q38.x;
-        y38 = (float)r;
-        if ((double)y38 > r) y38 = u2f(f2u(y38) - 1u);
-        a38 = (float)(r - (double)y38);
-    }
+    float ymin = __builtin_inff();
     const bool odd = lane & 1;
-    const uint32_t c00u = (uint32_t)c00;
+    // code dwords go out as buffer stores: one resource, the lane's byte
+    // offset in a VGPR and the uniform part of the address in an SGPR
+    const uint32_t coff = (uint32_t)c00 * 4u;
+    const __amdgpu_buffer_rsrc_t crs =
+        __builtin_amdgcn_make_buffer_rsrc(codes, (short)0, nchunks * 4, kBufferRsrcWord3);
     const int cs = odd ? c00 + stride : c00;  // this lane's scale chunk, relative to row 0
     // The quotient x / alpha, chosen once per call (uniformly: it depends on
     // s_g alone):
@@ -503,20 +534,25 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
             const int j1 = j0 + 1;
             const uint4 w0 = j0 < LC ? lds[j0 * RES_WG + tid] : v[j0 - LC];
             const uint4 w1 = j1 < LC ? lds[j1 * RES_WG + tid] : v[j1 - LC];
-            const PairScales t = pair_scales(w0, w1, R, G, y38, a38, odd, flags);
+            // widened first: the block amax comes from the fp32 values (finite
+            // here: a non-finite tensor returned before the barrier)
+            float fw[2][8];
+            widen_bf16x8(w0, fw[0]);
+            widen_bf16x8(w1, fw[1]);
+            const uint32_t ag = pair_amax(f2u(absmax8(fw[0])), f2u(absmax8(fw[1])), odd);
+            const PairScales t = pair_scales(ag, R, G, ymin);
             const int b0 = j0 * stride;
             if (EXACT || cs <= last - b0) (scales + (b0 >> 1))[(uint32_t)cs >> 1] = (uint8_t)t.c;
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
-                float f[8];
-                widen_bf16x8(k ? w1 : w0, f);
+                float(&f)[8] = fw[k];
                 const float y = __builtin_fabsf(t.ys[k]);
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     f[i] = SHORT ? __builtin_fmaf(f[i], y, f[i] * t.ad[k]) : div_rn(f[i], t.ad[k], y);
                 const uint32_t q = cvt_fp4x8_f32(f, e8m0_operand(E8M0_ONE));
                 const int bk = (j0 + k) * stride;  // uniform
-                if (EXACT || c00 <= last - bk) (codes + bk)[c00u] = q;
+                if (EXACT || c00 <= last - bk) __builtin_amdgcn_raw_buffer_store_b32(q, crs, (int)coff, bk * 4, 0);
             }
         }
     };
@@ -531,7 +567,8 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
                 const int bk = (j0 + k) * stride;
                 w[k] = ld_stream(x + bk + (EXACT ? c00 : min(c00, last - bk)));
             }
-            const PairScales t = pair_scales(w[0], w[1], R, G, y38, a38, odd, flags);
+            const uint32_t ag = pair_amax(amax_bf16x8(w[0]), amax_bf16x8(w[1]), odd) << 16;
+            const PairScales t = pair_scales(ag, R, G, ymin);
             const int b0 = j0 * stride;
             if (EXACT || cs <= last - b0) (scales + (b0 >> 1))[(uint32_t)cs >> 1] = (uint8_t)t.c;
             const float2 sa = R.sa[t.c];
@@ -545,10 +582,11 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
                 for (int i = 0; i < 8; ++i) f[i] = div_rn(f[i] * sc[k], ad[k], y);
                 const uint32_t q = cvt_fp4x8_f32(f, e8m0_operand(E8M0_ONE));
                 const int bk = (j0 + k) * stride;
-                if (EXACT || c00 <= last - bk) (codes + bk)[c00u] = q;
+                if (EXACT || c00 <= last - bk) __builtin_amdgcn_raw_buffer_store_b32(q, crs, (int)coff, bk * 4, 0);
             }
         }
     }
+    flags |= ymin == 0.0f ? FLAG_SCALE_UNDERFLOW : 0u;
     report_flags(status, flags);
 }
 

@@ -349,3 +349,45 @@ def test_nv_one_pass_forms(M, exp, form):
         x = x.clamp(-A, A)
         x[rows // 2, cols // 3] = -A
         check_nv(x.to(torch.bfloat16), f"one-pass form {form} amax {A!r} {rows}x{cols}")
+
+
+def _bf16_value(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def _amax_sweep_tensor(A: float, seed: int, rows: int, cols: int) -> torch.Tensor:
+    """bf16 blocks whose amaxes run through every bf16 magnitude that gets a
+    nonzero block scale under the tensor scale of amax A (A itself a bf16
+    value), repeated to fill rows x cols, with a zero block in every 64; the
+    other elements of a block are smaller, of random sign."""
+    a_bits = int(np.float32(A).view(np.uint32)) >> 16
+    assert _bf16_value(np.array([a_bits]))[0] == np.float32(A)
+    sg = np.float64(np.float32(np.float64(A) / 2688.0))
+    # E4M3 code >= 1 exactly when amax / (6 s_g) > 2^-10 (the tie goes to 0)
+    thr = 6.0 * sg * 2.0 ** -10
+    lo = int(np.float32(thr).view(np.uint32)) >> 16
+    while np.float64(_bf16_value(np.array([lo]))[0]) <= thr:
+        lo += 1
+    pats = np.arange(lo, a_bits + 1, dtype=np.uint32)
+    nblk = rows * cols // 16
+    rng = np.random.default_rng(seed)
+    amax = _bf16_value(pats[np.arange(nblk) % len(pats)]).astype(np.float64)
+    amax[rng.permutation(nblk)[: nblk // 64]] = 0.0
+    amax[0] = np.float64(np.float32(A))  # the tensor amax is present
+    x = rng.uniform(0.0, 1.0, (nblk, 16)) * amax[:, None]
+    x[np.arange(nblk), rng.integers(0, 16, nblk)] = amax
+    x *= np.where(rng.random((nblk, 16)) < 0.5, -1.0, 1.0)
+    # fp32 first (exact for the amaxes), then RNE to bf16: never above a
+    # block's amax, which is a bf16 value
+    return torch.from_numpy(x.astype(np.float32).reshape(rows, cols)).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("M,exp", [(231, -11), (235, -11), (131, -100), (3, -121), (255, 119)])
+def test_nv_every_block_amax_under_one_tensor_scale(M, exp):
+    # every reachable block amax, so every code guess and its two-threshold
+    # settlement runs against the oracle; tensor scales: short (231), generic
+    # (235), operands scaled (tiny), subnormal s_g, and near the bf16 maximum
+    A = float(M) * 2.0 ** exp
+    for rows, cols in [(2048, 4096), (333, 1040)]:   # exact cover, and ragged
+        x = _amax_sweep_tensor(A, M + exp + rows, rows, cols)
+        check_nv(x, f"every block amax under amax {A!r} ({_one_pass_form(A)}) {rows}x{cols}")
