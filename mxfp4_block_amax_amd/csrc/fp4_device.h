@@ -246,9 +246,8 @@ __device__ __forceinline__ void nv_table_build(NvScaleTable &T, float s_g) {
 //   ent[c+1] = {Y_c, D_c, c, 0} for codes c = 0..126, and ent[0] = the
 //              entry of code 0x38 (scale 1), which a zero block takes;
 // where, for code c,
-//   in general        Y = +-RN32(1/alpha'_c) (negated when the code needs the
-//                     full divide: marked, or operands scaled by sc != 1; 0
-//                     for alpha_c = 0) and D = alpha'_c;
+//   in general        Y = RN32(1/alpha'_c) (0 for alpha_c = 0) and
+//                     D = alpha'_c, for the reciprocal-correction divide;
 //   for a short s_g   Y = RD32(1/alpha_c) and D = RN32(1/alpha_c - Y) >= 0, a
 //   (<= 12 bits)      two-float reciprocal for the two-operation divide;
 //   sa[c] = {alpha'_c, sc_c}, always, for the compact full-divide pass.
@@ -272,30 +271,30 @@ __device__ __forceinline__ float nv_signed_recip(int c, float s_g) {
 }
 
 // Builds the table in two steps over the workgroup (per code, then per
-// guess); returns to every thread how many codes are marked and whether any
-// needs operand scaling, as marked + 1024 * scaled.  Ends with a barrier.
-__device__ __forceinline__ int nv_guess_table_build(NvGuessTable &R, float s_g) {
-    int marked = 0, scaled = 0;
+// guess); returns to every thread whether some code needs operand scaling.
+// Ends with a barrier.
+__device__ __forceinline__ bool nv_guess_table_build(NvGuessTable &R, float s_g) {
+    int scaled = 0;
     const int t = threadIdx.x;
     const bool shrt = short_tensor_scale(s_g);
     // step 1: per code c, sa[c] and ent[c + 1]; lo[k]
     if (t < 127) {
-        const float4 q = nv_divisor(t, s_g);
-        const float ys = q.w != 1.0f ? -__builtin_fabsf(q.z) : q.z;
-        float Y = ys, D = q.y;
-        if (shrt && q.x > 0.0f) {
+        const float a = s_g * e4m3_pos_value((uint32_t)t);
+        const float sc = a > 0.0f && a < kDivScaleBelow ? kDivScale : 1.0f;  // code 0: alpha = 0
+        const float ad = a * sc;  // exact
+        float Y = a > 0.0f ? 1.0f / ad : 0.0f, D = ad;
+        if (shrt && a > 0.0f) {
             // RD32 and the (non-negative) remainder of 1 / alpha
-            const double r = 1.0 / (double)q.x;
+            const double r = 1.0 / (double)a;
             float yh = (float)r;
             if ((double)yh > r) yh = u2f(f2u(yh) - 1u);
             Y = yh;
             D = (float)(r - (double)yh);
         }
-        R.sa[t] = make_float2(q.y, q.w);
+        R.sa[t] = make_float2(ad, sc);
         R.ent[t + 1] = make_float4(Y, D, u2f((uint32_t)t), 0.0f);
         if (t == 0x38) R.ent[0] = make_float4(Y, D, u2f(0x38u), 0.0f);
-        marked = ys < 0.0f;
-        scaled = q.w != 1.0f;
+        scaled = sc != 1.0f;
     } else if (t >= 128 && t < 128 + 127) {
         R.lo[t - 128] = nv_lo(t - 128, s_g);
     }
@@ -305,7 +304,7 @@ __device__ __forceinline__ int nv_guess_table_build(NvGuessTable &R, float s_g) 
         R.lohi[t] = make_uint2(t == 0 ? 1u : f2u(R.lo[t]), t < 126 ? f2u(R.lo[t + 1]) : 0x7F800000u);
     else if (t == 127)
         R.lohi[t] = make_uint2(~0u, ~0u);
-    return __syncthreads_count(marked) + 1024 * __syncthreads_count(scaled);
+    return __syncthreads_or(scaled) != 0;
 }
 
 // Truncated E4M3 code of an approximate quotient t >= 0 (saturating);

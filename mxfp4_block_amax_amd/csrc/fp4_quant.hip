@@ -332,8 +332,8 @@ __global__ __launch_bounds__(WG) void nv_quantize_kernel(const uint4 *__restrict
 // and they swap the table's reciprocal term Y and divisor term D.
 struct PairScales {
     uint32_t c;     // this lane's E4M3 code
-    float ys[2];    // signed reciprocal of each row's alpha'
-    float ad[2];    // each row's alpha'
+    float ys[2];    // each row's Y: RN32(1/alpha'), or RD32(1/alpha) for a short s_g
+    float ad[2];    // each row's D: alpha', or the reciprocal's remainder for a short s_g
 };
 
 // Largest magnitude of 8 finite fp32 values (three-input max with |.|
@@ -359,7 +359,7 @@ __device__ __forceinline__ uint32_t pair_amax(uint32_t m0, uint32_t m1, bool odd
 // The block scales of a chunk pair from this lane's block amax (fp32 bit
 // pattern): the code byte for this lane's row, and both rows' divide
 // operands.  A zero block resolves to the table's first entry (code 0x38,
-// scale 1).  ymin collects min |Y|: 0 marks a scale that underflowed.
+// scale 1).  ymin collects min Y (Y >= 0): 0 marks a scale that underflowed.
 __device__ __forceinline__ PairScales pair_scales(uint32_t ag, const NvGuessTable &R,
                                                   const CodeGuess &G, float &ymin) {
     const uint32_t g = code_guess_cvt(u2f(ag), G);
@@ -377,7 +377,7 @@ __device__ __forceinline__ PairScales pair_scales(uint32_t ag, const NvGuessTabl
     const float4 en = R.ent[c + 1];
     PairScales p;
     p.c = f2u(en.z);
-    asm("v_min_f32 %0, %1, |%2|" : "=v"(ymin) : "v"(ymin), "v"(en.x));
+    asm("v_min_f32 %0, %1, %2" : "=v"(ymin) : "v"(ymin), "v"(en.x));
     // row 0 takes the even lane's values, row 1 the odd lane's
     p.ys[0] = dppf<0xA0>(en.x);  // quad_perm [0,0,2,2]
     p.ys[1] = dppf<0xF5>(en.x);  // quad_perm [1,1,3,3]
@@ -493,7 +493,8 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
         report_flags(status, flags);
         return;
     }
-    const int table_info = nv_guess_table_build(R, ts.s_g);  // ends with a barrier
+    // ends with a barrier; true when some code needs operand scaling
+    const bool any_scaled = nv_guess_table_build(R, ts.s_g);
 
     // ---- phase 2: quantize from LDS and registers -----------------------
     // Four chunk rows per iteration: the even lane of a pair derives the block
@@ -525,7 +526,6 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
     //    goes through a compact loop that re-reads it from HBM.
     // Only the chosen loop is ever fetched: the unrolled loop's size, not its
     // arithmetic, is what limits it otherwise.
-    const bool any_scaled = (table_info >> 10) != 0;
     auto full_loop = [&](auto short_tag) {
         constexpr bool SHORT = decltype(short_tag)::value;
 #pragma unroll
@@ -546,7 +546,7 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
                 float(&f)[8] = fw[k];
-                const float y = __builtin_fabsf(t.ys[k]);
+                const float y = t.ys[k];
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     f[i] = SHORT ? __builtin_fmaf(f[i], y, f[i] * t.ad[k]) : div_rn(f[i], t.ad[k], y);
