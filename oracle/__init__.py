@@ -50,6 +50,10 @@ def lib():
         "or_f32_to_bf16": (ctypes.c_uint16, [F]),
         "or_mx_exponent": (I, [D]),
         "or_mx_quantize": (I, [P, I, I64, P, P]),
+        "or_mx_exponent_ceil": (I, [D]),
+        "or_block_loss32_pow2": (F, [P, I]),
+        "or_mx_quantize_rule": (I, [P, I, I64, I, P, P]),
+        "or_scale_search_all": (I, [P, I, I64, F, P, P, P]),
         "or_nv_global_scale": (I, [P, I, I64, P]),
         "or_nv_quantize": (I, [P, I, I64, F, P, P]),
         "or_dequantize": (None, [I, P, P, F, I64, I, P]),
@@ -165,6 +169,33 @@ def mx_quantize(x: np.ndarray):
     return packed, scales, flags
 
 
+MX_RULES = {"ocp": 0, "ceil": 1, "mse": 2}
+
+
+def mx_exponent_ceil(amax: float) -> int:
+    """Ceil-rule MX exponent: the smallest e with 6 * 2^e >= amax."""
+    return lib().or_mx_exponent_ceil(float(amax))
+
+
+def mx_block_loss32(xb: np.ndarray, e: int) -> float:
+    xb = np.ascontiguousarray(xb, dtype=np.float32)
+    assert xb.size == 32
+    return float(lib().or_block_loss32_pow2(_ptr(xb), int(e)))
+
+
+def mx_quantize_rule(x: np.ndarray, rule: str):
+    """MXFP4 quantize with exponent rule "ocp" (floor), "ceil" or "mse"
+    (search over e0 - 1, e0, e0 + 1).  Returns (packed, scales, flags)."""
+    x, dt = _as_input(x)
+    n = x.size
+    if n % 32:
+        raise ValueError("MXFP4 needs complete 32-element blocks")
+    packed = np.empty(n // 2, np.uint8)
+    scales = np.empty(n // 32, np.uint8)
+    flags = lib().or_mx_quantize_rule(_ptr(x), dt, n, MX_RULES[rule], _ptr(packed), _ptr(scales))
+    return packed, scales, flags
+
+
 def nv_global_scale(x: np.ndarray):
     """NVFP4 tensor scale s_g.  Returns (s_g as np.float32, flags)."""
     x, dt = _as_input(x)
@@ -230,6 +261,32 @@ def scale_search(x: np.ndarray, ncand=64, c_lo=0.5, c_hi=1.0):
         n = np.asarray(x).size
         return (np.zeros(n // 2, np.uint8), np.zeros(n // 16, np.uint8), s_g, f1)
     packed, scales, f2 = scale_search_with_scale(x, s_g, ncand, c_lo, c_hi)
+    return packed, scales, s_g, f1 | f2
+
+
+def scale_search_all_with_scale(x: np.ndarray, s_g, want_loss=False):
+    """Brute-force NVFP4 scale search over every E4M3 code, given s_g."""
+    x, dt = _as_input(x)
+    n = x.size
+    if n % 16:
+        raise ValueError("scale search needs complete 16-element blocks")
+    packed = np.empty(n // 2, np.uint8)
+    scales = np.empty(n // 16, np.uint8)
+    loss = np.empty(n // 16, np.float32) if want_loss else None
+    flags = lib().or_scale_search_all(_ptr(x), dt, n, float(np.float32(s_g)), _ptr(packed),
+                                      _ptr(scales), _ptr(loss) if want_loss else None)
+    if want_loss:
+        return packed, scales, flags, loss
+    return packed, scales, flags
+
+
+def scale_search_all(x: np.ndarray):
+    """Brute-force NVFP4 scale search.  Returns (packed, scales, s_g, flags)."""
+    s_g, f1 = nv_global_scale(x)
+    if f1:
+        n = np.asarray(x).size
+        return (np.zeros(n // 2, np.uint8), np.zeros(n // 16, np.uint8), s_g, f1)
+    packed, scales, f2 = scale_search_all_with_scale(x, s_g)
     return packed, scales, s_g, f1 | f2
 
 

@@ -220,6 +220,95 @@ int or_mx_quantize(const void *x, int dt, int64_t n, uint8_t *packed, uint8_t *s
 }
 
 /* ------------------------------------------------------------------------ */
+/* MXFP4 encoder variants ([FMT] section 5: the format fixes the scale set, */
+/* not the rule that picks a scale; the OCP floor rule above is one such    */
+/* rule).  Element rounding is the same RoundE2M1 in every variant.         */
+/* ------------------------------------------------------------------------ */
+
+/* Ceil rule, as the section describes ModelOpt's packed path: the scale is
+ * 2^ceil(log2(amax / 6)), i.e. the smallest power of two 2^e with
+ * 6 * 2^e >= amax, so the block maximum lands in (3, 6] and never
+ * saturates.  Found by exact comparisons (6 * 2^e is exact in binary64).
+ * Readings: the lower exponent limit the section mentions is the E8M0
+ * minimum -127; a zero block takes e = 0, as under the floor rule. */
+int or_mx_exponent_ceil(double amax) {
+    if (amax == 0.0) return 0;
+    int e = or_mx_exponent(amax); /* floor rule: 4 * 2^e <= amax < 8 * 2^e */
+    while (6.0 * ldexp(1.0, e) < amax) ++e;
+    while (e > -127 && 6.0 * ldexp(1.0, e - 1) >= amax) --e;
+    if (e < -127) e = -127;
+    return e;
+}
+
+/* Squared error of one 32-element block quantized with scale 2^e, in fp32
+ * as the NVFP4 search evaluates its 16-element loss: q = RN32(x / 2^e),
+ * x_hat = E2M1(q) * 2^e (exact), err = RN32(x - x_hat), t = RN32(err^2),
+ * summed as a balanced pairwise tree in index order. */
+float or_block_loss32_pow2(const float *xb, int e) {
+    float t[32];
+    float s = ldexpf(1.0f, e);
+    for (int i = 0; i < 32; ++i) {
+        float q = xb[i] / s;
+        int c = or_e2m1_round(q);
+        float xh = (float)(or_e2m1_value(c) * (double)s);
+        float err = xb[i] - xh;
+        t[i] = err * err;
+    }
+    for (int w = 16; w >= 1; w /= 2)
+        for (int i = 0; i < w; ++i) t[i] = t[2 * i] + t[2 * i + 1];
+    return t[0];
+}
+
+/* MXFP4 quantize with a chosen exponent rule:
+ *   rule 0: the OCP floor rule (or_mx_exponent);
+ *   rule 1: the ceil rule (or_mx_exponent_ceil);
+ *   rule 2: a squared-error search over the E8M0 exponents e0 - 1, e0,
+ *           e0 + 1 around the floor rule's e0 (the section's "other
+ *           algorithms"; the search objective is the same block MSE the
+ *           NVFP4 search minimises).  Readings: e0 is the incumbent and a
+ *           neighbour replaces it only with a strictly smaller loss; e0 - 1
+ *           is tried before e0 + 1, so of two neighbours with equal loss the
+ *           lower exponent wins; exponents below -127 are not candidates; a
+ *           zero block keeps e = 0.
+ * Outputs as or_mx_quantize. */
+int or_mx_quantize_rule(const void *x, int dt, int64_t n, int rule, uint8_t *packed,
+                        uint8_t *scales) {
+    int flags = 0;
+    float xb[32];
+    uint8_t codes[32];
+    for (int64_t b = 0; b < n / 32; ++b) {
+        double amax = 0.0;
+        for (int i = 0; i < 32; ++i) {
+            xb[i] = load_elem(x, dt, b * 32 + i);
+            if (!isfinite(xb[i])) flags |= OR_FLAG_NONFINITE;
+            else if (fabs((double)xb[i]) > amax) amax = fabs((double)xb[i]);
+        }
+        int e = rule == 1 ? or_mx_exponent_ceil(amax) : or_mx_exponent(amax);
+        if (rule == 2 && amax != 0.0 && !(flags & OR_FLAG_NONFINITE)) {
+            const int e0 = e;
+            float best = or_block_loss32_pow2(xb, e0);
+            const int alt[2] = {e0 - 1, e0 + 1};
+            for (int k = 0; k < 2; ++k) {
+                if (alt[k] < -127 || alt[k] > 127) continue;
+                float L = or_block_loss32_pow2(xb, alt[k]);
+                if (L < best) {
+                    best = L;
+                    e = alt[k];
+                }
+            }
+        }
+        float s = ldexpf(1.0f, e);
+        scales[b] = (uint8_t)(e + 127);
+        for (int i = 0; i < 32; ++i) {
+            int c = or_e2m1_round(xb[i] / s);
+            codes[i] = (uint8_t)(c < 0 ? 0 : c);
+        }
+        or_pack(codes, 32, packed + b * 16);
+    }
+    return flags;
+}
+
+/* ------------------------------------------------------------------------ */
 /* NVFP4 ([FMT] section 3: a = A/(6*448), b* = A_g/(6a), b = E4M3(b*),       */
 /* p = E2M1(x/(a b)); the block scale is encoded before it quantizes;       */
 /* [MATH] section 3 and section 10: alpha_b = s_b * g)                      */
@@ -386,6 +475,56 @@ int or_scale_search(const void *x, int dt, int64_t n, float s_g, int ncand, floa
                 float ck = or_candidate_c(k, ncand, c_lo, c_hi);
                 int code = or_e4m3_nearest((double)ck * amax, 6.0 * (double)s_g);
                 if (code == 0) continue;
+                float alpha = nv_alpha(s_g, code);
+                if (alpha == 0.0f) continue;
+                float L = or_block_loss_f32(xb, alpha);
+                if (win < 0 || L < winloss) {
+                    win = code;
+                    winloss = L;
+                }
+            }
+        }
+        if (win < 0) {
+            flags |= OR_FLAG_SCALE_UNDERFLOW;
+            win = 0;
+        }
+        float alpha = nv_alpha(s_g, win);
+        scales[b] = (uint8_t)win;
+        if (best_loss) best_loss[b] = winloss;
+        for (int i = 0; i < 16; ++i) {
+            int c = (alpha == 0.0f) ? -1 : or_e2m1_round(xb[i] / alpha);
+            codes[i] = (uint8_t)(c < 0 ? 0 : c);
+        }
+        or_pack(codes, 16, packed + b * 8);
+    }
+    return flags;
+}
+
+/* Brute force over every E4M3 block scale ([FMT] section 4: the worked
+ * block [0.4 x 15, 3.6] at a = 1, where the max-based 0.625 loses to 0.875,
+ * found by trying every legal E4M3 scale).  Per block with amax > 0, every
+ * code 1..126 whose alpha = RN32(s_g * E4M3(code)) is nonzero is a
+ * candidate; the loss is or_block_loss_f32; the winner is the smallest code
+ * with the least loss.  A zero block takes 0x38.  Outputs as
+ * or_scale_search. */
+int or_scale_search_all(const void *x, int dt, int64_t n, float s_g, uint8_t *packed,
+                        uint8_t *scales, float *best_loss) {
+    int flags = 0;
+    float xb[16];
+    uint8_t codes[16];
+    for (int64_t b = 0; b < n / 16; ++b) {
+        double amax = 0.0;
+        for (int i = 0; i < 16; ++i) {
+            xb[i] = load_elem(x, dt, b * 16 + i);
+            if (!isfinite(xb[i])) flags |= OR_FLAG_NONFINITE;
+            else if (fabs((double)xb[i]) > amax) amax = fabs((double)xb[i]);
+        }
+        int win = -1;
+        float winloss = 0.0f;
+        if (amax == 0.0) {
+            win = 0x38;
+        } else {
+            for (int code = 1; code <= 126; ++code) {
                 float alpha = nv_alpha(s_g, code);
                 if (alpha == 0.0f) continue;
                 float L = or_block_loss_f32(xb, alpha);

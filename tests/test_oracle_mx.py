@@ -124,3 +124,120 @@ def test_dequant_is_exact_and_bf16_matches_torch_rounding():
     tb = torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(yb, tb)
     assert np.isnan(oracle.dequantize(oracle.MX, p[:16], np.array([255], np.uint8))).all()
+
+
+# ---- encoder variants ("NVFP4 / MXFP4 format" page, section 5) ---------------
+
+def test_ceil_rule_amax_7_gives_scale_2():
+    amax, scale, reach = map(float, keyed("mx_examples.txt")["ceil_rule"][0])
+    packed, scales, flags = oracle.mx_quantize_rule(_block_with([amax]), "ceil")
+    assert flags == 0
+    assert 2.0 ** (int(scales[0]) - 127) == scale
+    assert 6 * scale == reach
+    # 7 / 2 = 3.5 is the midpoint of 3 and 4: the even code (4) reconstructs 8
+    y = oracle.dequantize(oracle.MX, packed, scales)
+    assert y[0] == 8.0
+
+
+def _ceil_exponent_exact(amax: float) -> int:
+    """Smallest e with 6 * 2^e >= amax, by exact rationals, clamped at -127."""
+    a = Fraction(amax)
+    e = 0
+    while Fraction(6) * Fraction(2) ** e < a:
+        e += 1
+    while Fraction(6) * Fraction(2) ** (e - 1) >= a:
+        e -= 1
+    return max(e, -127)
+
+
+def test_ceil_rule_exponent_is_the_smallest_power_covering_amax_over_6():
+    rng = np.random.default_rng(21)
+    cases = [6.0, 6.0 * (1 + 2 ** -23), 1.5, 1.5 * (1 + 2 ** -23), 3.0, 12.0, 4.0, 2.0 ** -126,
+             1e-45, 3e38, 0.75 * 2.0 ** -120]
+    cases += list((rng.uniform(1, 2, 300) * 2.0 ** rng.integers(-140, 120, 300)).astype(np.float32))
+    for a in cases:
+        a = float(np.float32(a))
+        assert oracle.mx_exponent_ceil(a) == _ceil_exponent_exact(a), a
+
+
+def test_ceil_rule_never_saturates_and_lands_the_max_in_3_to_6():
+    g = torch.Generator().manual_seed(22)
+    x = (torch.randn(64, 32, generator=g) * 2.0 ** torch.randint(-20, 20, (64, 1), generator=g))
+    x = x.numpy().astype(np.float32)
+    packed, scales, flags = oracle.mx_quantize_rule(x.reshape(-1), "ceil")
+    assert flags == 0
+    codes = oracle.unpack(packed).reshape(64, 32)
+    for b in range(64):
+        e = int(scales[b]) - 127
+        q = x[b].astype(np.float64) / 2.0 ** e
+        assert np.abs(q).max() <= 6.0 and np.abs(q).max() > 3.0
+        # the block maximum's magnitude code is 5, 6 or 7 (3, 4 or 6)
+        i = int(np.argmax(np.abs(x[b])))
+        assert (codes[b, i] & 7) in (5, 6, 7)
+    # and it never picks a smaller exponent than the floor rule
+    _, s_floor, _ = oracle.mx_quantize(x.reshape(-1))
+    assert np.all(scales.astype(int) >= s_floor.astype(int))
+    assert np.all(scales.astype(int) - s_floor.astype(int) <= 1)
+
+
+def _exact_sse32(block, e) -> Fraction:
+    """Exact sum of squared errors of a 32-block at scale 2^e."""
+    tot = Fraction(0)
+    s = Fraction(2) ** e
+    for v in block:
+        c = _exact.e2m1_code_of_f32(_exact.rn32(Fraction(float(v)) / s))
+        tot += (Fraction(float(v)) - Fraction(float(oracle.e2m1_value(c))) * s) ** 2
+    return tot
+
+
+def test_mse_rule_hand_worked_blocks():
+    # [7.5, 0 x 31]: OCP e = 0 saturates 7.5 to 6 (loss 2.25); e = 1 sends
+    # 3.75 to 4, i.e. 8 (loss 0.25); e = -1 saturates at 3 (loss 20.25)
+    b = _block_with([7.5])
+    _, s, f = oracle.mx_quantize_rule(b, "mse")
+    assert f == 0 and int(s[0]) - 127 == 1
+    assert [float(_exact_sse32(b, e)) for e in (-1, 0, 1)] == [20.25, 2.25, 0.25]
+    # [4, 0.2 x 31]: at e = 0 every 0.2 rounds to 0 (loss 31 * 0.04); at
+    # e = -1 they become 0.25 each (0.4 -> 0.5) and 4 saturates to 3
+    b = _block_with([4.0], fill=0.2)
+    _, s, _ = oracle.mx_quantize_rule(b, "mse")
+    assert int(s[0]) - 127 == -1
+    l = [_exact_sse32(b, e) for e in (-1, 0, 1)]
+    assert l[0] < l[1] and l[0] < l[2]
+    # [7, 0 x 31]: e = 0 (7 -> 6) and e = 1 (3.5 -> 4, i.e. 8) both lose 1:
+    # the OCP exponent stays
+    b = _block_with([7.0])
+    _, s, _ = oracle.mx_quantize_rule(b, "mse")
+    assert int(s[0]) - 127 == 0
+    assert _exact_sse32(b, 0) == _exact_sse32(b, 1) == 1
+
+
+def test_mse_rule_loss_is_the_fp32_pairwise_sum_within_its_error_bound():
+    g = torch.Generator().manual_seed(23)
+    x = (torch.randn(20, 32, generator=g) * 3).numpy().astype(np.float32)
+    for b in x:
+        for e in (-1, 0, 1, 2):
+            exact = _exact_sse32(b, e)
+            got = Fraction(oracle.mx_block_loss32(b, e))
+            # 32 squared terms and 31 additions, each one rounding of 2^-24
+            assert abs(got - exact) <= exact * Fraction(70, 2 ** 24) + Fraction(1, 2 ** 140)
+
+
+def test_mse_rule_never_worse_than_ocp_and_stays_within_one_exponent():
+    g = torch.Generator().manual_seed(24)
+    x = torch.randn(256, 32, generator=g) * torch.rand(256, 32, generator=g) ** 3
+    x = x.numpy().astype(np.float32)
+    _, s_mse, f = oracle.mx_quantize_rule(x.reshape(-1), "mse")
+    _, s_ocp, _ = oracle.mx_quantize(x.reshape(-1))
+    assert f == 0
+    d = s_mse.astype(int) - s_ocp.astype(int)
+    assert set(np.unique(d)) <= {-1, 0, 1} and (d != 0).any()
+    for b in range(256):
+        e0, e = int(s_ocp[b]) - 127, int(s_mse[b]) - 127
+        L = {k: oracle.mx_block_loss32(x[b], k) for k in (e0 - 1, e0, e0 + 1)}
+        assert L[e] == min(L.values())
+        assert e == e0 or L[e] < L[e0]
+    # the rule "ocp" reproduces the floor-rule encoder exactly
+    p1, s1, _ = oracle.mx_quantize_rule(x.reshape(-1), "ocp")
+    p2, s2, _ = oracle.mx_quantize(x.reshape(-1))
+    assert np.array_equal(p1, p2) and np.array_equal(s1, s2)

@@ -135,3 +135,59 @@ def test_equal_losses_go_to_the_smallest_candidate():
     p, sc, s_g, flags = oracle.scale_search(x, ncand=64, c_lo=0.5, c_hi=1.5)
     assert flags == 0 and oracle.e4m3_value(int(sc[1])) == 0.625
     assert oracle.block_loss(block, 0.9375) == 0.0 and oracle.block_loss(block, 0.625) == 0.0
+
+
+# ---- brute force over every E4M3 code, and the wider range ------------------
+
+def test_brute_force_search_finds_the_pages_better_scale():
+    v, n, big = G["counter"][0]
+    block = np.asarray([float(v)] * int(n) + [float(big)], np.float32)
+    x = np.concatenate([np.full(16, 2688.0, np.float32), block])
+    packed, scales, s_g, flags = oracle.scale_search_all(x)
+    assert flags == 0 and s_g == 1.0
+    sc2, num2, den2 = G["counter_better"][0]
+    assert oracle.e4m3_value(int(scales[1])) == float(sc2)
+    _, _, _, loss = oracle.scale_search_all_with_scale(block, 1.0, want_loss=True)
+    assert float(loss[0]) / 16 == pytest.approx(int(num2) / int(den2), rel=1e-6)
+
+
+def test_brute_force_winner_has_the_least_exact_loss():
+    g = torch.Generator().manual_seed(31)
+    x = (torch.randn(6 * 16, generator=g) * torch.rand(6 * 16, generator=g)).numpy().astype(np.float32)
+    s_g = np.float32(0.01)
+    _, scales, flags, loss = oracle.scale_search_all_with_scale(x, s_g, want_loss=True)
+    assert flags == 0
+    for b in range(6):
+        blk = x[16 * b: 16 * b + 16]
+        exact = {c: _exact_mse(blk, np.float32(s_g * np.float32(oracle.e4m3_value(c))))
+                 for c in range(1, 127)}
+        best = min(exact.values())
+        w = int(scales[b])
+        # the fp32 loss may reorder candidates whose exact losses differ by
+        # less than its rounding error; none does by more
+        assert exact[w] <= best * (1 + Fraction(80, 2 ** 24))
+
+
+def test_brute_force_never_worse_than_the_range_searches():
+    x = _blocks(32, 128)
+    s_g = np.float32(np.abs(x).max() / 2688)
+    _, s_all, f, l_all = oracle.scale_search_all_with_scale(x, s_g, want_loss=True)
+    for lo, hi in [(0.5, 1.0), (0.5, 1.5)]:
+        _, s_r, f_r, l_r = oracle.scale_search_with_scale(x, s_g, c_lo=lo, c_hi=hi, want_loss=True)
+        assert f == 0 and f_r == 0
+        assert np.all(l_all <= l_r)
+
+
+def test_wider_range_maps_the_max_to_4_for_the_pages_block():
+    gold = keyed("scale_choice_examples.txt")
+    vals = [float(v) for v in gold["four_over_six"][0]]
+    want_scale = float(gold["four_over_six_scale"][0][0])
+    block = np.asarray(vals * 4, np.float32)
+    packed, scales, flags, loss = oracle.scale_search_with_scale(block, 1.0, c_lo=0.5, c_hi=1.5,
+                                                                 want_loss=True)
+    assert flags == 0 and oracle.e4m3_value(int(scales[0])) == want_scale and loss[0] == 0.0
+    y = oracle.dequantize(oracle.NV, packed, scales, 1.0)
+    assert np.array_equal(y, block)
+    # the default range c in [0.5, 1] cannot reach amax / 4
+    _, s2, _, l2 = oracle.scale_search_with_scale(block, 1.0, want_loss=True)
+    assert oracle.e4m3_value(int(s2[0])) < want_scale and l2[0] > 0.0
