@@ -42,6 +42,7 @@ import os
 import sys
 import time
 
+import numpy as np
 import torch
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -211,18 +212,35 @@ class RoundTrip:
 
 
 def cpu_baseline(x_cpu: torch.Tensor, step_bytes: int):
-    """The oracle (plain C, one thread) on one full step of the same input."""
+    """The oracle (plain C) on one full step of the same input, its rows split
+    over the host's threads (at most 16); the C calls release the GIL.  The
+    NVFP4 tensor scale is the largest of the slices' (it is monotone in the
+    amax)."""
     import oracle
-    xo = workloads.bf16_bits(x_cpu).reshape(-1)
+    from concurrent.futures import ThreadPoolExecutor
+    xo = workloads.bf16_bits(x_cpu).reshape(x_cpu.shape[0], -1)
+    nt = max(1, min(16, len(os.sched_getaffinity(0))))
+    parts = [p.reshape(-1) for p in np.array_split(xo, nt) if p.size]
     t0 = time.perf_counter()
-    p, s, sg, f = oracle.nv_quantize(xo)
-    oracle.dequantize(oracle.NV, p, s, sg, out_bf16=True)
-    p, s, f = oracle.mx_quantize(xo)
-    oracle.dequantize(oracle.MX, p, s, out_bf16=True)
+    with ThreadPoolExecutor(nt) as pool:
+        sgs = list(pool.map(oracle.nv_global_scale, parts))
+        sg = max(v for v, _ in sgs)
+
+        def nv(part):
+            p, s, _ = oracle.nv_quantize_with_scale(part, sg)
+            oracle.dequantize(oracle.NV, p, s, sg, out_bf16=True)
+
+        def mx(part):
+            p, s, _ = oracle.mx_quantize(part)
+            oracle.dequantize(oracle.MX, p, s, out_bf16=True)
+        list(pool.map(nv, parts))
+        list(pool.map(mx, parts))
     dt = time.perf_counter() - t0
-    return {"value": round(step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": round(step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": len(parts),
+            "kind": "oracle",
             "sample": f"one full step (NVFP4 + MXFP4 quantize and dequantize) of the "
-                      f"{x_cpu.shape[0]}x{x_cpu.shape[1]} bf16 input; {dt:.2f} s wall"}
+                      f"{x_cpu.shape[0]}x{x_cpu.shape[1]} bf16 input, rows split over "
+                      f"{len(parts)} threads; {dt:.2f} s wall"}
 
 
 def _rate(b: int, ms: float, elements: int = None):
@@ -268,7 +286,32 @@ def extra_workloads():
     d = _rate(quantize_bytes(xs_cpu.numel(), 2, "nv"), ms, xs_cpu.numel())
     d["candidate_element_evals_per_s"] = f"{xs_cpu.numel() * 64 / ms / 1e-3:.3e}"
     out["nvfp4_scale_search_4096x14336_bf16"] = d
+    # the same search over c in [0.5, 1.5] (amax may map to 4), and over every
+    # E4M3 code
+    ms = time_rotating([lambda x=x, r=r: fp4.scale_search(x, 64, 0.5, 1.5, check=False, out=r,
+                                                          status=st, workspace=ws)
+                        for x, r in zip(xs, res)], launches=6)
+    out["nvfp4_scale_search_c0.5-1.5_4096x14336_bf16"] = _rate(
+        quantize_bytes(xs_cpu.numel(), 2, "nv"), ms, xs_cpu.numel())
+    ms = time_rotating([lambda x=x, r=r: fp4.scale_search_exhaustive(x, check=False, out=r,
+                                                                     status=st, workspace=ws)
+                        for x, r in zip(xs, res)], launches=3, reps=3)
+    d = _rate(quantize_bytes(xs_cpu.numel(), 2, "nv"), ms, xs_cpu.numel())
+    d["candidate_element_evals_per_s"] = f"{xs_cpu.numel() * 126 / ms / 1e-3:.3e}"
+    out["nvfp4_scale_search_all_codes_4096x14336_bf16"] = d
     del xs, res
+    # MXFP4 quantize of the 8192 x 8192 weight under the ceil rule and the
+    # three-exponent squared-error search
+    xw_cpu = workloads.nvfp4_weight()
+    xs = [xw_cpu.cuda() for _ in range(3)]
+    outs = [fp4.quantize_mxfp4(x) for x in xs]
+    for rule in ("ceil", "mse"):
+        ms = time_rotating([lambda x=x, o=o, rule=rule: fp4.quantize_mxfp4_rule(x, rule, check=False, out=o,
+                                                                    status=st)
+                            for x, o in zip(xs, outs)])
+        out[f"mxfp4_quantize_rule_{rule}_8192x8192_bf16"] = _rate(
+            quantize_bytes(xw_cpu.numel(), 2, "mx"), ms, xw_cpu.numel())
+    del xs, outs
     # MXFP4 GEMM 128 x 8192 x 8192: operands quantized on the GPU; eight
     # copies of B (36 MB each) rotate so B comes from HBM
     M, N, K = 128, 8192, 8192

@@ -64,6 +64,7 @@ typedef enum {
 
 typedef enum { FP4_F32 = 0, FP4_BF16 = 1 } fp4_dtype;
 typedef enum { FP4_MXFP4 = 0, FP4_NVFP4 = 1 } fp4_format;
+typedef enum { FP4_MX_RULE_OCP = 0, FP4_MX_RULE_CEIL = 1, FP4_MX_RULE_MSE = 2 } fp4_mx_rule;
 
 /*
  * MXFP4 quantize ("NVFP4 / MXFP4 format" page, sections 1, 2 and 5).
@@ -77,6 +78,27 @@ typedef enum { FP4_MXFP4 = 0, FP4_NVFP4 = 1 } fp4_format;
 fp4_status fp4_quantize_mxfp4(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
                               int32_t block, uint8_t *codes, uint8_t *scales,
                               int32_t *status, void *stream);
+
+/*
+ * MXFP4 quantize with another rule for the block exponent ("NVFP4 / MXFP4
+ * format" page, section 5: the format fixes the set of E8M0 scales, not how a
+ * block picks one).  Element rounding is the same as fp4_quantize_mxfp4.
+ *   rule  FP4_MX_RULE_OCP   e = floor(log2 amax) - 2 (as fp4_quantize_mxfp4);
+ *         FP4_MX_RULE_CEIL  the section's ModelOpt rule, scale
+ *                           2^ceil(log2(amax / 6)): the smallest e with
+ *                           6 * 2^e >= amax, so nothing saturates;
+ *         FP4_MX_RULE_MSE   the squared error of the block, an fp32 sum taken
+ *                           pairwise in index order, evaluated at e0 - 1, e0
+ *                           and e0 + 1 around the floor rule's e0; e0 stays
+ *                           unless a neighbour is strictly better, e0 - 1 is
+ *                           tried first.
+ *         In every rule e is clamped at -127 and a zero block takes e = 0.
+ *   Other arguments, errors and status as for fp4_quantize_mxfp4 (FP4_E_ARG
+ *   also for an unknown rule).  One pass over x.  Deterministic.
+ */
+fp4_status fp4_quantize_mxfp4_rule(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
+                                   int32_t block, fp4_mx_rule rule, uint8_t *codes,
+                                   uint8_t *scales, int32_t *status, void *stream);
 
 /*
  * NVFP4 quantize ("NVFP4 / MXFP4 format" page, section 3, two-level scale
@@ -141,6 +163,19 @@ fp4_status fp4_scale_search(const void *x, fp4_dtype xt, int64_t rows, int64_t c
                             uint8_t *codes, uint8_t *scales, float *global_scale,
                             void *workspace, size_t workspace_bytes, int32_t *status,
                             void *stream);
+
+/*
+ * Brute-force NVFP4 block-scale search ("NVFP4 / MXFP4 format" page, section
+ * 4: every legal E4M3 scale tried on the block [0.4 x 15, 3.6], where 0.875
+ * beats the max-based 0.625).  As fp4_scale_search, except that the
+ * candidates of a block with amax > 0 are all E4M3 codes 1..126 whose alpha
+ * is nonzero; the winner is the smallest code with the least loss.  About 14
+ * times the candidate evaluations of the 64-candidate search.  Deterministic.
+ */
+fp4_status fp4_scale_search_exhaustive(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
+                                       int32_t block, uint8_t *codes, uint8_t *scales,
+                                       float *global_scale, void *workspace,
+                                       size_t workspace_bytes, int32_t *status, void *stream);
 
 /*
  * MXFP4 x MXFP4 block-scaled GEMM ("FP4, FP8 and INT8/INT4" page,

@@ -40,8 +40,12 @@ FLAG_NONFINITE = 1
 FLAG_SCALE_UNDERFLOW = 2
 FLAG_BARRIER_TIMEOUT = 4
 
-EXPORTS = ("fp4_quantize_mxfp4", "fp4_quantize_nvfp4", "fp4_dequantize", "fp4_scale_search",
+EXPORTS = ("fp4_quantize_mxfp4", "fp4_quantize_mxfp4_rule", "fp4_quantize_nvfp4",
+           "fp4_dequantize", "fp4_scale_search", "fp4_scale_search_exhaustive",
            "fp4_gemm_mxfp4", "fp4_workspace_bytes", "fp4_status_str")
+
+# fp4_mx_rule: the MXFP4 block-exponent rules
+MX_RULES = {"ocp": 0, "ceil": 1, "mse": 2}
 
 _lib = None
 
@@ -62,6 +66,8 @@ def lib() -> ctypes.CDLL:
                          ctypes.c_size_t)
     I = ctypes.c_int
     L.fp4_quantize_mxfp4.argtypes = [P, I, I64, I64, I32, P, P, P, P]
+    L.fp4_quantize_mxfp4_rule.argtypes = [P, I, I64, I64, I32, I, P, P, P, P]
+    L.fp4_scale_search_exhaustive.argtypes = [P, I, I64, I64, I32, P, P, P, P, S, P, P]
     L.fp4_quantize_nvfp4.argtypes = [P, I, I64, I64, I32, P, P, P, P, S, P, P]
     L.fp4_dequantize.argtypes = [I, P, P, P, I64, I64, I32, P, I, P]
     L.fp4_scale_search.argtypes = [P, I, I64, I64, I32, I32, F, F, P, P, P, P, S, P, P]
@@ -70,8 +76,9 @@ def lib() -> ctypes.CDLL:
     L.fp4_workspace_bytes.restype = S
     L.fp4_status_str.argtypes = [I]
     L.fp4_status_str.restype = ctypes.c_char_p
-    for name in ("fp4_quantize_mxfp4", "fp4_quantize_nvfp4", "fp4_dequantize",
-                 "fp4_scale_search", "fp4_gemm_mxfp4"):
+    for name in ("fp4_quantize_mxfp4", "fp4_quantize_mxfp4_rule", "fp4_quantize_nvfp4",
+                 "fp4_dequantize", "fp4_scale_search", "fp4_scale_search_exhaustive",
+                 "fp4_gemm_mxfp4"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -153,6 +160,26 @@ def quantize_mxfp4(x: torch.Tensor, check: bool = True, out=None, status=None):
     return codes, scales
 
 
+def quantize_mxfp4_rule(x: torch.Tensor, rule: str = "ocp", check: bool = True, out=None,
+                       status=None):
+    """MXFP4 quantize with block-exponent rule "ocp" (floor), "ceil" or "mse"."""
+    rows, cols = _rows_cols(x)
+    if rule not in MX_RULES:
+        raise ValueError(f"unknown MX rule {rule!r}; one of {sorted(MX_RULES)}")
+    if out is None:
+        codes = torch.empty(*x.shape[:-1], cols // 2, dtype=torch.uint8, device=x.device)
+        scales = torch.empty(*x.shape[:-1], max(cols // 32, 1), dtype=torch.uint8, device=x.device)
+    else:
+        codes, scales = out
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _ok(lib().fp4_quantize_mxfp4_rule(_ptr(x), _dtype_code(x.dtype), rows, cols, 32,
+                                      MX_RULES[rule], _ptr(codes), _ptr(scales), _ptr(status),
+                                      _stream(x)))
+    _finish(status, check)
+    return codes, scales
+
+
 def quantize_nvfp4(x: torch.Tensor, check: bool = True, out=None, status=None, workspace=None):
     rows, cols = _rows_cols(x)
     if out is None:
@@ -200,6 +227,27 @@ def scale_search(x: torch.Tensor, n_candidates: int = 64, c_lo: float = 0.5, c_h
     _ok(lib().fp4_scale_search(_ptr(x), _dtype_code(x.dtype), rows, cols, 16, int(n_candidates),
                                float(c_lo), float(c_hi), _ptr(codes), _ptr(scales), _ptr(s_g),
                                _ptr(workspace), workspace.numel(), _ptr(status), _stream(x)))
+    _finish(status, check)
+    return codes, scales, s_g
+
+
+def scale_search_exhaustive(x: torch.Tensor, check: bool = True, out=None, status=None,
+                            workspace=None):
+    """NVFP4 scale search over every E4M3 code."""
+    rows, cols = _rows_cols(x)
+    if out is None:
+        codes = torch.empty(*x.shape[:-1], cols // 2, dtype=torch.uint8, device=x.device)
+        scales = torch.empty(*x.shape[:-1], max(cols // 16, 1), dtype=torch.uint8, device=x.device)
+        s_g = torch.empty(1, dtype=torch.float32, device=x.device)
+    else:
+        codes, scales, s_g = out
+    if workspace is None:
+        workspace = new_workspace(rows, cols, x.device)
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _ok(lib().fp4_scale_search_exhaustive(_ptr(x), _dtype_code(x.dtype), rows, cols, 16,
+                                          _ptr(codes), _ptr(scales), _ptr(s_g), _ptr(workspace),
+                                          workspace.numel(), _ptr(status), _stream(x)))
     _finish(status, check)
     return codes, scales, s_g
 

@@ -39,8 +39,23 @@ fp4_status fp4_quantize_mxfp4(const void *x, fp4_dtype xt, int64_t rows, int64_t
     fp4_status st = check_shape(rows, cols, block);
     if (st != FP4_OK) return st;
     if (!aligned(x, 16) || !aligned(codes, 4) || !aligned(status, 4)) return FP4_E_ALIGN;
-    return from_hip(fp4dev::launch_mx_quantize(x, xt == FP4_BF16, rows * cols, codes, scales,
+    return from_hip(fp4dev::launch_mx_quantize(x, xt == FP4_BF16, rows * cols, 0, codes, scales,
                                                status, (hipStream_t)stream));
+}
+
+fp4_status fp4_quantize_mxfp4_rule(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
+                                   int32_t block, fp4_mx_rule rule, uint8_t *codes,
+                                   uint8_t *scales, int32_t *status, void *stream) {
+    if (!x || !codes || !scales) return FP4_E_ARG;
+    if (block != 32) return FP4_E_ARG;
+    if (rule != FP4_MX_RULE_OCP && rule != FP4_MX_RULE_CEIL && rule != FP4_MX_RULE_MSE)
+        return FP4_E_ARG;
+    if (!valid_dtype(xt)) return FP4_E_DTYPE;
+    fp4_status st = check_shape(rows, cols, block);
+    if (st != FP4_OK) return st;
+    if (!aligned(x, 16) || !aligned(codes, 4) || !aligned(status, 4)) return FP4_E_ALIGN;
+    return from_hip(fp4dev::launch_mx_quantize(x, xt == FP4_BF16, rows * cols, (int)rule, codes,
+                                               scales, status, (hipStream_t)stream));
 }
 
 fp4_status fp4_quantize_nvfp4(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
@@ -98,9 +113,27 @@ fp4_status fp4_scale_search(const void *x, fp4_dtype xt, int64_t rows, int64_t c
     if (!aligned(x, 16) || !aligned(codes, 4) || !aligned(global_scale, 4) ||
         !aligned(workspace, 16) || !aligned(status, 4))
         return FP4_E_ALIGN;
-    return from_hip(fp4dev::launch_scale_search(x, xt == FP4_BF16, rows * cols, c_lo, c_hi,
-                                                codes, scales, global_scale, workspace,
+    return from_hip(fp4dev::launch_scale_search(x, xt == FP4_BF16, rows * cols, false, c_lo,
+                                                c_hi, codes, scales, global_scale, workspace,
                                                 status, (hipStream_t)stream));
+}
+
+fp4_status fp4_scale_search_exhaustive(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
+                                       int32_t block, uint8_t *codes, uint8_t *scales,
+                                       float *global_scale, void *workspace,
+                                       size_t workspace_bytes, int32_t *status, void *stream) {
+    if (!x || !codes || !scales || !global_scale) return FP4_E_ARG;
+    if (block != 16) return FP4_E_ARG;
+    if (!valid_dtype(xt)) return FP4_E_DTYPE;
+    fp4_status st = check_shape(rows, cols, block);
+    if (st != FP4_OK) return st;
+    if (!workspace || workspace_bytes < nv_workspace()) return FP4_E_WORKSPACE;
+    if (!aligned(x, 16) || !aligned(codes, 4) || !aligned(global_scale, 4) ||
+        !aligned(workspace, 16) || !aligned(status, 4))
+        return FP4_E_ALIGN;
+    return from_hip(fp4dev::launch_scale_search(x, xt == FP4_BF16, rows * cols, true, 0.0f, 0.0f,
+                                                codes, scales, global_scale, workspace, status,
+                                                (hipStream_t)stream));
 }
 
 fp4_status fp4_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales,

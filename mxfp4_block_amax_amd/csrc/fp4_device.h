@@ -136,6 +136,19 @@ __device__ __forceinline__ uint32_t mx_scale_byte(uint32_t amax_bits, int exp_sh
     return E > 2u ? E - 2u : 0u;
 }
 
+// Ceil rule (format page, section 5, the ModelOpt packed path): the smallest
+// e with 6 * 2^e >= amax, clamped at -127.  For a normal amax = m 2^(E-127),
+// m in [1, 2): e = E - 127 - 2 + [m > 1.5], since 6 * 2^(E-129) = 1.5 * 2^(E-127);
+// a subnormal amax gives e <= -128, clamped; a zero block takes byte 127.
+__device__ __forceinline__ uint32_t mx_scale_byte_ceil(uint32_t amax_bits, int exp_shift) {
+    if (amax_bits == 0) return E8M0_ONE;
+    const uint32_t E = amax_bits >> exp_shift;
+    if (E == 0) return 0u;
+    const uint32_t frac = amax_bits & ((1u << exp_shift) - 1u);
+    const int b = (int)E - 2 + (frac > (1u << (exp_shift - 1)) ? 1 : 0);
+    return b > 0 ? (uint32_t)b : 0u;
+}
+
 // ---- E4M3FN block scales --------------------------------------------------
 // Value of a non-negative finite code c in [0, 126].
 __device__ __forceinline__ float e4m3_pos_value(uint32_t c) {

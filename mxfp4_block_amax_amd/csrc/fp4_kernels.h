@@ -24,13 +24,15 @@ constexpr size_t kNvWorkspaceBytes = kResidentSlotsOffset + kResidentSlots * siz
 constexpr uint32_t kResidentSpinLimit = 1u << 19;
 constexpr int kMaxDevices = 64;
 
-hipError_t launch_mx_quantize(const void *x, bool bf16, int64_t n, uint8_t *codes,
+// rule: 0 the OCP floor rule, 1 the ceil rule, 2 the three-exponent search
+hipError_t launch_mx_quantize(const void *x, bool bf16, int64_t n, int rule, uint8_t *codes,
                               uint8_t *scales, int32_t *status, hipStream_t s);
 hipError_t launch_nv_quantize(const void *x, bool bf16, int64_t n, uint8_t *codes,
                               uint8_t *scales, float *global_scale, void *workspace,
                               int32_t *status, hipStream_t s);
-hipError_t launch_scale_search(const void *x, bool bf16, int64_t n, float c_lo, float c_hi,
-                               uint8_t *codes, uint8_t *scales, float *global_scale,
+// all: every E4M3 code is a candidate (c_lo and c_hi unused)
+hipError_t launch_scale_search(const void *x, bool bf16, int64_t n, bool all, float c_lo,
+                               float c_hi, uint8_t *codes, uint8_t *scales, float *global_scale,
                                void *workspace, int32_t *status, hipStream_t s);
 hipError_t launch_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales,
                              const float *global_scale, int64_t n, void *y, bool out_bf16,

@@ -73,9 +73,48 @@ __device__ __forceinline__ void chunk_values(const Chunk<BF16> &k, float (&v)[8]
 }
 
 // ---------------------------------------------------------------------------
-// MXFP4 quantize: one pass.
+// MXFP4 quantize: one pass.  RULE picks the block exponent (format page,
+// section 5: the format fixes the scale set, not the rule):
+//   0  the OCP floor rule, e = floor(log2 amax) - 2;
+//   1  the ceil rule, the smallest e with 6 * 2^e >= amax;
+//   2  a squared-error search over e0 - 1, e0, e0 + 1 around the floor
+//      rule's e0: e0 stays unless a neighbour has a strictly smaller fp32
+//      loss (e0 - 1 tried first); exponents below -127 are not candidates.
 // ---------------------------------------------------------------------------
-template <bool BF16>
+
+// Codes of this lane's 8 values at E8M0 scale byte sb, and their squared
+// error summed pairwise in index order: q = x / 2^e rounded to E2M1 by the
+// converter, x_hat = E2M1(q) 2^e exactly, err = RN32(x - x_hat).
+struct MxTry {
+    uint32_t code;
+    float loss;
+};
+__device__ __forceinline__ MxTry mx_try(const float (&v)[8], uint32_t sb) {
+    const float so = e8m0_operand(sb);
+    MxTry r;
+    r.code = cvt_fp4x8_f32(v, so);
+    float t[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f32x2_t p;
+        switch (j) {  // the byte selector must be a constant
+            case 0: p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.code, so, 0); break;
+            case 1: p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.code, so, 1); break;
+            case 2: p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.code, so, 2); break;
+            default: p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.code, so, 3); break;
+        }
+        const float e0 = v[2 * j] - p.x, e1 = v[2 * j + 1] - p.y;
+        t[2 * j] = e0 * e0;
+        t[2 * j + 1] = e1 * e1;
+    }
+    const float part = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+    // the block's four lanes: (L0 + L1) + (L2 + L3), the pairwise tree over 32
+    const float pair = part + dppf<QP_XOR1>(part);
+    r.loss = pair + dppf<QP_XOR2>(pair);
+    return r;
+}
+
+template <bool BF16, int RULE>
 __global__ __launch_bounds__(WG) void mx_quantize_kernel(const uint4 *__restrict__ x,
                                                          int64_t nchunks,
                                                          uint32_t *__restrict__ codes,
@@ -102,15 +141,33 @@ __global__ __launch_bounds__(WG) void mx_quantize_kernel(const uint4 *__restrict
             m = max(m, dpp<QP_XOR2>(m));
             const int sh = BF16 ? 7 : 23;
             if ((m >> sh) >= 0xFFu) flags |= FLAG_NONFINITE;
-            uint32_t sb = mx_scale_byte(m, sh);
-            float so = e8m0_operand(sb);
+            uint32_t sb = RULE == 1 ? mx_scale_byte_ceil(m, sh) : mx_scale_byte(m, sh);
             uint32_t q;
-            if (BF16) {
-                q = cvt_fp4x8_bf16(k[r].lo, so);
+            if (RULE == 2) {
+                float v[8];
+                chunk_values<BF16>(k[r], v);
+                const MxTry t0 = mx_try(v, sb);
+                const MxTry tp = mx_try(v, sb + 1u);
+                const MxTry tm = mx_try(v, sb > 0u ? sb - 1u : sb);
+                q = t0.code;
+                float best = t0.loss;
+                uint32_t nb = sb;
+                if (sb > 0u && tm.loss < best) {
+                    best = tm.loss;
+                    q = tm.code;
+                    nb = sb - 1u;
+                }
+                if (tp.loss < best) {
+                    q = tp.code;
+                    nb = sb + 1u;
+                }
+                sb = nb;
+            } else if (BF16) {
+                q = cvt_fp4x8_bf16(k[r].lo, e8m0_operand(sb));
             } else {
                 float v[8];
                 chunk_values<BF16>(k[r], v);
-                q = cvt_fp4x8_f32(v, so);
+                q = cvt_fp4x8_f32(v, e8m0_operand(sb));
             }
             if (c < nchunks) {
                 codes[c] = q;
@@ -738,7 +795,9 @@ __device__ __forceinline__ float half_block_loss(const float (&a)[8], float4 sq)
     return ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
 }
 
-template <bool BF16>
+// ALL: every E4M3 code 1..126 is a candidate (the format page's brute force,
+// section 4), instead of the codes the candidate range c_lo..c_hi reaches.
+template <bool BF16, bool ALL>
 __global__ __launch_bounds__(WG) void scale_search_kernel(
     const uint4 *__restrict__ x, int64_t nchunks, const uint32_t *__restrict__ partials,
     int npart, float c_lo, float c_hi, uint32_t *__restrict__ codes,
@@ -771,8 +830,8 @@ __global__ __launch_bounds__(WG) void scale_search_kernel(
         uint32_t best = 0x38u;
         if (ag_bits != 0) {
             const double ag = (double)u2f(ag_bits);
-            uint32_t lo = nv_code_real(T, (double)c_lo * ag, inv6sg);
-            uint32_t hi = nv_code_real(T, (double)c_hi * ag, inv6sg);
+            uint32_t lo = ALL ? 1u : nv_code_real(T, (double)c_lo * ag, inv6sg);
+            const uint32_t hi = ALL ? 126u : nv_code_real(T, (double)c_hi * ag, inv6sg);
             lo = lo < 1u ? 1u : lo;
             float bestL = 0.0f;
             bool have = false;
@@ -812,16 +871,16 @@ static inline int grid_for(int64_t waves_needed, int max_wg) {
     return (int)(g < 1 ? 1 : g);
 }
 
-hipError_t launch_mx_quantize(const void *x, bool bf16, int64_t n, uint8_t *codes,
+hipError_t launch_mx_quantize(const void *x, bool bf16, int64_t n, int rule, uint8_t *codes,
                               uint8_t *scales, int32_t *status, hipStream_t s) {
     const int64_t nchunks = n / 8;
     const int g = grid_for((nchunks + WAVE * 4 - 1) / (WAVE * 4), kMaxGrid);
-    if (bf16)
-        hipLaunchKernelGGL(mx_quantize_kernel<true>, dim3(g), dim3(WG), 0, s, (const uint4 *)x,
-                           nchunks, (uint32_t *)codes, scales, status);
-    else
-        hipLaunchKernelGGL(mx_quantize_kernel<false>, dim3(g), dim3(WG), 0, s, (const uint4 *)x,
-                           nchunks, (uint32_t *)codes, scales, status);
+    using K = void (*)(const uint4 *, int64_t, uint32_t *, uint8_t *, int32_t *);
+    static const K kernels[2][3] = {
+        {mx_quantize_kernel<false, 0>, mx_quantize_kernel<false, 1>, mx_quantize_kernel<false, 2>},
+        {mx_quantize_kernel<true, 0>, mx_quantize_kernel<true, 1>, mx_quantize_kernel<true, 2>}};
+    hipLaunchKernelGGL(kernels[bf16 ? 1 : 0][rule], dim3(g), dim3(WG), 0, s, (const uint4 *)x,
+                       nchunks, (uint32_t *)codes, scales, status);
     return hipGetLastError();
 }
 
@@ -917,8 +976,8 @@ hipError_t launch_nv_quantize(const void *x, bool bf16, int64_t n, uint8_t *code
     return hipGetLastError();
 }
 
-hipError_t launch_scale_search(const void *x, bool bf16, int64_t n, float c_lo, float c_hi,
-                               uint8_t *codes, uint8_t *scales, float *global_scale,
+hipError_t launch_scale_search(const void *x, bool bf16, int64_t n, bool all, float c_lo,
+                               float c_hi, uint8_t *codes, uint8_t *scales, float *global_scale,
                                void *workspace, int32_t *status, hipStream_t s) {
     const int64_t nchunks = n / 8;
     uint32_t *partials = (uint32_t *)workspace;
@@ -926,14 +985,14 @@ hipError_t launch_scale_search(const void *x, bool bf16, int64_t n, float c_lo, 
     hipError_t e = launch_amax(x, bf16, nchunks, partials, g1, s);
     if (e != hipSuccess) return e;
     const int g = grid_for((nchunks + WAVE - 1) / WAVE, kMaxGrid);
-    if (bf16)
-        hipLaunchKernelGGL(scale_search_kernel<true>, dim3(g), dim3(WG), 0, s, (const uint4 *)x,
-                           nchunks, partials, g1, c_lo, c_hi, (uint32_t *)codes, scales,
-                           global_scale, status);
-    else
-        hipLaunchKernelGGL(scale_search_kernel<false>, dim3(g), dim3(WG), 0, s, (const uint4 *)x,
-                           nchunks, partials, g1, c_lo, c_hi, (uint32_t *)codes, scales,
-                           global_scale, status);
+    using K = void (*)(const uint4 *, int64_t, const uint32_t *, int, float, float, uint32_t *,
+                       uint8_t *, float *, int32_t *);
+    static const K kernels[2][2] = {
+        {scale_search_kernel<false, false>, scale_search_kernel<false, true>},
+        {scale_search_kernel<true, false>, scale_search_kernel<true, true>}};
+    hipLaunchKernelGGL(kernels[bf16 ? 1 : 0][all ? 1 : 0], dim3(g), dim3(WG), 0, s,
+                       (const uint4 *)x, nchunks, partials, g1, c_lo, c_hi, (uint32_t *)codes,
+                       scales, global_scale, status);
     return hipGetLastError();
 }
 

@@ -102,6 +102,33 @@ def test_search_validation():
     assert s(cols=24) == E_SHAPE
 
 
+def test_mx_rule_validation():
+    L = fp4.lib()
+
+    def r(rule=1, block=32, cols=64, x=A16, dt=fp4.BF16):
+        return L.fp4_quantize_mxfp4_rule(x, dt, 4, cols, block, rule, A16, A16, NULL, NULL)
+    assert r(rule=3) == E_ARG
+    assert r(rule=-1) == E_ARG
+    assert r(block=16) == E_ARG
+    assert r(x=NULL) == E_ARG
+    assert r(dt=9) == E_DTYPE
+    assert r(cols=48) == E_SHAPE
+    assert r(x=A1) == E_ALIGN
+
+
+def test_exhaustive_search_validation():
+    L = fp4.lib()
+
+    def s(block=16, cols=64, ws=A16, wsb=1 << 20, sg=A16):
+        return L.fp4_scale_search_exhaustive(A16, fp4.BF16, 4, cols, block, A16, A16, sg, ws, wsb,
+                                             NULL, NULL)
+    assert s(block=32) == E_ARG
+    assert s(sg=NULL) == E_ARG
+    assert s(cols=24) == E_SHAPE
+    assert s(ws=NULL) == E_WORKSPACE
+    assert s(wsb=8) == E_WORKSPACE
+
+
 def test_gemm_validation():
     L = fp4.lib()
 

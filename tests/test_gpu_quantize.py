@@ -85,9 +85,9 @@ def test_mx_every_bf16_value_at_every_exponent():
     check_mx(_mx_sweep_tensor(), "exhaustive bf16 x E8M0 sweep")
 
 
-def test_mx_fp32_every_midpoint_and_subnormal():
-    # fp32 values on and one ulp around every E2M1 decision point, at several
-    # block exponents, plus signed zeros and subnormals
+def _mx_fp32_midpoint_tensor() -> torch.Tensor:
+    """fp32 values on and one ulp around every E2M1 decision point, at several
+    block exponents, plus signed zeros and subnormals."""
     pts = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.0, 0.5, 1.0, 4.0], np.float32)
     rows = []
     for e in (-127, -126, -100, -3, 0, 5, 60, 125):
@@ -102,8 +102,11 @@ def test_mx_fp32_every_midpoint_and_subnormal():
         vals = np.concatenate([vals, np.zeros((-vals.size) % 31, np.float32)]).reshape(-1, 31)
         rows.append(np.concatenate([np.full((vals.shape[0], 1), anchor, np.float32), vals], 1))
     x = torch.from_numpy(np.concatenate(rows).reshape(-1))
-    x = x[: (x.numel() // 32) * 32].reshape(-1, 32)
-    check_mx(x, "fp32 midpoints")
+    return x[: (x.numel() // 32) * 32].reshape(-1, 32)
+
+
+def test_mx_fp32_every_midpoint_and_subnormal():
+    check_mx(_mx_fp32_midpoint_tensor(), "fp32 midpoints")
 
 
 # ---- adversarial NVFP4 ------------------------------------------------------
