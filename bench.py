@@ -324,6 +324,21 @@ def extra_workloads():
     tf = gemm_flops(M, N, K) / ms / 1e9
     d.update({"TFLOP/s": round(tf, 1), "pct_fp4_mfma_peak": round(100 * tf / FP4_DENSE_PEAK_TFLOPS, 2)})
     out["mxfp4_gemm_128x8192x8192_bf16out"] = d
+    # W4A4 linear: bf16 activations quantized in the GEMM's launch (grid
+    # barrier), against the two launches of quantize then GEMM
+    xa = a.to(torch.bfloat16).cuda()
+    ws = fp4.new_workspace(M, K, "cuda")
+    aq = (torch.empty(M, K // 2, dtype=torch.uint8, device="cuda"),
+          torch.empty(M, K // 32, dtype=torch.uint8, device="cuda"))
+    ms = time_rotating([lambda b=b: fp4.linear_mxfp4(xa, b[0], b[1], out=c, a_out=aq, status=st,
+                                                     workspace=ws, check=False) for b in bq])
+    lin_bytes = (M * K * 2 + M * K // 2 + M * K // 32 + N * K // 2 + N * K // 32 + M * N * 2)
+    d = _rate(lin_bytes, ms)
+    ms2 = time_rotating([lambda b=b: fp4.linear_mxfp4(xa, b[0], b[1], out=c, a_out=aq, status=st,
+                                                      workspace=ws, check=False, one_launch=False)
+                         for b in bq])
+    d["two_launches_us"] = round(ms2 * 1e3, 2)
+    out["mxfp4_linear_w4a4_128x8192x8192_bf16"] = d
     if int(st.item()) != 0:
         raise RuntimeError(f"a timed call raised status flags {int(st.item())}")
     return out

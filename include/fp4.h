@@ -65,6 +65,7 @@ typedef enum {
 typedef enum { FP4_F32 = 0, FP4_BF16 = 1 } fp4_dtype;
 typedef enum { FP4_MXFP4 = 0, FP4_NVFP4 = 1 } fp4_format;
 typedef enum { FP4_MX_RULE_OCP = 0, FP4_MX_RULE_CEIL = 1, FP4_MX_RULE_MSE = 2 } fp4_mx_rule;
+typedef enum { FP4_LINEAR_ONE_LAUNCH = 0, FP4_LINEAR_TWO_LAUNCHES = 1 } fp4_linear_mode;
 
 /*
  * MXFP4 quantize ("NVFP4 / MXFP4 format" page, sections 1, 2 and 5).
@@ -193,6 +194,39 @@ fp4_status fp4_scale_search_exhaustive(const void *x, fp4_dtype xt, int64_t rows
 fp4_status fp4_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales,
                           const uint8_t *bt_codes, const uint8_t *bt_scales, int64_t M,
                           int64_t N, int64_t K, void *c, fp4_dtype ct, void *stream);
+
+/*
+ * W4A4 linear layer: the activations quantized to MXFP4, then the MXFP4 GEMM
+ * ("FP4, FP8 and INT8/INT4" page, tom-jerr.github.io, section 5: the cost of
+ * a low-bit linear layer is the activation quantize plus the block-scaled
+ * MMA; "NVFP4 / MXFP4 format" page, section 6: blocks along K).
+ *   x          [M, K] fp32 or bf16 activations, 16-byte aligned
+ *   bt_codes, bt_scales   the MXFP4 weight Bt [N, K] as for fp4_gemm_mxfp4
+ *   a_codes    [M, K/2] bytes, a_scales [M, K/32]: receive x quantized exactly
+ *              as fp4_quantize_mxfp4 does (OCP floor rule); 16-byte aligned
+ *   c          [M, N] fp32 or bf16, the GEMM of a_codes with Bt
+ *   workspace  as for fp4_quantize_nvfp4 (fp4_workspace_bytes(FP4_NVFP4, M, K)
+ *              bytes, zero-filled before its first use, then left to the
+ *              library; calls sharing it must be stream-ordered)
+ *   status     FP4_FLAG_NONFINITE (x), FP4_FLAG_BARRIER_TIMEOUT (then zero
+ *              the workspace again)
+ *   mode       FP4_LINEAR_ONE_LAUNCH: when the GEMM's grid (ceil(N/32) *
+ *              ceil(M/128) workgroups) fits on the device at once and K is a
+ *              multiple of 512 up to 8192, one kernel quantizes x (each
+ *              workgroup a share), meets at a grid barrier and multiplies;
+ *              else, and under FP4_LINEAR_TWO_LAUNCHES, the two steps run as
+ *              two launches on the stream.  The barrier and the cache
+ *              write-back and invalidation around it cost more than a kernel
+ *              boundary inside a captured graph; one launch pays where each
+ *              launch is submitted on its own.
+ * K must be a multiple of 32.  Results are identical in both modes and match
+ * fp4_quantize_mxfp4 followed by fp4_gemm_mxfp4.  Deterministic.
+ */
+fp4_status fp4_linear_mxfp4(const void *x, fp4_dtype xt, int64_t M, int64_t K,
+                            const uint8_t *bt_codes, const uint8_t *bt_scales, int64_t N,
+                            uint8_t *a_codes, uint8_t *a_scales, void *c, fp4_dtype ct,
+                            fp4_linear_mode mode, void *workspace, size_t workspace_bytes,
+                            int32_t *status, void *stream);
 
 /* Bytes of device workspace fp4_quantize_nvfp4 / fp4_scale_search need for a
  * [rows, cols] input (0 for MXFP4). */

@@ -42,7 +42,7 @@ FLAG_BARRIER_TIMEOUT = 4
 
 EXPORTS = ("fp4_quantize_mxfp4", "fp4_quantize_mxfp4_rule", "fp4_quantize_nvfp4",
            "fp4_dequantize", "fp4_scale_search", "fp4_scale_search_exhaustive",
-           "fp4_gemm_mxfp4", "fp4_workspace_bytes", "fp4_status_str")
+           "fp4_gemm_mxfp4", "fp4_linear_mxfp4", "fp4_workspace_bytes", "fp4_status_str")
 
 # fp4_mx_rule: the MXFP4 block-exponent rules
 MX_RULES = {"ocp": 0, "ceil": 1, "mse": 2}
@@ -72,13 +72,14 @@ def lib() -> ctypes.CDLL:
     L.fp4_dequantize.argtypes = [I, P, P, P, I64, I64, I32, P, I, P]
     L.fp4_scale_search.argtypes = [P, I, I64, I64, I32, I32, F, F, P, P, P, P, S, P, P]
     L.fp4_gemm_mxfp4.argtypes = [P, P, P, P, I64, I64, I64, P, I, P]
+    L.fp4_linear_mxfp4.argtypes = [P, I, I64, I64, P, P, I64, P, P, P, I, I, P, S, P, P]
     L.fp4_workspace_bytes.argtypes = [I, I64, I64]
     L.fp4_workspace_bytes.restype = S
     L.fp4_status_str.argtypes = [I]
     L.fp4_status_str.restype = ctypes.c_char_p
     for name in ("fp4_quantize_mxfp4", "fp4_quantize_mxfp4_rule", "fp4_quantize_nvfp4",
                  "fp4_dequantize", "fp4_scale_search", "fp4_scale_search_exhaustive",
-                 "fp4_gemm_mxfp4"):
+                 "fp4_gemm_mxfp4", "fp4_linear_mxfp4"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -264,3 +265,31 @@ def gemm_mxfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, bt_codes: torch.Te
     _ok(lib().fp4_gemm_mxfp4(_ptr(a_codes), _ptr(a_scales), _ptr(bt_codes), _ptr(bt_scales), M, N,
                              K, _ptr(c), _dtype_code(c.dtype), _stream(a_codes)))
     return c
+
+
+def linear_mxfp4(x: torch.Tensor, bt_codes: torch.Tensor, bt_scales: torch.Tensor,
+                 out_dtype=torch.bfloat16, out=None, a_out=None, status=None, workspace=None,
+                 check: bool = True, one_launch: bool = True):
+    """W4A4 linear: x [M, K] (fp32/bf16) quantized to MXFP4, times B with
+    Bt = B^T [N, K] in MXFP4.  Returns (C [M, N], (a_codes, a_scales)).
+    one_launch: quantize and multiply in one kernel when the grid fits."""
+    M, K = _rows_cols(x)
+    N, kh = _rows_cols(bt_codes)
+    if 2 * kh != K:
+        raise ValueError("x and Bt must share K")
+    if a_out is None:
+        a_codes = torch.empty(M, K // 2, dtype=torch.uint8, device=x.device)
+        a_scales = torch.empty(M, K // 32, dtype=torch.uint8, device=x.device)
+    else:
+        a_codes, a_scales = a_out
+    c = out if out is not None else torch.empty(M, N, dtype=out_dtype, device=x.device)
+    if workspace is None:
+        workspace = new_workspace(M, K, x.device)
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _ok(lib().fp4_linear_mxfp4(_ptr(x), _dtype_code(x.dtype), M, K, _ptr(bt_codes),
+                               _ptr(bt_scales), N, _ptr(a_codes), _ptr(a_scales), _ptr(c),
+                               _dtype_code(c.dtype), 0 if one_launch else 1, _ptr(workspace),
+                               workspace.numel(), _ptr(status), _stream(x)))
+    _finish(status, check)
+    return c, (a_codes, a_scales)

@@ -148,6 +148,27 @@ fp4_status fp4_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales,
                                               c, ct == FP4_BF16, (hipStream_t)stream));
 }
 
+fp4_status fp4_linear_mxfp4(const void *x, fp4_dtype xt, int64_t M, int64_t K,
+                            const uint8_t *bt_codes, const uint8_t *bt_scales, int64_t N,
+                            uint8_t *a_codes, uint8_t *a_scales, void *c, fp4_dtype ct,
+                            fp4_linear_mode mode, void *workspace, size_t workspace_bytes,
+                            int32_t *status, void *stream) {
+    if (!x || !bt_codes || !bt_scales || !a_codes || !a_scales || !c) return FP4_E_ARG;
+    if (mode != FP4_LINEAR_ONE_LAUNCH && mode != FP4_LINEAR_TWO_LAUNCHES) return FP4_E_ARG;
+    if (!valid_dtype(xt) || !valid_dtype(ct)) return FP4_E_DTYPE;
+    if (M < 1 || N < 1 || K < 32 || K % 32) return FP4_E_SHAPE;
+    if (M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return FP4_E_SHAPE;
+    if (M > kMaxElems / K) return FP4_E_SHAPE;
+    if (!workspace || workspace_bytes < nv_workspace()) return FP4_E_WORKSPACE;
+    if (!aligned(x, 16) || !aligned(a_codes, 16) || !aligned(bt_codes, 16) || !aligned(c, 4) ||
+        !aligned(workspace, 16) || !aligned(status, 4))
+        return FP4_E_ALIGN;
+    return from_hip(fp4dev::launch_linear_mxfp4(x, xt == FP4_BF16, bt_codes, bt_scales, M, N, K,
+                                                a_codes, a_scales, c, ct == FP4_BF16,
+                                                mode == FP4_LINEAR_ONE_LAUNCH, workspace, status,
+                                                (hipStream_t)stream));
+}
+
 size_t fp4_workspace_bytes(fp4_format fmt, int64_t rows, int64_t cols) {
     (void)rows;
     (void)cols;

@@ -421,4 +421,51 @@ __device__ __forceinline__ void report_flags(int32_t *status, uint32_t flags) {
     if (__lane_id() == (uint32_t)__builtin_ctzll(active)) atomicOr(status, (int32_t)any);
 }
 
+// ---- grid barrier ----------------------------------------------------------
+// For kernels whose whole grid is resident at once (at most one workgroup
+// per CU, no more workgroups than CUs).  The workspace keeps an epoch word
+// and one 64-bit slot per workgroup, zeroed before the first call and left
+// alone between calls.  Each call tags its slots with epoch + 1 (never 0),
+// read by every workgroup before any can pass the barrier; workgroup 0
+// stores the new epoch once it has passed, for the next call in stream order.
+__device__ __forceinline__ uint32_t barrier_tag(const uint32_t *epoch) {
+    const uint32_t e = __hip_atomic_load(epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return e + 1u == 0u ? 1u : e + 1u;
+}
+
+// Called by one whole wave of every workgroup: publishes (tag, value) in
+// this workgroup's slot and polls until every slot of the grid carries the
+// tag; returns the largest value.  A bounded wait: after spin_limit polls it
+// sets FLAG_BARRIER_TIMEOUT in flags and returns what it has.
+__device__ __forceinline__ uint32_t grid_barrier_max(uint64_t *slots, uint32_t *epoch, uint32_t tag,
+                                                     uint32_t value, uint32_t spin_limit,
+                                                     uint32_t &flags) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int G = gridDim.x * gridDim.y;
+    const int wg = blockIdx.y * gridDim.x + blockIdx.x;
+    if (lane == 0)
+        __hip_atomic_store(&slots[wg], ((uint64_t)tag << 32) | value, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t A = 0;
+    for (uint32_t it = 0;; ++it) {
+        bool ok = true;
+        uint32_t mm = 0;
+        for (int i = lane; i < G; i += WAVE) {
+            const uint64_t sl = __hip_atomic_load(&slots[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ok = ok && (uint32_t)(sl >> 32) == tag;
+            mm = max(mm, (uint32_t)sl);
+        }
+        const bool all = __ballot(!ok) == 0;
+        if (all || it >= spin_limit) {
+            if (!all) flags |= FLAG_BARRIER_TIMEOUT;
+            A = wave_max_u32(mm);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+    if (lane == 0 && wg == 0)
+        __hip_atomic_store(epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return A;
+}
+
 }  // namespace fp4dev

@@ -19,6 +19,7 @@
 // of K; wave w owns rows 32w..32w+31.  B (N x K, the large operand at M=128)
 // is read from HBM once in total; A is re-read by every workgroup from L2.
 // The K loop is unrolled with a register prefetch of the next steps' codes.
+#include <mutex>
 #include <type_traits>
 
 #include "fp4_device.h"
@@ -267,10 +268,13 @@ constexpr int GEMM_SCALE_COLS = GEMM_MAX_K / 32 / 16;  // 16-byte scale chunks p
 typedef __attribute__((address_space(1))) const void *gemm_gptr;
 typedef __attribute__((address_space(3))) void *gemm_lptr;
 
+// One workgroup's 128 x 32 tile of C (blockIdx.y, blockIdx.x), all of K.
 template <bool OUT_BF16>
-__global__ __launch_bounds__(GEMM_WG) void mxfp4_gemm_lds_kernel(
-    const uint4 *__restrict__ A, const uint8_t *__restrict__ As, const uint4 *__restrict__ Bt,
-    const uint8_t *__restrict__ Bs, int M, int N, int K, void *__restrict__ C) {
+__device__ __forceinline__ void gemm_lds_tile(const uint4 *__restrict__ A,
+                                              const uint8_t *__restrict__ As,
+                                              const uint4 *__restrict__ Bt,
+                                              const uint8_t *__restrict__ Bs, int M, int N,
+                                              int K, void *__restrict__ C) {
     // ring of code stages: A [128 rows][8 chunks], B [32][8];
     // the scales of all K, transposed: A [16-byte chunk][128 rows], B [chunk][32 rows]
     __shared__ uint4 ring[GEMM_S][GEMM_STAGE_CHUNKS];
@@ -419,6 +423,106 @@ __global__ __launch_bounds__(GEMM_WG) void mxfp4_gemm_lds_kernel(
     }
 }
 
+template <bool OUT_BF16>
+__global__ __launch_bounds__(GEMM_WG) void mxfp4_gemm_lds_kernel(
+    const uint4 *__restrict__ A, const uint8_t *__restrict__ As, const uint4 *__restrict__ Bt,
+    const uint8_t *__restrict__ Bs, int M, int N, int K, void *__restrict__ C) {
+    gemm_lds_tile<OUT_BF16>(A, As, Bt, Bs, M, N, K, C);
+}
+
+// ---------------------------------------------------------------------------
+// W4A4 linear: the activations [M, K] quantized to MXFP4 (OCP floor rule) in
+// the GEMM's own launch ("FP4, FP8 and INT8/INT4" page, section 5: the
+// quantize and MMA costs of a low-bit linear layer).  Every workgroup needs
+// all of A, so each quantizes a 1/G share and writes it out (a_codes,
+// a_scales are outputs too), the grid meets at a barrier, and the tiles then
+// read A as the plain GEMM does.  The grid must be resident at once.
+// ---------------------------------------------------------------------------
+template <bool XBF16>
+__device__ __forceinline__ uint32_t quantize_share(const uint4 *__restrict__ x, int64_t nchunks,
+                                                   uint32_t *__restrict__ a_codes,
+                                                   uint8_t *__restrict__ a_scales) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    constexpr int WPG = GEMM_WG / WAVE;
+    const int64_t wave = (int64_t)(blockIdx.y * gridDim.x + blockIdx.x) * WPG + threadIdx.x / WAVE;
+    const int64_t nwaves = (int64_t)gridDim.x * gridDim.y * WPG;
+    uint32_t flags = 0;
+    // a wave takes 64 consecutive chunks of 8 values; four lanes hold a block
+    for (int64_t t = wave; t * WAVE < nchunks; t += nwaves) {
+        const int64_t c = t * WAVE + lane;
+        const bool ok = c < nchunks;
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        const uint4 lo = ok ? ld_stream(x + (XBF16 ? c : 2 * c)) : z;
+        const uint4 hi = (!XBF16 && ok) ? ld_stream(x + 2 * c + 1) : z;
+        uint32_t m = XBF16 ? amax_bf16x8(lo) : amax_f32x8(lo, hi);
+        m = max(m, dpp<QP_XOR1>(m));
+        m = max(m, dpp<QP_XOR2>(m));
+        const int sh = XBF16 ? 7 : 23;
+        if ((m >> sh) >= 0xFFu) flags |= FLAG_NONFINITE;
+        const uint32_t sb = mx_scale_byte(m, sh);
+        uint32_t q;
+        if (XBF16) {
+            q = cvt_fp4x8_bf16(lo, e8m0_operand(sb));
+        } else {
+            float v[8];
+            widen_f32x8(lo, hi, v);
+            q = cvt_fp4x8_f32(v, e8m0_operand(sb));
+        }
+        if (ok) {
+            a_codes[c] = q;
+            if ((lane & 3) == 0) a_scales[c >> 2] = (uint8_t)sb;
+        }
+    }
+    return flags;
+}
+
+template <bool OUT_BF16, bool XBF16>
+__global__ __launch_bounds__(GEMM_WG) void mxfp4_linear_kernel(
+    const uint4 *__restrict__ x, uint32_t *__restrict__ a_codes, uint8_t *__restrict__ a_scales,
+    const uint4 *__restrict__ Bt, const uint8_t *__restrict__ Bs, int M, int N, int K,
+    void *__restrict__ C, uint64_t *slots, uint32_t *epoch, uint32_t spin_limit,
+    int32_t *status) {
+    const int wv = threadIdx.x / WAVE;
+    const uint32_t tag = wv == 0 ? barrier_tag(epoch) : 0u;
+    uint32_t flags = quantize_share<XBF16>(x, (int64_t)M * K / 8, a_codes, a_scales);
+    // Every wave's stores of its share have completed at the workgroup
+    // barrier; then one wave makes them visible to the device (the release
+    // writes back this XCD's L2) before it publishes its slot, and after the
+    // grid barrier drops stale copies of the other shares (the acquire
+    // invalidates the caches) before any wave reads A.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (wv == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        grid_barrier_max(slots, epoch, tag, 0u, spin_limit, flags);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+    report_flags(status, flags);
+    gemm_lds_tile<OUT_BF16>((const uint4 *)a_codes, a_scales, Bt, Bs, M, N, K, C);
+}
+
+// Workgroups one CU holds of the linear kernel's largest instance (its LDS
+// allows one), and the CU count: the grid of a fused call may not exceed
+// their product.  Probed once per device.
+static int linear_capacity() {
+    static int cap[kMaxDevices];
+    static std::once_flag once[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    std::call_once(once[dev], [dev] {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 0;
+        auto k = mxfp4_linear_kernel<false, false>;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, GEMM_WG, 0) != hipSuccess)
+            per_cu = 0;
+        const int c = cus * per_cu;
+        cap[dev] = c > kResidentSlots ? kResidentSlots : c;
+    });
+    return cap[dev];
+}
+
 static bool gemm_lds_ok(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *bt_codes,
                         const uint8_t *bt_scales, int64_t K) {
     auto al = [](const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; };
@@ -468,6 +572,34 @@ hipError_t launch_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales,
                            (const uint4 *)a_codes, a_scales, (const uint4 *)bt_codes, bt_scales,
                            (int)M, (int)N, (int)K, c);
     return hipGetLastError();
+}
+
+hipError_t launch_linear_mxfp4(const void *x, bool x_bf16, const uint8_t *bt_codes,
+                               const uint8_t *bt_scales, int64_t M, int64_t N, int64_t K,
+                               uint8_t *a_codes, uint8_t *a_scales, void *c, bool out_bf16,
+                               bool one_launch, void *workspace, int32_t *status, hipStream_t s) {
+    dim3 grid((unsigned)((N + GEMM_TN - 1) / GEMM_TN), (unsigned)((M + GEMM_TM - 1) / GEMM_TM));
+    const int64_t G = (int64_t)grid.x * grid.y;
+    if (one_launch && gemm_lds_ok(a_codes, a_scales, bt_codes, bt_scales, K) &&
+        G <= linear_capacity()) {
+        using Kn = void (*)(const uint4 *, uint32_t *, uint8_t *, const uint4 *, const uint8_t *,
+                            int, int, int, void *, uint64_t *, uint32_t *, uint32_t, int32_t *);
+        static const Kn kernels[2][2] = {
+            {mxfp4_linear_kernel<false, false>, mxfp4_linear_kernel<false, true>},
+            {mxfp4_linear_kernel<true, false>, mxfp4_linear_kernel<true, true>}};
+        uint8_t *ws = (uint8_t *)workspace;
+        hipLaunchKernelGGL(kernels[out_bf16 ? 1 : 0][x_bf16 ? 1 : 0], grid, dim3(GEMM_WG), 0, s,
+                           (const uint4 *)x, (uint32_t *)a_codes, a_scales,
+                           (const uint4 *)bt_codes, bt_scales, (int)M, (int)N, (int)K, c,
+                           (uint64_t *)(ws + kResidentSlotsOffset),
+                           (uint32_t *)(ws + kResidentEpochOffset), kResidentSpinLimit, status);
+        return hipGetLastError();
+    }
+    // the grid cannot be resident at once (or the shape takes another GEMM
+    // kernel): the same two steps as separate launches
+    hipError_t e = launch_mx_quantize(x, x_bf16, M * K, 0, a_codes, a_scales, status, s);
+    if (e != hipSuccess) return e;
+    return launch_gemm_mxfp4(a_codes, a_scales, bt_codes, bt_scales, M, N, K, c, out_bf16, s);
 }
 
 }  // namespace fp4dev

@@ -40,5 +40,12 @@ hipError_t launch_dequantize(int fmt, const uint8_t *codes, const uint8_t *scale
 hipError_t launch_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales,
                              const uint8_t *bt_codes, const uint8_t *bt_scales, int64_t M,
                              int64_t N, int64_t K, void *c, bool out_bf16, hipStream_t s);
+// Activations x [M, K] quantized to MXFP4 into a_codes / a_scales, then the
+// GEMM with Bt; with one_launch, one kernel (grid barrier, workspace as for
+// NVFP4) when the grid fits on the device at once, else two launches.
+hipError_t launch_linear_mxfp4(const void *x, bool x_bf16, const uint8_t *bt_codes,
+                               const uint8_t *bt_scales, int64_t M, int64_t N, int64_t K,
+                               uint8_t *a_codes, uint8_t *a_scales, void *c, bool out_bf16,
+                               bool one_launch, void *workspace, int32_t *status, hipStream_t s);
 
 }  // namespace fp4dev

@@ -494,11 +494,7 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
         const int j = LC + r;
         v[r] = ld_stream(x + j * stride + (EXACT ? c00 : min(c00, last - j * stride)));
     }
-    uint32_t tag = 0;
-    if (wv == 0) {
-        const uint32_t e = __hip_atomic_load(epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        tag = e + 1u == 0u ? 1u : e + 1u;
-    }
+    const uint32_t tag = wv == 0 ? barrier_tag(epoch) : 0u;
     uint32_t m = 0;
 #pragma unroll
     for (int r = 0; r < RC; ++r) m = max(m, amax_bf16x8(v[r]));
@@ -509,38 +505,13 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
     if (lane == 0) red[wv] = m;
     __syncthreads();
 
-    // ---- grid barrier: wave 0 publishes and polls -----------------------
+    // ---- grid barrier: wave 0 publishes the partial amax and polls --------
     uint32_t flags = 0;
     if (wv == 0) {
         uint32_t wm = lane < RES_WAVES ? red[lane] : 0u;
         wm = wave_max_u32(wm);
-        if (lane == 0)
-            __hip_atomic_store(&slots[blockIdx.x], ((uint64_t)tag << 32) | wm, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        const int G = gridDim.x;
-        uint32_t A = 0;
-        for (uint32_t it = 0;; ++it) {
-            bool ok = true;
-            uint32_t mm = 0;
-            for (int i = lane; i < G; i += WAVE) {
-                const uint64_t sl =
-                    __hip_atomic_load(&slots[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                ok = ok && (uint32_t)(sl >> 32) == tag;
-                mm = max(mm, (uint32_t)sl);
-            }
-            const bool all = __ballot(!ok) == 0;
-            if (all || it >= spin_limit) {
-                if (!all) flags |= FLAG_BARRIER_TIMEOUT;
-                A = wave_max_u32(mm);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-        }
-        if (lane == 0) {
-            tensor_amax = A;
-            if (blockIdx.x == 0)
-                __hip_atomic_store(epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        const uint32_t A = grid_barrier_max(slots, epoch, tag, wm, spin_limit, flags);
+        if (lane == 0) tensor_amax = A;
     }
     __syncthreads();
     const TensorScale ts = scale_from_amax(tensor_amax << 16);

@@ -129,6 +129,24 @@ def test_exhaustive_search_validation():
     assert s(wsb=8) == E_WORKSPACE
 
 
+def test_linear_validation():
+    L = fp4.lib()
+
+    def lin(x=A16, M=128, K=512, N=64, ws=A16, wsb=1 << 20, ac=A16, c=A16, xt=fp4.BF16, mode=0):
+        return L.fp4_linear_mxfp4(x, xt, M, K, A16, A16, N, ac, A16, c, fp4.BF16, mode, ws, wsb,
+                                  NULL, NULL)
+    assert lin(mode=2) == E_ARG
+    assert lin(x=NULL) == E_ARG
+    assert lin(ac=NULL) == E_ARG
+    assert lin(xt=4) == E_DTYPE
+    assert lin(K=48) == E_SHAPE
+    assert lin(M=0) == E_SHAPE
+    assert lin(ws=NULL) == E_WORKSPACE
+    assert lin(wsb=8) == E_WORKSPACE
+    assert lin(x=A1) == E_ALIGN
+    assert lin(ac=A1) == E_ALIGN
+
+
 def test_gemm_validation():
     L = fp4.lib()
 

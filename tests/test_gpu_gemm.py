@@ -16,7 +16,7 @@ import mxfp4_block_amax_amd as fp4
 import oracle
 import oracle.gemm as og
 import workloads
-from tests._gpu import announce, dev
+from tests._gpu import announce, assert_bytes_equal, dev, host_u8, oracle_view
 
 pytestmark = pytest.mark.gpu
 
@@ -85,3 +85,71 @@ def test_gemm_deterministic():
     c1 = _run(ap, asc, bp, bsc, 128, 1024, 2048, torch.float32)
     c2 = _run(ap, asc, bp, bsc, 128, 1024, 2048, torch.float32)
     assert torch.equal(c1, c2)
+
+
+# ---- W4A4 linear: activation quantize + GEMM in one call -----------------------
+
+def _check_linear(M, N, K, x_dtype=torch.float32, seed=0, workspace=None):
+    a, bt = workloads.gemm_operands(M, N, K, seed_a=seed, seed_b=seed + 1)
+    x = a.to(x_dtype)
+    bp, bsc, f2 = oracle.mx_quantize(bt.numpy())
+    assert f2 == 0
+    ap, asc, f1 = oracle.mx_quantize(oracle_view(x))
+    assert f1 == 0
+    bt_d = dev(torch.from_numpy(bp.reshape(N, K // 2)))
+    bs_d = dev(torch.from_numpy(bsc.reshape(N, K // 32)))
+    ref = og.gemm_f64(ap, asc, bp, bsc, M, N, K)
+    ws = workspace if workspace is not None else fp4.new_workspace(M, K, "cuda")
+    announce(f"linear mxfp4 {M}x{N}x{K} x {x_dtype} fp32 out")
+    c32, (ac, asd) = fp4.linear_mxfp4(dev(x), bt_d, bs_d, torch.float32, workspace=ws)
+    announce(f"linear mxfp4 {M}x{N}x{K} x {x_dtype} bf16 out")
+    c16, _ = fp4.linear_mxfp4(dev(x), bt_d, bs_d, torch.bfloat16, workspace=ws)
+    torch.cuda.synchronize()
+    assert_bytes_equal(host_u8(asd), asc, f"linear {M}x{N}x{K}: A scales")
+    assert_bytes_equal(host_u8(ac), ap, f"linear {M}x{N}x{K}: A codes")
+    got = c32.cpu().numpy().astype(np.float64)
+    err = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
+    assert err <= REL_FROB, f"linear {M}x{N}x{K}: relative Frobenius error {err:.3e}"
+    want16 = c32.cpu().to(torch.bfloat16)
+    assert torch.equal(c16.cpu().view(torch.int16), want16.view(torch.int16))
+    # the same as the separate entry points, bit for bit, and as two launches
+    c_sep = _run(ap, asc, bp, bsc, M, N, K, torch.float32)
+    assert torch.equal(c32.cpu(), c_sep.cpu())
+    announce(f"linear mxfp4 {M}x{N}x{K} two launches")
+    c2, (ac2, as2) = fp4.linear_mxfp4(dev(x), bt_d, bs_d, torch.float32, workspace=ws,
+                                      one_launch=False)
+    assert torch.equal(c2.cpu(), c32.cpu())
+    assert torch.equal(ac2.cpu(), ac.cpu()) and torch.equal(as2.cpu(), asd.cpu())
+    return err
+
+
+@pytest.mark.parametrize("M,N,K,dt", [(128, 8192, 8192, torch.float32),    # one launch, full size
+                                      (128, 8192, 8192, torch.bfloat16),
+                                      (128, 256, 512, torch.bfloat16),      # one launch, small grid
+                                      (70, 50, 1024, torch.float32),        # ragged M and N
+                                      (96, 40, 96, torch.float32),          # K % 512 != 0: two launches
+                                      (128, 16384, 1024, torch.bfloat16)])  # grid above the CU count
+def test_linear_matches_quantize_then_gemm(M, N, K, dt):
+    _check_linear(M, N, K, dt)
+
+
+def test_linear_workspace_shared_with_nvfp4_and_reused():
+    ws = fp4.new_workspace(128, 8192, "cuda")
+    for seed in range(3):
+        _check_linear(128, 1024, 2048, torch.bfloat16, seed=seed, workspace=ws)
+        x = workloads.nvfp4_weight(512, 4096, seed=seed).cuda()
+        announce(f"nvfp4 quantize on the shared workspace, seed {seed}")
+        codes, scales, sg = fp4.quantize_nvfp4(x, workspace=ws)
+        p, s, sgo, f = oracle.nv_quantize(oracle_view(x.cpu()))
+        assert_bytes_equal(host_u8(scales), s, "nvfp4 scales after linear")
+
+
+def test_linear_flags_nonfinite_activations():
+    M, N, K = 128, 256, 512
+    a, bt = workloads.gemm_operands(M, N, K)
+    bp, bsc, _ = oracle.mx_quantize(bt.numpy())
+    x = a.clone()
+    x[5, 7] = float("inf")
+    with pytest.raises(ValueError):
+        fp4.linear_mxfp4(dev(x), dev(torch.from_numpy(bp.reshape(N, K // 2))),
+                         dev(torch.from_numpy(bsc.reshape(N, K // 32))))
