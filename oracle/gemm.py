@@ -17,7 +17,7 @@ weight as N x K makes its last-dimension groups the K groups).
 """
 import numpy as np
 
-from . import MX, dequantize
+from . import MX, dequantize, e2m1_value, e4m3_value, unpack
 
 
 def dequant_matrix(packed: np.ndarray, scales: np.ndarray, rows: int, cols: int) -> np.ndarray:
@@ -43,3 +43,32 @@ def block_scaled_dot(pa: np.ndarray, sa: np.ndarray, pb: np.ndarray, sb: np.ndar
         total += float(sa[g]) * float(sb[g]) * float(np.dot(pa[sl].astype(np.float64),
                                                             pb[sl].astype(np.float64)))
     return total
+
+
+# ---- NVFP4 x NVFP4 ------------------------------------------------------------
+#
+# The same equation with 16-element blocks, E4M3 block scales and one fp32
+# tensor scale per operand ("NVFP4 / MXFP4 format" page, section 6:
+# Y = a_X a_W sum_g b^X_g b^W_g sum_{k in g} p^X_k p^W_k).  Reading: the
+# tensor scales multiply once, outside the sum, as the page factors them; the
+# block scales are the exact E4M3 values.  Each dequantized value
+# p * b * a carries at most 2 + 4 + 24 significant bits, so it is exact in
+# binary64, and the binary64 matrix product equals the equation up to
+# binary64 rounding.
+
+def nv_dequant_matrix_exact(packed: np.ndarray, scales: np.ndarray, s_g, rows: int,
+                            cols: int) -> np.ndarray:
+    """p * E4M3(s_b) * s_g in binary64 for a [rows, cols] NVFP4 operand."""
+    codes = unpack(np.ascontiguousarray(packed, dtype=np.uint8).reshape(-1))
+    pv = np.array([e2m1_value(c) for c in range(16)])[codes]
+    sv = np.array([e4m3_value(c) if c < 127 else np.nan for c in range(128)])
+    sb = sv[np.ascontiguousarray(scales, dtype=np.uint8).reshape(-1) & 0x7F]
+    return (pv.reshape(-1, 16) * sb[:, None] * float(np.float32(s_g))).reshape(rows, cols)
+
+
+def nv_gemm_f64(a_packed, a_scales, sg_a, bt_packed, bt_scales, sg_b, M: int, N: int,
+                K: int) -> np.ndarray:
+    """C = A @ B in binary64 from NVFP4 operands A [M, K] and Bt [N, K]."""
+    A = nv_dequant_matrix_exact(a_packed, a_scales, sg_a, M, K)
+    Bt = nv_dequant_matrix_exact(bt_packed, bt_scales, sg_b, N, K)
+    return A @ Bt.T

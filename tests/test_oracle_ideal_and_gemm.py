@@ -1,6 +1,7 @@
 """Pins for the ideal-scale teaching mode (the pages' printed examples) and
 for the block-scaled GEMM reference."""
 import numpy as np
+import torch
 import pytest
 
 import oracle
@@ -76,3 +77,56 @@ def test_gemm_reference_equals_group_formula_and_integer_case():
     p1, s1, _ = oracle.mx_quantize(ai)
     p2, s2, _ = oracle.mx_quantize(bi)
     assert np.all(og.gemm_f64(p1, s1, p2, s2, 2, 3, 64) == 64 * 6.0)
+
+
+# ---- NVFP4 x NVFP4 GEMM reference --------------------------------------------
+
+def _e4m3_code(v: float) -> int:
+    return [c for c in range(127) if oracle.e4m3_value(c) == v][0]
+
+
+def test_nv_gemm_reproduces_the_pages_group_dot():
+    g = keyed("group_dot.txt")
+    bx = [float(v) for v in g["group_scales_x"][0]]
+    bw = [float(v) for v in g["group_scales_w"][0]]
+    # payloads 1 | 2 against 1 | -1 (codes 2, 4, 2, 10), global scales 1
+    ca = np.array([2] * 16 + [4] * 16, np.uint8)
+    cb = np.array([2] * 16 + [10] * 16, np.uint8)
+    sa = np.array([_e4m3_code(v) for v in bx], np.uint8)
+    sb = np.array([_e4m3_code(v) for v in bw], np.uint8)
+    C = og.nv_gemm_f64(oracle.pack(ca), sa, 1.0, oracle.pack(cb), sb, 1.0, 1, 1, 32)
+    assert C[0, 0] == float(g["correct"][0][0])
+
+
+def test_nv_gemm_equals_the_group_formula():
+    g = torch.Generator().manual_seed(51)
+    a = (torch.randn(6, 64, generator=g) * 3).numpy()
+    b = (torch.randn(5, 64, generator=g) * 0.1).numpy()
+    ap, asc, sga, f1 = oracle.nv_quantize(a.reshape(-1))
+    bp, bsc, sgb, f2 = oracle.nv_quantize(b.reshape(-1))
+    assert f1 == 0 and f2 == 0
+    C = og.nv_gemm_f64(ap, asc, sga, bp, bsc, sgb, 6, 5, 64)
+    val = np.vectorize(oracle.e2m1_value)
+    pa = val(oracle.unpack(ap).reshape(6, 64))
+    pb = val(oracle.unpack(bp).reshape(5, 64))
+    sa = np.vectorize(oracle.e4m3_value)(asc.reshape(6, 4))
+    sb = np.vectorize(oracle.e4m3_value)(bsc.reshape(5, 4))
+    for m in range(6):
+        for n in range(5):
+            want = float(sga) * float(sgb) * og.block_scaled_dot(pa[m], sa[m], pb[n], sb[n], 16)
+            assert C[m, n] == pytest.approx(want, rel=1e-13, abs=1e-300)
+    # and the operands dequantize to the NVFP4 values up to the fp32 rounding
+    # of s_g * s_b that the elementwise dequantizer applies
+    y = oracle.dequantize(oracle.NV, ap, asc, sga).reshape(6, 64)
+    Ad = og.nv_dequant_matrix_exact(ap, asc, sga, 6, 64)
+    assert np.allclose(y, Ad, rtol=2 ** -22, atol=0)
+
+
+def test_nv_gemm_integer_case_is_exact():
+    # codes 4 (2.0) and 5 (3.0) at block scale 1 (0x38), tensor scales 1 and 2
+    ap = oracle.pack(np.full(2 * 64, 4, np.uint8))
+    bp = oracle.pack(np.full(3 * 64, 5, np.uint8))
+    one = _e4m3_code(1.0)
+    asc = np.full(2 * 4, one, np.uint8)
+    bsc = np.full(3 * 4, one, np.uint8)
+    assert np.all(og.nv_gemm_f64(ap, asc, 1.0, bp, bsc, 2.0, 2, 3, 64) == 64 * 6.0 * 2.0)
