@@ -196,6 +196,25 @@ fp4_status fp4_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales,
                           int64_t N, int64_t K, void *c, fp4_dtype ct, void *stream);
 
 /*
+ * NVFP4 x NVFP4 GEMM ("NVFP4 / MXFP4 format" page, section 6:
+ * Y = a_X a_W sum_g b^X_g b^W_g sum_{k in g} p^X_k p^W_k, 16-element groups
+ * along K, E4M3 block scales b, one fp32 tensor scale a per operand).
+ *   a_codes [M, K/2], a_scales [M, K/16] E4M3, a_global_scale device float
+ *   bt_codes [N, K/2], bt_scales [N, K/16], bt_global_scale   (B as Bt [N, K])
+ *   c       [M, N] fp32 or bf16
+ * The products of FP4 values and block scales are exact (fp16 operands of
+ * the fp16 MFMA), the sums fp32; the tensor scales multiply the fp32 result
+ * once: c = RN(acc * RN32(a_X a_W)).  K must be a multiple of 16; a multiple
+ * of 256 up to 8192 with 16-byte aligned codes and scales takes the staged
+ * kernel, other shapes a slow one-output-per-thread kernel.  Scale bytes are
+ * read as E4M3FN (sign bit honoured, 0x7F NaN).  Deterministic.
+ */
+fp4_status fp4_gemm_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales,
+                          const float *a_global_scale, const uint8_t *bt_codes,
+                          const uint8_t *bt_scales, const float *bt_global_scale, int64_t M,
+                          int64_t N, int64_t K, void *c, fp4_dtype ct, void *stream);
+
+/*
  * W4A4 linear layer: the activations quantized to MXFP4, then the MXFP4 GEMM
  * ("FP4, FP8 and INT8/INT4" page, tom-jerr.github.io, section 5: the cost of
  * a low-bit linear layer is the activation quantize plus the block-scaled

@@ -42,7 +42,8 @@ FLAG_BARRIER_TIMEOUT = 4
 
 EXPORTS = ("fp4_quantize_mxfp4", "fp4_quantize_mxfp4_rule", "fp4_quantize_nvfp4",
            "fp4_dequantize", "fp4_scale_search", "fp4_scale_search_exhaustive",
-           "fp4_gemm_mxfp4", "fp4_linear_mxfp4", "fp4_workspace_bytes", "fp4_status_str")
+           "fp4_gemm_mxfp4", "fp4_gemm_nvfp4", "fp4_linear_mxfp4", "fp4_workspace_bytes",
+           "fp4_status_str")
 
 # fp4_mx_rule: the MXFP4 block-exponent rules
 MX_RULES = {"ocp": 0, "ceil": 1, "mse": 2}
@@ -72,6 +73,7 @@ def lib() -> ctypes.CDLL:
     L.fp4_dequantize.argtypes = [I, P, P, P, I64, I64, I32, P, I, P]
     L.fp4_scale_search.argtypes = [P, I, I64, I64, I32, I32, F, F, P, P, P, P, S, P, P]
     L.fp4_gemm_mxfp4.argtypes = [P, P, P, P, I64, I64, I64, P, I, P]
+    L.fp4_gemm_nvfp4.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, I, P]
     L.fp4_linear_mxfp4.argtypes = [P, I, I64, I64, P, P, I64, P, P, P, I, I, P, S, P, P]
     L.fp4_workspace_bytes.argtypes = [I, I64, I64]
     L.fp4_workspace_bytes.restype = S
@@ -79,7 +81,7 @@ def lib() -> ctypes.CDLL:
     L.fp4_status_str.restype = ctypes.c_char_p
     for name in ("fp4_quantize_mxfp4", "fp4_quantize_mxfp4_rule", "fp4_quantize_nvfp4",
                  "fp4_dequantize", "fp4_scale_search", "fp4_scale_search_exhaustive",
-                 "fp4_gemm_mxfp4", "fp4_linear_mxfp4"):
+                 "fp4_gemm_mxfp4", "fp4_gemm_nvfp4", "fp4_linear_mxfp4"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -264,6 +266,22 @@ def gemm_mxfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, bt_codes: torch.Te
     c = out if out is not None else torch.empty(M, N, dtype=out_dtype, device=a_codes.device)
     _ok(lib().fp4_gemm_mxfp4(_ptr(a_codes), _ptr(a_scales), _ptr(bt_codes), _ptr(bt_scales), M, N,
                              K, _ptr(c), _dtype_code(c.dtype), _stream(a_codes)))
+    return c
+
+
+def gemm_nvfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, a_global_scale: torch.Tensor,
+               bt_codes: torch.Tensor, bt_scales: torch.Tensor, bt_global_scale: torch.Tensor,
+               out_dtype=torch.bfloat16, out=None):
+    """C [M, N] = A [M, K] @ B [K, N] with A and Bt = B^T [N, K] in NVFP4."""
+    M, kh = _rows_cols(a_codes)
+    N, kh2 = _rows_cols(bt_codes)
+    if kh != kh2:
+        raise ValueError("A and Bt must share K")
+    K = 2 * kh
+    c = out if out is not None else torch.empty(M, N, dtype=out_dtype, device=a_codes.device)
+    _ok(lib().fp4_gemm_nvfp4(_ptr(a_codes), _ptr(a_scales), _ptr(a_global_scale), _ptr(bt_codes),
+                             _ptr(bt_scales), _ptr(bt_global_scale), M, N, K, _ptr(c),
+                             _dtype_code(c.dtype), _stream(a_codes)))
     return c
 
 

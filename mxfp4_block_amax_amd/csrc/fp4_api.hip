@@ -148,6 +148,23 @@ fp4_status fp4_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales,
                                               c, ct == FP4_BF16, (hipStream_t)stream));
 }
 
+fp4_status fp4_gemm_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales,
+                          const float *a_global_scale, const uint8_t *bt_codes,
+                          const uint8_t *bt_scales, const float *bt_global_scale, int64_t M,
+                          int64_t N, int64_t K, void *c, fp4_dtype ct, void *stream) {
+    if (!a_codes || !a_scales || !a_global_scale || !bt_codes || !bt_scales ||
+        !bt_global_scale || !c)
+        return FP4_E_ARG;
+    if (!valid_dtype(ct)) return FP4_E_DTYPE;
+    if (M < 1 || N < 1 || K < 16 || K % 16) return FP4_E_SHAPE;
+    if (M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return FP4_E_SHAPE;
+    if (!aligned(c, 4) || !aligned(a_global_scale, 4) || !aligned(bt_global_scale, 4))
+        return FP4_E_ALIGN;
+    return from_hip(fp4dev::launch_gemm_nvfp4(a_codes, a_scales, a_global_scale, bt_codes,
+                                              bt_scales, bt_global_scale, M, N, K, c,
+                                              ct == FP4_BF16, (hipStream_t)stream));
+}
+
 fp4_status fp4_linear_mxfp4(const void *x, fp4_dtype xt, int64_t M, int64_t K,
                             const uint8_t *bt_codes, const uint8_t *bt_scales, int64_t N,
                             uint8_t *a_codes, uint8_t *a_scales, void *c, fp4_dtype ct,

@@ -431,6 +431,226 @@ __global__ __launch_bounds__(GEMM_WG) void mxfp4_gemm_lds_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// NVFP4 x NVFP4 GEMM ("NVFP4 / MXFP4 format" page, section 6:
+// Y = a_X a_W sum_g b^X_g b^W_g sum_{k in g} p^X_k p^W_k over 16-element
+// groups).  The scaled MFMA applies one power of two per 32 K values; an
+// E4M3 block scale is not a power of two and p * b needs up to 6 significant
+// bits, which no FP8/FP6/FP4 operand holds but fp16 does.  So each operand
+// value is decoded to fp16 (the FP4 converter), multiplied by its block's
+// E4M3 value (one packed fp16 multiply per pair, exact), and fed to the fp16
+// MFMA 32x32x16 with fp32 accumulation; the two tensor scales multiply the
+// fp32 result once: C = RN32(acc * RN32(a_X a_W)).
+//
+// Tiling as the MXFP4 kernel: a 128 x 32 tile per workgroup, K staged
+// through an XOR-swizzled ring in LDS (three stages of 256 K), the E4M3
+// scales of all K preloaded (16 K per byte: 80 KB for K = 8192).  Lane half h
+// takes the stage's K values [128h, 128h + 128): its 64 code bytes are
+// contiguous, and MFMA step j uses bytes 4j..4j+3 (K 128h + 8j .. + 8), which
+// lie in one 16-block (8h + j/2).  A and B lanes use the same permutation of
+// K, so the sum is unchanged.
+// ---------------------------------------------------------------------------
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
+constexpr int NVG_S = 3;                                // stages in flight
+constexpr int NVG_SCALE_COLS = GEMM_MAX_K / 16 / 16;    // 16-byte chunks of E4M3 scales per row
+
+// Eight fp16 operand values: the 8 codes of dword w times the block scale
+// held in half `hi` of s2 (selected per MFMA step, a constant).
+__device__ __forceinline__ half8_t nv_operand(uint32_t w, half2_t s2, bool hi) {
+    const _Float16 s = hi ? s2.y : s2.x;
+    const half2_t b = {s, s};
+    const half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * b;
+    const half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * b;
+    const half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * b;
+    const half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * b;
+    const half8_t r = {p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+    return r;
+}
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(GEMM_WG) void nvfp4_gemm_lds_kernel(
+    const uint4 *__restrict__ A, const uint8_t *__restrict__ As, const float *__restrict__ sgA,
+    const uint4 *__restrict__ Bt, const uint8_t *__restrict__ Bs, const float *__restrict__ sgB,
+    int M, int N, int K, void *__restrict__ C) {
+    __shared__ uint4 ring[NVG_S][GEMM_STAGE_CHUNKS];
+    __shared__ uint4 a_scales[NVG_SCALE_COLS][GEMM_TM];
+    __shared__ uint4 b_scales[NVG_SCALE_COLS][GEMM_TN];
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int r32 = lane & 31;
+    const int kh = lane >> 5;
+    const int nblk = K / 32;       // 16-byte code chunks per row
+    const int nst = K / GEMM_STAGE_K;
+    const int ncols = K / 256;     // 16-byte scale chunks per row (one per stage)
+    const int srow = K / 16;       // scale bytes per row
+    const int m0 = blockIdx.y * GEMM_TM, n0 = blockIdx.x * GEMM_TN;
+
+    // ---- the scales, once, transposed: A [chunk][128 rows], B [chunk][32 rows]
+    for (int i = w; i < 2 * ncols; i += 4) {
+        const int c = i >> 1, row = 64 * (i & 1) + lane;
+        const uint8_t *src = As + (int64_t)min(m0 + row, M - 1) * srow + 16 * c;
+        __builtin_amdgcn_global_load_lds((gemm_gptr)src, (gemm_lptr)&a_scales[c][64 * (i & 1)], 16, 0, 0);
+    }
+    for (int j = w; 2 * j < ncols; j += 4) {
+        const int c = 2 * j + kh;
+        const uint8_t *src = Bs + (int64_t)min(n0 + r32, N - 1) * srow + 16 * min(c, ncols - 1);
+        __builtin_amdgcn_global_load_lds((gemm_gptr)src, (gemm_lptr)&b_scales[2 * j][0], 16, 0, 0);
+    }
+
+    // code loads, as the MXFP4 kernel: lane l of a load covers row
+    // (8i + l / 8) of its group and LDS chunk l % 8, holding the row's chunk
+    // (l % 8) ^ (row & 7)
+    const int lrow = lane >> 3, lpc = lane & 7;
+    const uint4 *ga[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 32 * w + 8 * i + lrow;
+        ga[i] = A + (int64_t)min(m0 + row, M - 1) * nblk + (lpc ^ (row & 7));
+    }
+    const int brow = 8 * w + lrow;
+    const uint4 *gb = Bt + (int64_t)min(n0 + brow, N - 1) * nblk + (lpc ^ (brow & 7));
+    auto issue = [&](int st, uint32_t slot) {
+        st = min(st, nst - 1);
+        uint4 *sb = &ring[0][0] + slot * GEMM_STAGE_CHUNKS;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_global_load_lds((gemm_gptr)(ga[i] + st * 8),
+                                             (gemm_lptr)&sb[(32 * w + 8 * i) * 8], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gemm_gptr)(gb + st * 8),
+                                         (gemm_lptr)&sb[GEMM_A_CHUNKS + 8 * w * 8], 16, 0, 0);
+    };
+
+    f32x16_t acc0 = {}, acc1 = {};
+    const int arow = 32 * w + r32;
+    const int sw = r32 & 7;
+    // this lane's operand chunks in slot 0: (4 kh + i) ^ swizzle, i = 0..3
+    uint32_t la[4], lb[4];
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(gemm_lptr)&ring[0][0];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t c = (uint32_t)((4 * kh + i) ^ sw);
+        la[i] = lds0 + (uint32_t)(arow * 8 + c) * 16u;
+        lb[i] = lds0 + (uint32_t)(GEMM_A_CHUNKS + r32 * 8 + c) * 16u;
+    }
+    // the lane's 8 scale bytes of stage st: blocks 8 kh .. 8 kh + 7
+    const uint32_t lsa = (uint32_t)(uintptr_t)(gemm_lptr)&a_scales[0][arow] + 8u * kh;
+    const uint32_t lsb = (uint32_t)(uintptr_t)(gemm_lptr)&b_scales[0][r32] + 8u * kh;
+    constexpr uint32_t kSlotBytes = GEMM_STAGE_CHUNKS * 16u;
+
+#pragma unroll
+    for (int st = 0; st < NVG_S - 1; ++st) issue(st, (uint32_t)st);
+    uint32_t slot = 0, fill = NVG_S - 1;
+    for (int st = 0; st < nst; ++st) {
+        constexpr int kLater = GEMM_LOADS * (NVG_S - 2);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (kLater & 15) | ((kLater >> 4) << 14));
+        __builtin_amdgcn_s_barrier();
+        issue(st + NVG_S - 1, fill);
+        const uint32_t off = slot * kSlotBytes;
+        const uint32_t soa = (uint32_t)st * 16u * GEMM_TM, sob = (uint32_t)st * 16u * GEMM_TN;
+        u32x4_t a0, a1, a2, a3, b0, b1, b2, b3;
+        uint2 sa, sb;
+        asm volatile(
+            "ds_read_b128 %0, %10\n\t"
+            "ds_read_b128 %4, %14\n\t"
+            "ds_read_b128 %1, %11\n\t"
+            "ds_read_b128 %5, %15\n\t"
+            "ds_read_b128 %2, %12\n\t"
+            "ds_read_b128 %6, %16\n\t"
+            "ds_read_b128 %3, %13\n\t"
+            "ds_read_b128 %7, %17\n\t"
+            "ds_read_b64 %8, %18\n\t"
+            "ds_read_b64 %9, %19\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(b0), "=&v"(b1), "=&v"(b2),
+              "=&v"(b3), "=&v"(sa), "=&v"(sb)
+            : "v"(la[0] + off), "v"(la[1] + off), "v"(la[2] + off), "v"(la[3] + off),
+              "v"(lb[0] + off), "v"(lb[1] + off), "v"(lb[2] + off), "v"(lb[3] + off),
+              "v"(lsa + soa), "v"(lsb + sob)
+            : "memory");
+        slot = slot + 1 == NVG_S ? 0 : slot + 1;
+        fill = fill + 1 == NVG_S ? 0 : fill + 1;
+        // block scales as fp16 pairs: blocks (0,1) (2,3) (4,5) (6,7)
+        const half2_t as2[4] = {__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sa.x, 1.0f, false),
+                                __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sa.x, 1.0f, true),
+                                __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sa.y, 1.0f, false),
+                                __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sa.y, 1.0f, true)};
+        const half2_t bs2[4] = {__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb.x, 1.0f, false),
+                                __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb.x, 1.0f, true),
+                                __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb.y, 1.0f, false),
+                                __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb.y, 1.0f, true)};
+        const u32x4_t av[4] = {a0, a1, a2, a3}, bv[4] = {b0, b1, b2, b3};
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const uint32_t wa = av[j >> 2][j & 3], wb = bv[j >> 2][j & 3];
+            const int blk = j >> 1;  // 16-block within the lane's eight
+            const half8_t ao = nv_operand(wa, as2[blk >> 1], blk & 1);
+            const half8_t bo = nv_operand(wb, bs2[blk >> 1], blk & 1);
+            if (j & 1)
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ao, bo, acc1, 0, 0, 0);
+            else
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ao, bo, acc0, 0, 0, 0);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    const f32x16_t acc = acc0 + acc1;
+    const float g = sgA[0] * sgB[0];
+    const int col = n0 + r32;
+    if (col >= N) return;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int row = m0 + 32 * w + 8 * (j / 4) + 4 * kh + (j % 4);
+        if (row < M) {
+            const float v = acc[j] * g;
+            if (OUT_BF16)
+                ((uint16_t *)C)[(int64_t)row * N + col] = (uint16_t)bf16_rne_bits(v);
+            else
+                ((float *)C)[(int64_t)row * N + col] = v;
+        }
+    }
+}
+
+// Value of any E4M3FN byte: sign bit, magnitude code; 0x7F is NaN.
+__device__ __forceinline__ float e4m3_any_value_g(uint32_t s) {
+    const uint32_t mag = s & 0x7Fu;
+    const float v = mag == 0x7Fu ? __builtin_nanf("") : e4m3_pos_value(mag);
+    return (s & 0x80u) ? -v : v;
+}
+
+// Any K (a multiple of 16) and alignment: one output per thread, the
+// equation's sums in fp32 block by block.  For shapes the staged kernel does
+// not take; slow.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(GEMM_WG) void nvfp4_gemm_simple_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ As, const float *__restrict__ sgA,
+    const uint8_t *__restrict__ Bt, const uint8_t *__restrict__ Bs, const float *__restrict__ sgB,
+    int M, int N, int K, void *__restrict__ C) {
+    const int64_t idx = (int64_t)blockIdx.x * GEMM_WG + threadIdx.x;
+    if (idx >= (int64_t)M * N) return;
+    const int m = (int)(idx / N), n = (int)(idx % N);
+    const uint8_t *pa = A + (int64_t)m * (K / 2), *pb = Bt + (int64_t)n * (K / 2);
+    float acc = 0.0f;
+    for (int t = 0; t < K / 16; ++t) {
+        float dot = 0.0f;
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t ca = pa[8 * t + i], cb = pb[8 * t + i];
+            const f32x2_t va = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ca, 1.0f, 0);
+            const f32x2_t vb = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cb, 1.0f, 0);
+            dot = __builtin_fmaf(va.x, vb.x, dot);
+            dot = __builtin_fmaf(va.y, vb.y, dot);
+        }
+        const float s = e4m3_any_value_g(As[(int64_t)m * (K / 16) + t]) *
+                        e4m3_any_value_g(Bs[(int64_t)n * (K / 16) + t]);
+        acc = __builtin_fmaf(s, dot, acc);
+    }
+    const float v = acc * (sgA[0] * sgB[0]);
+    if (OUT_BF16)
+        ((uint16_t *)C)[idx] = (uint16_t)bf16_rne_bits(v);
+    else
+        ((float *)C)[idx] = v;
+}
+
+// ---------------------------------------------------------------------------
 // W4A4 linear: the activations [M, K] quantized to MXFP4 (OCP floor rule) in
 // the GEMM's own launch ("FP4, FP8 and INT8/INT4" page, section 5: the
 // quantize and MMA costs of a low-bit linear layer).  Every workgroup needs
@@ -600,6 +820,27 @@ hipError_t launch_linear_mxfp4(const void *x, bool x_bf16, const uint8_t *bt_cod
     hipError_t e = launch_mx_quantize(x, x_bf16, M * K, 0, a_codes, a_scales, status, s);
     if (e != hipSuccess) return e;
     return launch_gemm_mxfp4(a_codes, a_scales, bt_codes, bt_scales, M, N, K, c, out_bf16, s);
+}
+
+hipError_t launch_gemm_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, const float *sg_a,
+                             const uint8_t *bt_codes, const uint8_t *bt_scales, const float *sg_b,
+                             int64_t M, int64_t N, int64_t K, void *c, bool out_bf16,
+                             hipStream_t s) {
+    auto al = [](const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; };
+    if (K % 256 == 0 && K <= GEMM_MAX_K && al(a_codes, 16) && al(bt_codes, 16) &&
+        al(a_scales, 16) && al(bt_scales, 16)) {
+        dim3 grid((unsigned)((N + GEMM_TN - 1) / GEMM_TN), (unsigned)((M + GEMM_TM - 1) / GEMM_TM));
+        auto k = out_bf16 ? nvfp4_gemm_lds_kernel<true> : nvfp4_gemm_lds_kernel<false>;
+        hipLaunchKernelGGL(k, grid, dim3(GEMM_WG), 0, s, (const uint4 *)a_codes, a_scales, sg_a,
+                           (const uint4 *)bt_codes, bt_scales, sg_b, (int)M, (int)N, (int)K, c);
+        return hipGetLastError();
+    }
+    const int64_t nout = M * N;
+    auto k = out_bf16 ? nvfp4_gemm_simple_kernel<true> : nvfp4_gemm_simple_kernel<false>;
+    hipLaunchKernelGGL(k, dim3((unsigned)((nout + GEMM_WG - 1) / GEMM_WG)), dim3(GEMM_WG), 0, s,
+                       a_codes, a_scales, sg_a, bt_codes, bt_scales, sg_b, (int)M, (int)N, (int)K,
+                       c);
+    return hipGetLastError();
 }
 
 }  // namespace fp4dev

@@ -40,6 +40,12 @@ hipError_t launch_dequantize(int fmt, const uint8_t *codes, const uint8_t *scale
 hipError_t launch_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales,
                              const uint8_t *bt_codes, const uint8_t *bt_scales, int64_t M,
                              int64_t N, int64_t K, void *c, bool out_bf16, hipStream_t s);
+// NVFP4 x NVFP4: C = (s_gA s_gB) * sum over 16-blocks of the E4M3 scale
+// products times the FP4 dot products.
+hipError_t launch_gemm_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, const float *sg_a,
+                             const uint8_t *bt_codes, const uint8_t *bt_scales, const float *sg_b,
+                             int64_t M, int64_t N, int64_t K, void *c, bool out_bf16,
+                             hipStream_t s);
 // Activations x [M, K] quantized to MXFP4 into a_codes / a_scales, then the
 // GEMM with Bt; with one_launch, one kernel (grid barrier, workspace as for
 // NVFP4) when the grid fits on the device at once, else two launches.

@@ -61,8 +61,10 @@ def nv_dequant_matrix_exact(packed: np.ndarray, scales: np.ndarray, s_g, rows: i
     """p * E4M3(s_b) * s_g in binary64 for a [rows, cols] NVFP4 operand."""
     codes = unpack(np.ascontiguousarray(packed, dtype=np.uint8).reshape(-1))
     pv = np.array([e2m1_value(c) for c in range(16)])[codes]
-    sv = np.array([e4m3_value(c) if c < 127 else np.nan for c in range(128)])
-    sb = sv[np.ascontiguousarray(scales, dtype=np.uint8).reshape(-1) & 0x7F]
+    # any E4M3FN byte: the sign bit, then the magnitude code (0x7F is NaN)
+    mag = np.array([e4m3_value(c) if c < 127 else np.nan for c in range(128)])
+    sv = np.concatenate([mag, -mag])
+    sb = sv[np.ascontiguousarray(scales, dtype=np.uint8).reshape(-1)]
     return (pv.reshape(-1, 16) * sb[:, None] * float(np.float32(s_g))).reshape(rows, cols)
 
 

@@ -147,6 +147,18 @@ def test_linear_validation():
     assert lin(ac=A1) == E_ALIGN
 
 
+def test_gemm_nvfp4_validation():
+    L = fp4.lib()
+
+    def g(M=128, N=64, K=512, sga=A16, c=A16, ct=fp4.BF16):
+        return L.fp4_gemm_nvfp4(A16, A16, sga, A16, A16, A16, M, N, K, c, ct, NULL)
+    assert g(sga=NULL) == E_ARG
+    assert g(ct=6) == E_DTYPE
+    assert g(K=24) == E_SHAPE
+    assert g(N=0) == E_SHAPE
+    assert g(c=A1) == E_ALIGN
+
+
 def test_gemm_validation():
     L = fp4.lib()
 

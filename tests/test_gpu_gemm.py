@@ -153,3 +153,76 @@ def test_linear_flags_nonfinite_activations():
     with pytest.raises(ValueError):
         fp4.linear_mxfp4(dev(x), dev(torch.from_numpy(bp.reshape(N, K // 2))),
                          dev(torch.from_numpy(bsc.reshape(N, K // 32))))
+
+
+# ---- NVFP4 x NVFP4 ---------------------------------------------------------------
+
+def _nv_operands(M, N, K, seed=0):
+    a, bt = workloads.gemm_operands(M, N, K, seed_a=seed, seed_b=seed + 1)
+    ap, asc, sga, f1 = oracle.nv_quantize(a.numpy().reshape(-1))
+    bp, bsc, sgb, f2 = oracle.nv_quantize(bt.numpy().reshape(-1))
+    assert f1 == 0 and f2 == 0
+    return ap, asc, sga, bp, bsc, sgb
+
+
+def _run_nv(ap, asc, sga, bp, bsc, sgb, M, N, K, out_dtype):
+    t = lambda v: dev(torch.tensor([float(v)], dtype=torch.float32))
+    return fp4.gemm_nvfp4(dev(torch.from_numpy(ap.reshape(M, K // 2))),
+                          dev(torch.from_numpy(asc.reshape(M, K // 16))), t(sga),
+                          dev(torch.from_numpy(bp.reshape(N, K // 2))),
+                          dev(torch.from_numpy(bsc.reshape(N, K // 16))), t(sgb), out_dtype)
+
+
+def _check_nv(ops, M, N, K, what):
+    ap, asc, sga, bp, bsc, sgb = ops
+    announce(f"gemm nvfp4 {what} {M}x{N}x{K} fp32 out")
+    c32 = _run_nv(ap, asc, sga, bp, bsc, sgb, M, N, K, torch.float32)
+    announce(f"gemm nvfp4 {what} {M}x{N}x{K} bf16 out")
+    c16 = _run_nv(ap, asc, sga, bp, bsc, sgb, M, N, K, torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = og.nv_gemm_f64(ap, asc, sga, bp, bsc, sgb, M, N, K)
+    got = c32.cpu().numpy().astype(np.float64)
+    err = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert err <= REL_FROB, f"nvfp4 {what} {M}x{N}x{K}: relative Frobenius error {err:.3e}"
+    assert torch.equal(c16.cpu().view(torch.int16), c32.cpu().to(torch.bfloat16).view(torch.int16))
+    return err
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 256, 512), (70, 50, 256), (1, 33, 4096), (200, 72, 1536),
+                                   (96, 40, 272), (64, 64, 8448), (3, 5, 16)])
+def test_gemm_nvfp4_small_and_ragged(M, N, K):
+    _check_nv(_nv_operands(M, N, K), M, N, K, "random")
+
+
+def test_gemm_nvfp4_full_size_128x8192x8192():
+    err = _check_nv(_nv_operands(128, 8192, 8192), 128, 8192, 8192, "full size")
+    print(f"relative Frobenius error {err:.3e}")
+
+
+def test_gemm_nvfp4_every_code_under_every_scale():
+    # A: row r takes block scale code (r % 126) + 1 on every block and the
+    # sixteen FP4 codes in each block; B: a fixed random NVFP4 operand
+    M, N, K = 126, 64, 512
+    codes = np.tile(np.arange(16, dtype=np.uint8), M * K // 16)
+    ap = oracle.pack(codes)
+    asc = np.repeat((np.arange(M) % 126 + 1).astype(np.uint8), K // 16)
+    _, _, _, bp, bsc, sgb = _nv_operands(8, N, K, seed=7)
+    for sga in (1.0, 2.0 ** -20, 3.0):
+        _check_nv((ap, asc, np.float32(sga), bp, bsc, sgb), M, N, K, f"every code, s_gA={sga}")
+
+
+def test_gemm_nvfp4_integer_case_is_exact():
+    M, N, K = 64, 48, 256
+    ap = oracle.pack(np.full(M * K, 4, np.uint8))          # 2.0
+    bp = oracle.pack(np.full(N * K, 5, np.uint8))          # 3.0
+    asc = np.full(M * K // 16, 0x38, np.uint8)             # scale 1
+    bsc = np.full(N * K // 16, 0x38, np.uint8)
+    c = _run_nv(ap, asc, 1.0, bp, bsc, 2.0, M, N, K, torch.float32).cpu().numpy()
+    assert np.all(c == K * 6.0 * 2.0)
+
+
+def test_gemm_nvfp4_deterministic():
+    ops = _nv_operands(128, 1024, 2048, seed=4)
+    c1 = _run_nv(*ops, 128, 1024, 2048, torch.float32)
+    c2 = _run_nv(*ops, 128, 1024, 2048, torch.float32)
+    assert torch.equal(c1, c2)
