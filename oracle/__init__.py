@@ -54,6 +54,10 @@ def lib():
         "or_block_loss32_pow2": (F, [P, I]),
         "or_mx_quantize_rule": (I, [P, I, I64, I, P, P]),
         "or_scale_search_all": (I, [P, I, I64, F, P, P, P]),
+        "or_padded_storage_bytes": (I64, [I64, I64, I, I64]),
+        "or_mx_quantize_padded": (I, [P, I, I64, I64, P, P]),
+        "or_nv_quantize_padded": (I, [P, I, I64, I64, P, P, P]),
+        "or_dequantize_padded": (I, [I, P, P, F, I64, I64, I, P]),
         "or_nv_global_scale": (I, [P, I, I64, P]),
         "or_nv_quantize": (I, [P, I, I64, F, P, P]),
         "or_dequantize": (None, [I, P, P, F, I64, I, P]),
@@ -134,6 +138,53 @@ def block_loss(xb: np.ndarray, alpha: float) -> float:
 
 def storage_bytes(elements: int, block: int, global_bytes: int) -> int:
     return lib().or_storage_bytes(elements, block, global_bytes)
+
+
+def padded_storage_bytes(rows: int, cols: int, block: int, global_bytes: int) -> int:
+    return lib().or_padded_storage_bytes(rows, cols, block, global_bytes)
+
+
+def _padded_cols(cols: int, block: int) -> int:
+    return (cols + block - 1) // block * block
+
+
+def mx_quantize_padded(x: np.ndarray, rows: int, cols: int):
+    """MXFP4 quantize of a [rows, cols] matrix, rows zero-padded to whole
+    blocks.  Returns (packed [rows * pc / 2], scales [rows * pc / 32], flags)."""
+    x, dt = _as_input(x)
+    assert x.size == rows * cols
+    pc = _padded_cols(cols, 32)
+    packed = np.empty(rows * pc // 2, np.uint8)
+    scales = np.empty(rows * pc // 32, np.uint8)
+    flags = lib().or_mx_quantize_padded(_ptr(x), dt, rows, cols, _ptr(packed), _ptr(scales))
+    assert flags >= 0
+    return packed, scales, flags
+
+
+def nv_quantize_padded(x: np.ndarray, rows: int, cols: int):
+    """NVFP4 quantize, rows zero-padded to whole 16-blocks.  Returns
+    (packed, scales, s_g, flags)."""
+    x, dt = _as_input(x)
+    assert x.size == rows * cols
+    pc = _padded_cols(cols, 16)
+    packed = np.zeros(rows * pc // 2, np.uint8)
+    scales = np.zeros(rows * pc // 16, np.uint8)
+    sg = np.zeros(1, np.float32)
+    flags = lib().or_nv_quantize_padded(_ptr(x), dt, rows, cols, _ptr(packed), _ptr(scales), _ptr(sg))
+    assert flags >= 0
+    return packed, scales, sg[0], flags
+
+
+def dequantize_padded(fmt: int, packed: np.ndarray, scales: np.ndarray, rows: int, cols: int,
+                      s_g=1.0, out_bf16=False):
+    """Dequantize a row-padded layout and crop to [rows, cols]."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    y = np.empty(rows * cols, np.uint16 if out_bf16 else np.float32)
+    r = lib().or_dequantize_padded(int(fmt), _ptr(packed), _ptr(scales), float(np.float32(s_g)),
+                                   rows, cols, DT_BF16 if out_bf16 else DT_F32, _ptr(y))
+    assert r == 0
+    return y
 
 
 def pack(codes: np.ndarray) -> np.ndarray:

@@ -23,6 +23,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define OR_FLAG_NONFINITE 1
@@ -581,3 +582,70 @@ int or_ideal_code(float x, float alpha) { return or_e2m1_round(x / alpha); }
 int64_t or_storage_bytes(int64_t elements, int block, int64_t global_bytes) {
     return elements / 2 + elements / block + global_bytes;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Row-padded layout ([FMT] section 8: an R x K matrix whose rows are padded */
+/* to whole blocks holds B = R * ceil(K / G) blocks and B (G/2 + 1) bytes,   */
+/* plus 4 for the NVFP4 tensor scale; decoding restores the padded layout   */
+/* and crops each row to the logical shape kept as metadata).  Readings:    */
+/* the padding elements are zeros (code 0), so they change no block amax;   */
+/* the NVFP4 tensor scale is that of the logical elements.  Each routine    */
+/* builds the zero-padded matrix and runs the complete-block routine on it. */
+/* ------------------------------------------------------------------------ */
+
+static float *padded_copy(const void *x, int dt, int64_t rows, int64_t cols, int block,
+                          int64_t *pcols) {
+    int64_t pc = (cols + block - 1) / block * block;
+    float *xp = (float *)calloc((size_t)(rows * pc), sizeof(float));
+    if (!xp) return NULL;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) xp[r * pc + c] = load_elem(x, dt, r * cols + c);
+    *pcols = pc;
+    return xp;
+}
+
+int64_t or_padded_storage_bytes(int64_t rows, int64_t cols, int block, int64_t global_bytes) {
+    int64_t nb = rows * ((cols + block - 1) / block);
+    return nb * (block / 2 + 1) + global_bytes;
+}
+
+/* packed: rows * pcols / 2 bytes; scales: rows * pcols / 32.  Returns flags,
+ * or -1 if memory ran out. */
+int or_mx_quantize_padded(const void *x, int dt, int64_t rows, int64_t cols, uint8_t *packed,
+                          uint8_t *scales) {
+    int64_t pc;
+    float *xp = padded_copy(x, dt, rows, cols, 32, &pc);
+    if (!xp) return -1;
+    int f = or_mx_quantize(xp, OR_DT_F32, rows * pc, packed, scales);
+    free(xp);
+    return f;
+}
+
+/* s_g is read from the logical elements (or_nv_global_scale), then the
+ * padded matrix is quantized with it.  Returns flags, or -1. */
+int or_nv_quantize_padded(const void *x, int dt, int64_t rows, int64_t cols, uint8_t *packed,
+                          uint8_t *scales, float *s_g) {
+    int f = or_nv_global_scale(x, dt, rows * cols, s_g);
+    if (f) return f;
+    int64_t pc;
+    float *xp = padded_copy(x, dt, rows, cols, 16, &pc);
+    if (!xp) return -1;
+    f |= or_nv_quantize(xp, OR_DT_F32, rows * pc, *s_g, packed, scales);
+    free(xp);
+    return f;
+}
+
+/* Dequantize a padded layout and crop each row to cols values. */
+int or_dequantize_padded(int fmt, const uint8_t *packed, const uint8_t *scales, float s_g,
+                         int64_t rows, int64_t cols, int out_dt, void *y) {
+    int block = fmt == 0 ? 32 : 16;
+    int64_t pc = (cols + block - 1) / block * block;
+    float *yp = (float *)malloc((size_t)(rows * pc) * sizeof(float));
+    if (!yp) return -1;
+    or_dequantize(fmt, packed, scales, s_g, rows * pc, OR_DT_F32, yp);
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) store_out(y, out_dt, r * cols + c, yp[r * pc + c]);
+    free(yp);
+    return 0;
+}
+

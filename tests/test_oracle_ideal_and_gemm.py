@@ -39,7 +39,10 @@ def test_block_size_mae_matches_glossary():
 
 
 def test_storage_bytes_match_page():
-    for n, block, gb, want in rows("storage_bytes.txt"):
+    for r in rows("storage_bytes.txt"):
+        if r[0] == "padded":        # the row-padded layout, pinned with its encoders
+            continue
+        n, block, gb, want = r
         assert oracle.storage_bytes(int(n), int(block), int(gb)) == int(want)
 
 
