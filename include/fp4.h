@@ -247,6 +247,34 @@ fp4_status fp4_linear_mxfp4(const void *x, fp4_dtype xt, int64_t M, int64_t K,
                             fp4_linear_mode mode, void *workspace, size_t workspace_bytes,
                             int32_t *status, void *stream);
 
+/*
+ * Row-padded layout ("NVFP4 / MXFP4 format" page, section 8): each row of a
+ * [rows, cols] matrix is padded with zeros to whole blocks (32 for MXFP4, 16
+ * for NVFP4), pcols = ceil(cols / block) * block, and the padded matrix is
+ * quantized: codes [rows, pcols/2] (padding codes are 0), scales
+ * [rows, pcols/block]; the NVFP4 tensor scale is that of the rows*cols
+ * logical values.  The logical cols is the metadata the decode needs.
+ *   fp4_quantize_padded: any cols >= 1; x 2-byte (bf16) or 4-byte (fp32)
+ *     aligned, codes 4-byte aligned; global_scale, workspace and
+ *     workspace_bytes as for fp4_quantize_nvfp4 (NVFP4 only, ignored for
+ *     MXFP4); status as for the format's quantize.  Identical to
+ *     fp4_quantize_mxfp4 / _nvfp4 when cols is a multiple of the block.
+ *   fp4_dequantize_padded: decodes the padded layout and writes only the
+ *     logical [rows, cols] values of y (fp32 or bf16), as fp4_dequantize.
+ *   fp4_padded_storage_bytes: rows * ceil(cols/block) * (block/2 + 1), plus
+ *     4 for NVFP4's tensor scale (-1 for invalid arguments).
+ * Values are moved one by one (rows need not be aligned): these are for
+ * shapes the block-aligned entry points reject.  Deterministic.
+ */
+fp4_status fp4_quantize_padded(fp4_format fmt, const void *x, fp4_dtype xt, int64_t rows,
+                               int64_t cols, uint8_t *codes, uint8_t *scales,
+                               float *global_scale, void *workspace, size_t workspace_bytes,
+                               int32_t *status, void *stream);
+fp4_status fp4_dequantize_padded(fp4_format fmt, const uint8_t *codes, const uint8_t *scales,
+                                 const float *global_scale, int64_t rows, int64_t cols, void *y,
+                                 fp4_dtype yt, void *stream);
+int64_t fp4_padded_storage_bytes(fp4_format fmt, int64_t rows, int64_t cols);
+
 /* Bytes of device workspace fp4_quantize_nvfp4 / fp4_scale_search need for a
  * [rows, cols] input (0 for MXFP4). */
 size_t fp4_workspace_bytes(fp4_format fmt, int64_t rows, int64_t cols);

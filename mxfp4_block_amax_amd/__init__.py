@@ -42,7 +42,8 @@ FLAG_BARRIER_TIMEOUT = 4
 
 EXPORTS = ("fp4_quantize_mxfp4", "fp4_quantize_mxfp4_rule", "fp4_quantize_nvfp4",
            "fp4_dequantize", "fp4_scale_search", "fp4_scale_search_exhaustive",
-           "fp4_gemm_mxfp4", "fp4_gemm_nvfp4", "fp4_linear_mxfp4", "fp4_workspace_bytes",
+           "fp4_gemm_mxfp4", "fp4_gemm_nvfp4", "fp4_linear_mxfp4", "fp4_quantize_padded",
+           "fp4_dequantize_padded", "fp4_padded_storage_bytes", "fp4_workspace_bytes",
            "fp4_status_str")
 
 # fp4_mx_rule: the MXFP4 block-exponent rules
@@ -74,6 +75,10 @@ def lib() -> ctypes.CDLL:
     L.fp4_scale_search.argtypes = [P, I, I64, I64, I32, I32, F, F, P, P, P, P, S, P, P]
     L.fp4_gemm_mxfp4.argtypes = [P, P, P, P, I64, I64, I64, P, I, P]
     L.fp4_gemm_nvfp4.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, I, P]
+    L.fp4_quantize_padded.argtypes = [I, P, I, I64, I64, P, P, P, P, S, P, P]
+    L.fp4_dequantize_padded.argtypes = [I, P, P, P, I64, I64, P, I, P]
+    L.fp4_padded_storage_bytes.argtypes = [I, I64, I64]
+    L.fp4_padded_storage_bytes.restype = I64
     L.fp4_linear_mxfp4.argtypes = [P, I, I64, I64, P, P, I64, P, P, P, I, I, P, S, P, P]
     L.fp4_workspace_bytes.argtypes = [I, I64, I64]
     L.fp4_workspace_bytes.restype = S
@@ -81,7 +86,8 @@ def lib() -> ctypes.CDLL:
     L.fp4_status_str.restype = ctypes.c_char_p
     for name in ("fp4_quantize_mxfp4", "fp4_quantize_mxfp4_rule", "fp4_quantize_nvfp4",
                  "fp4_dequantize", "fp4_scale_search", "fp4_scale_search_exhaustive",
-                 "fp4_gemm_mxfp4", "fp4_gemm_nvfp4", "fp4_linear_mxfp4"):
+                 "fp4_gemm_mxfp4", "fp4_gemm_nvfp4", "fp4_linear_mxfp4", "fp4_quantize_padded",
+                 "fp4_dequantize_padded"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -311,3 +317,44 @@ def linear_mxfp4(x: torch.Tensor, bt_codes: torch.Tensor, bt_scales: torch.Tenso
                                workspace.numel(), _ptr(status), _stream(x)))
     _finish(status, check)
     return c, (a_codes, a_scales)
+
+
+def _padded_cols(cols: int, fmt: int) -> int:
+    block = 32 if fmt == MXFP4 else 16
+    return (cols + block - 1) // block * block
+
+
+def quantize_padded(fmt: int, x: torch.Tensor, check: bool = True, status=None, workspace=None):
+    """Quantize a [rows, cols] tensor, rows zero-padded to whole blocks.
+    Returns (codes [rows, pcols/2], scales [rows, pcols/block], s_g or None)."""
+    rows, cols = _rows_cols(x)
+    pc = _padded_cols(cols, fmt)
+    block = 32 if fmt == MXFP4 else 16
+    codes = torch.empty(rows, pc // 2, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(rows, pc // block, dtype=torch.uint8, device=x.device)
+    s_g = torch.empty(1, dtype=torch.float32, device=x.device) if fmt == NVFP4 else None
+    if fmt == NVFP4 and workspace is None:
+        workspace = new_workspace(rows, pc, x.device)
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _ok(lib().fp4_quantize_padded(int(fmt), _ptr(x), _dtype_code(x.dtype), rows, cols, _ptr(codes),
+                                  _ptr(scales), _ptr(s_g), _ptr(workspace),
+                                  0 if workspace is None else workspace.numel(), _ptr(status),
+                                  _stream(x)))
+    _finish(status, check)
+    return codes, scales, s_g
+
+
+def dequantize_padded(fmt: int, codes: torch.Tensor, scales: torch.Tensor, cols: int,
+                      global_scale=None, out_dtype=torch.bfloat16):
+    """Decode a row-padded layout to [rows, cols]."""
+    rows = codes.shape[0]
+    y = torch.empty(rows, cols, dtype=out_dtype, device=codes.device)
+    _ok(lib().fp4_dequantize_padded(int(fmt), _ptr(codes), _ptr(scales), _ptr(global_scale), rows,
+                                    cols, _ptr(y), _dtype_code(out_dtype), _stream(codes)))
+    return y
+
+
+def padded_storage_bytes(fmt: int, rows: int, cols: int) -> int:
+    return int(lib().fp4_padded_storage_bytes(int(fmt), int(rows), int(cols)))
+

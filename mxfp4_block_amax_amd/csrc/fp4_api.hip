@@ -186,6 +186,51 @@ fp4_status fp4_linear_mxfp4(const void *x, fp4_dtype xt, int64_t M, int64_t K,
                                                 (hipStream_t)stream));
 }
 
+fp4_status fp4_quantize_padded(fp4_format fmt, const void *x, fp4_dtype xt, int64_t rows,
+                               int64_t cols, uint8_t *codes, uint8_t *scales,
+                               float *global_scale, void *workspace, size_t workspace_bytes,
+                               int32_t *status, void *stream) {
+    if (fmt != FP4_MXFP4 && fmt != FP4_NVFP4) return FP4_E_DTYPE;
+    if (!valid_dtype(xt)) return FP4_E_DTYPE;
+    if (!x || !codes || !scales) return FP4_E_ARG;
+    if (fmt == FP4_NVFP4 && !global_scale) return FP4_E_ARG;
+    const int64_t block = fmt == FP4_MXFP4 ? 32 : 16;
+    if (rows < 1 || cols < 1 || cols > kMaxElems) return FP4_E_SHAPE;
+    const int64_t pcols = (cols + block - 1) / block * block;
+    if (rows > kMaxElems / pcols) return FP4_E_SHAPE;
+    if (fmt == FP4_NVFP4 && (!workspace || workspace_bytes < nv_workspace())) return FP4_E_WORKSPACE;
+    if (!aligned(x, xt == FP4_BF16 ? 2 : 4) || !aligned(codes, 4) || !aligned(status, 4) ||
+        !aligned(global_scale, 4) || !aligned(workspace, 16))
+        return FP4_E_ALIGN;
+    return from_hip(fp4dev::launch_quantize_padded((int)fmt, x, xt == FP4_BF16, rows, cols, codes,
+                                                   scales, global_scale, workspace, status,
+                                                   (hipStream_t)stream));
+}
+
+fp4_status fp4_dequantize_padded(fp4_format fmt, const uint8_t *codes, const uint8_t *scales,
+                                 const float *global_scale, int64_t rows, int64_t cols, void *y,
+                                 fp4_dtype yt, void *stream) {
+    if (fmt != FP4_MXFP4 && fmt != FP4_NVFP4) return FP4_E_DTYPE;
+    if (!valid_dtype(yt)) return FP4_E_DTYPE;
+    if (!codes || !scales || !y) return FP4_E_ARG;
+    if (fmt == FP4_NVFP4 && !global_scale) return FP4_E_ARG;
+    const int64_t block = fmt == FP4_MXFP4 ? 32 : 16;
+    if (rows < 1 || cols < 1 || cols > kMaxElems) return FP4_E_SHAPE;
+    if (rows > kMaxElems / ((cols + block - 1) / block * block)) return FP4_E_SHAPE;
+    if (!aligned(codes, 4) || !aligned(y, yt == FP4_BF16 ? 2 : 4) || !aligned(global_scale, 4))
+        return FP4_E_ALIGN;
+    return from_hip(fp4dev::launch_dequantize_padded((int)fmt, codes, scales, global_scale, rows,
+                                                     cols, y, yt == FP4_BF16,
+                                                     (hipStream_t)stream));
+}
+
+int64_t fp4_padded_storage_bytes(fp4_format fmt, int64_t rows, int64_t cols) {
+    if ((fmt != FP4_MXFP4 && fmt != FP4_NVFP4) || rows < 1 || cols < 1) return -1;
+    const int64_t block = fmt == FP4_MXFP4 ? 32 : 16;
+    const int64_t blocks = rows * ((cols + block - 1) / block);
+    return blocks * (block / 2 + 1) + (fmt == FP4_NVFP4 ? 4 : 0);
+}
+
 size_t fp4_workspace_bytes(fp4_format fmt, int64_t rows, int64_t cols) {
     (void)rows;
     (void)cols;

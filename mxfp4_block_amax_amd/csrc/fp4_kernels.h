@@ -37,6 +37,14 @@ hipError_t launch_scale_search(const void *x, bool bf16, int64_t n, bool all, fl
 hipError_t launch_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales,
                              const float *global_scale, int64_t n, void *y, bool out_bf16,
                              hipStream_t s);
+// Row-padded layout: rows of cols values padded with zeros to whole blocks
+// (32 MXFP4, 16 NVFP4); codes [rows, pcols/2], scales [rows, pcols/block].
+hipError_t launch_quantize_padded(int fmt, const void *x, bool bf16, int64_t rows, int64_t cols,
+                                  uint8_t *codes, uint8_t *scales, float *global_scale,
+                                  void *workspace, int32_t *status, hipStream_t s);
+hipError_t launch_dequantize_padded(int fmt, const uint8_t *codes, const uint8_t *scales,
+                                    const float *global_scale, int64_t rows, int64_t cols,
+                                    void *y, bool out_bf16, hipStream_t s);
 hipError_t launch_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales,
                              const uint8_t *bt_codes, const uint8_t *bt_scales, int64_t M,
                              int64_t N, int64_t K, void *c, bool out_bf16, hipStream_t s);

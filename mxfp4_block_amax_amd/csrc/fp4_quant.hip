@@ -834,6 +834,157 @@ __global__ __launch_bounds__(WG) void scale_search_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Row-padded layout ("NVFP4 / MXFP4 format" page, section 8): each row of
+// cols values is padded with zeros to whole blocks of the format, and codes
+// and scales are those of the padded [rows, pcols] matrix; decoding crops
+// each row back to cols.  Padded chunk c (8 values) is row c / cpr, columns
+// (c % cpr) * 8 .. + 8 (cpr = pcols / 8); columns at or past cols read as 0.
+// Rows need not be aligned, so values move one by one (this layout is for
+// shapes the block-aligned kernels do not take).
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__device__ __forceinline__ uint32_t padded_values(const void *__restrict__ x, int64_t cols,
+                                                  int64_t cpr, int64_t c, bool ok, float (&v)[8]) {
+    const int64_t r = ok ? c / cpr : 0, j0 = ok ? (c % cpr) * 8 : 0;
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t j = j0 + i;
+        uint32_t b = 0;
+        if (ok && j < cols)
+            b = BF16 ? (uint32_t)((const uint16_t *)x)[r * cols + j] << 16
+                     : ((const uint32_t *)x)[r * cols + j];
+        v[i] = u2f(b);
+        m = max(m, b & 0x7FFFFFFFu);
+    }
+    return m;  // fp32 pattern of the chunk amax (non-finite patterns sort above)
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(WG) void mx_quantize_padded_kernel(const void *__restrict__ x,
+                                                                int64_t cols, int64_t cpr,
+                                                                int64_t nchunks,
+                                                                uint32_t *__restrict__ codes,
+                                                                uint8_t *__restrict__ scales,
+                                                                int32_t *status) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int64_t wave = (int64_t)blockIdx.x * WAVES_PER_WG + (threadIdx.x / WAVE);
+    const int64_t nwaves = (int64_t)gridDim.x * WAVES_PER_WG;
+    uint32_t flags = 0;
+    for (int64_t t = wave; t * WAVE < nchunks; t += nwaves) {
+        const int64_t c = t * WAVE + lane;  // four lanes hold a block (cpr is a multiple of 4)
+        float v[8];
+        uint32_t m = padded_values<BF16>(x, cols, cpr, c, c < nchunks, v);
+        m = max(m, dpp<QP_XOR1>(m));
+        m = max(m, dpp<QP_XOR2>(m));
+        if ((m >> 23) >= 0xFFu) flags |= FLAG_NONFINITE;
+        const uint32_t sb = mx_scale_byte(m, 23);
+        const uint32_t q = cvt_fp4x8_f32(v, e8m0_operand(sb));
+        if (c < nchunks) {
+            codes[c] = q;
+            if ((lane & 3) == 0) scales[c >> 2] = (uint8_t)sb;
+        }
+    }
+    report_flags(status, flags);
+}
+
+// NVFP4 pass 1 on the padded layout: one partial max (fp32 pattern) per
+// workgroup; the zero padding changes no amax.
+template <bool BF16>
+__global__ __launch_bounds__(WG) void padded_amax_kernel(const void *__restrict__ x, int64_t cols,
+                                                         int64_t cpr, int64_t nchunks,
+                                                         uint32_t *__restrict__ partials) {
+    __shared__ uint32_t red[WAVES_PER_WG];
+    uint32_t m = 0;
+    const int64_t stride = (int64_t)gridDim.x * WG;
+    for (int64_t c = (int64_t)blockIdx.x * WG + threadIdx.x; c < nchunks; c += stride) {
+        float v[8];
+        m = max(m, padded_values<BF16>(x, cols, cpr, c, true, v));
+    }
+    m = wave_max_u32(m);
+    if ((threadIdx.x & (WAVE - 1)) == 0) red[threadIdx.x / WAVE] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = red[0];
+        for (int i = 1; i < WAVES_PER_WG; ++i) r = max(r, red[i]);
+        partials[blockIdx.x] = r;
+    }
+}
+
+// NVFP4 pass 2 on the padded layout: a lane pair holds a block; each lane
+// derives the block scale (the same in both) and divides with the
+// reciprocal-correction divide.
+template <bool BF16>
+__global__ __launch_bounds__(WG) void nv_quantize_padded_kernel(
+    const void *__restrict__ x, int64_t cols, int64_t cpr, int64_t nchunks,
+    const uint32_t *__restrict__ partials, int npart, uint32_t *__restrict__ codes,
+    uint8_t *__restrict__ scales, float *__restrict__ global_scale, int32_t *status) {
+    __shared__ NvScaleTable T;
+    TensorScale ts = tensor_scale<false>(partials, npart);  // fp32 patterns
+    if (blockIdx.x == 0 && threadIdx.x == 0) *global_scale = ts.s_g;
+    if (ts.flags) {
+        if (blockIdx.x == 0 && threadIdx.x == 0 && status) atomicOr(status, (int32_t)ts.flags);
+        return;
+    }
+    nv_table_build(T, ts.s_g);
+    __syncthreads();
+    const CodeGuess G = make_code_guess(ts.s_g);
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int64_t wave = (int64_t)blockIdx.x * WAVES_PER_WG + (threadIdx.x / WAVE);
+    const int64_t nwaves = (int64_t)gridDim.x * WAVES_PER_WG;
+    uint32_t flags = 0;
+    for (int64_t t = wave; t * WAVE < nchunks; t += nwaves) {
+        const int64_t c = t * WAVE + lane;
+        float v[8];
+        uint32_t m = padded_values<BF16>(x, cols, cpr, c, c < nchunks, v);
+        m = max(m, dpp<QP_XOR1>(m));
+        const BlockScale b = nv_block_scale(T, m, G, flags);
+        const uint32_t q = nv_quant8<false>(v, b.ad, b.y, b.sc);
+        if (c < nchunks) {
+            codes[c] = q;
+            if ((lane & 1) == 0) scales[c >> 1] = (uint8_t)b.code;
+        }
+    }
+    report_flags(status, flags);
+}
+
+// Decode of the padded layout, cropped to cols per row: the values of
+// dequant_chunk, stored one by one.
+template <int FMT, bool OUT_BF16>
+__global__ __launch_bounds__(WG) void dequant_padded_kernel(const uint32_t *__restrict__ codes,
+                                                            const uint8_t *__restrict__ scales,
+                                                            const float *__restrict__ global_scale,
+                                                            int64_t cols, int64_t cpr,
+                                                            int64_t nchunks, void *__restrict__ y) {
+    const float s_g = (FMT == 1) ? *global_scale : 1.0f;
+    const int64_t stride = (int64_t)gridDim.x * WG;
+    for (int64_t c = (int64_t)blockIdx.x * WG + threadIdx.x; c < nchunks; c += stride) {
+        const uint32_t q = codes[c];
+        const uint32_t sb = scales[FMT == 0 ? (c >> 2) : (c >> 1)];
+        const float so = FMT == 0 ? e8m0_operand(sb) : e8m0_operand(E8M0_ONE);
+        const float alpha = FMT == 0 ? 1.0f : s_g * e4m3_any_value(sb);
+        float v[8];
+        const f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, so, 0);
+        const f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, so, 1);
+        const f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, so, 2);
+        const f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, so, 3);
+        v[0] = p0.x; v[1] = p0.y; v[2] = p1.x; v[3] = p1.y;
+        v[4] = p2.x; v[5] = p2.y; v[6] = p3.x; v[7] = p3.y;
+        const int64_t r = c / cpr, j0 = (c % cpr) * 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float o = FMT == 0 ? v[i] : v[i] * alpha;
+            if (FMT == 0 && sb == 0xFFu) o = __builtin_nanf("");
+            const int64_t j = j0 + i;
+            if (j < cols) {
+                if (OUT_BF16) ((uint16_t *)y)[r * cols + j] = (uint16_t)bf16_rne(o);
+                else ((float *)y)[r * cols + j] = o;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 static inline int grid_for(int64_t waves_needed, int max_wg) {
@@ -983,6 +1134,46 @@ hipError_t launch_dequantize(int fmt, const uint8_t *codes, const uint8_t *scale
         else FP4_DQ(1, false);
     }
 #undef FP4_DQ
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_padded(int fmt, const void *x, bool bf16, int64_t rows, int64_t cols,
+                                  uint8_t *codes, uint8_t *scales, float *global_scale,
+                                  void *workspace, int32_t *status, hipStream_t s) {
+    const int block = fmt == 0 ? 32 : 16;
+    const int64_t pcols = (cols + block - 1) / block * block;
+    const int64_t cpr = pcols / 8, nchunks = rows * cpr;
+    const int g = grid_for((nchunks + WAVE - 1) / WAVE, kMaxGrid);
+    if (fmt == 0) {
+        auto k = bf16 ? mx_quantize_padded_kernel<true> : mx_quantize_padded_kernel<false>;
+        hipLaunchKernelGGL(k, dim3(g), dim3(WG), 0, s, x, cols, cpr, nchunks, (uint32_t *)codes,
+                           scales, status);
+        return hipGetLastError();
+    }
+    uint32_t *partials = (uint32_t *)workspace;
+    const int g1 = amax_grid(nchunks);
+    auto ka = bf16 ? padded_amax_kernel<true> : padded_amax_kernel<false>;
+    hipLaunchKernelGGL(ka, dim3(g1), dim3(WG), 0, s, x, cols, cpr, nchunks, partials);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    auto kq = bf16 ? nv_quantize_padded_kernel<true> : nv_quantize_padded_kernel<false>;
+    hipLaunchKernelGGL(kq, dim3(g), dim3(WG), 0, s, x, cols, cpr, nchunks, partials, g1,
+                       (uint32_t *)codes, scales, global_scale, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequantize_padded(int fmt, const uint8_t *codes, const uint8_t *scales,
+                                    const float *global_scale, int64_t rows, int64_t cols,
+                                    void *y, bool out_bf16, hipStream_t s) {
+    const int block = fmt == 0 ? 32 : 16;
+    const int64_t cpr = (cols + block - 1) / block * block / 8, nchunks = rows * cpr;
+    const int g = grid_for((nchunks + WAVE - 1) / WAVE, kMaxGrid);
+    using K = void (*)(const uint32_t *, const uint8_t *, const float *, int64_t, int64_t,
+                       int64_t, void *);
+    static const K kernels[2][2] = {{dequant_padded_kernel<0, false>, dequant_padded_kernel<0, true>},
+                                    {dequant_padded_kernel<1, false>, dequant_padded_kernel<1, true>}};
+    hipLaunchKernelGGL(kernels[fmt][out_bf16 ? 1 : 0], dim3(g), dim3(WG), 0, s,
+                       (const uint32_t *)codes, scales, global_scale, cols, cpr, nchunks, y);
     return hipGetLastError();
 }
 

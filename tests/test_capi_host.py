@@ -159,6 +159,25 @@ def test_gemm_nvfp4_validation():
     assert g(c=A1) == E_ALIGN
 
 
+def test_padded_storage_and_validation():
+    # the format page's section 8: two rows of 17 values, NVFP4 -> 40 bytes
+    assert fp4.padded_storage_bytes(fp4.NVFP4, 2, 17) == 40
+    assert fp4.padded_storage_bytes(fp4.MXFP4, 2, 17) == 2 * (16 + 1)
+    assert fp4.padded_storage_bytes(fp4.NVFP4, 0, 17) == -1
+    L = fp4.lib()
+
+    def q(fmt=fp4.NVFP4, rows=2, cols=17, sg=A16, ws=A16, wsb=1 << 20, x=A16, codes=A16):
+        return L.fp4_quantize_padded(fmt, x, fp4.BF16, rows, cols, codes, A16, sg, ws, wsb, NULL,
+                                     NULL)
+    assert q(fmt=5) == E_DTYPE
+    assert q(sg=NULL) == E_ARG
+    assert q(cols=0) == E_SHAPE
+    assert q(ws=NULL) == E_WORKSPACE
+    assert q(x=A1) == E_ALIGN
+    assert q(codes=ctypes.c_void_p(0x10002)) == E_ALIGN
+    assert L.fp4_dequantize_padded(fp4.MXFP4, A16, A16, NULL, 2, 0, A16, fp4.BF16, NULL) == E_SHAPE
+
+
 def test_gemm_validation():
     L = fp4.lib()
 
