@@ -54,6 +54,7 @@ import workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 FP4_DENSE_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 MFMA, published
+FP16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 MFMA, published
 METRIC = "quantize GB/s (bytes in+out) and % of HBM peak; Gelem/s, NVFP4 & MXFP4"
 
 
@@ -339,6 +340,18 @@ def extra_workloads():
                          for b in bq])
     d["two_launches_us"] = round(ms2 * 1e3, 2)
     out["mxfp4_linear_w4a4_128x8192x8192_bf16"] = d
+    # NVFP4 x NVFP4 GEMM, same shape: operands NVFP4-quantized on the GPU,
+    # eight copies of B rotate
+    an = fp4.quantize_nvfp4(a.cuda())
+    bn = [fp4.quantize_nvfp4(bt.cuda()) for _ in range(8)]
+    ms = time_rotating([lambda b=b: fp4.gemm_nvfp4(an[0], an[1], an[2], b[0], b[1], b[2], out=c)
+                        for b in bn])
+    nv_bytes = M * K // 2 + M * K // 16 + N * K // 2 + N * K // 16 + 8 + M * N * 2
+    d = _rate(nv_bytes, ms)
+    tf = gemm_flops(M, N, K) / ms / 1e9
+    d.update({"TFLOP/s": round(tf, 1),
+              "pct_fp16_mfma_peak": round(100 * tf / FP16_DENSE_PEAK_TFLOPS, 2)})
+    out["nvfp4_gemm_128x8192x8192_bf16out"] = d
     if int(st.item()) != 0:
         raise RuntimeError(f"a timed call raised status flags {int(st.item())}")
     return out
