@@ -67,6 +67,10 @@ def lib():
         "or_ideal_roundtrip": (None, [P, I64, I, P]),
         "or_ideal_code": (I, [F, F]),
         "or_storage_bytes": (I64, [I64, I, I64]),
+        "or_sr_bits": (ctypes.c_uint32, [ctypes.c_uint64, I64]),
+        "or_e2m1_round_sr": (I, [F, ctypes.c_uint32]),
+        "or_mx_quantize_sr": (I, [P, I, I64, ctypes.c_uint64, P, P]),
+        "or_nv_quantize_sr": (I, [P, I, I64, F, ctypes.c_uint64, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -275,6 +279,48 @@ def nv_quantize(x: np.ndarray):
         return (np.zeros(n // 2, np.uint8), np.zeros(n // 16, np.uint8), s_g, f1)
     packed, scales, f2 = nv_quantize_with_scale(x, s_g)
     return packed, scales, s_g, f1 | f2
+
+
+# ---- stochastic rounding ----------------------------------------------------
+
+def sr_bits(seed: int, i: int) -> int:
+    """The 24 random bits element i draws (SplitMix64 on the counter)."""
+    return int(lib().or_sr_bits(int(seed) & (2**64 - 1), int(i)))
+
+
+def e2m1_round_sr(q: float, r24: int) -> int:
+    """Stochastic E2M1 code of fp32 q given 24 random bits."""
+    return lib().or_e2m1_round_sr(float(np.float32(q)), int(r24))
+
+
+def mx_quantize_sr(x: np.ndarray, seed: int):
+    """MXFP4 quantize (OCP floor scale) with stochastic element rounding."""
+    x, dt = _as_input(x)
+    n = x.size
+    if n % 32:
+        raise ValueError("MXFP4 needs complete 32-element blocks")
+    packed = np.empty(n // 2, np.uint8)
+    scales = np.empty(n // 32, np.uint8)
+    flags = lib().or_mx_quantize_sr(_ptr(x), dt, n, int(seed) & (2**64 - 1), _ptr(packed),
+                                    _ptr(scales))
+    return packed, scales, flags
+
+
+def nv_quantize_sr(x: np.ndarray, seed: int):
+    """NVFP4 quantize with stochastic element rounding (block scales and
+    s_g as the deterministic encoder).  Returns (packed, scales, s_g, flags)."""
+    s_g, f1 = nv_global_scale(x)
+    x, dt = _as_input(x)
+    n = x.size
+    if n % 16:
+        raise ValueError("NVFP4 needs complete 16-element blocks")
+    if f1:
+        return (np.zeros(n // 2, np.uint8), np.zeros(n // 16, np.uint8), s_g, f1)
+    packed = np.empty(n // 2, np.uint8)
+    scales = np.empty(n // 16, np.uint8)
+    f2 = lib().or_nv_quantize_sr(_ptr(x), dt, n, float(s_g), int(seed) & (2**64 - 1),
+                                 _ptr(packed), _ptr(scales))
+    return packed, scales, s_g, f2
 
 
 def dequantize(fmt: int, packed: np.ndarray, scales: np.ndarray, s_g=1.0, out_bf16=False):

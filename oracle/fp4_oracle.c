@@ -649,3 +649,98 @@ int or_dequantize_padded(int fmt, const uint8_t *packed, const uint8_t *scales, 
     return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Stochastic rounding to E2M1 ([GLOS] section "Inferenza e addestramento   */
+/* FP4": NVFP4 pretraining rounds gradients stochastically; the pages give   */
+/* no rule, only the name).                                                  */
+/* Readings: the quotient q is the deterministic path's (fp32 correctly      */
+/* rounded); |q| >= 6 saturates; otherwise with lo <= |q| < hi the two       */
+/* neighbouring E2M1 magnitudes, q rounds up with probability (|q| - lo) /    */
+/* (hi - lo), decided by 24 random bits r as r * (hi - lo) * 2^-24 < |q| - lo */
+/* (exact: both sides are exact in binary64); grid values never move; the    */
+/* sign comes from the sign bit, as in RoundE2M1.                            */
+/* Random bits: SplitMix64 (Steele, Lea and Flood, "Fast splittable          */
+/* pseudorandom number generators", 2014; the finalizer with Stafford's       */
+/* "Mix13" constants) on the counter seed + (i/2 + 1) * 0x9E3779B97F4A7C15,  */
+/* i the flat element index; element i takes the top 24 bits of the low (i   */
+/* even) or high (i odd) 32-bit half.                                        */
+/* ------------------------------------------------------------------------ */
+
+static uint64_t splitmix64(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+uint32_t or_sr_bits(uint64_t seed, int64_t i) {
+    uint64_t z = splitmix64(seed + ((uint64_t)i / 2 + 1) * 0x9E3779B97F4A7C15ull);
+    uint32_t half = (i & 1) ? (uint32_t)(z >> 32) : (uint32_t)z;
+    return half >> 8;
+}
+
+int or_e2m1_round_sr(float q, uint32_t r24) {
+    static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    int s = signbit(q) ? 8 : 0;
+    double m = fabs((double)q);
+    if (m >= 6.0) return s | 7;
+    int k = 0;
+    while (k < 7 && mag[k + 1] <= m) ++k; /* mag[k] <= m < mag[k+1] */
+    if (m == mag[k]) return s | k;
+    double gap = mag[k + 1] - mag[k];
+    int up = (double)r24 * gap * 0x1p-24 < m - mag[k];
+    return s | (k + up);
+}
+
+/* MXFP4 / NVFP4 quantize with stochastic element rounding; scales as the
+ * deterministic encoders (OCP floor rule; NVFP4 max-based E4M3 with the
+ * given s_g).  Outputs and flags as or_mx_quantize / or_nv_quantize. */
+int or_mx_quantize_sr(const void *x, int dt, int64_t n, uint64_t seed, uint8_t *packed,
+                      uint8_t *scales) {
+    int flags = 0;
+    uint8_t codes[32];
+    for (int64_t b = 0; b < n / 32; ++b) {
+        double amax = 0.0;
+        for (int i = 0; i < 32; ++i) {
+            float v = load_elem(x, dt, b * 32 + i);
+            if (!isfinite(v)) flags |= OR_FLAG_NONFINITE;
+            else if (fabs((double)v) > amax) amax = fabs((double)v);
+        }
+        int e = or_mx_exponent(amax);
+        float sc = ldexpf(1.0f, e);
+        scales[b] = (uint8_t)(e + 127);
+        for (int i = 0; i < 32; ++i) {
+            int64_t idx = b * 32 + i;
+            float q = load_elem(x, dt, idx) / sc;
+            codes[i] = (uint8_t)or_e2m1_round_sr(q, or_sr_bits(seed, idx));
+        }
+        or_pack(codes, 32, packed + b * 16);
+    }
+    return flags;
+}
+
+int or_nv_quantize_sr(const void *x, int dt, int64_t n, float s_g, uint64_t seed,
+                      uint8_t *packed, uint8_t *scales) {
+    int flags = 0;
+    uint8_t codes[16];
+    for (int64_t b = 0; b < n / 16; ++b) {
+        double amax = 0.0;
+        for (int i = 0; i < 16; ++i) {
+            float v = load_elem(x, dt, b * 16 + i);
+            if (!isfinite(v)) flags |= OR_FLAG_NONFINITE;
+            else if (fabs((double)v) > amax) amax = fabs((double)v);
+        }
+        int under = 0;
+        int code = amax == 0.0 ? 0x38 : nv_block_code(amax, s_g, &under);
+        float alpha = nv_alpha(s_g, code);
+        if (under || alpha == 0.0f) flags |= OR_FLAG_SCALE_UNDERFLOW;
+        scales[b] = (uint8_t)code;
+        for (int i = 0; i < 16; ++i) {
+            int64_t idx = b * 16 + i;
+            float q = alpha == 0.0f ? 0.0f : load_elem(x, dt, idx) / alpha;
+            codes[i] = (uint8_t)or_e2m1_round_sr(q, or_sr_bits(seed, idx));
+        }
+        or_pack(codes, 16, packed + b * 8);
+    }
+    return flags;
+}
+
