@@ -312,7 +312,21 @@ def extra_workloads():
                             for x, o in zip(xs, outs)])
         out[f"mxfp4_quantize_rule_{rule}_8192x8192_bf16"] = _rate(
             quantize_bytes(xw_cpu.numel(), 2, "mx"), ms, xw_cpu.numel())
-    del xs, outs
+    # stochastic rounding of the same weight: MXFP4 (one pass) and NVFP4
+    # (tensor amax, then quantize)
+    ms = time_rotating([lambda x=x, o=o: fp4.quantize_sr(fp4.MXFP4, x, 0x5EED, check=False, out=o,
+                                                         status=st)
+                        for x, o in zip(xs, outs)])
+    out["mxfp4_quantize_stochastic_8192x8192_bf16"] = _rate(
+        quantize_bytes(xw_cpu.numel(), 2, "mx"), ms, xw_cpu.numel())
+    nouts = [fp4.quantize_nvfp4(x) for x in xs]
+    wss = [fp4.new_workspace(8192, 8192, "cuda") for _ in range(3)]
+    ms = time_rotating([lambda x=x, o=o, w=w: fp4.quantize_sr(fp4.NVFP4, x, 0x5EED, check=False,
+                                                              out=o, status=st, workspace=w)
+                        for x, o, w in zip(xs, nouts, wss)])
+    out["nvfp4_quantize_stochastic_8192x8192_bf16"] = _rate(
+        quantize_bytes(xw_cpu.numel(), 2, "nv"), ms, xw_cpu.numel())
+    del xs, outs, nouts, wss
     # MXFP4 GEMM 128 x 8192 x 8192: operands quantized on the GPU; eight
     # copies of B (36 MB each) rotate so B comes from HBM
     M, N, K = 128, 8192, 8192

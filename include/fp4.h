@@ -128,6 +128,34 @@ fp4_status fp4_quantize_nvfp4(const void *x, fp4_dtype xt, int64_t rows, int64_t
                               int32_t *status, void *stream);
 
 /*
+ * Quantize with stochastic element rounding (Ultralytics glossary "FP4",
+ * section "Inferenza e addestramento FP4": NVFP4 pretraining rounds
+ * gradients stochastically; the pages name the technique, not a rule).
+ *   fmt     FP4_MXFP4 (block 32: scales as fp4_quantize_mxfp4) or FP4_NVFP4
+ *           (block 16: s_g and block scales as fp4_quantize_nvfp4)
+ *   seed    64-bit seed of the random bits
+ *   global_scale, workspace, workspace_bytes  NVFP4 as for
+ *           fp4_quantize_nvfp4; ignored (may be NULL) for MXFP4
+ *   Other arguments, errors and status flags as for the deterministic
+ *   quantizer of the format.
+ * Element rounding: q = RN32(x / scale) as in the deterministic encoder; with
+ * lo <= |q| < hi the neighbouring E2M1 magnitudes, q rounds to hi iff
+ * r * (hi - lo) * 2^-24 < |q| - lo, where r is the element's 24 random bits
+ * (so up with probability (|q| - lo) / (hi - lo), the expected value being
+ * q); grid values stay, |q| >= 6 gives 6, the sign bit is kept.
+ * Random bits of element i (flat row-major index): the (i/2 + 1)-th output of
+ * SplitMix64 (Steele, Lea and Flood, OOPSLA 2014) started at state seed,
+ * i.e. its finalizer applied to seed + (i/2 + 1) * 0x9E3779B97F4A7C15; even
+ * i take the top 24 bits of the low 32-bit half, odd i of the high half.
+ * Results depend on (x, seed) only: deterministic for a given seed.  NVFP4
+ * runs two kernels (tensor amax, then quantize).
+ */
+fp4_status fp4_quantize_sr(fp4_format fmt, const void *x, fp4_dtype xt, int64_t rows,
+                           int64_t cols, int32_t block, uint64_t seed, uint8_t *codes,
+                           uint8_t *scales, float *global_scale, void *workspace,
+                           size_t workspace_bytes, int32_t *status, void *stream);
+
+/*
  * Dequantize ("FP4 / NVFP4 math summary" page, section 10: x_hat = q * alpha).
  *   fmt           FP4_MXFP4 (block 32) or FP4_NVFP4 (block 16)
  *   codes, scales as produced by the quantizers (any byte values accepted)

@@ -43,8 +43,8 @@ FLAG_BARRIER_TIMEOUT = 4
 EXPORTS = ("fp4_quantize_mxfp4", "fp4_quantize_mxfp4_rule", "fp4_quantize_nvfp4",
            "fp4_dequantize", "fp4_scale_search", "fp4_scale_search_exhaustive",
            "fp4_gemm_mxfp4", "fp4_gemm_nvfp4", "fp4_linear_mxfp4", "fp4_quantize_padded",
-           "fp4_dequantize_padded", "fp4_padded_storage_bytes", "fp4_workspace_bytes",
-           "fp4_status_str")
+           "fp4_dequantize_padded", "fp4_padded_storage_bytes", "fp4_quantize_sr",
+           "fp4_workspace_bytes", "fp4_status_str")
 
 # fp4_mx_rule: the MXFP4 block-exponent rules
 MX_RULES = {"ocp": 0, "ceil": 1, "mse": 2}
@@ -77,6 +77,7 @@ def lib() -> ctypes.CDLL:
     L.fp4_gemm_nvfp4.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, I, P]
     L.fp4_quantize_padded.argtypes = [I, P, I, I64, I64, P, P, P, P, S, P, P]
     L.fp4_dequantize_padded.argtypes = [I, P, P, P, I64, I64, P, I, P]
+    L.fp4_quantize_sr.argtypes = [I, P, I, I64, I64, I32, ctypes.c_uint64, P, P, P, P, S, P, P]
     L.fp4_padded_storage_bytes.argtypes = [I, I64, I64]
     L.fp4_padded_storage_bytes.restype = I64
     L.fp4_linear_mxfp4.argtypes = [P, I, I64, I64, P, P, I64, P, P, P, I, I, P, S, P, P]
@@ -87,7 +88,7 @@ def lib() -> ctypes.CDLL:
     for name in ("fp4_quantize_mxfp4", "fp4_quantize_mxfp4_rule", "fp4_quantize_nvfp4",
                  "fp4_dequantize", "fp4_scale_search", "fp4_scale_search_exhaustive",
                  "fp4_gemm_mxfp4", "fp4_gemm_nvfp4", "fp4_linear_mxfp4", "fp4_quantize_padded",
-                 "fp4_dequantize_padded"):
+                 "fp4_dequantize_padded", "fp4_quantize_sr"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -206,6 +207,31 @@ def quantize_nvfp4(x: torch.Tensor, check: bool = True, out=None, status=None, w
                                  _ptr(status), _stream(x)))
     _finish(status, check)
     return codes, scales, s_g
+
+
+def quantize_sr(fmt: int, x: torch.Tensor, seed: int, check: bool = True, out=None, status=None,
+                workspace=None):
+    """Quantize with stochastic element rounding (MXFP4 or NVFP4).  Returns
+    (codes, scales) for MXFP4, (codes, scales, s_g) for NVFP4."""
+    rows, cols = _rows_cols(x)
+    block = 32 if fmt == MXFP4 else 16
+    if out is None:
+        codes = torch.empty(*x.shape[:-1], cols // 2, dtype=torch.uint8, device=x.device)
+        scales = torch.empty(*x.shape[:-1], max(cols // block, 1), dtype=torch.uint8,
+                             device=x.device)
+        s_g = torch.empty(1, dtype=torch.float32, device=x.device) if fmt == NVFP4 else None
+    else:
+        codes, scales, s_g = out if fmt == NVFP4 else (*out, None)
+    if fmt == NVFP4 and workspace is None:
+        workspace = new_workspace(rows, cols, x.device)
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _ok(lib().fp4_quantize_sr(int(fmt), _ptr(x), _dtype_code(x.dtype), rows, cols, block,
+                              int(seed) & (2**64 - 1), _ptr(codes), _ptr(scales), _ptr(s_g),
+                              _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                              _ptr(status), _stream(x)))
+    _finish(status, check)
+    return (codes, scales, s_g) if fmt == NVFP4 else (codes, scales)
 
 
 def dequantize(fmt: int, codes: torch.Tensor, scales: torch.Tensor, global_scale=None,

@@ -16,9 +16,11 @@ SOURCES = ["fp4_api.hip", "fp4_quant.hip", "fp4_gemm.hip"]
 
 # -ffp-contract=off: no implicit fused multiply-add; the kernels spell every
 # fused operation explicitly (the method's fp32 steps are separate roundings).
+# fp32 division is the IEEE correctly rounded one (HIP's default, stated).
 # Packed fp32 instructions are disabled (-packed-fp32-ops).
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
-         "-fno-fast-math", "-Wall", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+         "-fno-fast-math", "-fhip-fp32-correctly-rounded-divide-sqrt", "-Wall", "-Xclang",
+         "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
 def _compile(src: str, verbose: bool) -> str:

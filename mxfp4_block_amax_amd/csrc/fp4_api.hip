@@ -76,6 +76,27 @@ fp4_status fp4_quantize_nvfp4(const void *x, fp4_dtype xt, int64_t rows, int64_t
                                                (hipStream_t)stream));
 }
 
+fp4_status fp4_quantize_sr(fp4_format fmt, const void *x, fp4_dtype xt, int64_t rows,
+                           int64_t cols, int32_t block, uint64_t seed, uint8_t *codes,
+                           uint8_t *scales, float *global_scale, void *workspace,
+                           size_t workspace_bytes, int32_t *status, void *stream) {
+    if (fmt != FP4_MXFP4 && fmt != FP4_NVFP4) return FP4_E_DTYPE;
+    if (!valid_dtype(xt)) return FP4_E_DTYPE;
+    if (!x || !codes || !scales) return FP4_E_ARG;
+    if (fmt == FP4_NVFP4 && !global_scale) return FP4_E_ARG;
+    if (block != (fmt == FP4_MXFP4 ? 32 : 16)) return FP4_E_ARG;
+    fp4_status st = check_shape(rows, cols, block);
+    if (st != FP4_OK) return st;
+    if (fmt == FP4_NVFP4 && (!workspace || workspace_bytes < nv_workspace()))
+        return FP4_E_WORKSPACE;
+    if (!aligned(x, 16) || !aligned(codes, 4) || !aligned(status, 4)) return FP4_E_ALIGN;
+    if (fmt == FP4_NVFP4 && (!aligned(global_scale, 4) || !aligned(workspace, 16)))
+        return FP4_E_ALIGN;
+    return from_hip(fp4dev::launch_quantize_sr((int)fmt, x, xt == FP4_BF16, rows * cols, seed,
+                                               codes, scales, global_scale, workspace, status,
+                                               (hipStream_t)stream));
+}
+
 fp4_status fp4_dequantize(fp4_format fmt, const uint8_t *codes, const uint8_t *scales,
                           const float *global_scale, int64_t rows, int64_t cols,
                           int32_t block, void *y, fp4_dtype yt, void *stream) {

@@ -30,6 +30,11 @@ hipError_t launch_mx_quantize(const void *x, bool bf16, int64_t n, int rule, uin
 hipError_t launch_nv_quantize(const void *x, bool bf16, int64_t n, uint8_t *codes,
                               uint8_t *scales, float *global_scale, void *workspace,
                               int32_t *status, hipStream_t s);
+// Stochastic element rounding (fmt 0 MXFP4, 1 NVFP4 in two passes); the
+// random bits of element i depend on seed and i only.
+hipError_t launch_quantize_sr(int fmt, const void *x, bool bf16, int64_t n, uint64_t seed,
+                              uint8_t *codes, uint8_t *scales, float *global_scale,
+                              void *workspace, int32_t *status, hipStream_t s);
 // all: every E4M3 code is a candidate (c_lo and c_hi unused)
 hipError_t launch_scale_search(const void *x, bool bf16, int64_t n, bool all, float c_lo,
                                float c_hi, uint8_t *codes, uint8_t *scales, float *global_scale,

@@ -179,6 +179,114 @@ __global__ __launch_bounds__(WG) void mx_quantize_kernel(const uint4 *__restrict
 }
 
 // ---------------------------------------------------------------------------
+// Stochastic element rounding (Ultralytics glossary "FP4", section
+// "Inferenza e addestramento FP4": NVFP4 pretraining rounds gradients
+// stochastically; the pages give no rule).  The quotient q is the
+// deterministic encoder's; |q| rounds to the E2M1 magnitude below (lo) or
+// above (hi) it, up with probability (|q| - lo) / (hi - lo) at 24-bit
+// resolution: with r the element's 24 random bits, up iff
+// r 2^-24 (hi - lo) < |q| - lo.  Both sides are exact in fp32 (r < 2^24,
+// hi - lo a power of two, |q| - lo exact by Sterbenz), so the decision is
+// exact.  Grid values never move, |q| >= 6 saturates, the sign is kept.
+//
+// Random bits: SplitMix64 (Steele, Lea and Flood, "Fast splittable
+// pseudorandom number generators", OOPSLA 2014) evaluated at the counter
+// seed + (i/2 + 1) 0x9E3779B97F4A7C15 for flat element index i, i.e. the
+// (i/2 + 1)-th output of the generator started at state seed; element i
+// takes the top 24 bits of the low (even i) or high (odd i) 32-bit half.
+// Every element's bits depend on its index alone, so any grid, tiling or
+// chunking gives the same codes.
+//
+// gfx950 also converts with stochastic rounding in hardware
+// (v_cvt_scalef32_sr_pk_fp4_*), but how it consumes its random operand is
+// not published, so the rounding is done here in VALU arithmetic and the
+// converter only encodes the chosen (exact) grid value.
+// ---------------------------------------------------------------------------
+constexpr uint64_t kSplitMixGamma = 0x9E3779B97F4A7C15ull;
+
+__device__ __forceinline__ uint64_t splitmix64_mix(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+// The E2M1 grid value |q| rounds to, with q's sign, given 24 random bits r.
+// For |q| >= 1, lo keeps the exponent and the top mantissa bit of |q| and
+// hi - lo is half the exponent's power of two; below 1 the grid step is 0.5.
+// A NaN comes out as a signed zero (its input is flagged non-finite).
+__device__ __forceinline__ float sr_e2m1_value(float q, uint32_t r) {
+    const float m = __builtin_fabsf(q);
+    const uint32_t b = f2u(m);
+    const bool big = m >= 1.0f;
+    const float lo = big ? u2f(b & 0xFFC00000u) : (m >= 0.5f ? 0.5f : 0.0f);
+    const float gap = big ? u2f((b & 0x7F800000u) - 0x00800000u) : 0.5f;
+    const float t = (float)r * 0x1p-24f * gap;  // exact
+    float v = t < m - lo ? lo + gap : lo;
+    v = m >= 6.0f ? 6.0f : v;
+    return __builtin_copysignf(v, q);
+}
+
+// Packed E2M1 codes of chunk c (elements 8c .. 8c+7, quotients q[0..7]).
+__device__ __forceinline__ uint32_t sr_codes8(const float (&q)[8], uint64_t seed, int64_t c) {
+    float v[8];
+    uint64_t ctr = seed + (uint64_t)(4 * c + 1) * kSplitMixGamma;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint64_t z = splitmix64_mix(ctr);
+        ctr += kSplitMixGamma;
+        v[2 * j] = sr_e2m1_value(q[2 * j], (uint32_t)z >> 8);
+        v[2 * j + 1] = sr_e2m1_value(q[2 * j + 1], (uint32_t)(z >> 32) >> 8);
+    }
+    return cvt_fp4x8_f32(v, e8m0_operand(E8M0_ONE));  // exact: grid values
+}
+
+// MXFP4 quantize with stochastic rounding: block exponents by the OCP floor
+// rule, q = x / 2^e (exact: a multiply by 2^-e, which is normal for every
+// finite block since e <= 125), then the stochastic grid value.
+template <bool BF16>
+__global__ __launch_bounds__(WG) void mx_quantize_sr_kernel(const uint4 *__restrict__ x,
+                                                            int64_t nchunks, uint64_t seed,
+                                                            uint32_t *__restrict__ codes,
+                                                            uint8_t *__restrict__ scales,
+                                                            int32_t *status) {
+    constexpr int U = 4;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int64_t wave = (int64_t)blockIdx.x * WAVES_PER_WG + (threadIdx.x / WAVE);
+    const int64_t nwaves = (int64_t)gridDim.x * WAVES_PER_WG;
+    const int64_t ntiles = (nchunks + WAVE * U - 1) / (WAVE * U);
+    uint32_t flags = 0;
+    for (int64_t t = wave; t < ntiles; t += nwaves) {
+        Chunk<BF16> k[U];
+#pragma unroll
+        for (int r = 0; r < U; ++r) {
+            int64_t c = t * (WAVE * U) + r * WAVE + lane;
+            k[r] = load_chunk<BF16>(x, c, c < nchunks);
+        }
+#pragma unroll
+        for (int r = 0; r < U; ++r) {
+            int64_t c = t * (WAVE * U) + r * WAVE + lane;
+            uint32_t m = chunk_amax<BF16>(k[r]);
+            m = max(m, dpp<QP_XOR1>(m));
+            m = max(m, dpp<QP_XOR2>(m));
+            const int sh = BF16 ? 7 : 23;
+            if ((m >> sh) >= 0xFFu) flags |= FLAG_NONFINITE;
+            const uint32_t sb = mx_scale_byte(m, sh);
+            const float inv = u2f((254u - sb) << 23);  // 2^-e
+            float v[8];
+            chunk_values<BF16>(k[r], v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] *= inv;
+            const uint32_t q = sr_codes8(v, seed, c);
+            if (c < nchunks) {
+                codes[c] = q;
+                if ((lane & 3) == 0) scales[c >> 2] = (uint8_t)sb;
+            }
+        }
+    }
+    report_flags(status, flags);
+}
+
+// ---------------------------------------------------------------------------
 // Tensor amax (NVFP4 and scale search, pass 1): one partial max of the
 // sign-cleared bit patterns per workgroup.  No atomics, no initialisation.
 // ---------------------------------------------------------------------------
@@ -251,7 +359,7 @@ __device__ TensorScale tensor_scale(const uint32_t *__restrict__ partials, int n
 // quotient may differ for some bf16 input).  A zero block takes scale 1
 // (code 0x38).
 struct BlockScale {
-    float ad, y, sc;
+    float a, ad, y, sc;  // a: alpha itself
     uint32_t code;
 };
 
@@ -261,6 +369,7 @@ __device__ __forceinline__ BlockScale nv_block_scale(const NvScaleTable &T, uint
     const uint32_t c = nv_code(T, u2f(ag_bits), G);  // 0 for a zero amax
     b.code = ag_bits == 0 ? 0x38u : c;
     const float4 q = T.q[b.code];
+    b.a = q.x;
     b.ad = q.y;
     b.y = q.z;
     b.sc = q.w;
@@ -297,17 +406,34 @@ __device__ __forceinline__ uint32_t nv_quant8(float (&v)[8], float ad, float ys,
     return cvt_fp4x8_f32(q, e8m0_operand(E8M0_ONE));
 }
 
+// Stochastic NVFP4 codes of 8 values with block scale alpha.  The quotient
+// must be RN32(x / alpha) for every size of it (the decision reads it down to
+// 2^-25, and below that whether it is zero), which the reciprocal-corrected
+// divide of the deterministic path does not promise for tiny alpha, so this
+// takes the IEEE fp32 divide (the library is built with correctly rounded
+// fp32 division and fp32 denormals kept).  alpha = 0 (a flagged scale
+// underflow) gives zero quotients.
+__device__ __forceinline__ uint32_t nv_sr8(const float (&v)[8], float alpha, uint64_t seed,
+                                           int64_t c) {
+    float q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = alpha == 0.0f ? 0.0f : v[i] / alpha;
+    return sr_codes8(q, seed, c);
+}
+
 // ---------------------------------------------------------------------------
 // NVFP4 quantize, pass 2.  Each wave tile is two chunk-rows; a lane pair holds
 // one block of each row.  The even lane derives row 0's block scale and the
 // odd lane row 1's, and they swap results, so no block scale is computed
-// twice.
+// twice.  SR: stochastic element rounding with the given seed (block scales
+// and s_g unchanged).
 // ---------------------------------------------------------------------------
-template <bool BF16>
+template <bool BF16, bool SR>
 __global__ __launch_bounds__(WG) void nv_quantize_kernel(const uint4 *__restrict__ x,
                                                          int64_t nchunks,
                                                          const uint32_t *__restrict__ partials,
-                                                         int npart, uint32_t *__restrict__ codes,
+                                                         int npart, uint64_t seed,
+                                                         uint32_t *__restrict__ codes,
                                                          uint8_t *__restrict__ scales,
                                                          float *__restrict__ global_scale,
                                                          int32_t *status) {
@@ -342,10 +468,19 @@ __global__ __launch_bounds__(WG) void nv_quantize_kernel(const uint4 *__restrict
         const float a0 = odd ? pa : mine.ad, y0 = odd ? py : mine.y, s0 = odd ? ps : mine.sc;
         const float a1 = odd ? mine.ad : pa, y1 = odd ? mine.y : py, s1 = odd ? mine.sc : ps;
         float v[8];
-        chunk_values<BF16>(k0, v);
-        uint32_t q0 = nv_quant8<BF16>(v, a0, y0, s0);
-        chunk_values<BF16>(k1, v);
-        uint32_t q1 = nv_quant8<BF16>(v, a1, y1, s1);
+        uint32_t q0, q1;
+        if (SR) {
+            const float pal = dppf<QP_XOR1>(mine.a);
+            chunk_values<BF16>(k0, v);
+            q0 = nv_sr8(v, odd ? pal : mine.a, seed, c0);
+            chunk_values<BF16>(k1, v);
+            q1 = nv_sr8(v, odd ? mine.a : pal, seed, c1);
+        } else {
+            chunk_values<BF16>(k0, v);
+            q0 = nv_quant8<BF16>(v, a0, y0, s0);
+            chunk_values<BF16>(k1, v);
+            q1 = nv_quant8<BF16>(v, a1, y1, s1);
+        }
         if (c0 < nchunks) codes[c0] = q0;
         if (c1 < nchunks) codes[c1] = q1;
         const int64_t cs = odd ? c1 : c0;  // chunk whose block this lane's scale belongs to
@@ -1089,12 +1224,31 @@ hipError_t launch_nv_quantize(const void *x, bool bf16, int64_t n, uint8_t *code
     hipError_t e = launch_amax(x, bf16, nchunks, partials, g1, s);
     if (e != hipSuccess) return e;
     const int g = grid_for((nchunks + WAVE * 2 - 1) / (WAVE * 2), kMaxGrid);
-    if (bf16)
-        hipLaunchKernelGGL(nv_quantize_kernel<true>, dim3(g), dim3(WG), 0, s, (const uint4 *)x,
-                           nchunks, partials, g1, (uint32_t *)codes, scales, global_scale, status);
-    else
-        hipLaunchKernelGGL(nv_quantize_kernel<false>, dim3(g), dim3(WG), 0, s, (const uint4 *)x,
-                           nchunks, partials, g1, (uint32_t *)codes, scales, global_scale, status);
+    auto kernel = bf16 ? nv_quantize_kernel<true, false> : nv_quantize_kernel<false, false>;
+    hipLaunchKernelGGL(kernel, dim3(g), dim3(WG), 0, s, (const uint4 *)x, nchunks, partials, g1,
+                       (uint64_t)0, (uint32_t *)codes, scales, global_scale, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_sr(int fmt, const void *x, bool bf16, int64_t n, uint64_t seed,
+                              uint8_t *codes, uint8_t *scales, float *global_scale,
+                              void *workspace, int32_t *status, hipStream_t s) {
+    const int64_t nchunks = n / 8;
+    if (fmt == 0) {
+        const int g = grid_for((nchunks + WAVE * 4 - 1) / (WAVE * 4), kMaxGrid);
+        auto kernel = bf16 ? mx_quantize_sr_kernel<true> : mx_quantize_sr_kernel<false>;
+        hipLaunchKernelGGL(kernel, dim3(g), dim3(WG), 0, s, (const uint4 *)x, nchunks, seed,
+                           (uint32_t *)codes, scales, status);
+        return hipGetLastError();
+    }
+    uint32_t *partials = (uint32_t *)workspace;
+    const int g1 = amax_grid(nchunks);
+    hipError_t e = launch_amax(x, bf16, nchunks, partials, g1, s);
+    if (e != hipSuccess) return e;
+    const int g = grid_for((nchunks + WAVE * 2 - 1) / (WAVE * 2), kMaxGrid);
+    auto kernel = bf16 ? nv_quantize_kernel<true, true> : nv_quantize_kernel<false, true>;
+    hipLaunchKernelGGL(kernel, dim3(g), dim3(WG), 0, s, (const uint4 *)x, nchunks, partials, g1,
+                       seed, (uint32_t *)codes, scales, global_scale, status);
     return hipGetLastError();
 }
 

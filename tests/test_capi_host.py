@@ -178,6 +178,29 @@ def test_padded_storage_and_validation():
     assert L.fp4_dequantize_padded(fp4.MXFP4, A16, A16, NULL, 2, 0, A16, fp4.BF16, NULL) == E_SHAPE
 
 
+def test_sr_validation():
+    L = fp4.lib()
+
+    def q(fmt=fp4.NVFP4, x=A16, dt=fp4.BF16, rows=4, cols=64, block=16, codes=A16, sg=A16,
+          ws=A16, wsb=1 << 20, status=NULL):
+        return L.fp4_quantize_sr(fmt, x, dt, rows, cols, block, 2**64 - 1, codes, A16, sg, ws,
+                                 wsb, status, NULL)
+    assert q(fmt=2) == E_DTYPE
+    assert q(dt=9) == E_DTYPE
+    assert q(x=NULL) == E_ARG
+    assert q(sg=NULL) == E_ARG                       # NVFP4 needs s_g
+    assert q(block=32) == E_ARG                      # NVFP4 blocks are 16
+    assert q(fmt=fp4.MXFP4, block=16) == E_ARG       # MXFP4 blocks are 32
+    assert q(cols=17) == E_SHAPE
+    assert q(fmt=fp4.MXFP4, block=32, cols=48) == E_SHAPE
+    assert q(rows=0) == E_SHAPE
+    assert q(ws=NULL) == E_WORKSPACE
+    assert q(wsb=16) == E_WORKSPACE
+    assert q(x=A1) == E_ALIGN
+    assert q(status=A1) == E_ALIGN
+    assert q(ws=ctypes.c_void_p(0x10004)) == E_ALIGN
+
+
 def test_gemm_validation():
     L = fp4.lib()
 

@@ -19,6 +19,7 @@ import pytest
 import oracle
 from tests._exact import E2M1_MAG
 from tests._golden import rows
+from tests._sr_cases import mean_within_bounds, neighbour_values, neighbours, threshold_blocks
 
 M64 = 2**64 - 1
 TWO24 = 2**24
@@ -58,14 +59,6 @@ def test_generator_bits_are_24_bit_and_roughly_uniform():
 
 def _f32(v) -> float:
     return float(np.float32(v))
-
-
-def _neighbours(m: Fraction):
-    """(lo, hi, code_lo) with lo <= m < hi consecutive E2M1 magnitudes."""
-    for k in range(7):
-        if E2M1_MAG[k] <= m < E2M1_MAG[k + 1]:
-            return E2M1_MAG[k], E2M1_MAG[k + 1], k
-    raise AssertionError(m)
 
 
 def _threshold(q: float) -> int:
@@ -108,7 +101,7 @@ def test_round_up_probability_is_the_distance_ratio(sign):
     for m in _sample_quotients():
         q = sign * m
         fm = Fraction(m)
-        lo, hi, k = _neighbours(fm)
+        lo, hi, k = neighbours(fm)
         d = fm - lo
         expect = 0 if d == 0 else math.ceil(d / (hi - lo) * TWO24)
         assert _threshold(q) == expect, q
@@ -126,7 +119,7 @@ def test_rounding_is_unbiased_at_24_bit_resolution():
     exactly; for any q it is within gap 2^-24 above it."""
     for m in _sample_quotients(1):
         fm = Fraction(m)
-        lo, hi, _ = _neighbours(fm)
+        lo, hi, _ = neighbours(fm)
         gap = hi - lo
         up = _threshold(m)
         mean = lo + gap * Fraction(up, TWO24)
@@ -161,26 +154,15 @@ def test_result_is_a_neighbour_of_the_nearest_even_result():
         if m >= 6:
             assert c == d
             continue
-        lo, hi, k = _neighbours(m)
+        lo, hi, k = neighbours(m)
         assert c & 7 in (k, k + 1) and d & 7 in (k, k + 1)
         assert c & 8 == d & 8 == (8 if q < 0 else 0)
 
 
 def _neighbour_values(x: np.ndarray, scale: np.ndarray):
-    """Per element: the two E2M1 neighbours of RN32(x / scale), times scale
-    (exact: every value here is a short binary fraction)."""
+    """The two E2M1 neighbours of RN32(x / scale), times scale."""
     q = (x.astype(np.float32) / scale.astype(np.float32)).astype(np.float32)
-    lo = np.empty(q.size)
-    hi = np.empty(q.size)
-    for i, v in enumerate(q):
-        m = Fraction(abs(float(v)))
-        if m >= 6:
-            lo[i] = hi[i] = 6.0
-        else:
-            a, b, _ = _neighbours(m)
-            lo[i], hi[i] = float(a), float(b)
-    sgn = np.where(np.signbit(q), -1.0, 1.0)
-    return sgn * lo * scale, sgn * hi * scale
+    return neighbour_values(q, scale)
 
 
 def _mx_scale_values(scales: np.ndarray) -> np.ndarray:
@@ -232,27 +214,42 @@ def test_draws_follow_the_element_index_not_the_block():
 
 def test_mean_over_seeds_recovers_the_input():
     """End to end unbiasedness: averaged over many seeds, the dequantized
-    tensor approaches x (each element within 5 standard errors of the
-    two-point distribution it is drawn from)."""
+    tensor is consistent with expectation x (per element and summed), while
+    nearest rounding on the same data is several times further off."""
     rng = np.random.default_rng(9)
-    x = rng.standard_normal(64).astype(np.float32)
+    x = rng.standard_normal(256).astype(np.float32)
     x[5] = 0.0
     x[9] = -0.0
-    nseed = 3000
-    acc = np.zeros(64)
+    nseed = 2000
+    acc = np.zeros(x.size)
     for sd in range(nseed):
         p, s, _ = oracle.mx_quantize_sr(x, seed=1000 + sd)
         acc += oracle.dequantize(oracle.MX, p, s).astype(np.float64)
     mean = acc / nseed
     s_det = oracle.mx_quantize(x)[1]
     lo, hi = _neighbour_values(x, _mx_scale_values(s_det))
-    p_up = np.where(hi != lo, (x.astype(np.float64) - lo) / np.where(hi != lo, hi - lo, 1), 0)
-    se = np.abs(hi - lo) * np.sqrt(p_up * (1 - p_up) / nseed)
-    assert np.all(np.abs(mean - x) <= 5 * se + 1e-12)
-    # deterministic rounding is biased on the same data (a sanity check on
-    # the statistic's power)
+    assert mean_within_bounds(x.astype(np.float64), lo, hi, mean, nseed)
     det = oracle.dequantize(oracle.MX, *oracle.mx_quantize(x)[:2]).astype(np.float64)
-    assert np.max(np.abs(det - x)) > 10 * np.max(se)
+    assert np.abs(det - x).mean() > 5 * np.abs(mean - x).mean()
+    # a planted bias of a tenth of a step is caught
+    assert not mean_within_bounds(x.astype(np.float64), lo, hi, mean + 0.1 * np.abs(hi - lo),
+                                  nseed)
+
+
+@pytest.mark.parametrize("block,lead", [(32, 0), (16, 16)])
+@pytest.mark.parametrize("seed", [3, 2**63 + 11])
+def test_quotients_one_step_either_side_of_each_threshold(block, lead, seed):
+    """Quotients placed at each element's own threshold round down, one fp32
+    step above it round up: the decisions built from exact fractions."""
+    x, want = threshold_blocks(block, 48, seed, offset=lead)
+    if lead:  # NVFP4: a leading 2688 block fixes s_g = 1
+        x = np.concatenate([np.full(lead, 2688.0, np.float32), x])
+        p, s, sg, f = oracle.nv_quantize_sr(x, seed)
+        assert float(sg) == 1.0
+    else:
+        p, s, f = oracle.mx_quantize_sr(x, seed)
+    assert f == 0
+    assert np.array_equal(oracle.unpack(p)[lead:], want)
 
 
 def test_bf16_input_equals_widened_fp32_input():
