@@ -222,8 +222,7 @@ def cpu_baseline(x_cpu: torch.Tensor, step_bytes: int):
     xo = workloads.bf16_bits(x_cpu).reshape(x_cpu.shape[0], -1)
     nt = max(1, min(16, len(os.sched_getaffinity(0))))
     parts = [p.reshape(-1) for p in np.array_split(xo, nt) if p.size]
-    t0 = time.perf_counter()
-    with ThreadPoolExecutor(nt) as pool:
+    def one_step(pool):
         sgs = list(pool.map(oracle.nv_global_scale, parts))
         sg = max(v for v, _ in sgs)
 
@@ -236,10 +235,21 @@ def cpu_baseline(x_cpu: torch.Tensor, step_bytes: int):
             oracle.dequantize(oracle.MX, p, s, out_bf16=True)
         list(pool.map(nv, parts))
         list(pool.map(mx, parts))
-    dt = time.perf_counter() - t0
-    return {"value": round(step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": len(parts),
+
+    # whole steps until the threads have done at least ~10 s of CPU work (at
+    # most 8 steps)
+    steps = 0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(nt) as pool:
+        while True:
+            one_step(pool)
+            steps += 1
+            dt = time.perf_counter() - t0
+            if dt * len(parts) >= 10.0 or steps >= 8:
+                break
+    return {"value": round(steps * step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": len(parts),
             "kind": "oracle",
-            "sample": f"one full step (NVFP4 + MXFP4 quantize and dequantize) of the "
+            "sample": f"{steps} full step(s) (NVFP4 + MXFP4 quantize and dequantize) of the "
                       f"{x_cpu.shape[0]}x{x_cpu.shape[1]} bf16 input, rows split over "
                       f"{len(parts)} threads; {dt:.2f} s wall"}
 
@@ -338,7 +348,29 @@ def extra_workloads():
     d = _rate(gemm_bytes(M, N, K), ms)
     tf = gemm_flops(M, N, K) / ms / 1e9
     d.update({"TFLOP/s": round(tf, 1), "pct_fp4_mfma_peak": round(100 * tf / FP4_DENSE_PEAK_TFLOPS, 2)})
+    # the same product split over K (fp32 partials in a workspace, then a
+    # fixed-order reduction)
+    ws = torch.empty(fp4.gemm_splitk_workspace_bytes(M, N, K), dtype=torch.uint8, device="cuda")
+    ms2 = time_rotating([lambda b=b: fp4.gemm_mxfp4_splitk(ac, asc, b[0], b[1], out=c, workspace=ws)
+                         for b in bq])
+    d["split_k_us"] = round(ms2 * 1e3, 2)
     out["mxfp4_gemm_128x8192x8192_bf16out"] = d
+    # K = 16384, beyond the staged kernel's scale capacity: the split-K path
+    # against the entry point's register-fed fallback
+    K2 = 16384
+    a2, bt2 = workloads.gemm_operands(M, N, K2)
+    ac2, asc2 = fp4.quantize_mxfp4(a2.cuda())
+    bq2 = [fp4.quantize_mxfp4(bt2.cuda()) for _ in range(4)]
+    ws2 = torch.empty(fp4.gemm_splitk_workspace_bytes(M, N, K2), dtype=torch.uint8, device="cuda")
+    ms = time_rotating([lambda b=b: fp4.gemm_mxfp4_splitk(ac2, asc2, b[0], b[1], out=c, workspace=ws2)
+                        for b in bq2])
+    d = _rate(gemm_bytes(M, N, K2), ms)
+    tf = gemm_flops(M, N, K2) / ms / 1e9
+    d.update({"TFLOP/s": round(tf, 1), "pct_fp4_mfma_peak": round(100 * tf / FP4_DENSE_PEAK_TFLOPS, 2)})
+    ms2 = time_rotating([lambda b=b: fp4.gemm_mxfp4(ac2, asc2, b[0], b[1], out=c) for b in bq2])
+    d["unsplit_us"] = round(ms2 * 1e3, 2)
+    out["mxfp4_gemm_splitk_128x8192x16384_bf16out"] = d
+    del bq2, ws2
     # W4A4 linear: bf16 activations quantized in the GEMM's launch (grid
     # barrier), against the two launches of quantize then GEMM
     xa = a.to(torch.bfloat16).cuda()

@@ -224,6 +224,36 @@ fp4_status fp4_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales,
                           int64_t N, int64_t K, void *c, fp4_dtype ct, void *stream);
 
 /*
+ * The same MXFP4 x MXFP4 GEMM split over K, for short A (the operation and
+ * the sources as fp4_gemm_mxfp4).  With one 128-row tile of A or two, the
+ * tiling of fp4_gemm_mxfp4 makes every workgroup read all of A; here each of
+ * S workgroups per 128 x 128 tile of C takes one of S equal K ranges (at most
+ * 2048 K each, a multiple of 512) and writes fp32 partial sums, then a second
+ * kernel adds the S partials of each output in increasing K-range order and
+ * rounds once (bf16 = RNE of the fp32 sum).
+ *   a_codes .. c, ct   as for fp4_gemm_mxfp4; K a multiple of 512, N a
+ *                      multiple of 4; codes and scales 16-byte aligned, c 16
+ *                      (fp32) or 8 (bf16) byte aligned
+ *   workspace          device memory of at least
+ *                      fp4_gemm_splitk_workspace_bytes(M, N, K) bytes,
+ *                      16-byte aligned; its contents are scratch (S x M x N
+ *                      fp32), overwritten by each call.  Calls that share a
+ *                      workspace must be stream-ordered.
+ * Errors: FP4_E_SHAPE for shapes this path does not take (use
+ * fp4_gemm_mxfp4), FP4_E_WORKSPACE for a missing or short workspace.  The
+ * summation differs from fp4_gemm_mxfp4's (fp32 partial sums per K range)
+ * but is fixed, so results are deterministic.
+ */
+fp4_status fp4_gemm_mxfp4_splitk(const uint8_t *a_codes, const uint8_t *a_scales,
+                                 const uint8_t *bt_codes, const uint8_t *bt_scales, int64_t M,
+                                 int64_t N, int64_t K, void *c, fp4_dtype ct, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace fp4_gemm_mxfp4_splitk needs for this shape: S * M * N *
+ * 4 with S = the number of K ranges; 0 if the shape is not supported. */
+size_t fp4_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
  * NVFP4 x NVFP4 GEMM ("NVFP4 / MXFP4 format" page, section 6:
  * Y = a_X a_W sum_g b^X_g b^W_g sum_{k in g} p^X_k p^W_k, 16-element groups
  * along K, E4M3 block scales b, one fp32 tensor scale a per operand).

@@ -42,7 +42,8 @@ FLAG_BARRIER_TIMEOUT = 4
 
 EXPORTS = ("fp4_quantize_mxfp4", "fp4_quantize_mxfp4_rule", "fp4_quantize_nvfp4",
            "fp4_dequantize", "fp4_scale_search", "fp4_scale_search_exhaustive",
-           "fp4_gemm_mxfp4", "fp4_gemm_nvfp4", "fp4_linear_mxfp4", "fp4_quantize_padded",
+           "fp4_gemm_mxfp4", "fp4_gemm_mxfp4_splitk", "fp4_gemm_splitk_workspace_bytes",
+           "fp4_gemm_nvfp4", "fp4_linear_mxfp4", "fp4_quantize_padded",
            "fp4_dequantize_padded", "fp4_padded_storage_bytes", "fp4_quantize_sr",
            "fp4_workspace_bytes", "fp4_status_str")
 
@@ -75,6 +76,9 @@ def lib() -> ctypes.CDLL:
     L.fp4_scale_search.argtypes = [P, I, I64, I64, I32, I32, F, F, P, P, P, P, S, P, P]
     L.fp4_gemm_mxfp4.argtypes = [P, P, P, P, I64, I64, I64, P, I, P]
     L.fp4_gemm_nvfp4.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, I, P]
+    L.fp4_gemm_mxfp4_splitk.argtypes = [P, P, P, P, I64, I64, I64, P, I, P, S, P]
+    L.fp4_gemm_splitk_workspace_bytes.argtypes = [I64, I64, I64]
+    L.fp4_gemm_splitk_workspace_bytes.restype = S
     L.fp4_quantize_padded.argtypes = [I, P, I, I64, I64, P, P, P, P, S, P, P]
     L.fp4_dequantize_padded.argtypes = [I, P, P, P, I64, I64, P, I, P]
     L.fp4_quantize_sr.argtypes = [I, P, I, I64, I64, I32, ctypes.c_uint64, P, P, P, P, S, P, P]
@@ -87,8 +91,9 @@ def lib() -> ctypes.CDLL:
     L.fp4_status_str.restype = ctypes.c_char_p
     for name in ("fp4_quantize_mxfp4", "fp4_quantize_mxfp4_rule", "fp4_quantize_nvfp4",
                  "fp4_dequantize", "fp4_scale_search", "fp4_scale_search_exhaustive",
-                 "fp4_gemm_mxfp4", "fp4_gemm_nvfp4", "fp4_linear_mxfp4", "fp4_quantize_padded",
-                 "fp4_dequantize_padded", "fp4_quantize_sr"):
+                 "fp4_gemm_mxfp4", "fp4_gemm_mxfp4_splitk", "fp4_gemm_nvfp4",
+                 "fp4_linear_mxfp4", "fp4_quantize_padded", "fp4_dequantize_padded",
+                 "fp4_quantize_sr"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -298,6 +303,29 @@ def gemm_mxfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, bt_codes: torch.Te
     c = out if out is not None else torch.empty(M, N, dtype=out_dtype, device=a_codes.device)
     _ok(lib().fp4_gemm_mxfp4(_ptr(a_codes), _ptr(a_scales), _ptr(bt_codes), _ptr(bt_scales), M, N,
                              K, _ptr(c), _dtype_code(c.dtype), _stream(a_codes)))
+    return c
+
+
+def gemm_splitk_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().fp4_gemm_splitk_workspace_bytes(int(M), int(N), int(K)))
+
+
+def gemm_mxfp4_splitk(a_codes: torch.Tensor, a_scales: torch.Tensor, bt_codes: torch.Tensor,
+                      bt_scales: torch.Tensor, out_dtype=torch.bfloat16, out=None, workspace=None):
+    """The MXFP4 GEMM split over K (fp32 partials in `workspace`, then a
+    fixed-order reduction); for short A."""
+    M, kh = _rows_cols(a_codes)
+    N, kh2 = _rows_cols(bt_codes)
+    if kh != kh2:
+        raise ValueError("A and Bt must share K")
+    K = 2 * kh
+    c = out if out is not None else torch.empty(M, N, dtype=out_dtype, device=a_codes.device)
+    if workspace is None:
+        need = gemm_splitk_workspace_bytes(M, N, K)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=a_codes.device)
+    _ok(lib().fp4_gemm_mxfp4_splitk(_ptr(a_codes), _ptr(a_scales), _ptr(bt_codes),
+                                    _ptr(bt_scales), M, N, K, _ptr(c), _dtype_code(c.dtype),
+                                    _ptr(workspace), workspace.numel(), _stream(a_codes)))
     return c
 
 

@@ -169,6 +169,30 @@ fp4_status fp4_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales,
                                               c, ct == FP4_BF16, (hipStream_t)stream));
 }
 
+size_t fp4_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || N < 1 || M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return 0;
+    const int S = fp4dev::gemm_splitk_parts(M, N, K);
+    return S < 1 ? 0 : (size_t)S * (size_t)M * (size_t)N * sizeof(float);
+}
+
+fp4_status fp4_gemm_mxfp4_splitk(const uint8_t *a_codes, const uint8_t *a_scales,
+                                 const uint8_t *bt_codes, const uint8_t *bt_scales, int64_t M,
+                                 int64_t N, int64_t K, void *c, fp4_dtype ct, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+    if (!a_codes || !a_scales || !bt_codes || !bt_scales || !c) return FP4_E_ARG;
+    if (!valid_dtype(ct)) return FP4_E_DTYPE;
+    const size_t need = fp4_gemm_splitk_workspace_bytes(M, N, K);
+    if (need == 0) return FP4_E_SHAPE;
+    if (!workspace || workspace_bytes < need) return FP4_E_WORKSPACE;
+    if (!aligned(a_codes, 16) || !aligned(bt_codes, 16) || !aligned(a_scales, 16) ||
+        !aligned(bt_scales, 16) || !aligned(workspace, 16) ||
+        !aligned(c, ct == FP4_BF16 ? 8 : 16))
+        return FP4_E_ALIGN;
+    return from_hip(fp4dev::launch_gemm_mxfp4_splitk(a_codes, a_scales, bt_codes, bt_scales, M, N,
+                                                     K, c, ct == FP4_BF16, (float *)workspace,
+                                                     (hipStream_t)stream));
+}
+
 fp4_status fp4_gemm_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales,
                           const float *a_global_scale, const uint8_t *bt_codes,
                           const uint8_t *bt_scales, const float *bt_global_scale, int64_t M,

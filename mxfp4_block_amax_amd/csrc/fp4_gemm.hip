@@ -252,8 +252,10 @@ __global__ __launch_bounds__(GEMM_WG) void mxfp4_gemm_fast_kernel(
 // stage the workgroup stages A 128 x 128 B and B 32 x 128 B, GEMM_S stages in
 // flight.  Each wave loads its own 32 rows of A and 8 of the 32 rows of B;
 // a barrier per stage makes the shared B rows visible.  Within a row the
-// 16-byte chunk c of a stage sits at chunk c ^ (row & 7) of the LDS row, so
-// the MFMA-layout reads (32 rows, one chunk each) hit distinct banks.
+// 16-byte chunk c of row r of a stage sits at chunk c ^ ((r >> 1) & 7) of its
+// LDS row: a ds_read_b128 serves 16 lanes per pass, rows r and r + 1 fall in
+// different halves of the 64 banks, so the 16 rows of a pass of the
+// MFMA-layout reads (one chunk each) hit 16 distinct 4-bank groups.
 // Scale bytes go to registers: one 8-byte load per operand row per stage.
 // ---------------------------------------------------------------------------
 constexpr int GEMM_S = 5;                   // stages in flight
@@ -267,6 +269,8 @@ constexpr int GEMM_SCALE_COLS = GEMM_MAX_K / 32 / 16;  // 16-byte scale chunks p
 
 typedef __attribute__((address_space(1))) const void *gemm_gptr;
 typedef __attribute__((address_space(3))) void *gemm_lptr;
+
+__device__ __forceinline__ int gemm_swizzle(int row) { return (row >> 1) & 7; }
 
 // One workgroup's 128 x 32 tile of C (blockIdx.y, blockIdx.x), all of K.
 template <bool OUT_BF16>
@@ -303,17 +307,17 @@ __device__ __forceinline__ void gemm_lds_tile(const uint4 *__restrict__ A,
     }
 
     // code loads: lane l of a load covers row (8i + l / 8) of its group and
-    // LDS chunk l % 8, which holds the row's chunk (l % 8) ^ (row & 7)
+    // LDS chunk l % 8, which holds the row's chunk (l % 8) ^ swizzle
     const int lrow = lane >> 3, lpc = lane & 7;
     const uint4 *ga[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = 32 * w + 8 * i + lrow;  // row within the A tile
         const int am = min(m0 + row, M - 1);
-        ga[i] = A + (int64_t)am * nblk + (lpc ^ (row & 7));
+        ga[i] = A + (int64_t)am * nblk + (lpc ^ gemm_swizzle(row));
     }
     const int brow = 8 * w + lrow;
-    const uint4 *gb = Bt + (int64_t)min(n0 + brow, N - 1) * nblk + (lpc ^ (brow & 7));
+    const uint4 *gb = Bt + (int64_t)min(n0 + brow, N - 1) * nblk + (lpc ^ gemm_swizzle(brow));
 
     // Five code loads per wave per stage: its 32 rows of A and 8 of the 32
     // rows of B, global -> LDS.  Stages past the end re-read the last one
@@ -334,7 +338,7 @@ __device__ __forceinline__ void gemm_lds_tile(const uint4 *__restrict__ A,
     // not wait for each other; summed once at the end, in a fixed order
     f32x16_t acc0 = {}, acc1 = {};
     const int arow = 32 * w + r32;  // this lane's A operand row in the tile
-    const int sw = r32 & 7;         // its swizzle (same for the B row r32)
+    const int sw = gemm_swizzle(r32);  // its swizzle (= that of arow and of the B row r32)
     // LDS byte addresses of this lane's operands in slot 0: chunk
     // (2 s4 + kh) ^ swizzle of its A row and of its B row for steps s4 = 0..3
     uint32_t la[4], lb[4];
@@ -431,6 +435,200 @@ __global__ __launch_bounds__(GEMM_WG) void mxfp4_gemm_lds_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Split-K MXFP4 GEMM, for short A (the 128 x 32 tiling above makes every CU
+// read all of A, 512 KB at K = 8192, against 128 KB of its own B).
+//
+// A workgroup owns a 128 x 128 tile of C and one of S equal K ranges (at most
+// 2048 K, a multiple of 512): 128 KB of A and 128 KB of B at K = 8192, S = 4.
+// Eight waves, two per SIMD so that one's LDS reads overlap the other's
+// MFMAs: wave w computes rows 32 (w % 4) .. + 32 against columns 64 (w / 4)
+// .. + 64, two 32 x 32 MFMA tiles sharing each A operand read.  K is staged
+// through LDS (256 K per stage, four stages in flight, 32 KB per stage, the
+// swizzle above), and the E8M0 scales of the workgroup's K range are
+// preloaded transposed ([16-byte chunk][row], 16 KB).  The fp32 partial sums go
+// to the workspace, P[s][m][n]; a second kernel adds the S partials of each
+// output in increasing s, ((P0 + P1) + P2) + ..., and rounds once to the
+// output type, so the result does not depend on scheduling.  The kernel
+// boundary between the two makes the partials written on one XCD visible to
+// the others without in-kernel cache maintenance.
+// ---------------------------------------------------------------------------
+constexpr int SK_WG = 512;
+constexpr int SK_TN = 128;                                 // columns of C per workgroup
+constexpr int SK_RING = 4;                                 // stages in flight
+constexpr int SK_KS_MAX = 2048;                            // K values of one split, at most
+constexpr int SK_SCALE_COLS = SK_KS_MAX / 32 / 16;         // 16-byte scale chunks per row
+constexpr int SK_A_CHUNKS = GEMM_TM * 8;                   // 16-byte chunks of A per stage
+constexpr int SK_B_CHUNKS = SK_TN * 8;
+constexpr int SK_STAGE_CHUNKS = SK_A_CHUNKS + SK_B_CHUNKS;
+constexpr int SK_LOADS = 4;                                // code loads per wave per stage
+
+__global__ __launch_bounds__(SK_WG) void mxfp4_gemm_splitk_kernel(
+    const uint4 *__restrict__ A, const uint8_t *__restrict__ As, const uint4 *__restrict__ Bt,
+    const uint8_t *__restrict__ Bs, int M, int N, int K, int ks, float *__restrict__ P) {
+    __shared__ uint4 ring[SK_RING][SK_STAGE_CHUNKS];
+    __shared__ uint4 a_scales[SK_SCALE_COLS][GEMM_TM];
+    __shared__ uint4 b_scales[SK_SCALE_COLS][SK_TN];
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int wr = w & 3, wc = w >> 2;     // row tile, column half
+    const int r32 = lane & 31;
+    const int kh = lane >> 5;
+    const int nblk = K / 32;               // blocks (16-byte chunks) per row
+    const int split = blockIdx.y;
+    const int kb0 = split * (ks / 32);     // the split's first block
+    const int nst = ks / GEMM_STAGE_K;
+    const int ncols = ks / 512;            // 16-byte scale chunks per row in the split
+    const int m0 = blockIdx.z * GEMM_TM, n0 = blockIdx.x * SK_TN;
+
+    // ---- the split's scales, once: lane l of a load moves 16 bytes (two
+    // stages) of row 64h + l of chunk column c
+    for (int i = w; i < 2 * ncols; i += SK_WG / 64) {
+        const int c = i >> 1, h = i & 1, row = 64 * h + lane;
+        const uint8_t *sa = As + (int64_t)min(m0 + row, M - 1) * nblk + kb0 + 16 * c;
+        const uint8_t *sb = Bs + (int64_t)min(n0 + row, N - 1) * nblk + kb0 + 16 * c;
+        __builtin_amdgcn_global_load_lds((gemm_gptr)sa, (gemm_lptr)&a_scales[c][64 * h], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gemm_gptr)sb, (gemm_lptr)&b_scales[c][64 * h], 16, 0, 0);
+    }
+
+    // code loads: lane l of a load covers row (8i + l / 8) of the wave's 16
+    // rows and LDS chunk l % 8, which holds the row's chunk (l % 8) ^ swizzle
+    const int lrow = lane >> 3, lpc = lane & 7;
+    const uint4 *ga[2], *gb[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int row = 16 * w + 8 * i + lrow;
+        const int c = lpc ^ gemm_swizzle(row);
+        ga[i] = A + (int64_t)min(m0 + row, M - 1) * nblk + kb0 + c;
+        gb[i] = Bt + (int64_t)min(n0 + row, N - 1) * nblk + kb0 + c;
+    }
+    // Four code loads per wave per stage: its 16 rows of A and of B.  Stages
+    // past the end re-read the last one into a slot that is never read, so
+    // every iteration issues the same loads and the wait is one constant.
+    auto issue = [&](int st, uint32_t slot) {
+        st = min(st, nst - 1);
+        uint4 *sb = &ring[0][0] + slot * SK_STAGE_CHUNKS;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            __builtin_amdgcn_global_load_lds((gemm_gptr)(ga[i] + st * 8),
+                                             (gemm_lptr)&sb[(16 * w + 8 * i) * 8], 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            __builtin_amdgcn_global_load_lds((gemm_gptr)(gb[i] + st * 8),
+                                             (gemm_lptr)&sb[SK_A_CHUNKS + (16 * w + 8 * i) * 8],
+                                             16, 0, 0);
+    };
+
+    f32x16_t acc0 = {}, acc1 = {};  // column tiles 2 wc and 2 wc + 1
+    const int arow = 32 * wr + r32;
+    const int brow = 64 * wc + r32;  // tile 1: brow + 32 (same swizzle)
+    const int sw = gemm_swizzle(r32);  // = that of arow, brow and brow + 32
+    uint32_t la[4], lb[4];
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(gemm_lptr)&ring[0][0];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+        const uint32_t c = (uint32_t)((2 * s4 + kh) ^ sw);
+        la[s4] = lds0 + (uint32_t)(arow * 8 + c) * 16u;
+        lb[s4] = lds0 + (uint32_t)(SK_A_CHUNKS + brow * 8 + c) * 16u;
+    }
+    const uint32_t lsa = (uint32_t)(uintptr_t)(gemm_lptr)&a_scales[0][arow];
+    const uint32_t lsb = (uint32_t)(uintptr_t)(gemm_lptr)&b_scales[0][brow];
+    constexpr uint32_t kSlotBytes = SK_STAGE_CHUNKS * 16u;
+    constexpr uint32_t kTileB = 32u * 8u * 16u;   // 32 rows of a stage
+    constexpr uint32_t kTileS = 32u * 16u;        // 32 rows of a scale column
+
+#pragma unroll
+    for (int st = 0; st < SK_RING - 1; ++st) issue(st, (uint32_t)st);
+    uint32_t slot = 0, fill = SK_RING - 1;
+    for (int st = 0; st < nst; ++st) {
+        constexpr int kLater = SK_LOADS * (SK_RING - 2);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (kLater & 15) | ((kLater >> 4) << 14));
+        __builtin_amdgcn_s_barrier();  // every wave's part visible; slot `fill` is free
+        issue(st + SK_RING - 1, fill);
+        const uint32_t off = slot * kSlotBytes;
+        const uint32_t soff = (uint32_t)(st >> 1) * 16u * GEMM_TM + (uint32_t)(st & 1) * 8u;
+        const uint32_t soffb = (uint32_t)(st >> 1) * 16u * SK_TN + (uint32_t)(st & 1) * 8u;
+        uint2 sa, sb0, sb1;
+        asm volatile(
+            "ds_read_b64 %0, %3\n\t"
+            "ds_read_b64 %1, %4\n\t"
+            "ds_read_b64 %2, %5\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(sa), "=&v"(sb0), "=&v"(sb1)
+            : "v"(lsa + soff), "v"(lsb + soffb), "v"(lsb + soffb + kTileS)
+            : "memory");
+        slot = slot + 1 == SK_RING ? 0 : slot + 1;
+        fill = fill + 1 == SK_RING ? 0 : fill + 1;
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            u32x4_t a, b0, b1;
+            asm volatile(
+                "ds_read_b128 %0, %3\n\t"
+                "ds_read_b128 %1, %4\n\t"
+                "ds_read_b128 %2, %5\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(a), "=&v"(b0), "=&v"(b1)
+                : "v"(la[s4] + off), "v"(lb[s4] + off), "v"(lb[s4] + off + kTileB)
+                : "memory");
+            const int i = 2 * s4 + kh;  // scale byte of this step and half
+            const int sh = 8 * (i & 3);
+            const int ea = (int)((i < 4 ? sa.x : sa.y) >> sh);
+            const i32x8_t ao = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+            const i32x8_t bo0 = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, 0, 0, 0, 0};
+            const i32x8_t bo1 = {(int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w, 0, 0, 0, 0};
+            acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                ao, bo0, acc0, 4, 4, 0, ea, 0, (int)((i < 4 ? sb0.x : sb0.y) >> sh));
+            acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                ao, bo1, acc1, 4, 4, 0, ea, 0, (int)((i < 4 ? sb1.x : sb1.y) >> sh));
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // the trailing re-reads land before the workgroup ends
+
+    // accumulator layout of the 32x32 MFMA: lane l holds column l % 32 and
+    // rows 8 (j / 4) + 4 (l / 32) + (j % 4), j = 0..15
+    float *Ps = P + (int64_t)split * M * N;
+    const f32x16_t acc[2] = {acc0, acc1};
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int col = n0 + 64 * wc + 32 * t + r32;
+        if (col < N) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int row = m0 + 32 * wr + 8 * (j / 4) + 4 * kh + (j % 4);
+                if (row < M) Ps[(int64_t)row * N + col] = acc[t][j];
+            }
+        }
+    }
+}
+
+// C = the S partials of each output added in increasing s, rounded once.
+// Four outputs per thread (M N is a multiple of 4).
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const uint4 *__restrict__ P,
+                                                            int64_t n4, int S,
+                                                            void *__restrict__ C) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+        const uint4 p = ld_stream(P + i);
+        float4 acc = make_float4(u2f(p.x), u2f(p.y), u2f(p.z), u2f(p.w));
+        for (int k = 1; k < S; ++k) {
+            const uint4 q = ld_stream(P + (int64_t)k * n4 + i);
+            acc.x += u2f(q.x);
+            acc.y += u2f(q.y);
+            acc.z += u2f(q.z);
+            acc.w += u2f(q.w);
+        }
+        if (OUT_BF16) {
+            uint2 o;
+            o.x = bf16_rne_bits(acc.x) | (bf16_rne_bits(acc.y) << 16);
+            o.y = bf16_rne_bits(acc.z) | (bf16_rne_bits(acc.w) << 16);
+            ((uint2 *)C)[i] = o;
+        } else {
+            ((float4 *)C)[i] = acc;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // NVFP4 x NVFP4 GEMM ("NVFP4 / MXFP4 format" page, section 6:
 // Y = a_X a_W sum_g b^X_g b^W_g sum_{k in g} p^X_k p^W_k over 16-element
 // groups).  The scaled MFMA applies one power of two per 32 K values; an
@@ -500,16 +698,16 @@ __global__ __launch_bounds__(GEMM_WG) void nvfp4_gemm_lds_kernel(
 
     // code loads, as the MXFP4 kernel: lane l of a load covers row
     // (8i + l / 8) of its group and LDS chunk l % 8, holding the row's chunk
-    // (l % 8) ^ (row & 7)
+    // (l % 8) ^ swizzle
     const int lrow = lane >> 3, lpc = lane & 7;
     const uint4 *ga[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = 32 * w + 8 * i + lrow;
-        ga[i] = A + (int64_t)min(m0 + row, M - 1) * nblk + (lpc ^ (row & 7));
+        ga[i] = A + (int64_t)min(m0 + row, M - 1) * nblk + (lpc ^ gemm_swizzle(row));
     }
     const int brow = 8 * w + lrow;
-    const uint4 *gb = Bt + (int64_t)min(n0 + brow, N - 1) * nblk + (lpc ^ (brow & 7));
+    const uint4 *gb = Bt + (int64_t)min(n0 + brow, N - 1) * nblk + (lpc ^ gemm_swizzle(brow));
     auto issue = [&](int st, uint32_t slot) {
         st = min(st, nst - 1);
         uint4 *sb = &ring[0][0] + slot * GEMM_STAGE_CHUNKS;
@@ -523,7 +721,7 @@ __global__ __launch_bounds__(GEMM_WG) void nvfp4_gemm_lds_kernel(
 
     f32x16_t acc0 = {}, acc1 = {};
     const int arow = 32 * w + r32;
-    const int sw = r32 & 7;
+    const int sw = gemm_swizzle(r32);  // = that of arow and of the B row r32
     // this lane's operand chunks in slot 0: (4 kh + i) ^ swizzle, i = 0..3
     uint32_t la[4], lb[4];
     const uint32_t lds0 = (uint32_t)(uintptr_t)(gemm_lptr)&ring[0][0];
@@ -791,6 +989,35 @@ hipError_t launch_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales,
         hipLaunchKernelGGL(mxfp4_gemm_kernel<false>, grid, dim3(GEMM_WG), 0, s,
                            (const uint4 *)a_codes, a_scales, (const uint4 *)bt_codes, bt_scales,
                            (int)M, (int)N, (int)K, c);
+    return hipGetLastError();
+}
+
+int gemm_splitk_parts(int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || N < 1 || N % 4 != 0 || K < 512 || K % 512 != 0) return 0;
+    // the fewest equal splits of at most SK_KS_MAX K, each a multiple of 512
+    for (int64_t S = (K + SK_KS_MAX - 1) / SK_KS_MAX; S <= K / 512; ++S)
+        if (K % S == 0 && (K / S) % 512 == 0) return (int)S;
+    return 0;
+}
+
+hipError_t launch_gemm_mxfp4_splitk(const uint8_t *a_codes, const uint8_t *a_scales,
+                                    const uint8_t *bt_codes, const uint8_t *bt_scales, int64_t M,
+                                    int64_t N, int64_t K, void *c, bool out_bf16, float *workspace,
+                                    hipStream_t s) {
+    const int S = gemm_splitk_parts(M, N, K);
+    if (S < 1) return hipErrorInvalidValue;
+    dim3 grid((unsigned)((N + SK_TN - 1) / SK_TN), (unsigned)S,
+              (unsigned)((M + GEMM_TM - 1) / GEMM_TM));
+    hipLaunchKernelGGL(mxfp4_gemm_splitk_kernel, grid, dim3(SK_WG), 0, s, (const uint4 *)a_codes,
+                       a_scales, (const uint4 *)bt_codes, bt_scales, (int)M, (int)N, (int)K,
+                       (int)(K / S), workspace);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n4 = M * N / 4;
+    int64_t g = (n4 + 255) / 256;
+    if (g > kMaxGrid) g = kMaxGrid;
+    auto k = out_bf16 ? splitk_reduce_kernel<true> : splitk_reduce_kernel<false>;
+    hipLaunchKernelGGL(k, dim3((unsigned)g), dim3(256), 0, s, (const uint4 *)workspace, n4, S, c);
     return hipGetLastError();
 }
 

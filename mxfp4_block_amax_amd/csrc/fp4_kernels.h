@@ -53,6 +53,14 @@ hipError_t launch_dequantize_padded(int fmt, const uint8_t *codes, const uint8_t
 hipError_t launch_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales,
                              const uint8_t *bt_codes, const uint8_t *bt_scales, int64_t M,
                              int64_t N, int64_t K, void *c, bool out_bf16, hipStream_t s);
+// Split-K MXFP4 GEMM: S equal K ranges (gemm_splitk_parts; 0 when the shape
+// is not supported), fp32 partials in workspace [S][M][N], then a reduction
+// in increasing split order.
+int gemm_splitk_parts(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_mxfp4_splitk(const uint8_t *a_codes, const uint8_t *a_scales,
+                                    const uint8_t *bt_codes, const uint8_t *bt_scales, int64_t M,
+                                    int64_t N, int64_t K, void *c, bool out_bf16, float *workspace,
+                                    hipStream_t s);
 // NVFP4 x NVFP4: C = (s_gA s_gB) * sum over 16-blocks of the E4M3 scale
 // products times the FP4 dot products.
 hipError_t launch_gemm_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, const float *sg_a,

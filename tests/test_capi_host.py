@@ -201,6 +201,41 @@ def test_sr_validation():
     assert q(ws=ctypes.c_void_p(0x10004)) == E_ALIGN
 
 
+def test_splitk_workspace_sizes():
+    # S = the fewest equal K ranges of at most 2048 K, each a multiple of 512
+    ws = fp4.gemm_splitk_workspace_bytes
+    assert ws(128, 8192, 8192) == 4 * 128 * 8192 * 4
+    assert ws(128, 8192, 4096) == 2 * 128 * 8192 * 4
+    assert ws(128, 8192, 2048) == 1 * 128 * 8192 * 4
+    assert ws(1, 8, 512) == 1 * 1 * 8 * 4
+    assert ws(64, 512, 3072) == 2 * 64 * 512 * 4      # 2 x 1536
+    assert ws(64, 512, 2560) == 5 * 64 * 512 * 4      # 5 x 512 (2 x 1280 is not allowed)
+    assert ws(64, 512, 16384) == 8 * 64 * 512 * 4
+    assert ws(128, 8192, 256) == 0                     # K below 512
+    assert ws(128, 8192, 8192 + 32) == 0               # K not a multiple of 512
+    assert ws(128, 6, 8192) == 0                       # N not a multiple of 4
+    assert ws(0, 8, 512) == 0
+
+
+def test_splitk_validation():
+    L = fp4.lib()
+
+    def g(M=128, N=256, K=1024, a=A16, sa=A16, c=A16, ws=A16, wsb=1 << 30, ct=fp4.BF16):
+        return L.fp4_gemm_mxfp4_splitk(a, sa, A16, A16, M, N, K, c, ct, ws, wsb, NULL)
+    assert g(a=NULL) == E_ARG
+    assert g(c=NULL) == E_ARG
+    assert g(ct=5) == E_DTYPE
+    assert g(K=480) == E_SHAPE
+    assert g(N=6) == E_SHAPE
+    assert g(M=0) == E_SHAPE
+    assert g(ws=NULL) == E_WORKSPACE
+    assert g(wsb=fp4.gemm_splitk_workspace_bytes(128, 256, 1024) - 1) == E_WORKSPACE
+    assert g(a=A1) == E_ALIGN
+    assert g(sa=ctypes.c_void_p(0x10008)) == E_ALIGN    # scales need 16 bytes
+    assert g(c=ctypes.c_void_p(0x10008), ct=fp4.F32) == E_ALIGN
+    assert g(ws=ctypes.c_void_p(0x10004)) == E_ALIGN
+
+
 def test_gemm_validation():
     L = fp4.lib()
 

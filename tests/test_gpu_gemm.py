@@ -87,6 +87,74 @@ def test_gemm_deterministic():
     assert torch.equal(c1, c2)
 
 
+# ---- split over K: fp32 partials per K range, fixed-order reduction ------------
+
+def _run_splitk(ap, asc, bp, bsc, M, N, K, out_dtype, workspace=None):
+    return fp4.gemm_mxfp4_splitk(dev(torch.from_numpy(ap.reshape(M, K // 2))),
+                                 dev(torch.from_numpy(asc.reshape(M, K // 32))),
+                                 dev(torch.from_numpy(bp.reshape(N, K // 2))),
+                                 dev(torch.from_numpy(bsc.reshape(N, K // 32))), out_dtype,
+                                 workspace=workspace)
+
+
+def _check_splitk(M, N, K, seed=0, workspace=None):
+    ap, asc, bp, bsc = _operands(M, N, K, seed)
+    parts = fp4.gemm_splitk_workspace_bytes(M, N, K) // (4 * M * N)
+    announce(f"gemm mxfp4 split-K ({parts} ranges) {M}x{N}x{K} fp32 out")
+    c32 = _run_splitk(ap, asc, bp, bsc, M, N, K, torch.float32, workspace)
+    announce(f"gemm mxfp4 split-K {M}x{N}x{K} bf16 out")
+    c16 = _run_splitk(ap, asc, bp, bsc, M, N, K, torch.bfloat16, workspace)
+    torch.cuda.synchronize()
+    ref = og.gemm_f64(ap, asc, bp, bsc, M, N, K)
+    got = c32.cpu().numpy().astype(np.float64)
+    err = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert err <= REL_FROB, f"split-K {M}x{N}x{K}: relative Frobenius error {err:.3e}"
+    # bf16 is the same fixed-order fp32 sum, rounded once
+    want16 = c32.cpu().to(torch.bfloat16)
+    assert torch.equal(c16.cpu().view(torch.int16), want16.view(torch.int16))
+    return err
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 256, 512), (1, 8, 512), (70, 52, 2560), (200, 72, 3072),
+                                   (256, 132, 4096), (33, 516, 1024), (130, 100, 16384)])
+def test_gemm_splitk_small_and_ragged(M, N, K):
+    _check_splitk(M, N, K)
+
+
+def test_gemm_splitk_full_size_128x8192x8192():
+    err = _check_splitk(128, 8192, 8192)
+    print(f"relative Frobenius error {err:.3e}")
+
+
+def test_gemm_splitk_integer_valued_is_exact():
+    # small-integer products and sums: every partial and their sum are exact
+    M, N, K = 64, 64, 4096
+    a = np.ones((M, K), np.float32) * np.arange(1, M + 1, dtype=np.float32)[:, None] % 4
+    b = np.ones((N, K), np.float32) * (np.arange(N, dtype=np.float32)[:, None] % 3 - 1)
+    ap, asc, _ = oracle.mx_quantize(a)
+    bp, bsc, _ = oracle.mx_quantize(b)
+    announce("gemm split-K integer-valued 64x64x4096")
+    c = _run_splitk(ap, asc, bp, bsc, M, N, K, torch.float32).cpu().numpy()
+    ref = og.gemm_f64(ap, asc, bp, bsc, M, N, K)
+    assert np.array_equal(c.astype(np.float64), ref)
+
+
+def test_gemm_splitk_deterministic_and_workspace_reuse():
+    ws = torch.empty(fp4.gemm_splitk_workspace_bytes(128, 8192, 8192), dtype=torch.uint8,
+                     device="cuda")
+    ap, asc, bp, bsc = _operands(128, 1024, 8192, seed=4)
+    announce("gemm split-K determinism 128x1024x8192")
+    c1 = _run_splitk(ap, asc, bp, bsc, 128, 1024, 8192, torch.float32, ws)
+    # a smaller call in between leaves other partials in the same workspace
+    _check_splitk(70, 52, 2560, seed=5, workspace=ws)
+    c2 = _run_splitk(ap, asc, bp, bsc, 128, 1024, 8192, torch.float32, ws)
+    assert torch.equal(c1, c2)
+    # the unsplit kernel sums in another order: both within the bound
+    c0 = _run(ap, asc, bp, bsc, 128, 1024, 8192, torch.float32)
+    rel = (torch.linalg.norm((c1 - c0).double()) / torch.linalg.norm(c0.double())).item()
+    assert rel <= 2 * REL_FROB
+
+
 # ---- W4A4 linear: activation quantize + GEMM in one call -----------------------
 
 def _check_linear(M, N, K, x_dtype=torch.float32, seed=0, workspace=None):
