@@ -15,10 +15,18 @@
 // block, so the per-block scaling of the formula happens inside the MFMA and
 // the fp32 accumulator spans all of K.
 //
-// Work split: a workgroup (4 waves) owns a 128 x 32 tile of C and walks all
-// of K; wave w owns rows 32w..32w+31.  B (N x K, the large operand at M=128)
-// is read from HBM once in total; A is re-read by every workgroup from L2.
-// The K loop is unrolled with a register prefetch of the next steps' codes.
+// Kernels here:
+//  - mxfp4_gemm_lds_kernel: a workgroup (4 waves) owns a 128 x 32 tile of C
+//    and walks all of K, staged through an LDS ring; wave w owns rows
+//    32w..32w+31.  B (N x K, the large operand at M = 128) is read from HBM
+//    once in total; A is re-read by every workgroup from L2.
+//  - mxfp4_gemm_fast_kernel (register-fed) and mxfp4_gemm_kernel (one K step
+//    at a time): the same product for shapes the staged kernel does not take.
+//  - mxfp4_gemm_splitk_kernel + splitk_reduce_kernel: 128 x 128 tiles over
+//    K ranges, fp32 partials, a fixed-order reduction.
+//  - nvfp4_gemm_lds_kernel / nvfp4_gemm_simple_kernel: NVFP4 x NVFP4 on the
+//    fp16 MFMA.
+//  - mxfp4_linear_kernel: activation quantize + the staged GEMM in one launch.
 #include <mutex>
 #include <type_traits>
 

@@ -211,18 +211,18 @@ __device__ __forceinline__ uint64_t splitmix64_mix(uint64_t z) {
 }
 
 // The E2M1 grid value |q| rounds to, with q's sign, given 24 random bits r.
-// For |q| >= 1, lo keeps the exponent and the top mantissa bit of |q| and
-// hi - lo is half the exponent's power of two; below 1 the grid step is 0.5.
-// A NaN comes out as a signed zero (its input is flagged non-finite).
+// |q| is clamped to 6 first (6 is a grid value, so it then stays).  For
+// |q| >= 1, lo keeps the exponent and the top mantissa bit of |q| and hi - lo
+// is half the exponent's power of two; below 1 the grid step is 0.5.  A NaN
+// comes out as +-6 (its input is flagged non-finite).
 __device__ __forceinline__ float sr_e2m1_value(float q, uint32_t r) {
-    const float m = __builtin_fabsf(q);
+    const float m = __builtin_fminf(__builtin_fabsf(q), 6.0f);
     const uint32_t b = f2u(m);
     const bool big = m >= 1.0f;
     const float lo = big ? u2f(b & 0xFFC00000u) : (m >= 0.5f ? 0.5f : 0.0f);
     const float gap = big ? u2f((b & 0x7F800000u) - 0x00800000u) : 0.5f;
     const float t = (float)r * 0x1p-24f * gap;  // exact
-    float v = t < m - lo ? lo + gap : lo;
-    v = m >= 6.0f ? 6.0f : v;
+    const float v = t < m - lo ? lo + gap : lo;
     return __builtin_copysignf(v, q);
 }
 
@@ -234,8 +234,13 @@ __device__ __forceinline__ uint32_t sr_codes8(const float (&q)[8], uint64_t seed
     for (int j = 0; j < 4; ++j) {
         const uint64_t z = splitmix64_mix(ctr);
         ctr += kSplitMixGamma;
-        v[2 * j] = sr_e2m1_value(q[2 * j], (uint32_t)z >> 8);
-        v[2 * j + 1] = sr_e2m1_value(q[2 * j + 1], (uint32_t)(z >> 32) >> 8);
+        // the top 24 bits of each 32-bit half; the empty asm hides the
+        // halves' origin so the conversion to float stays a 32-bit one (the
+        // optimiser would otherwise convert z >> 40 as a 64-bit integer)
+        uint32_t lo = (uint32_t)z, hi = (uint32_t)(z >> 32);
+        asm volatile("" : "+v"(lo), "+v"(hi));
+        v[2 * j] = sr_e2m1_value(q[2 * j], lo >> 8);
+        v[2 * j + 1] = sr_e2m1_value(q[2 * j + 1], hi >> 8);
     }
     return cvt_fp4x8_f32(v, e8m0_operand(E8M0_ONE));  // exact: grid values
 }
