@@ -414,6 +414,29 @@ def calibrate_copy(iters: int = 5):
     return {"bytes_read": n, "bytes_written": n, "iters": iters}
 
 
+def copy_ceiling(iters: int = 20):
+    """Measured device-to-device copy rate (bytes read + written per second)
+    of a 256 MiB buffer, alternating two source/destination pairs so that
+    neither is served from the 256 MB MALL: a practical HBM ceiling beside
+    the published peak."""
+    n = 256 << 20
+    bufs = [torch.empty(n, dtype=torch.uint8, device="cuda").fill_(i) for i in range(4)]
+    for i in range(2):
+        bufs[2 * i + 1].copy_(bufs[2 * i])
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(iters):
+        bufs[2 * (i & 1) + 1].copy_(bufs[2 * (i & 1)])
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / iters
+    gbs = 2 * n / (ms * 1e-3) / 1e9
+    return {"GB/s": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+            "method": "torch copy_ of 256 MiB, two buffer pairs alternating, HIP events; "
+                      "bytes read + written"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -501,6 +524,7 @@ def main():
                              "of back-to-back launches over 3 rotating buffer sets"},
         "breakdown": breakdown,
         "roofline": roofline,
+        "copy_ceiling": copy_ceiling(),
     }
     if not args.no_extra:
         line["extra"] = extra_workloads()
