@@ -3,9 +3,11 @@
  *
  * C ABI of libfp4.so.  Every tensor argument is a DEVICE pointer into memory
  * the caller owns (allocates and frees); the library allocates nothing.  Its
- * only global state is a per-device record, filled once, of whether the
- * one-pass NVFP4 kernel fits (CU count and occupancy).  Calls on different
- * streams may run concurrently unless they share a workspace.  All work is
+ * only global state is two per-device records, each filled once: whether the
+ * one-pass NVFP4 kernel fits (CU count and occupancy), and how many
+ * workgroups of the one-launch W4A4 linear kernel the device holds at once.
+ * Calls on different streams may run concurrently unless they share a
+ * workspace.  All work is
  * enqueued asynchronously on `stream` (a hipStream_t passed as void*; NULL is
  * the null stream).
  *
@@ -53,7 +55,8 @@ typedef enum {
     FP4_E_SHAPE = 2,     /* rows < 1, cols < 1, or cols not a multiple of block   */
     FP4_E_DTYPE = 3,     /* unknown fp4_dtype / fp4_format                        */
     FP4_E_ALIGN = 4,     /* a pointer is not aligned as documented                */
-    FP4_E_WORKSPACE = 5, /* workspace missing or smaller than fp4_workspace_bytes */
+    FP4_E_WORKSPACE = 5, /* workspace missing or smaller than the *_workspace_bytes
+                            call of the entry point reports                        */
     FP4_E_HIP = 6        /* a HIP runtime call (e.g. a launch) failed             */
 } fp4_status;
 
