@@ -413,16 +413,38 @@ __device__ __forceinline__ uint32_t nv_quant8(float (&v)[8], float ad, float ys,
 
 // Stochastic NVFP4 codes of 8 values with block scale alpha.  The quotient
 // must be RN32(x / alpha) for every size of it (the decision reads it down to
-// 2^-25, and below that whether it is zero), which the reciprocal-corrected
-// divide of the deterministic path does not promise for tiny alpha, so this
-// takes the IEEE fp32 divide (the library is built with correctly rounded
-// fp32 division and fp32 denormals kept).  alpha = 0 (a flagged scale
-// underflow) gives zero quotients.
+// 2^-25, and below that whether it is zero).  It is taken as
+// RN32(RN64(x * RN64(1 / alpha))): within 2^-52 (relative) of x / alpha, while
+// for a normal quotient no fp32 rounding boundary lies closer than 2^-49
+// (x - alpha m, m a midpoint, is a nonzero multiple of 2^(ea + eq - 47)), so the
+// fp32 result is exact.  Below 2^-100 only zero versus nonzero matters, and
+// RN32(x / alpha) is zero exactly when |x| <= alpha 2^-150, a comparison done
+// exactly in fp64 (a wave-uniform branch, taken only for such tiny
+// quotients).  alpha = 0 (a flagged scale underflow) gives zero quotients.
 __device__ __forceinline__ uint32_t nv_sr8(const float (&v)[8], float alpha, uint64_t seed,
                                            int64_t c) {
     float q[8];
+    const double ra = 1.0 / (double)alpha;
+    bool tiny = false;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = alpha == 0.0f ? 0.0f : v[i] / alpha;
+    for (int i = 0; i < 8; ++i) {
+        const double p = (double)v[i] * ra;
+        q[i] = (float)p;
+        tiny |= v[i] != 0.0f && __builtin_fabs(p) < 0x1p-100;
+    }
+    if (__ballot(tiny)) {
+        const double z = (double)alpha * 0x1p-150;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const double p = (double)v[i] * ra;
+            if (__builtin_fabs(p) < 0x1p-100)
+                q[i] = __builtin_copysignf(__builtin_fabs((double)v[i]) > z ? 0x1p-149f : 0.0f, v[i]);
+        }
+    }
+    if (alpha == 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = 0.0f;
+    }
     return sr_codes8(q, seed, c);
 }
 
