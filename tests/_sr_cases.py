@@ -84,3 +84,36 @@ def mean_within_bounds(x: np.ndarray, lo: np.ndarray, hi: np.ndarray, mean: np.n
     tot = np.sqrt(np.sum(se * se))
     ok_sum = bool(abs(dev.sum()) <= 6 * tot + 1e-12)
     return ok_each and ok_sum
+
+
+# A seed whose 24 random bits are zero at element 16 (found by search; the
+# tests check it): with r = 0 every nonzero quotient rounds up, so quotients
+# far below 2^-25 decide only by whether they are zero.
+SEED_ZERO_BITS_AT_16 = 1269119
+
+
+def tiny_quotient_cases():
+    """(value at element 16, expected NVFP4 code there, expected MXFP4 code)
+    for the tensors built by tiny_quotient_tensor: NVFP4 alpha = 2 (a 2688
+    block fixes s_g = 1, the test block holds 12), MXFP4 scale 1 (the block
+    holds 4).  RN32(x / alpha) is zero exactly when |x / alpha| <= 2^-150."""
+    return [
+        (2.0**-148, 1, 1),    # NV q = 2^-149: nonzero, up.  MX q = 2^-148: up
+        (-(2.0**-148), 9, 9),
+        (2.0**-149, 0, 1),    # NV q = 2^-150, the tie, rounds to 0: stays 0.  MX q = 2^-149: up
+        (1e-35, 1, 1),        # normal fp32, quotient below 2^-100: up
+        (0.0, 0, 0),
+        (-0.0, 8, 8),
+    ]
+
+
+def tiny_quotient_tensor(fmt_block: int, value: float) -> np.ndarray:
+    if fmt_block == 16:
+        x = np.zeros(32, np.float32)
+        x[:16] = 2688.0
+        x[17] = 12.0
+    else:
+        x = np.zeros(32, np.float32)
+        x[0] = 4.0
+    x[16] = np.float32(value)
+    return x

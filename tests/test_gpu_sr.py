@@ -12,7 +12,8 @@ import mxfp4_block_amax_amd as fp4
 import oracle
 import workloads
 from tests._gpu import announce, assert_bytes_equal, dev, f32_bits, host_u8, oracle_view
-from tests._sr_cases import mean_within_bounds, neighbour_values, threshold_blocks
+from tests._sr_cases import (SEED_ZERO_BITS_AT_16, mean_within_bounds, neighbour_values,
+                             threshold_blocks, tiny_quotient_cases, tiny_quotient_tensor)
 from tests.test_gpu_quantize import _mx_fp32_midpoint_tensor, _mx_sweep_tensor
 
 pytestmark = pytest.mark.gpu
@@ -58,6 +59,19 @@ def test_quotients_at_each_elements_threshold(fmt, seed):
         assert float(sg) == 1.0
     assert np.array_equal(oracle.unpack(p)[lead:], want)
     check_sr(fmt, t, seed, "threshold quotients")
+
+
+def test_tiny_quotients_with_zero_random_bits():
+    """Quotients far below 2^-25 (down to the fp32 subnormals and the tie at
+    2^-150) at an element whose random bits are zero: they round up exactly
+    when the fp32 quotient is nonzero, on both sides."""
+    for value, nv_code, mx_code in tiny_quotient_cases():
+        codes = check_sr(fp4.NVFP4, torch.from_numpy(tiny_quotient_tensor(16, value)).reshape(1, -1),
+                         SEED_ZERO_BITS_AT_16, f"tiny quotient {value!r}")[0]
+        assert oracle.unpack(host_u8(codes))[16] == nv_code
+        codes = check_sr(fp4.MXFP4, torch.from_numpy(tiny_quotient_tensor(32, value)).reshape(1, -1),
+                         SEED_ZERO_BITS_AT_16, f"tiny quotient {value!r}")[0]
+        assert oracle.unpack(host_u8(codes))[16] == mx_code
 
 
 # ---- exhaustive and adversarial value sets -------------------------------------

@@ -19,7 +19,8 @@ import pytest
 import oracle
 from tests._exact import E2M1_MAG
 from tests._golden import rows
-from tests._sr_cases import mean_within_bounds, neighbour_values, neighbours, threshold_blocks
+from tests._sr_cases import (SEED_ZERO_BITS_AT_16, mean_within_bounds, neighbour_values, neighbours,
+                             threshold_blocks, tiny_quotient_cases, tiny_quotient_tensor)
 
 M64 = 2**64 - 1
 TWO24 = 2**24
@@ -270,3 +271,20 @@ def test_nonfinite_flagged():
     x[3] = np.nan
     assert oracle.mx_quantize_sr(x, 1)[2] & oracle.FLAG_NONFINITE
     assert oracle.nv_quantize_sr(x, 1)[3] & oracle.FLAG_NONFINITE
+
+
+def test_tiny_quotients_round_up_only_when_nonzero():
+    """With zero random bits every nonzero quotient rounds up to 0.5 and a
+    zero one stays: quotients far below 2^-25 decide only by being zero,
+    which RN32(x / alpha) is exactly when |x / alpha| <= 2^-150 (the tie at
+    2^-150 goes to the even value 0)."""
+    assert oracle.sr_bits(SEED_ZERO_BITS_AT_16, 16) == 0
+    for value, nv_code, mx_code in tiny_quotient_cases():
+        xn = tiny_quotient_tensor(16, value)
+        p, s, sg, f = oracle.nv_quantize_sr(xn, SEED_ZERO_BITS_AT_16)
+        assert f == 0 and float(sg) == 1.0 and int(s[1]) == 0x40   # alpha = 2
+        assert oracle.unpack(p)[16] == nv_code, value
+        xm = tiny_quotient_tensor(32, value)
+        p, s, f = oracle.mx_quantize_sr(xm, SEED_ZERO_BITS_AT_16)
+        assert f == 0 and int(s[0]) == 127
+        assert oracle.unpack(p)[16] == mx_code, value
