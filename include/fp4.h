@@ -336,6 +336,19 @@ fp4_status fp4_dequantize_padded(fp4_format fmt, const uint8_t *codes, const uin
                                  fp4_dtype yt, void *stream);
 int64_t fp4_padded_storage_bytes(fp4_format fmt, int64_t rows, int64_t cols);
 
+/*
+ * For tests of the failure path of the grid barrier (the one-pass NVFP4
+ * quantize and the one-launch W4A4 linear): sets how many times a workgroup
+ * polls the other workgroups' slots before it gives up and raises
+ * FP4_FLAG_BARRIER_TIMEOUT (0 = after the first poll), for launches enqueued
+ * from then on, process-wide; returns the previous value.  The default is
+ * FP4_BARRIER_SPIN_LIMIT_DEFAULT polls (about a second).  Every kernel exits
+ * normally whatever the value; after a timeout the workspace must be zeroed
+ * again.
+ */
+#define FP4_BARRIER_SPIN_LIMIT_DEFAULT 524288u
+uint32_t fp4_debug_barrier_spin_limit(uint32_t polls);
+
 /* Bytes of device workspace fp4_quantize_nvfp4 / fp4_scale_search need for a
  * [rows, cols] input (0 for MXFP4). */
 size_t fp4_workspace_bytes(fp4_format fmt, int64_t rows, int64_t cols);

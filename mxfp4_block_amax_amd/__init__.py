@@ -45,7 +45,7 @@ EXPORTS = ("fp4_quantize_mxfp4", "fp4_quantize_mxfp4_rule", "fp4_quantize_nvfp4"
            "fp4_gemm_mxfp4", "fp4_gemm_mxfp4_splitk", "fp4_gemm_splitk_workspace_bytes",
            "fp4_gemm_nvfp4", "fp4_linear_mxfp4", "fp4_quantize_padded",
            "fp4_dequantize_padded", "fp4_padded_storage_bytes", "fp4_quantize_sr",
-           "fp4_workspace_bytes", "fp4_status_str")
+           "fp4_debug_barrier_spin_limit", "fp4_workspace_bytes", "fp4_status_str")
 
 # fp4_mx_rule: the MXFP4 block-exponent rules
 MX_RULES = {"ocp": 0, "ceil": 1, "mse": 2}
@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
     L.fp4_padded_storage_bytes.argtypes = [I, I64, I64]
     L.fp4_padded_storage_bytes.restype = I64
     L.fp4_linear_mxfp4.argtypes = [P, I, I64, I64, P, P, I64, P, P, P, I, I, P, S, P, P]
+    L.fp4_debug_barrier_spin_limit.argtypes = [ctypes.c_uint32]
+    L.fp4_debug_barrier_spin_limit.restype = ctypes.c_uint32
     L.fp4_workspace_bytes.argtypes = [I, I64, I64]
     L.fp4_workspace_bytes.restype = S
     L.fp4_status_str.argtypes = [I]
@@ -141,12 +143,22 @@ def _raise_flags(flags: int):
     if flags & FLAG_SCALE_UNDERFLOW:
         raise ValueError("a nonzero scale rounded to zero (tensor, block scale or alpha underflow)")
     if flags & FLAG_BARRIER_TIMEOUT:
-        raise Fp4Error("the one-pass NVFP4 grid barrier timed out; re-zero the workspace")
+        raise Fp4Error("a grid barrier timed out (one-pass NVFP4 quantize or one-launch linear); "
+                       "re-zero the workspace")
 
 
 def _finish(status: torch.Tensor, check: bool):
     if check:
         _raise_flags(int(status.item()))
+
+
+BARRIER_SPIN_LIMIT_DEFAULT = 524288
+
+
+def debug_barrier_spin_limit(polls: int) -> int:
+    """Set the grid barrier's poll limit (tests of the timeout path); returns
+    the previous value.  BARRIER_SPIN_LIMIT_DEFAULT restores the default."""
+    return int(lib().fp4_debug_barrier_spin_limit(int(polls)))
 
 
 def workspace_bytes(fmt: int, rows: int, cols: int) -> int:

@@ -276,6 +276,10 @@ int64_t fp4_padded_storage_bytes(fp4_format fmt, int64_t rows, int64_t cols) {
     return blocks * (block / 2 + 1) + (fmt == FP4_NVFP4 ? 4 : 0);
 }
 
+uint32_t fp4_debug_barrier_spin_limit(uint32_t polls) {
+    return fp4dev::set_barrier_spin_limit(polls);
+}
+
 size_t fp4_workspace_bytes(fp4_format fmt, int64_t rows, int64_t cols) {
     (void)rows;
     (void)cols;

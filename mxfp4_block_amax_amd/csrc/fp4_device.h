@@ -436,7 +436,8 @@ __device__ __forceinline__ uint32_t barrier_tag(const uint32_t *epoch) {
 // Called by one whole wave of every workgroup: publishes (tag, value) in
 // this workgroup's slot and polls until every slot of the grid carries the
 // tag; returns the largest value.  A bounded wait: after spin_limit polls it
-// sets FLAG_BARRIER_TIMEOUT in flags and returns what it has.
+// sets FLAG_BARRIER_TIMEOUT in flags and returns what it has, never less than
+// its own value (so a workgroup's own amax stays within the scale it uses).
 __device__ __forceinline__ uint32_t grid_barrier_max(uint64_t *slots, uint32_t *epoch, uint32_t tag,
                                                      uint32_t value, uint32_t spin_limit,
                                                      uint32_t &flags) {
@@ -458,7 +459,7 @@ __device__ __forceinline__ uint32_t grid_barrier_max(uint64_t *slots, uint32_t *
         const bool all = __ballot(!ok) == 0;
         if (all || it >= spin_limit) {
             if (!all) flags |= FLAG_BARRIER_TIMEOUT;
-            A = wave_max_u32(mm);
+            A = max(wave_max_u32(mm), value);
             break;
         }
         __builtin_amdgcn_s_sleep(2);

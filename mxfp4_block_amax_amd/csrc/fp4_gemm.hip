@@ -1047,7 +1047,7 @@ hipError_t launch_linear_mxfp4(const void *x, bool x_bf16, const uint8_t *bt_cod
                            (const uint4 *)x, (uint32_t *)a_codes, a_scales,
                            (const uint4 *)bt_codes, bt_scales, (int)M, (int)N, (int)K, c,
                            (uint64_t *)(ws + kResidentSlotsOffset),
-                           (uint32_t *)(ws + kResidentEpochOffset), kResidentSpinLimit, status);
+                           (uint32_t *)(ws + kResidentEpochOffset), barrier_spin_limit(), status);
         return hipGetLastError();
     }
     // the grid cannot be resident at once (or the shape takes another GEMM

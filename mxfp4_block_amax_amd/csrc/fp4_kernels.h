@@ -22,6 +22,10 @@ constexpr int kResidentSlots = 1024;
 constexpr size_t kNvWorkspaceBytes = kResidentSlotsOffset + kResidentSlots * sizeof(uint64_t);
 // Polls of the one-pass grid barrier before it gives up (about a second).
 constexpr uint32_t kResidentSpinLimit = 1u << 19;
+// The limit launches use: kResidentSpinLimit unless a test of the timeout
+// path has set another (fp4_debug_barrier_spin_limit).
+uint32_t barrier_spin_limit();
+uint32_t set_barrier_spin_limit(uint32_t polls);  // returns the previous value
 constexpr int kMaxDevices = 64;
 
 // rule: 0 the OCP floor rule, 1 the ceil rule, 2 the three-exponent search

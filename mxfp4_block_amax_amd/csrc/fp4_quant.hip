@@ -20,6 +20,7 @@
 //     an s_g that underflows, raises FP4_FLAG_SCALE_UNDERFLOW.
 // Scale search ("FP4 / NVFP4 math summary" page, devpress.csdn.net, section 9):
 //   per block, the candidate E4M3 scale with the least fp32 squared error.
+#include <atomic>
 #include <mutex>
 #include <type_traits>
 
@@ -1147,6 +1148,18 @@ __global__ __launch_bounds__(WG) void dequant_padded_kernel(const uint32_t *__re
 }
 
 // ---------------------------------------------------------------------------
+// the grid barrier's poll limit (a process-wide setting for tests of the
+// timeout path; launches read it when they are enqueued)
+// ---------------------------------------------------------------------------
+static std::atomic<uint32_t> g_spin_limit{kResidentSpinLimit};
+
+uint32_t barrier_spin_limit() { return g_spin_limit.load(std::memory_order_relaxed); }
+
+uint32_t set_barrier_spin_limit(uint32_t polls) {
+    return g_spin_limit.exchange(polls, std::memory_order_relaxed);
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 static inline int grid_for(int64_t waves_needed, int max_wg) {
@@ -1221,7 +1234,7 @@ static void launch_resident(int g, const void *x, int64_t nchunks, uint8_t *code
     hipLaunchKernelGGL(kernel, dim3(g), dim3(RES_WG), 0, s, (const uint4 *)x,
                        (int)nchunks, (uint32_t *)codes, scales, global_scale,
                        (uint64_t *)(ws + kResidentSlotsOffset),
-                       (uint32_t *)(ws + kResidentEpochOffset), kResidentSpinLimit, status);
+                       (uint32_t *)(ws + kResidentEpochOffset), barrier_spin_limit(), status);
 }
 
 hipError_t launch_nv_quantize(const void *x, bool bf16, int64_t n, uint8_t *codes,

@@ -245,3 +245,18 @@ def test_gemm_validation():
     assert g(K=48) == E_SHAPE
     assert g(M=0) == E_SHAPE
     assert g(a=A1) == E_ALIGN
+
+
+def test_barrier_spin_limit_round_trip():
+    """The poll limit is a host-side setting: set, read back through the
+    previous value, restored; the header's default matches the binding's."""
+    m = re.search(r"#define FP4_BARRIER_SPIN_LIMIT_DEFAULT (\d+)u", open(HEADER).read())
+    assert m and int(m.group(1)) == fp4.BARRIER_SPIN_LIMIT_DEFAULT
+    prev = fp4.debug_barrier_spin_limit(7)
+    try:
+        assert prev == fp4.BARRIER_SPIN_LIMIT_DEFAULT
+        assert fp4.debug_barrier_spin_limit(0) == 7
+        assert fp4.debug_barrier_spin_limit(2**32 - 1) == 0
+    finally:
+        fp4.debug_barrier_spin_limit(prev)
+    assert fp4.debug_barrier_spin_limit(prev) == fp4.BARRIER_SPIN_LIMIT_DEFAULT
