@@ -355,6 +355,18 @@ def extra_workloads():
                          for b in bq])
     d["split_k_us"] = round(ms2 * 1e3, 2)
     out["mxfp4_gemm_128x8192x8192_bf16out"] = d
+    # the same product on packed operands (MFMA operand order): B packed once
+    # (a weight), A packed per call (pack_a_us, timed on its own)
+    bps = [fp4.pack_mxfp4_operand(*b) for b in bq]
+    pa = fp4.pack_mxfp4_operand(ac, asc)
+    ms = time_rotating([lambda b=b: fp4.gemm_mxfp4_packed(pa, b, M, N, K, out=c) for b in bps])
+    d = _rate(gemm_bytes(M, N, K), ms)
+    tf = gemm_flops(M, N, K) / ms / 1e9
+    d.update({"TFLOP/s": round(tf, 1), "pct_fp4_mfma_peak": round(100 * tf / FP4_DENSE_PEAK_TFLOPS, 2)})
+    ms2 = time_rotating([lambda: fp4.pack_mxfp4_operand(ac, asc, out=pa)])
+    d["pack_a_us"] = round(ms2 * 1e3, 2)
+    out["mxfp4_gemm_packed_128x8192x8192_bf16out"] = d
+    del bps
     # K = 16384, beyond the staged kernel's scale capacity: the split-K path
     # against the entry point's register-fed fallback
     K2 = 16384

@@ -257,6 +257,44 @@ fp4_status fp4_gemm_mxfp4_splitk(const uint8_t *a_codes, const uint8_t *a_scales
 size_t fp4_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
+ * MFMA operand order for MXFP4 operands.  OCP leaves the physical layout of
+ * elements and scales to the implementation ("NVFP4 / MXFP4 format" page,
+ * section 7); this one serves the GEMM below.  An MXFP4 matrix X with rows
+ * rows and K values per row (codes [rows, K/2], scales [rows, K/32], the
+ * layout the quantizers write) becomes one buffer:
+ *   codes, for each row tile rt of 32 rows (the last one padded with zero
+ *   codes) and each K step ks of 64 values, 1024 bytes: bytes 16 l .. 16 l +
+ *   15 hold the codes of row 32 rt + l % 32, K block 2 ks + l / 32
+ *   (l = 0..63), as stored in that row;
+ *   then scales, for each row tile and each group q of eight K steps, 512
+ *   bytes: byte 8 l + i is the E8M0 byte of row 32 rt + l % 32 and K block
+ *   2 (8 q + i) + l / 32 (127 on padding rows).
+ * fp4_packed_operand_bytes(rows, K) is its size: 32 ceil(rows / 32) (K/2 +
+ * K/32) bytes, or 0 unless rows >= 1 and K is a positive multiple of 512.
+ *   codes, scales  the row-major operand (device); codes 16-byte aligned
+ *   packed         device output of at least that many bytes, 16-byte aligned
+ * Errors: FP4_E_SHAPE (size 0), FP4_E_WORKSPACE (packed_bytes too small),
+ * FP4_E_ALIGN.  Packing moves bytes only (bit-exact).
+ */
+int64_t fp4_packed_operand_bytes(int64_t rows, int64_t K);
+fp4_status fp4_pack_mxfp4_operand(const uint8_t *codes, const uint8_t *scales, int64_t rows,
+                                  int64_t K, uint8_t *packed, size_t packed_bytes, void *stream);
+
+/*
+ * The MXFP4 x MXFP4 GEMM of fp4_gemm_mxfp4 (same operation and sources) on
+ * packed operands: a_packed = A [M, K] and bt_packed = Bt [N, K], each made
+ * by fp4_pack_mxfp4_operand (a weight is packed once).  Every operand load
+ * is one contiguous kilobyte.  K must be a multiple of 2048, at most 16384;
+ * each packed operand at most 1 GiB; operands 16-byte aligned, c 4-byte
+ * aligned (FP4_E_SHAPE / FP4_E_ALIGN otherwise).  A workgroup's four waves
+ * take the four quarters of K for a 128 x 32 tile of C and add their partial
+ * tiles in a fixed order, so results are deterministic; the summation order
+ * differs from fp4_gemm_mxfp4's.
+ */
+fp4_status fp4_gemm_mxfp4_packed(const uint8_t *a_packed, const uint8_t *bt_packed, int64_t M,
+                                 int64_t N, int64_t K, void *c, fp4_dtype ct, void *stream);
+
+/*
  * NVFP4 x NVFP4 GEMM ("NVFP4 / MXFP4 format" page, section 6:
  * Y = a_X a_W sum_g b^X_g b^W_g sum_{k in g} p^X_k p^W_k, 16-element groups
  * along K, E4M3 block scales b, one fp32 tensor scale a per operand).

@@ -45,7 +45,8 @@ EXPORTS = ("fp4_quantize_mxfp4", "fp4_quantize_mxfp4_rule", "fp4_quantize_nvfp4"
            "fp4_gemm_mxfp4", "fp4_gemm_mxfp4_splitk", "fp4_gemm_splitk_workspace_bytes",
            "fp4_gemm_nvfp4", "fp4_linear_mxfp4", "fp4_quantize_padded",
            "fp4_dequantize_padded", "fp4_padded_storage_bytes", "fp4_quantize_sr",
-           "fp4_debug_barrier_spin_limit", "fp4_workspace_bytes", "fp4_status_str")
+           "fp4_debug_barrier_spin_limit", "fp4_packed_operand_bytes", "fp4_pack_mxfp4_operand",
+           "fp4_gemm_mxfp4_packed", "fp4_workspace_bytes", "fp4_status_str")
 
 # fp4_mx_rule: the MXFP4 block-exponent rules
 MX_RULES = {"ocp": 0, "ceil": 1, "mse": 2}
@@ -85,6 +86,10 @@ def lib() -> ctypes.CDLL:
     L.fp4_padded_storage_bytes.argtypes = [I, I64, I64]
     L.fp4_padded_storage_bytes.restype = I64
     L.fp4_linear_mxfp4.argtypes = [P, I, I64, I64, P, P, I64, P, P, P, I, I, P, S, P, P]
+    L.fp4_packed_operand_bytes.argtypes = [I64, I64]
+    L.fp4_packed_operand_bytes.restype = I64
+    L.fp4_pack_mxfp4_operand.argtypes = [P, P, I64, I64, P, S, P]
+    L.fp4_gemm_mxfp4_packed.argtypes = [P, P, I64, I64, I64, P, I, P]
     L.fp4_debug_barrier_spin_limit.argtypes = [ctypes.c_uint32]
     L.fp4_debug_barrier_spin_limit.restype = ctypes.c_uint32
     L.fp4_workspace_bytes.argtypes = [I, I64, I64]
@@ -315,6 +320,34 @@ def gemm_mxfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, bt_codes: torch.Te
     c = out if out is not None else torch.empty(M, N, dtype=out_dtype, device=a_codes.device)
     _ok(lib().fp4_gemm_mxfp4(_ptr(a_codes), _ptr(a_scales), _ptr(bt_codes), _ptr(bt_scales), M, N,
                              K, _ptr(c), _dtype_code(c.dtype), _stream(a_codes)))
+    return c
+
+
+def packed_operand_bytes(rows: int, K: int) -> int:
+    return int(lib().fp4_packed_operand_bytes(int(rows), int(K)))
+
+
+def pack_mxfp4_operand(codes: torch.Tensor, scales: torch.Tensor, out=None) -> torch.Tensor:
+    """An MXFP4 operand [rows, K] (codes [rows, K/2], scales [rows, K/32]) in
+    MFMA operand order, one uint8 buffer, for gemm_mxfp4_packed."""
+    rows, kh = _rows_cols(codes)
+    n = packed_operand_bytes(rows, 2 * kh)
+    if n == 0:
+        raise ValueError("packing needs K a positive multiple of 512")
+    packed = out if out is not None else torch.empty(n, dtype=torch.uint8, device=codes.device)
+    _ok(lib().fp4_pack_mxfp4_operand(_ptr(codes), _ptr(scales), rows, 2 * kh, _ptr(packed),
+                                     packed.numel(), _stream(codes)))
+    return packed
+
+
+def gemm_mxfp4_packed(a_packed: torch.Tensor, bt_packed: torch.Tensor, M: int, N: int, K: int,
+                      out_dtype=torch.bfloat16, out=None):
+    """C [M, N] = A @ B from packed A [M, K] and packed Bt [N, K]."""
+    if a_packed.numel() < packed_operand_bytes(M, K) or bt_packed.numel() < packed_operand_bytes(N, K):
+        raise ValueError("packed operand smaller than its shape")
+    c = out if out is not None else torch.empty(M, N, dtype=out_dtype, device=a_packed.device)
+    _ok(lib().fp4_gemm_mxfp4_packed(_ptr(a_packed), _ptr(bt_packed), int(M), int(N), int(K),
+                                    _ptr(c), _dtype_code(c.dtype), _stream(a_packed)))
     return c
 
 

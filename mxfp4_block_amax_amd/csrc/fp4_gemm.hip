@@ -247,6 +247,157 @@ __global__ __launch_bounds__(GEMM_WG) void mxfp4_gemm_fast_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// MFMA operand order ("packed" layout).  An MXFP4 matrix X with R rows and K
+// values per row is rearranged so that one 64-lane load of 16 bytes per lane
+// is exactly one operand of the scaled MFMA:
+//   codes:  row tile rt (32 rows; rows past R are zero), K step ks (64
+//           values): 1024 bytes in which lane l holds row 32 rt + l % 32,
+//           K block 2 ks + l / 32 (that block's 16 code bytes);
+//   scales: after all codes; per row tile and group q of eight K steps, 512
+//           bytes in which byte 8 l + i is the E8M0 byte of lane l's row and
+//           K half in step 8 q + i, i.e. of block 2 (8 q + i) + l / 32 (127
+//           on padding rows).
+// Weights are packed once; each operand load of the GEMM below is then one
+// contiguous kilobyte, instead of 32 rows x 32 bytes at the row stride, the
+// pattern that keeps the address unit of the register-fed kernel above busy.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pack_codes_kernel(const uint4 *__restrict__ codes,
+                                                         int64_t rows, int64_t nks,
+                                                         int64_t total, uint4 *__restrict__ out) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const int l = (int)(i & 63);
+        const int64_t t = i >> 6, ks = t % nks, rt = t / nks;
+        const int64_t r = rt * 32 + (l & 31);
+        out[i] = r < rows ? codes[r * (2 * nks) + 2 * ks + (l >> 5)] : make_uint4(0, 0, 0, 0);
+    }
+}
+
+__global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t *__restrict__ scales,
+                                                          int64_t rows, int64_t nks,
+                                                          int64_t total, uint32_t *__restrict__ out) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t nkq = nks / 8;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const int j = (int)(i & 1), l = (int)((i >> 1) & 63);
+        const int64_t t = i >> 7, q = t % nkq, rt = t / nkq;
+        const int64_t r = rt * 32 + (l & 31);
+        uint32_t v = 0x7F7F7F7Fu;
+        if (r < rows) {
+            // steps 8 q + 4 j + b, b = 0..3: blocks 2 step + l / 32
+            const uint8_t *s = scales + r * (2 * nks) + 2 * (8 * q + 4 * j) + (l >> 5);
+            v = (uint32_t)s[0] | ((uint32_t)s[2] << 8) | ((uint32_t)s[4] << 16) | ((uint32_t)s[6] << 24);
+        }
+        out[i] = v;
+    }
+}
+
+constexpr int PK_RING = 8;  // K steps in flight per wave
+
+// The GEMM on packed operands.  A workgroup owns a 128 x 32 tile of C; wave w
+// takes the w-th quarter of the K steps (SW = K / 256 of them) for all four
+// 32-row slices of A against the 32 columns of B.  The K walk is unrolled:
+// step st's five code loads (four A slices, one B) sit in ring slot st % 8,
+// issued eight steps ahead, so the load waits are exact constants; each
+// wave's scales (one 8-byte load per operand per eight steps) stay in
+// registers.  The four partial tiles are summed through LDS in a fixed order
+// (wave 0 + 1 + 2 + 3), so results are deterministic.
+template <bool OUT_BF16, int SW>
+__global__ __launch_bounds__(GEMM_WG) void mxfp4_gemm_packed_kernel(
+    const uint4 *__restrict__ Ap, const uint4 *__restrict__ Asp, const uint4 *__restrict__ Bp,
+    const uint4 *__restrict__ Bsp, int M, int N, void *__restrict__ C) {
+    constexpr int R = PK_RING;
+    constexpr int NQ = SW / 8;  // scale loads (8 steps each) per operand
+    constexpr int nks = 4 * SW, nkq = nks / 8;
+    __shared__ float part[4][4][16][64];  // [wave][row slice][acc element][lane]
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r32 = lane & 31;
+    const int kh = lane >> 5;
+    const int s0 = w * SW;
+    const int nrt_a = (M + 31) / 32, nrt_b = (N + 31) / 32;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void *)Ap, (short)0, nrt_a * nks * 1024, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)Bp, (short)0, nrt_b * nks * 1024, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void *)Asp, (short)0, nrt_a * nkq * 512, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void *)Bsp, (short)0, nrt_b * nkq * 512, kBufferRsrcWord3);
+    const int vo = lane * 16;
+    int oa[4], osa[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        const int rt = min((int)blockIdx.y * 4 + mi, nrt_a - 1);
+        oa[mi] = (rt * nks + s0) * 1024;
+        osa[mi] = (rt * nkq + s0 / 8) * 512;
+    }
+    const int ob = ((int)blockIdx.x * nks + s0) * 1024;
+    const int osb = ((int)blockIdx.x * nkq + s0 / 8) * 512;
+    auto ld = [&](__amdgpu_buffer_rsrc_t r, int off) {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, vo, off, 0);
+        return make_uint4(v.x, v.y, v.z, v.w);
+    };
+
+    auto ld2 = [&](__amdgpu_buffer_rsrc_t r, int off) {
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, lane * 8, off, 0);
+        return make_uint2(v.x, v.y);
+    };
+    // this wave's scales: NQ 8-byte loads per operand, kept in registers
+    uint2 sca[4][NQ], scb[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) sca[mi][q] = ld2(rsa, osa[mi] + q * 512);
+        scb[q] = ld2(rsb, osb + q * 512);
+    }
+    // the code ring: step st lives in slot st % R, loaded R steps ahead
+    uint4 ga[R][4], gb[R];
+    auto issue = [&](int slot, int st) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) ga[slot][mi] = ld(ra, oa[mi] + st * 1024);
+        gb[slot] = ld(rb, ob + st * 1024);
+    };
+#pragma unroll
+    for (int i = 0; i < R; ++i) issue(i, i);
+    auto sel = [](uint2 v, int j) { return j == 0 ? v.x : v.y; };
+
+    f32x16_t acc[4] = {};
+#pragma unroll
+    for (int st = 0; st < SW; ++st) {
+        const int slot = st % R, q = st / 8, j = (st / 4) % 2, sh = 8 * (st % 4);
+        const int sb = (int)(sel(scb[q], j) >> sh);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+            acc[mi] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                as_operand(ga[slot][mi]), as_operand(gb[slot]), acc[mi], 4, 4, 0,
+                (int)(sel(sca[mi][q], j) >> sh), 0, sb);
+        if (st + R < SW) issue(slot, st + R);
+        // keep each step's loads right after its MFMAs (sunk together they
+        // would empty the ring)
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) part[w][mi][j][lane] = acc[mi][j];
+    __syncthreads();
+    const int mi = w;  // wave w finishes row slice w
+    const int col = blockIdx.x * GEMM_TN + r32;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        float v = part[0][mi][j][lane];
+        v = v + part[1][mi][j][lane];
+        v = v + part[2][mi][j][lane];
+        v = v + part[3][mi][j][lane];
+        const int row = blockIdx.y * GEMM_TM + 32 * mi + 8 * (j / 4) + 4 * kh + (j % 4);
+        if (row < M && col < N) {
+            if (OUT_BF16)
+                ((uint16_t *)C)[(int64_t)row * N + col] = (uint16_t)bf16_rne_bits(v);
+            else
+                ((float *)C)[(int64_t)row * N + col] = v;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // LDS-staged kernel (K a multiple of 256; code rows 16-byte and scale rows
 // 8-byte aligned).  The operand layout of the scaled MFMA wants, per load
 // instruction, 32 rows x 32 bytes at the row stride, which keeps the address
@@ -997,6 +1148,54 @@ hipError_t launch_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales,
         hipLaunchKernelGGL(mxfp4_gemm_kernel<false>, grid, dim3(GEMM_WG), 0, s,
                            (const uint4 *)a_codes, a_scales, (const uint4 *)bt_codes, bt_scales,
                            (int)M, (int)N, (int)K, c);
+    return hipGetLastError();
+}
+
+int64_t packed_operand_bytes(int64_t rows, int64_t K) {
+    if (rows < 1 || K < 512 || K % 512 != 0) return 0;
+    const int64_t padded = (rows + 31) / 32 * 32;
+    return padded * (K / 2) + padded * (K / 32);
+}
+
+hipError_t launch_pack_mxfp4(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t K,
+                             uint8_t *packed, hipStream_t s) {
+    const int64_t nrt = (rows + 31) / 32, nks = K / 64;
+    const int64_t nc = nrt * nks * 64, ns = nrt * (nks / 8) * 128;
+    auto grid = [](int64_t n) {
+        int64_t g = (n + 255) / 256;
+        return (unsigned)(g > kMaxGrid ? kMaxGrid : g);
+    };
+    hipLaunchKernelGGL(pack_codes_kernel, dim3(grid(nc)), dim3(256), 0, s, (const uint4 *)codes,
+                       rows, nks, nc, (uint4 *)packed);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(pack_scales_kernel, dim3(grid(ns)), dim3(256), 0, s, scales, rows, nks, ns,
+                       (uint32_t *)(packed + nrt * 32 * (K / 2)));
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_mxfp4_packed(const uint8_t *a_packed, const uint8_t *bt_packed, int64_t M,
+                                    int64_t N, int64_t K, void *c, bool out_bf16, hipStream_t s) {
+    const int64_t nrt_a = (M + 31) / 32, nrt_b = (N + 31) / 32;
+    const uint4 *ap = (const uint4 *)a_packed, *bp = (const uint4 *)bt_packed;
+    const uint4 *asp = (const uint4 *)(a_packed + nrt_a * 32 * (K / 2));
+    const uint4 *bsp = (const uint4 *)(bt_packed + nrt_b * 32 * (K / 2));
+    dim3 grid((unsigned)nrt_b, (unsigned)((M + GEMM_TM - 1) / GEMM_TM));
+    using Kn = void (*)(const uint4 *, const uint4 *, const uint4 *, const uint4 *, int, int, void *);
+    // K steps per wave = K / 256: one instance per multiple of 2048 up to 16384
+    static const Kn kernels[2][8] = {
+        {mxfp4_gemm_packed_kernel<false, 8>, mxfp4_gemm_packed_kernel<false, 16>,
+         mxfp4_gemm_packed_kernel<false, 24>, mxfp4_gemm_packed_kernel<false, 32>,
+         mxfp4_gemm_packed_kernel<false, 40>, mxfp4_gemm_packed_kernel<false, 48>,
+         mxfp4_gemm_packed_kernel<false, 56>, mxfp4_gemm_packed_kernel<false, 64>},
+        {mxfp4_gemm_packed_kernel<true, 8>, mxfp4_gemm_packed_kernel<true, 16>,
+         mxfp4_gemm_packed_kernel<true, 24>, mxfp4_gemm_packed_kernel<true, 32>,
+         mxfp4_gemm_packed_kernel<true, 40>, mxfp4_gemm_packed_kernel<true, 48>,
+         mxfp4_gemm_packed_kernel<true, 56>, mxfp4_gemm_packed_kernel<true, 64>}};
+    const int idx = (int)(K / 2048) - 1;
+    if (idx < 0 || idx > 7 || K % 2048 != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kernels[out_bf16 ? 1 : 0][idx], grid, dim3(GEMM_WG), 0, s, ap, asp, bp, bsp,
+                       (int)M, (int)N, c);
     return hipGetLastError();
 }
 

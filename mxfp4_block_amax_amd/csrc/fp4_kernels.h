@@ -57,6 +57,14 @@ hipError_t launch_dequantize_padded(int fmt, const uint8_t *codes, const uint8_t
 hipError_t launch_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales,
                              const uint8_t *bt_codes, const uint8_t *bt_scales, int64_t M,
                              int64_t N, int64_t K, void *c, bool out_bf16, hipStream_t s);
+// MFMA operand order: bytes of a packed MXFP4 operand with rows x K values
+// (0 unless K is a positive multiple of 512), the pack, and the GEMM on two
+// packed operands (K a multiple of 2048, at most 16384).
+int64_t packed_operand_bytes(int64_t rows, int64_t K);
+hipError_t launch_pack_mxfp4(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t K,
+                             uint8_t *packed, hipStream_t s);
+hipError_t launch_gemm_mxfp4_packed(const uint8_t *a_packed, const uint8_t *bt_packed, int64_t M,
+                                    int64_t N, int64_t K, void *c, bool out_bf16, hipStream_t s);
 // Split-K MXFP4 GEMM: S equal K ranges (gemm_splitk_parts; 0 when the shape
 // is not supported), fp32 partials in workspace [S][M][N], then a reduction
 // in increasing split order.

@@ -74,3 +74,69 @@ def nv_gemm_f64(a_packed, a_scales, sg_a, bt_packed, bt_scales, sg_b, M: int, N:
     A = nv_dequant_matrix_exact(a_packed, a_scales, sg_a, M, K)
     Bt = nv_dequant_matrix_exact(bt_packed, bt_scales, sg_b, N, K)
     return A @ Bt.T
+
+
+# ---- MFMA operand order (the packed operand layout) ----------------------------
+#
+# Not a layout the pages fix: OCP leaves the physical arrangement of elements
+# and scales to the implementation ("NVFP4 / MXFP4 format" page, section 7).
+# It is the arrangement the library's packed GEMM reads.  For row tile rt
+# (32 rows, the last padded with zero codes and scale byte 127) and K step ks
+# (64 values), lane l of a 64-lane operand holds row 32 rt + l % 32 and K
+# block 2 ks + l // 32 (16 code bytes); after all codes, the scale of that
+# lane's block in step 8 q + i sits at byte 8 l + i of the tile's 512-byte
+# scale group q.
+
+def packed_bytes(rows: int, K: int) -> int:
+    nrt = (rows + 31) // 32
+    return nrt * 32 * (K // 2) + nrt * 32 * (K // 32)
+
+
+def pack_operand(codes: np.ndarray, scales: np.ndarray, rows: int, K: int) -> np.ndarray:
+    """Row-major MXFP4 operand (codes [rows, K/2], scales [rows, K/32]) to the
+    packed layout, one byte at a time in the order the layout lists them."""
+    nrt, nks = (rows + 31) // 32, K // 64
+    c = np.zeros((nrt * 32, K // 2), np.uint8)
+    c[:rows] = np.asarray(codes, np.uint8).reshape(rows, K // 2)
+    s = np.full((nrt * 32, K // 32), 127, np.uint8)
+    s[:rows] = np.asarray(scales, np.uint8).reshape(rows, K // 32)
+    out_c = np.zeros((nrt, nks, 64, 16), np.uint8)
+    out_s = np.zeros((nrt, nks // 8, 64, 8), np.uint8)
+    for l in range(64):
+        row = np.arange(nrt)[:, None] * 32 + l % 32          # [nrt, 1]
+        blk = 2 * np.arange(nks)[None, :] + l // 32          # [1, nks]
+        for b in range(16):
+            out_c[:, :, l, b] = c[row, 16 * blk + b]
+        for i in range(8):
+            step = 8 * np.arange(nks // 8)[None, :] + i
+            out_s[:, :, l, i] = s[row, 2 * step + l // 32]
+    return np.concatenate([out_c.reshape(-1), out_s.reshape(-1)])
+
+
+def gemm_from_packed(a_packed: np.ndarray, bt_packed: np.ndarray, M: int, N: int,
+                     K: int) -> np.ndarray:
+    """C = A @ B in binary64, reading both operands the way the scaled MFMA
+    consumes them (v_mfma_scale_f32_32x32x64_f8f6f4 with E2M1 operands: lane l
+    supplies row or column l % 32 and the 32 K values from 32 (l // 32) of
+    the 64-wide step, with its own E8M0 byte): for every pair of row tiles and
+    every K step, the 32 x 64 slices from the 64 lanes, multiplied and added.
+    Written from the consumer's side, independently of pack_operand."""
+    mag = np.array([e2m1_value(c) for c in range(16)])
+
+    def tiles(packed, rows):
+        nrt, nks = (rows + 31) // 32, K // 64
+        codes = np.asarray(packed[:nrt * nks * 1024], np.uint8).reshape(nrt, nks, 64, 16)
+        scl = np.asarray(packed[nrt * nks * 1024:], np.uint8).reshape(nrt, nks // 8, 64, 8)
+        vals = np.zeros((nrt, nks, 32, 64))                   # [tile, step, row, K in step]
+        for l in range(64):
+            lo, hi = codes[:, :, l, :] & 15, codes[:, :, l, :] >> 4
+            v = np.stack([mag[lo], mag[hi]], axis=-1).reshape(nrt, nks, 32)  # even element low
+            e = scl[:, :, l, :].reshape(nrt, nks).astype(np.int64) - 127
+            vals[:, :, l % 32, 32 * (l // 32):32 * (l // 32) + 32] = v * np.ldexp(1.0, e)[:, :, None]
+        return vals
+
+    A, B = tiles(a_packed, M), tiles(bt_packed, N)
+    C = np.zeros((A.shape[0] * 32, B.shape[0] * 32))
+    for ks in range(K // 64):
+        C += np.einsum("irk,jck->irjc", A[:, ks], B[:, ks]).reshape(A.shape[0] * 32, B.shape[0] * 32)
+    return C[:M, :N]

@@ -260,3 +260,36 @@ def test_barrier_spin_limit_round_trip():
     finally:
         fp4.debug_barrier_spin_limit(prev)
     assert fp4.debug_barrier_spin_limit(prev) == fp4.BARRIER_SPIN_LIMIT_DEFAULT
+
+
+def test_packed_sizes_and_validation():
+    L = fp4.lib()
+    assert fp4.packed_operand_bytes(1, 512) == 32 * 256 + 32 * 16
+    assert fp4.packed_operand_bytes(33, 1024) == 64 * 512 + 64 * 32
+    assert fp4.packed_operand_bytes(128, 8192) == 128 * 4096 + 128 * 256
+    assert fp4.packed_operand_bytes(1, 256) == 0        # K below 512
+    assert fp4.packed_operand_bytes(1, 1000) == 0
+    assert fp4.packed_operand_bytes(0, 512) == 0
+
+    def p(c=A16, s=A16, rows=64, K=1024, out=A16, nb=1 << 20):
+        return L.fp4_pack_mxfp4_operand(c, s, rows, K, out, nb, NULL)
+    assert p(c=NULL) == E_ARG
+    assert p(out=NULL) == E_ARG
+    assert p(K=256) == E_SHAPE
+    assert p(rows=0) == E_SHAPE
+    assert p(nb=fp4.packed_operand_bytes(64, 1024) - 1) == E_WORKSPACE
+    assert p(c=A1) == E_ALIGN
+    assert p(out=ctypes.c_void_p(0x10008)) == E_ALIGN
+
+    def g(a=A16, b=A16, M=128, N=256, K=2048, c=A16, ct=fp4.BF16):
+        return L.fp4_gemm_mxfp4_packed(a, b, M, N, K, c, ct, NULL)
+    assert g(a=NULL) == E_ARG
+    assert g(c=NULL) == E_ARG
+    assert g(ct=7) == E_DTYPE
+    assert g(K=1024) == E_SHAPE
+    assert g(K=3072) == E_SHAPE
+    assert g(K=18432) == E_SHAPE
+    assert g(M=0) == E_SHAPE
+    assert g(N=1 << 20, K=16384) == E_SHAPE   # packed Bt above 1 GiB
+    assert g(a=A1) == E_ALIGN
+    assert g(c=ctypes.c_void_p(0x10002)) == E_ALIGN

@@ -294,3 +294,61 @@ def test_gemm_nvfp4_deterministic():
     c1 = _run_nv(*ops, 128, 1024, 2048, torch.float32)
     c2 = _run_nv(*ops, 128, 1024, 2048, torch.float32)
     assert torch.equal(c1, c2)
+
+
+# ---- packed operands (MFMA operand order) ---------------------------------------
+
+def _packed_case(M, N, K, seed=0):
+    ap, asc, bp, bsc = _operands(M, N, K, seed)
+    announce(f"pack mxfp4 operands {M}x{K} and {N}x{K}")
+    pa = fp4.pack_mxfp4_operand(dev(torch.from_numpy(ap.reshape(M, K // 2))),
+                                dev(torch.from_numpy(asc.reshape(M, K // 32))))
+    pb = fp4.pack_mxfp4_operand(dev(torch.from_numpy(bp.reshape(N, K // 2))),
+                                dev(torch.from_numpy(bsc.reshape(N, K // 32))))
+    torch.cuda.synchronize()
+    assert_bytes_equal(host_u8(pa), og.pack_operand(ap, asc, M, K), f"packed A {M}x{K}")
+    if N * K <= 2048 * 8192:
+        assert_bytes_equal(host_u8(pb), og.pack_operand(bp, bsc, N, K), f"packed Bt {N}x{K}")
+    return ap, asc, bp, bsc, pa, pb
+
+
+def _check_packed(M, N, K, seed=0):
+    ap, asc, bp, bsc, pa, pb = _packed_case(M, N, K, seed)
+    announce(f"gemm mxfp4 packed {M}x{N}x{K} fp32 and bf16 out")
+    c32 = fp4.gemm_mxfp4_packed(pa, pb, M, N, K, torch.float32)
+    c16 = fp4.gemm_mxfp4_packed(pa, pb, M, N, K, torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = og.gemm_f64(ap, asc, bp, bsc, M, N, K)
+    err = np.linalg.norm(c32.cpu().numpy().astype(np.float64) - ref) / np.linalg.norm(ref)
+    assert err <= REL_FROB, f"packed {M}x{N}x{K}: relative Frobenius error {err:.3e}"
+    want16 = c32.cpu().to(torch.bfloat16)
+    assert torch.equal(c16.cpu().view(torch.int16), want16.view(torch.int16))
+    return err
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 256, 2048), (1, 32, 2048), (70, 100, 2048),
+                                   (130, 64, 6144), (256, 512, 4096), (33, 40, 16384),
+                                   (96, 33, 10240)])
+def test_gemm_packed_small_and_ragged(M, N, K):
+    _check_packed(M, N, K)
+
+
+def test_gemm_packed_full_size_128x8192x8192():
+    err = _check_packed(128, 8192, 8192)
+    print(f"relative Frobenius error {err:.3e}")
+
+
+def test_gemm_packed_integer_valued_is_exact_and_deterministic():
+    M, N, K = 64, 96, 2048
+    a = np.ones((M, K), np.float32) * np.arange(1, M + 1, dtype=np.float32)[:, None] % 4
+    b = np.ones((N, K), np.float32) * (np.arange(N, dtype=np.float32)[:, None] % 3 - 1)
+    ap, asc, _ = oracle.mx_quantize(a)
+    bp, bsc, _ = oracle.mx_quantize(b)
+    announce("gemm packed integer-valued 64x96x2048")
+    pa = dev(torch.from_numpy(og.pack_operand(ap, asc, M, K)))
+    pb = dev(torch.from_numpy(og.pack_operand(bp, bsc, N, K)))
+    c1 = fp4.gemm_mxfp4_packed(pa, pb, M, N, K, torch.float32)
+    c2 = fp4.gemm_mxfp4_packed(pa, pb, M, N, K, torch.float32)
+    ref = og.gemm_f64(ap, asc, bp, bsc, M, N, K)
+    assert np.array_equal(c1.cpu().numpy().astype(np.float64), ref)
+    assert torch.equal(c1, c2)
