@@ -895,19 +895,28 @@ template <bool BF16>
 __device__ __forceinline__ float half_block_loss(const float (&a)[8], float4 sq) {
     // sq = {alpha, alpha', +-1/alpha', sc}: divide as (a sc) / alpha' (one
     // multiply for bf16 input when no lane's scale is marked), rebuild with alpha
+    // Both choices are wave-uniform; operands are scaled (x sc, exact) only
+    // when some lane of the wave needs it (tensors with a tiny s_g).
     const float alpha = sq.x;
-    float xs[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) xs[i] = a[i];
-    scale_values(xs, sq.w);
     const float y = __builtin_fabsf(sq.z);
+    const bool scaled = __ballot(sq.w != 1.0f) != 0;
     float q[8];
     if (BF16 && !__ballot(sq.z < 0.0f)) {
+        if (!scaled) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = xs[i] * y;
+            for (int i = 0; i < 8; ++i) q[i] = a[i] * y;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) q[i] = (a[i] * sq.w) * y;
+        }
     } else {
+        if (!scaled) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = div_rn(xs[i], sq.y, y);
+            for (int i = 0; i < 8; ++i) q[i] = div_rn(a[i], sq.y, y);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) q[i] = div_rn(a[i] * sq.w, sq.y, y);
+        }
     }
     const float one = e8m0_operand(E8M0_ONE);
     uint32_t code = cvt_fp4x8_f32(q, one);
@@ -967,14 +976,29 @@ __global__ __launch_bounds__(WG) void scale_search_kernel(
             uint32_t lo = ALL ? 1u : nv_code_real(T, (double)c_lo * ag, inv6sg);
             const uint32_t hi = ALL ? 126u : nv_code_real(T, (double)c_hi * ag, inv6sg);
             lo = lo < 1u ? 1u : lo;
-            float bestL = 0.0f;
+            // Codes from the largest down; a loss equal to the incumbent's
+            // replaces it, so the smallest code wins ties, as in increasing
+            // order with strict improvement.  Every term of the loss is >= 0
+            // and the fp32 pairwise sum of such terms is at least each of
+            // them, so once the block maximum saturates (amax >= RN(6 alpha),
+            // hence its quotient exceeds 5 and it quantizes to 6 alpha) its
+            // own term RN(RN(amax - RN(6 alpha))^2) bounds the loss from
+            // below; that bound only grows as the code falls, so the walk
+            // stops at the first code whose bound exceeds the best loss.
+            const float agf = u2f(ag_bits);
+            float bestL = __builtin_inff();
             bool have = false;
-            for (uint32_t code = lo; code <= hi; ++code) {
+            for (uint32_t code = hi; code >= lo; --code) {
                 const float4 sq = T.q[code];
-                if (sq.x == 0.0f) continue;
+                const float x6 = 6.0f * sq.x;
+                const float e6 = agf - x6;
+                const float bound = agf >= x6 ? e6 * e6 : 0.0f;
+                if (bound > bestL) break;
+                // a code whose alpha underflowed to 0 is evaluated (its loss
+                // is finite) but never taken
                 float part = half_block_loss<BF16>(a, sq);
                 float L = part + dppf<QP_XOR1>(part);
-                if (!have || L < bestL) {
+                if (sq.x != 0.0f && L <= bestL) {
                     best = code;
                     bestL = L;
                     have = true;
