@@ -398,6 +398,14 @@ def extra_workloads():
                          for b in bq])
     d["two_launches_us"] = round(ms2 * 1e3, 2)
     out["mxfp4_linear_w4a4_128x8192x8192_bf16"] = d
+    # the same linear on a packed weight: activations quantized straight into
+    # the packed layout, then the packed GEMM (two launches)
+    bps = [fp4.pack_mxfp4_operand(*b) for b in bq]
+    apk = torch.empty(fp4.packed_operand_bytes(M, K), dtype=torch.uint8, device="cuda")
+    ms = time_rotating([lambda b=b: fp4.linear_mxfp4_packed(xa, b, N, out=c, a_out=apk, status=st,
+                                                            check=False) for b in bps])
+    out["mxfp4_linear_w4a4_packed_128x8192x8192_bf16"] = _rate(lin_bytes, ms)
+    del bps
     # NVFP4 x NVFP4 GEMM, same shape: operands NVFP4-quantized on the GPU,
     # eight copies of B rotate
     an = fp4.quantize_nvfp4(a.cuda())

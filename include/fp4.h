@@ -295,6 +295,34 @@ fp4_status fp4_gemm_mxfp4_packed(const uint8_t *a_packed, const uint8_t *bt_pack
                                  int64_t N, int64_t K, void *c, fp4_dtype ct, void *stream);
 
 /*
+ * MXFP4 quantize of x [rows, cols] (fp32 or bf16) by the OCP floor rule, as
+ * fp4_quantize_mxfp4 (same codes and scale bytes, "NVFP4 / MXFP4 format"
+ * page, section 5), written directly in the packed layout of
+ * fp4_pack_mxfp4_operand (padding rows come out as zero codes with scale
+ * byte 127).  cols must be a multiple of 512; packed must hold
+ * fp4_packed_operand_bytes(rows, cols) bytes, 16-byte aligned; x 16-byte
+ * aligned.  status as for fp4_quantize_mxfp4 (FP4_FLAG_NONFINITE).
+ * Errors: FP4_E_SHAPE, FP4_E_WORKSPACE (packed too small), FP4_E_ALIGN.
+ */
+fp4_status fp4_quantize_mxfp4_packed(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
+                                     uint8_t *packed, size_t packed_bytes, int32_t *status,
+                                     void *stream);
+
+/*
+ * W4A4 linear on a packed weight: x [M, K] (fp32 or bf16) quantized to
+ * MXFP4 by the floor rule into a_packed (packed layout), then
+ * fp4_gemm_mxfp4_packed with bt_packed = Bt [N, K] packed once (the
+ * operation of fp4_linear_mxfp4; "FP4, FP8 and INT8/INT4" page, section
+ * 5.1).  Two launches on one stream.  K a multiple of 2048, at most 16384;
+ * a_packed at least fp4_packed_operand_bytes(M, K) bytes; alignment as for
+ * the two calls.  status receives FP4_FLAG_NONFINITE for x.
+ */
+fp4_status fp4_linear_mxfp4_packed(const void *x, fp4_dtype xt, int64_t M, int64_t K,
+                                   const uint8_t *bt_packed, int64_t N, uint8_t *a_packed,
+                                   size_t a_packed_bytes, void *c, fp4_dtype ct, int32_t *status,
+                                   void *stream);
+
+/*
  * NVFP4 x NVFP4 GEMM ("NVFP4 / MXFP4 format" page, section 6:
  * Y = a_X a_W sum_g b^X_g b^W_g sum_{k in g} p^X_k p^W_k, 16-element groups
  * along K, E4M3 block scales b, one fp32 tensor scale a per operand).

@@ -46,7 +46,8 @@ EXPORTS = ("fp4_quantize_mxfp4", "fp4_quantize_mxfp4_rule", "fp4_quantize_nvfp4"
            "fp4_gemm_nvfp4", "fp4_linear_mxfp4", "fp4_quantize_padded",
            "fp4_dequantize_padded", "fp4_padded_storage_bytes", "fp4_quantize_sr",
            "fp4_debug_barrier_spin_limit", "fp4_packed_operand_bytes", "fp4_pack_mxfp4_operand",
-           "fp4_gemm_mxfp4_packed", "fp4_workspace_bytes", "fp4_status_str")
+           "fp4_gemm_mxfp4_packed", "fp4_quantize_mxfp4_packed", "fp4_linear_mxfp4_packed",
+           "fp4_workspace_bytes", "fp4_status_str")
 
 # fp4_mx_rule: the MXFP4 block-exponent rules
 MX_RULES = {"ocp": 0, "ceil": 1, "mse": 2}
@@ -90,6 +91,8 @@ def lib() -> ctypes.CDLL:
     L.fp4_packed_operand_bytes.restype = I64
     L.fp4_pack_mxfp4_operand.argtypes = [P, P, I64, I64, P, S, P]
     L.fp4_gemm_mxfp4_packed.argtypes = [P, P, I64, I64, I64, P, I, P]
+    L.fp4_quantize_mxfp4_packed.argtypes = [P, I, I64, I64, P, S, P, P]
+    L.fp4_linear_mxfp4_packed.argtypes = [P, I, I64, I64, P, I64, P, S, P, I, P, P]
     L.fp4_debug_barrier_spin_limit.argtypes = [ctypes.c_uint32]
     L.fp4_debug_barrier_spin_limit.restype = ctypes.c_uint32
     L.fp4_workspace_bytes.argtypes = [I, I64, I64]
@@ -349,6 +352,41 @@ def gemm_mxfp4_packed(a_packed: torch.Tensor, bt_packed: torch.Tensor, M: int, N
     _ok(lib().fp4_gemm_mxfp4_packed(_ptr(a_packed), _ptr(bt_packed), int(M), int(N), int(K),
                                     _ptr(c), _dtype_code(c.dtype), _stream(a_packed)))
     return c
+
+
+def quantize_mxfp4_packed(x: torch.Tensor, check: bool = True, out=None, status=None):
+    """MXFP4 quantize (floor rule) of x [rows, cols] written in MFMA operand
+    order: the bytes pack_mxfp4_operand(*quantize_mxfp4(x)) would give."""
+    rows, cols = _rows_cols(x)
+    n = packed_operand_bytes(rows, cols)
+    if n == 0:
+        raise ValueError("the packed layout needs cols a positive multiple of 512")
+    packed = out if out is not None else torch.empty(n, dtype=torch.uint8, device=x.device)
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _ok(lib().fp4_quantize_mxfp4_packed(_ptr(x), _dtype_code(x.dtype), rows, cols, _ptr(packed),
+                                        packed.numel(), _ptr(status), _stream(x)))
+    _finish(status, check)
+    return packed
+
+
+def linear_mxfp4_packed(x: torch.Tensor, bt_packed: torch.Tensor, N: int,
+                        out_dtype=torch.bfloat16, out=None, a_out=None, status=None,
+                        check: bool = True):
+    """W4A4 linear on a packed weight: x [M, K] quantized into packed A, then
+    the packed GEMM.  Returns (C [M, N], a_packed)."""
+    M, K = _rows_cols(x)
+    n = packed_operand_bytes(M, K)
+    a_packed = a_out if a_out is not None else torch.empty(max(n, 16), dtype=torch.uint8,
+                                                           device=x.device)
+    c = out if out is not None else torch.empty(M, N, dtype=out_dtype, device=x.device)
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _ok(lib().fp4_linear_mxfp4_packed(_ptr(x), _dtype_code(x.dtype), M, K, _ptr(bt_packed), int(N),
+                                      _ptr(a_packed), a_packed.numel(), _ptr(c),
+                                      _dtype_code(c.dtype), _ptr(status), _stream(x)))
+    _finish(status, check)
+    return c, a_packed
 
 
 def gemm_splitk_workspace_bytes(M: int, N: int, K: int) -> int:

@@ -196,6 +196,40 @@ fp4_status fp4_gemm_mxfp4_packed(const uint8_t *a_packed, const uint8_t *bt_pack
                                                      ct == FP4_BF16, (hipStream_t)stream));
 }
 
+fp4_status fp4_quantize_mxfp4_packed(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
+                                     uint8_t *packed, size_t packed_bytes, int32_t *status,
+                                     void *stream) {
+    if (!x || !packed) return FP4_E_ARG;
+    if (!valid_dtype(xt)) return FP4_E_DTYPE;
+    const int64_t need = fp4_packed_operand_bytes(rows, cols);
+    if (need == 0) return FP4_E_SHAPE;
+    if (packed_bytes < (size_t)need) return FP4_E_WORKSPACE;
+    if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(status, 4)) return FP4_E_ALIGN;
+    return from_hip(fp4dev::launch_mx_quantize_packed(x, xt == FP4_BF16, rows, cols, packed, status,
+                                                      (hipStream_t)stream));
+}
+
+fp4_status fp4_linear_mxfp4_packed(const void *x, fp4_dtype xt, int64_t M, int64_t K,
+                                   const uint8_t *bt_packed, int64_t N, uint8_t *a_packed,
+                                   size_t a_packed_bytes, void *c, fp4_dtype ct, int32_t *status,
+                                   void *stream) {
+    if (!x || !bt_packed || !a_packed || !c) return FP4_E_ARG;
+    if (!valid_dtype(xt) || !valid_dtype(ct)) return FP4_E_DTYPE;
+    if (M < 1 || N < 1 || K < 2048 || K % 2048 != 0 || K > 16384) return FP4_E_SHAPE;
+    if (M > INT32_MAX / 2 || N > INT32_MAX / 2) return FP4_E_SHAPE;
+    if (fp4_packed_operand_bytes(M, K) > (1 << 30) || fp4_packed_operand_bytes(N, K) > (1 << 30))
+        return FP4_E_SHAPE;
+    if (a_packed_bytes < (size_t)fp4_packed_operand_bytes(M, K)) return FP4_E_WORKSPACE;
+    if (!aligned(x, 16) || !aligned(bt_packed, 16) || !aligned(a_packed, 16) || !aligned(c, 4) ||
+        !aligned(status, 4))
+        return FP4_E_ALIGN;
+    hipError_t e = fp4dev::launch_mx_quantize_packed(x, xt == FP4_BF16, M, K, a_packed, status,
+                                                     (hipStream_t)stream);
+    if (e != hipSuccess) return from_hip(e);
+    return from_hip(fp4dev::launch_gemm_mxfp4_packed(a_packed, bt_packed, M, N, K, c,
+                                                     ct == FP4_BF16, (hipStream_t)stream));
+}
+
 size_t fp4_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (M < 1 || N < 1 || M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return 0;
     const int S = fp4dev::gemm_splitk_parts(M, N, K);

@@ -65,6 +65,9 @@ hipError_t launch_pack_mxfp4(const uint8_t *codes, const uint8_t *scales, int64_
                              uint8_t *packed, hipStream_t s);
 hipError_t launch_gemm_mxfp4_packed(const uint8_t *a_packed, const uint8_t *bt_packed, int64_t M,
                                     int64_t N, int64_t K, void *c, bool out_bf16, hipStream_t s);
+// MXFP4 quantize (floor rule) of x [rows, cols] written in the packed layout.
+hipError_t launch_mx_quantize_packed(const void *x, bool bf16, int64_t rows, int64_t cols,
+                                     uint8_t *packed, int32_t *status, hipStream_t s);
 // Split-K MXFP4 GEMM: S equal K ranges (gemm_splitk_parts; 0 when the shape
 // is not supported), fp32 partials in workspace [S][M][N], then a reduction
 // in increasing split order.

@@ -180,6 +180,61 @@ __global__ __launch_bounds__(WG) void mx_quantize_kernel(const uint4 *__restrict
 }
 
 // ---------------------------------------------------------------------------
+// MXFP4 quantize (OCP floor rule) written in MFMA operand order (the packed
+// operand layout of the packed GEMM).  One wave per 1 KB code tile (row
+// tile rt, K step ks): lane l quantizes block 2 ks + l / 32 of row
+// 32 rt + l % 32 (32 values, its own amax) and stores its 16 code bytes at
+// byte 16 l of the tile, so a wave writes one contiguous kilobyte; the
+// scale byte goes to byte 8 l + ks % 8 of the tile's scale group ks / 8.
+// Rows past the tensor read as zeros, whose blocks encode as the layout's
+// padding (codes 0, scale byte 127).
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(WG) void mx_quantize_packed_kernel(const uint4 *__restrict__ x,
+                                                                int64_t rows, int64_t K,
+                                                                int64_t ntiles,
+                                                                uint4 *__restrict__ codes,
+                                                                uint8_t *__restrict__ scales,
+                                                                int32_t *status) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int64_t wave = (int64_t)blockIdx.x * WAVES_PER_WG + (threadIdx.x / WAVE);
+    const int64_t nwaves = (int64_t)gridDim.x * WAVES_PER_WG;
+    const int64_t nks = K / 64;
+    uint32_t flags = 0;
+    for (int64_t t = wave; t < ntiles; t += nwaves) {
+        const int64_t rt = t / nks, ks = t % nks;
+        const int64_t row = rt * 32 + (lane & 31);
+        const bool ok = row < rows;
+        // chunk index (8 values) of the block's first chunk
+        const int64_t c0 = (row * K + (2 * ks + (lane >> 5)) * 32) / 8;
+        Chunk<BF16> k[4];
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            k[i] = load_chunk<BF16>(x, c0 + i, ok);
+            m = max(m, chunk_amax<BF16>(k[i]));
+        }
+        const int sh = BF16 ? 7 : 23;
+        if ((m >> sh) >= 0xFFu) flags |= FLAG_NONFINITE;
+        const uint32_t sb = mx_scale_byte(m, sh);
+        uint32_t q[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (BF16) {
+                q[i] = cvt_fp4x8_bf16(k[i].lo, e8m0_operand(sb));
+            } else {
+                float v[8];
+                chunk_values<BF16>(k[i], v);
+                q[i] = cvt_fp4x8_f32(v, e8m0_operand(sb));
+            }
+        }
+        codes[t * 64 + lane] = make_uint4(q[0], q[1], q[2], q[3]);
+        scales[((rt * (nks / 8) + ks / 8) * 64 + lane) * 8 + ks % 8] = (uint8_t)sb;
+    }
+    report_flags(status, flags);
+}
+
+// ---------------------------------------------------------------------------
 // Stochastic element rounding (Ultralytics glossary "FP4", section
 // "Inferenza e addestramento FP4": NVFP4 pretraining rounds gradients
 // stochastically; the pages give no rule).  The quotient q is the
@@ -1202,6 +1257,18 @@ hipError_t launch_mx_quantize(const void *x, bool bf16, int64_t n, int rule, uin
         {mx_quantize_kernel<true, 0>, mx_quantize_kernel<true, 1>, mx_quantize_kernel<true, 2>}};
     hipLaunchKernelGGL(kernels[bf16 ? 1 : 0][rule], dim3(g), dim3(WG), 0, s, (const uint4 *)x,
                        nchunks, (uint32_t *)codes, scales, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_quantize_packed(const void *x, bool bf16, int64_t rows, int64_t cols,
+                                     uint8_t *packed, int32_t *status, hipStream_t s) {
+    const int64_t nrt = (rows + 31) / 32, ntiles = nrt * (cols / 64);
+    int64_t g = (ntiles + WAVES_PER_WG - 1) / WAVES_PER_WG;
+    if (g > kMaxGrid) g = kMaxGrid;
+    uint8_t *scales = packed + nrt * 32 * (cols / 2);
+    auto k = bf16 ? mx_quantize_packed_kernel<true> : mx_quantize_packed_kernel<false>;
+    hipLaunchKernelGGL(k, dim3((unsigned)g), dim3(WG), 0, s, (const uint4 *)x, rows, cols, ntiles,
+                       (uint4 *)packed, scales, status);
     return hipGetLastError();
 }
 

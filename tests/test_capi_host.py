@@ -293,3 +293,29 @@ def test_packed_sizes_and_validation():
     assert g(N=1 << 20, K=16384) == E_SHAPE   # packed Bt above 1 GiB
     assert g(a=A1) == E_ALIGN
     assert g(c=ctypes.c_void_p(0x10002)) == E_ALIGN
+
+
+def test_packed_quantize_and_linear_validation():
+    L = fp4.lib()
+
+    def q(x=A16, rows=64, cols=1024, out=A16, nb=1 << 20, xt=fp4.BF16, st=NULL):
+        return L.fp4_quantize_mxfp4_packed(x, xt, rows, cols, out, nb, st, NULL)
+    assert q(x=NULL) == E_ARG
+    assert q(out=NULL) == E_ARG
+    assert q(xt=9) == E_DTYPE
+    assert q(cols=1056) == E_SHAPE                   # not a multiple of 512
+    assert q(rows=0) == E_SHAPE
+    assert q(nb=fp4.packed_operand_bytes(64, 1024) - 1) == E_WORKSPACE
+    assert q(x=A1) == E_ALIGN
+    assert q(out=ctypes.c_void_p(0x10008)) == E_ALIGN
+    assert q(st=ctypes.c_void_p(0x10002)) == E_ALIGN
+
+    def lin(x=A16, M=128, K=2048, bt=A16, N=256, a=A16, nb=1 << 20, c=A16, ct=fp4.BF16):
+        return L.fp4_linear_mxfp4_packed(x, fp4.F32, M, K, bt, N, a, nb, c, ct, NULL, NULL)
+    assert lin(bt=NULL) == E_ARG
+    assert lin(a=NULL) == E_ARG
+    assert lin(ct=4) == E_DTYPE
+    assert lin(K=1024) == E_SHAPE
+    assert lin(K=20480) == E_SHAPE
+    assert lin(nb=fp4.packed_operand_bytes(128, 2048) - 1) == E_WORKSPACE
+    assert lin(a=ctypes.c_void_p(0x10008)) == E_ALIGN

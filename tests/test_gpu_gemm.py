@@ -352,3 +352,49 @@ def test_gemm_packed_integer_valued_is_exact_and_deterministic():
     ref = og.gemm_f64(ap, asc, bp, bsc, M, N, K)
     assert np.array_equal(c1.cpu().numpy().astype(np.float64), ref)
     assert torch.equal(c1, c2)
+
+
+# ---- quantize straight into the packed layout, and the packed W4A4 linear ------
+
+@pytest.mark.parametrize("rows,cols,dt", [(1, 512, torch.float32), (70, 2048, torch.bfloat16),
+                                          (128, 8192, torch.bfloat16), (33, 1536, torch.float32)])
+def test_quantize_mxfp4_packed_matches_oracle(rows, cols, dt):
+    g = torch.Generator().manual_seed(rows + cols)
+    x = (torch.randn(rows, cols, generator=g) * torch.rand(rows, cols, generator=g) ** 3).to(dt)
+    announce(f"quantize mxfp4 packed {rows}x{cols} {dt}")
+    got = fp4.quantize_mxfp4_packed(dev(x))
+    torch.cuda.synchronize()
+    p, s, flags = oracle.mx_quantize(oracle_view(x))
+    assert flags == 0
+    assert_bytes_equal(host_u8(got), og.pack_operand(p, s, rows, cols), f"packed quantize {rows}x{cols}")
+
+
+def test_quantize_mxfp4_packed_flags_nonfinite():
+    x = torch.zeros(32, 512)
+    x[3, 100] = float("inf")
+    announce("quantize mxfp4 packed non-finite")
+    with pytest.raises(ValueError):
+        fp4.quantize_mxfp4_packed(dev(x))
+
+
+@pytest.mark.parametrize("M,N,K,dt", [(128, 8192, 8192, torch.bfloat16), (70, 100, 2048, torch.float32),
+                                      (200, 96, 4096, torch.bfloat16)])
+def test_linear_packed_matches_oracle(M, N, K, dt):
+    a, bt = workloads.gemm_operands(M, N, K, seed_a=2, seed_b=3)
+    x = a.to(dt)
+    bp, bsc, f2 = oracle.mx_quantize(bt.numpy())
+    ap, asc, f1 = oracle.mx_quantize(oracle_view(x))
+    assert f1 == 0 and f2 == 0
+    bt_packed = dev(torch.from_numpy(og.pack_operand(bp, bsc, N, K)))
+    announce(f"linear mxfp4 packed {M}x{N}x{K} {dt}")
+    c32, a_packed = fp4.linear_mxfp4_packed(dev(x), bt_packed, N, torch.float32)
+    c16, _ = fp4.linear_mxfp4_packed(dev(x), bt_packed, N, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert_bytes_equal(host_u8(a_packed), og.pack_operand(ap, asc, M, K), f"linear {M}x{N}x{K}: packed A")
+    ref = og.gemm_f64(ap, asc, bp, bsc, M, N, K)
+    err = np.linalg.norm(c32.cpu().numpy().astype(np.float64) - ref) / np.linalg.norm(ref)
+    assert err <= REL_FROB, f"linear packed {M}x{N}x{K}: relative Frobenius error {err:.3e}"
+    assert torch.equal(c16.cpu().view(torch.int16), c32.cpu().to(torch.bfloat16).view(torch.int16))
+    # the same bits as the packed GEMM on the same packed operands
+    c2 = fp4.gemm_mxfp4_packed(a_packed, bt_packed, M, N, K, torch.float32)
+    assert torch.equal(c2, c32)

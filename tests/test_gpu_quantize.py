@@ -218,6 +218,13 @@ def test_nv_bf16_beyond_on_chip_capacity_takes_two_passes():
     check_nv(x, "weight 10240x8192 bf16")
 
 
+def test_nv_bf16_largest_one_pass_with_ragged_tail():
+    # just below the on-chip capacity: 64 chunks per lane, the last grid step
+    # partly outside the tensor (clamped loads, predicated stores)
+    for i, (r, c) in enumerate([(8191, 8192), (8192, 8176)]):
+        check_nv(workloads.nvfp4_weight(r, c, seed=40 + i), f"weight {r}x{c} bf16")
+
+
 def test_nv_workspace_reused_across_sizes_and_graph_replays():
     # the barrier epoch lives in the workspace: reuse it across calls of
     # different grid sizes (stale slots from larger grids must never match)
