@@ -142,3 +142,18 @@ def test_exhaustive_search_full_size_sampled():
     sample = np.unique(np.concatenate([np.arange(0, 896), rng.integers(0, nblocks, 4000),
                                        np.arange(nblocks - 896, nblocks)]))
     check_search_all(x, "laplace 4096x14336 (sampled blocks)", sample=sample)
+
+
+def test_search_exact_loss_ties_go_to_the_smaller_code():
+    """Blocks [A, 0 x 15] for every bf16 A in [4, 16) behind a 2688 block
+    (s_g = 1): the clipped and the unclipped neighbour codes often give
+    bit-equal losses (two- and three-way ties), and the smaller code must
+    win, as in the oracle's increasing-order search; the kernel walks codes
+    downward with an early stop."""
+    A = (np.arange(0x4080, 0x4180, dtype=np.uint32) << 16).view(np.float32)
+    blocks = np.zeros((A.size, 16), np.float32)
+    blocks[:, 0] = A
+    x = torch.from_numpy(np.concatenate([np.full(16, 2688.0, np.float32), blocks.reshape(-1)]))
+    x = x.reshape(1, -1).to(torch.bfloat16)
+    _search_check(x, "exact loss ties, c in [0.5, 1]")
+    _search_check(x, "exact loss ties, c in [0.5, 1.5]", c_hi=1.5)
