@@ -212,6 +212,17 @@ class RoundTrip:
         self.op("mxfp4_dequantize", 1)()
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(x_cpu: torch.Tensor, step_bytes: int):
     """The oracle (plain C) on one full step of the same input, its rows split
     over the host's threads (at most 16); the C calls release the GIL.  The
@@ -248,7 +259,7 @@ def cpu_baseline(x_cpu: torch.Tensor, step_bytes: int):
             if dt * len(parts) >= 10.0 or steps >= 8:
                 break
     return {"value": round(steps * step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": len(parts),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": _cpu_model(),
             "sample": f"{steps} full step(s) (NVFP4 + MXFP4 quantize and dequantize) of the "
                       f"{x_cpu.shape[0]}x{x_cpu.shape[1]} bf16 input, rows split over "
                       f"{len(parts)} threads; {dt:.2f} s wall"}
