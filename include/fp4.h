@@ -3,9 +3,11 @@
  *
  * C ABI of libfp4.so.  Every tensor argument is a DEVICE pointer into memory
  * the caller owns (allocates and frees); the library allocates nothing.  Its
- * only global state is two per-device records, each filled once: whether the
- * one-pass NVFP4 kernel fits (CU count and occupancy), and how many
- * workgroups of the one-launch W4A4 linear kernel the device holds at once.
+ * global state is two per-device records, each filled once (whether the
+ * one-pass NVFP4 kernel fits, from the CU count and occupancy, and how many
+ * workgroups of the one-launch W4A4 linear kernel the device holds at once),
+ * and the grid barrier's poll limit, a process-wide setting that only
+ * fp4_debug_barrier_spin_limit changes.
  * Calls on different streams may run concurrently unless they share a
  * workspace.  All work is
  * enqueued asynchronously on `stream` (a hipStream_t passed as void*; NULL is
@@ -31,7 +33,9 @@
  *   codes  [rows, cols/2]      uint8, two codes per byte (even element low)
  *   scales [rows, cols/block]  uint8, one scale byte per block, row-major
  * Because every row holds whole blocks, the flat order of elements, codes and
- * scales is the row-major order; the library treats the tensor as flat.
+ * scales is the row-major order; the library treats the tensor as flat.  The
+ * *_packed entry points use the MFMA operand order instead, described at
+ * fp4_pack_mxfp4_operand.
  *
  * Errors.  Argument errors are returned synchronously, before any HIP call
  * (so they are testable without a GPU).  Data-dependent conditions are found
