@@ -114,3 +114,34 @@ def test_sweep(i):
     if f == 0:
         assert_bytes_equal(host_u8(scales), s, f"{what}: NV SR scales")
         assert_bytes_equal(host_u8(codes), p, f"{what}: NV SR codes")
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_sweep_padded(i):
+    """The row-padded layout on generated shapes whose rows are not whole
+    blocks (any column count), both formats, with the cropping decode."""
+    rng = np.random.default_rng(3000 + i)
+    rows, cols = int(rng.integers(1, 120)), int(rng.integers(1, 3000))
+    g = torch.Generator().manual_seed(4000 + i)
+    x = torch.randn(rows, cols, generator=g) / torch.sqrt(torch.rand(rows, cols, generator=g) + 1e-3)
+    x = x.to(torch.bfloat16 if i % 2 else torch.float32)
+    what = f"padded case {i}: {rows}x{cols} {x.dtype}"
+    xo = oracle_view(x)
+    for fmt in (fp4.MXFP4, fp4.NVFP4):
+        announce(f"{what} fmt={fmt}")
+        codes, scales, s_g = fp4.quantize_padded(fmt, dev(x))
+        if fmt == fp4.MXFP4:
+            p, s, f = oracle.mx_quantize_padded(xo, rows, cols)
+            sg = 1.0
+        else:
+            p, s, sg, f = oracle.nv_quantize_padded(xo, rows, cols)
+            assert f32_bits(s_g.cpu().numpy())[0] == f32_bits([sg])[0], f"{what}: s_g"
+        assert f == 0
+        assert_bytes_equal(host_u8(scales), s, f"{what}: padded scales fmt={fmt}")
+        assert_bytes_equal(host_u8(codes), p, f"{what}: padded codes fmt={fmt}")
+        for out_dtype, bf in ((torch.float32, False), (torch.bfloat16, True)):
+            y = fp4.dequantize_padded(fmt, codes, scales, cols,
+                                      s_g if fmt == fp4.NVFP4 else None, out_dtype)
+            want = oracle.dequantize_padded(fmt, p, s, rows, cols, sg, out_bf16=bf)
+            got = workloads.bf16_bits(y.cpu()).reshape(-1) if bf else y.cpu().numpy().reshape(-1)
+            assert_float_bits_equal(got, want, f"{what}: padded decode fmt={fmt} -> {out_dtype}")
