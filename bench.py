@@ -108,6 +108,25 @@ def measured_traffic():
     return None
 
 
+VALU_PROFILE = os.path.join(ROOT, "profiles", "valu_issue_arithmetic_kernels.md")
+
+
+def measured_valu_issue():
+    """VALU issue of the arithmetic-bound kernels (percent of one wave64
+    instruction per SIMD every two cycles at 2.4 GHz), by extra-workload
+    name, from the committed SQ-counter profile; None if the kernels changed."""
+    try:
+        with open(VALU_PROFILE) as f:
+            for line in f:
+                if line.startswith("valu_record:"):
+                    rec = json.loads(line.split(":", 1)[1])
+                    if rec.get("source_sha256_16") == kernel_source_hash():
+                        return rec["pct_of_peak"]
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
+
+
 # ---------------------------------------------------------------------------
 # timing helpers
 # ---------------------------------------------------------------------------
@@ -431,6 +450,12 @@ def extra_workloads():
     out["nvfp4_gemm_128x8192x8192_bf16out"] = d
     if int(st.item()) != 0:
         raise RuntimeError(f"a timed call raised status flags {int(st.item())}")
+    # arithmetic-bound workloads: their profiled VALU issue (SQ counters)
+    valu = measured_valu_issue()
+    if valu:
+        for k, pct in valu.items():
+            if k in out:
+                out[k]["valu_issue_pct_of_peak_profiled"] = pct
     return out
 
 
