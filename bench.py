@@ -448,6 +448,19 @@ def extra_workloads():
     d.update({"TFLOP/s": round(tf, 1),
               "pct_fp16_mfma_peak": round(100 * tf / FP16_DENSE_PEAK_TFLOPS, 2)})
     out["nvfp4_gemm_128x8192x8192_bf16out"] = d
+    # the same product on packed NVFP4 operands (each B packed once)
+    bnp = [fp4.pack_nvfp4_operand(b[0], b[1]) for b in bn]
+    anp = fp4.pack_nvfp4_operand(an[0], an[1])
+    ms = time_rotating([lambda b=b, bb=bb: fp4.gemm_nvfp4_packed(anp, an[2], bb, b[2], M, N, K, out=c)
+                        for b, bb in zip(bn, bnp)])
+    d = _rate(nv_bytes, ms)
+    tf = gemm_flops(M, N, K) / ms / 1e9
+    d.update({"TFLOP/s": round(tf, 1),
+              "pct_fp16_mfma_peak": round(100 * tf / FP16_DENSE_PEAK_TFLOPS, 2)})
+    ms2 = time_rotating([lambda: fp4.pack_nvfp4_operand(an[0], an[1], out=anp)])
+    d["pack_a_us"] = round(ms2 * 1e3, 2)
+    out["nvfp4_gemm_packed_128x8192x8192_bf16out"] = d
+    del bnp
     if int(st.item()) != 0:
         raise RuntimeError(f"a timed call raised status flags {int(st.item())}")
     # arithmetic-bound workloads: their profiled VALU issue (SQ counters)

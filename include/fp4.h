@@ -346,6 +346,46 @@ fp4_status fp4_gemm_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales,
                           int64_t N, int64_t K, void *c, fp4_dtype ct, void *stream);
 
 /*
+ * MFMA operand order for NVFP4 operands (the physical layout is the
+ * implementation's choice, "NVFP4 / MXFP4 format" page, section 7).  An
+ * NVFP4 matrix X with rows rows and K values per row (codes [rows, K/2],
+ * E4M3 scales [rows, K/16]) becomes one buffer:
+ *   codes exactly as in fp4_pack_mxfp4_operand (1024 bytes per row tile of
+ *   32 rows and K step of 64 values; bytes 16 l .. 16 l + 15 hold row
+ *   32 rt + l % 32, values 32 (2 ks + l / 32) .. + 31);
+ *   then scales, for each row tile and each group q of eight K steps, 1024
+ *   bytes: byte 16 l + 2 i + b is the E4M3 byte of row 32 rt + l % 32 and
+ *   16-element block 4 (8 q + i) + 2 (l / 32) + b (0 on padding rows).
+ * fp4_nv_packed_operand_bytes(rows, K) is its size: 32 ceil(rows / 32)
+ * (K/2 + K/16) bytes, or 0 unless rows >= 1 and K is a positive multiple
+ * of 512.  The tensor scale is not part of the buffer.
+ *   codes, scales  the row-major operand (device); codes 16-byte aligned
+ *   packed         device output of at least that many bytes, 16-byte aligned
+ * Errors: FP4_E_SHAPE (size 0), FP4_E_WORKSPACE (packed_bytes too small),
+ * FP4_E_ALIGN.  Packing moves bytes only (bit-exact).
+ */
+int64_t fp4_nv_packed_operand_bytes(int64_t rows, int64_t K);
+fp4_status fp4_pack_nvfp4_operand(const uint8_t *codes, const uint8_t *scales, int64_t rows,
+                                  int64_t K, uint8_t *packed, size_t packed_bytes, void *stream);
+
+/*
+ * The NVFP4 x NVFP4 GEMM of fp4_gemm_nvfp4 (same operation and sources) on
+ * packed operands: a_packed = A [M, K] and bt_packed = Bt [N, K], each made
+ * by fp4_pack_nvfp4_operand, with their tensor scales a_global_scale and
+ * bt_global_scale (device floats, 4-byte aligned).  K must be a multiple of
+ * 2048, at most 16384; each packed operand at most 1 GiB; operands 16-byte
+ * aligned, c 4-byte aligned (FP4_E_SHAPE / FP4_E_ALIGN otherwise).  Products
+ * of FP4 values and block scales are exact, sums fp32; a workgroup's four
+ * waves take the four quarters of K for a 128 x 32 tile of C and add their
+ * partial tiles in a fixed order, then c = RN(acc * RN32(a_X a_W)).
+ * Deterministic; the summation order differs from fp4_gemm_nvfp4's.
+ */
+fp4_status fp4_gemm_nvfp4_packed(const uint8_t *a_packed, const float *a_global_scale,
+                                 const uint8_t *bt_packed, const float *bt_global_scale,
+                                 int64_t M, int64_t N, int64_t K, void *c, fp4_dtype ct,
+                                 void *stream);
+
+/*
  * W4A4 linear layer: the activations quantized to MXFP4, then the MXFP4 GEMM
  * ("FP4, FP8 and INT8/INT4" page, tom-jerr.github.io, section 5: the cost of
  * a low-bit linear layer is the activation quantize plus the block-scaled

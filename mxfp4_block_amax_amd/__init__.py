@@ -47,6 +47,7 @@ EXPORTS = ("fp4_quantize_mxfp4", "fp4_quantize_mxfp4_rule", "fp4_quantize_nvfp4"
            "fp4_dequantize_padded", "fp4_padded_storage_bytes", "fp4_quantize_sr",
            "fp4_debug_barrier_spin_limit", "fp4_packed_operand_bytes", "fp4_pack_mxfp4_operand",
            "fp4_gemm_mxfp4_packed", "fp4_quantize_mxfp4_packed", "fp4_linear_mxfp4_packed",
+           "fp4_nv_packed_operand_bytes", "fp4_pack_nvfp4_operand", "fp4_gemm_nvfp4_packed",
            "fp4_workspace_bytes", "fp4_status_str")
 
 # fp4_mx_rule: the MXFP4 block-exponent rules
@@ -91,6 +92,10 @@ def lib() -> ctypes.CDLL:
     L.fp4_packed_operand_bytes.restype = I64
     L.fp4_pack_mxfp4_operand.argtypes = [P, P, I64, I64, P, S, P]
     L.fp4_gemm_mxfp4_packed.argtypes = [P, P, I64, I64, I64, P, I, P]
+    L.fp4_nv_packed_operand_bytes.argtypes = [I64, I64]
+    L.fp4_nv_packed_operand_bytes.restype = I64
+    L.fp4_pack_nvfp4_operand.argtypes = [P, P, I64, I64, P, S, P]
+    L.fp4_gemm_nvfp4_packed.argtypes = [P, P, P, P, I64, I64, I64, P, I, P]
     L.fp4_quantize_mxfp4_packed.argtypes = [P, I, I64, I64, P, S, P, P]
     L.fp4_linear_mxfp4_packed.argtypes = [P, I, I64, I64, P, I64, P, S, P, I, P, P]
     L.fp4_debug_barrier_spin_limit.argtypes = [ctypes.c_uint32]
@@ -425,6 +430,38 @@ def gemm_nvfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, a_global_scale: to
     _ok(lib().fp4_gemm_nvfp4(_ptr(a_codes), _ptr(a_scales), _ptr(a_global_scale), _ptr(bt_codes),
                              _ptr(bt_scales), _ptr(bt_global_scale), M, N, K, _ptr(c),
                              _dtype_code(c.dtype), _stream(a_codes)))
+    return c
+
+
+def nv_packed_operand_bytes(rows: int, K: int) -> int:
+    return int(lib().fp4_nv_packed_operand_bytes(int(rows), int(K)))
+
+
+def pack_nvfp4_operand(codes: torch.Tensor, scales: torch.Tensor, out=None) -> torch.Tensor:
+    """An NVFP4 operand [rows, K] (codes [rows, K/2], E4M3 scales [rows, K/16])
+    in MFMA operand order, one uint8 buffer, for gemm_nvfp4_packed."""
+    rows, kh = _rows_cols(codes)
+    n = nv_packed_operand_bytes(rows, 2 * kh)
+    if n == 0:
+        raise ValueError("packing needs K a positive multiple of 512")
+    packed = out if out is not None else torch.empty(n, dtype=torch.uint8, device=codes.device)
+    _ok(lib().fp4_pack_nvfp4_operand(_ptr(codes), _ptr(scales), rows, 2 * kh, _ptr(packed),
+                                     packed.numel(), _stream(codes)))
+    return packed
+
+
+def gemm_nvfp4_packed(a_packed: torch.Tensor, a_global_scale: torch.Tensor,
+                      bt_packed: torch.Tensor, bt_global_scale: torch.Tensor, M: int, N: int,
+                      K: int, out_dtype=torch.bfloat16, out=None):
+    """C [M, N] = A @ B from packed NVFP4 A [M, K] and Bt [N, K] with their
+    tensor scales."""
+    if (a_packed.numel() < nv_packed_operand_bytes(M, K)
+            or bt_packed.numel() < nv_packed_operand_bytes(N, K)):
+        raise ValueError("packed operand smaller than its shape")
+    c = out if out is not None else torch.empty(M, N, dtype=out_dtype, device=a_packed.device)
+    _ok(lib().fp4_gemm_nvfp4_packed(_ptr(a_packed), _ptr(a_global_scale), _ptr(bt_packed),
+                                    _ptr(bt_global_scale), int(M), int(N), int(K), _ptr(c),
+                                    _dtype_code(c.dtype), _stream(a_packed)))
     return c
 
 

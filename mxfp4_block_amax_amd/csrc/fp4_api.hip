@@ -196,6 +196,40 @@ fp4_status fp4_gemm_mxfp4_packed(const uint8_t *a_packed, const uint8_t *bt_pack
                                                      ct == FP4_BF16, (hipStream_t)stream));
 }
 
+int64_t fp4_nv_packed_operand_bytes(int64_t rows, int64_t K) {
+    if (rows > INT32_MAX / 2 || K > INT32_MAX / 2) return 0;
+    return fp4dev::nv_packed_operand_bytes(rows, K);
+}
+
+fp4_status fp4_pack_nvfp4_operand(const uint8_t *codes, const uint8_t *scales, int64_t rows,
+                                  int64_t K, uint8_t *packed, size_t packed_bytes, void *stream) {
+    if (!codes || !scales || !packed) return FP4_E_ARG;
+    const int64_t need = fp4_nv_packed_operand_bytes(rows, K);
+    if (need == 0) return FP4_E_SHAPE;
+    if (packed_bytes < (size_t)need) return FP4_E_WORKSPACE;
+    if (!aligned(codes, 16) || !aligned(packed, 16)) return FP4_E_ALIGN;
+    return from_hip(fp4dev::launch_pack_nvfp4(codes, scales, rows, K, packed, (hipStream_t)stream));
+}
+
+fp4_status fp4_gemm_nvfp4_packed(const uint8_t *a_packed, const float *a_global_scale,
+                                 const uint8_t *bt_packed, const float *bt_global_scale,
+                                 int64_t M, int64_t N, int64_t K, void *c, fp4_dtype ct,
+                                 void *stream) {
+    if (!a_packed || !a_global_scale || !bt_packed || !bt_global_scale || !c) return FP4_E_ARG;
+    if (!valid_dtype(ct)) return FP4_E_DTYPE;
+    if (M < 1 || N < 1 || K < 2048 || K % 2048 != 0 || K > 16384) return FP4_E_SHAPE;
+    if (M > INT32_MAX / 2 || N > INT32_MAX / 2) return FP4_E_SHAPE;
+    if (fp4_nv_packed_operand_bytes(M, K) > (1 << 30) ||
+        fp4_nv_packed_operand_bytes(N, K) > (1 << 30))
+        return FP4_E_SHAPE;
+    if (!aligned(a_packed, 16) || !aligned(bt_packed, 16) || !aligned(c, 4) ||
+        !aligned(a_global_scale, 4) || !aligned(bt_global_scale, 4))
+        return FP4_E_ALIGN;
+    return from_hip(fp4dev::launch_gemm_nvfp4_packed(a_packed, a_global_scale, bt_packed,
+                                                     bt_global_scale, M, N, K, c, ct == FP4_BF16,
+                                                     (hipStream_t)stream));
+}
+
 fp4_status fp4_quantize_mxfp4_packed(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
                                      uint8_t *packed, size_t packed_bytes, int32_t *status,
                                      void *stream) {

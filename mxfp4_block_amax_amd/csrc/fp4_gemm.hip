@@ -825,6 +825,148 @@ __device__ __forceinline__ half8_t nv_operand(uint32_t w, half2_t s2, bool hi) {
     return r;
 }
 
+// ---------------------------------------------------------------------------
+// NVFP4 operands in fp16-MFMA operand order ("packed" NVFP4 layout).  Codes as
+// in the MXFP4 packed layout: per 32-row tile and 64-value K step, 1 KB in
+// which lane l holds the 32 codes of row l % 32 in the step's K half l / 32.
+// Scales after all codes: per tile and group q of eight K steps, 1 KB in which
+// byte 2 i + b of lane l is the E4M3 scale of its row and 16-block
+// 4 (8 q + i) + 2 (l / 32) + b (padding rows: 0).  The fp16 MFMA's 16 K slots
+// may take any K values as long as A and B agree: in sub-step u of a step,
+// lane half h feeds K values 32 h + 8 u .. + 8, which lie in one 16-block.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pack_nv_scales_kernel(const uint8_t *__restrict__ scales,
+                                                             int64_t rows, int64_t nks,
+                                                             int64_t total,
+                                                             uint4 *__restrict__ out) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t nkq = nks / 8;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
+        const int l = (int)(t & 63);
+        const int64_t g = t >> 6, q = g % nkq, rt = g / nkq;
+        const int64_t r = rt * 32 + (l & 31);
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        if (r < rows) {
+            const uint8_t *s = scales + r * (nks * 4) + 32 * q + 2 * (l >> 5);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                w[i / 2] |= ((uint32_t)s[4 * i] | ((uint32_t)s[4 * i + 1] << 8)) << (16 * (i & 1));
+        }
+        out[t] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+constexpr int NVPK_RING = 8;  // K steps in flight per wave
+
+// The NVFP4 GEMM on packed operands: a workgroup owns a 128 x 32 tile of C,
+// its four waves take the four quarters of the K steps (SW each, unrolled,
+// step st's loads in ring slot st % 6, issued six steps ahead); each wave
+// decodes its own operands once (FP4 -> fp16 times the E4M3 scale, exact),
+// 16 fp16 MFMAs per step; the partial tiles are added through LDS in a fixed
+// order and C = RN32(sum * RN32(s_gA s_gB)).
+template <bool OUT_BF16, int SW>
+__global__ __launch_bounds__(GEMM_WG) void nvfp4_gemm_packed_kernel(
+    const uint4 *__restrict__ Ap, const uint4 *__restrict__ Asp, const float *__restrict__ sgA,
+    const uint4 *__restrict__ Bp, const uint4 *__restrict__ Bsp, const float *__restrict__ sgB,
+    int M, int N, void *__restrict__ C) {
+    constexpr int R = NVPK_RING;
+    constexpr int NQ = SW / 8;
+    constexpr int nks = 4 * SW, nkq = nks / 8;
+    __shared__ float part[4][4][16][64];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r32 = lane & 31;
+    const int kh = lane >> 5;
+    const int s0 = w * SW;
+    const int nrt_a = (M + 31) / 32, nrt_b = (N + 31) / 32;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void *)Ap, (short)0, nrt_a * nks * 1024, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)Bp, (short)0, nrt_b * nks * 1024, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void *)Asp, (short)0, nrt_a * nkq * 1024, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void *)Bsp, (short)0, nrt_b * nkq * 1024, kBufferRsrcWord3);
+    const int vo = lane * 16;
+    int oa[4], osa[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        const int rt = min((int)blockIdx.y * 4 + mi, nrt_a - 1);
+        oa[mi] = (rt * nks + s0) * 1024;
+        osa[mi] = (rt * nkq + s0 / 8) * 1024;
+    }
+    const int ob = ((int)blockIdx.x * nks + s0) * 1024;
+    const int osb = ((int)blockIdx.x * nkq + s0 / 8) * 1024;
+    auto ld = [&](__amdgpu_buffer_rsrc_t r, int off) {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, vo, off, 0);
+        return make_uint4(v.x, v.y, v.z, v.w);
+    };
+    // scales, one 16-byte load per operand per eight steps, double-buffered:
+    // group q + 1 is requested when group q starts
+    uint4 sca[2][4], scb[2];
+    auto issue_scales = [&](int q) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) sca[q & 1][mi] = ld(rsa, osa[mi] + q * 1024);
+        scb[q & 1] = ld(rsb, osb + q * 1024);
+    };
+    uint4 ga[R][4], gb[R];
+    auto issue = [&](int slot, int st) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) ga[slot][mi] = ld(ra, oa[mi] + st * 1024);
+        gb[slot] = ld(rb, ob + st * 1024);
+    };
+    issue_scales(0);
+#pragma unroll
+    for (int i = 0; i < R; ++i) issue(i, i);
+    auto word = [](uint4 v, int j) { return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w; };
+    // E4M3 bytes 2 (i % 2), 2 (i % 2) + 1 of a word as an fp16 pair
+    auto scale2 = [](uint32_t v, bool hi) {
+        return hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, true)
+                  : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, false);
+    };
+
+    f32x16_t acc[4] = {};
+#pragma unroll
+    for (int st = 0; st < SW; ++st) {
+        const int slot = st % R, q = st / 8, i = st % 8;
+        if (i == 0 && q + 1 < NQ) issue_scales(q + 1);
+        const half2_t bs2 = scale2(word(scb[q & 1], i / 2), (i & 1) != 0);
+        half2_t as2[4];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) as2[mi] = scale2(word(sca[q & 1][mi], i / 2), (i & 1) != 0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const half8_t bo = nv_operand(word(gb[slot], u), bs2, u >= 2);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+                acc[mi] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                    nv_operand(word(ga[slot][mi], u), as2[mi], u >= 2), bo, acc[mi], 0, 0, 0);
+        }
+        if (st + R < SW) issue(slot, st + R);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) part[w][mi][j][lane] = acc[mi][j];
+    __syncthreads();
+    const int mi = w;
+    const float g = sgA[0] * sgB[0];
+    const int col = blockIdx.x * GEMM_TN + r32;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        float v = part[0][mi][j][lane];
+        v = v + part[1][mi][j][lane];
+        v = v + part[2][mi][j][lane];
+        v = v + part[3][mi][j][lane];
+        v = v * g;
+        const int row = blockIdx.y * GEMM_TM + 32 * mi + 8 * (j / 4) + 4 * kh + (j % 4);
+        if (row < M && col < N) {
+            if (OUT_BF16)
+                ((uint16_t *)C)[(int64_t)row * N + col] = (uint16_t)bf16_rne_bits(v);
+            else
+                ((float *)C)[(int64_t)row * N + col] = v;
+        }
+    }
+}
+
 template <bool OUT_BF16>
 __global__ __launch_bounds__(GEMM_WG) void nvfp4_gemm_lds_kernel(
     const uint4 *__restrict__ A, const uint8_t *__restrict__ As, const float *__restrict__ sgA,
@@ -1196,6 +1338,56 @@ hipError_t launch_gemm_mxfp4_packed(const uint8_t *a_packed, const uint8_t *bt_p
     if (idx < 0 || idx > 7 || K % 2048 != 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL(kernels[out_bf16 ? 1 : 0][idx], grid, dim3(GEMM_WG), 0, s, ap, asp, bp, bsp,
                        (int)M, (int)N, c);
+    return hipGetLastError();
+}
+
+int64_t nv_packed_operand_bytes(int64_t rows, int64_t K) {
+    if (rows < 1 || K < 512 || K % 512 != 0) return 0;
+    const int64_t padded = (rows + 31) / 32 * 32;
+    return padded * (K / 2) + padded * (K / 16);
+}
+
+hipError_t launch_pack_nvfp4(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t K,
+                             uint8_t *packed, hipStream_t s) {
+    const int64_t nrt = (rows + 31) / 32, nks = K / 64;
+    const int64_t nc = nrt * nks * 64, ns = nrt * (nks / 8) * 64;
+    auto grid = [](int64_t n) {
+        int64_t g = (n + 255) / 256;
+        return (unsigned)(g > kMaxGrid ? kMaxGrid : g);
+    };
+    hipLaunchKernelGGL(pack_codes_kernel, dim3(grid(nc)), dim3(256), 0, s, (const uint4 *)codes,
+                       rows, nks, nc, (uint4 *)packed);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(pack_nv_scales_kernel, dim3(grid(ns)), dim3(256), 0, s, scales, rows, nks,
+                       ns, (uint4 *)(packed + nrt * 32 * (K / 2)));
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_nvfp4_packed(const uint8_t *a_packed, const float *sg_a,
+                                    const uint8_t *bt_packed, const float *sg_b, int64_t M,
+                                    int64_t N, int64_t K, void *c, bool out_bf16, hipStream_t s) {
+    const int64_t nrt_a = (M + 31) / 32, nrt_b = (N + 31) / 32;
+    const uint4 *ap = (const uint4 *)a_packed, *bp = (const uint4 *)bt_packed;
+    const uint4 *asp = (const uint4 *)(a_packed + nrt_a * 32 * (K / 2));
+    const uint4 *bsp = (const uint4 *)(bt_packed + nrt_b * 32 * (K / 2));
+    dim3 grid((unsigned)nrt_b, (unsigned)((M + GEMM_TM - 1) / GEMM_TM));
+    using Kn = void (*)(const uint4 *, const uint4 *, const float *, const uint4 *, const uint4 *,
+                        const float *, int, int, void *);
+    // K steps per wave = K / 256: one instance per multiple of 2048 up to 16384
+    static const Kn kernels[2][8] = {
+        {nvfp4_gemm_packed_kernel<false, 8>, nvfp4_gemm_packed_kernel<false, 16>,
+         nvfp4_gemm_packed_kernel<false, 24>, nvfp4_gemm_packed_kernel<false, 32>,
+         nvfp4_gemm_packed_kernel<false, 40>, nvfp4_gemm_packed_kernel<false, 48>,
+         nvfp4_gemm_packed_kernel<false, 56>, nvfp4_gemm_packed_kernel<false, 64>},
+        {nvfp4_gemm_packed_kernel<true, 8>, nvfp4_gemm_packed_kernel<true, 16>,
+         nvfp4_gemm_packed_kernel<true, 24>, nvfp4_gemm_packed_kernel<true, 32>,
+         nvfp4_gemm_packed_kernel<true, 40>, nvfp4_gemm_packed_kernel<true, 48>,
+         nvfp4_gemm_packed_kernel<true, 56>, nvfp4_gemm_packed_kernel<true, 64>}};
+    const int idx = (int)(K / 2048) - 1;
+    if (idx < 0 || idx > 7 || K % 2048 != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kernels[out_bf16 ? 1 : 0][idx], grid, dim3(GEMM_WG), 0, s, ap, asp, sg_a, bp,
+                       bsp, sg_b, (int)M, (int)N, c);
     return hipGetLastError();
 }
 

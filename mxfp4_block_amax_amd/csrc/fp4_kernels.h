@@ -65,6 +65,15 @@ hipError_t launch_pack_mxfp4(const uint8_t *codes, const uint8_t *scales, int64_
                              uint8_t *packed, hipStream_t s);
 hipError_t launch_gemm_mxfp4_packed(const uint8_t *a_packed, const uint8_t *bt_packed, int64_t M,
                                     int64_t N, int64_t K, void *c, bool out_bf16, hipStream_t s);
+// The NVFP4 operands in fp16-MFMA operand order: bytes of a packed operand
+// (0 when K is not a multiple of 512), its packing, and the GEMM on two packed
+// operands (K a multiple of 2048, at most 16384).
+int64_t nv_packed_operand_bytes(int64_t rows, int64_t K);
+hipError_t launch_pack_nvfp4(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t K,
+                             uint8_t *packed, hipStream_t s);
+hipError_t launch_gemm_nvfp4_packed(const uint8_t *a_packed, const float *sg_a,
+                                    const uint8_t *bt_packed, const float *sg_b, int64_t M,
+                                    int64_t N, int64_t K, void *c, bool out_bf16, hipStream_t s);
 // MXFP4 quantize (floor rule) of x [rows, cols] written in the packed layout.
 hipError_t launch_mx_quantize_packed(const void *x, bool bf16, int64_t rows, int64_t cols,
                                      uint8_t *packed, int32_t *status, hipStream_t s);

@@ -140,3 +140,73 @@ def gemm_from_packed(a_packed: np.ndarray, bt_packed: np.ndarray, M: int, N: int
     for ks in range(K // 64):
         C += np.einsum("irk,jck->irjc", A[:, ks], B[:, ks]).reshape(A.shape[0] * 32, B.shape[0] * 32)
     return C[:M, :N]
+
+
+# ---- NVFP4 in MFMA operand order ------------------------------------------------
+#
+# Also the implementation's own arrangement (section 7 of the format page
+# leaves it open).  Codes are arranged as for MXFP4 above; the E4M3 block
+# scales (16 values each) follow all codes: for row tile rt and group q of
+# eight K steps, 1024 bytes, byte 16 l + 2 i + b holding the scale of row
+# 32 rt + l % 32 and block 4 (8 q + i) + 2 (l // 32) + b; padding rows hold 0.
+
+def nv_packed_bytes(rows: int, K: int) -> int:
+    nrt = (rows + 31) // 32
+    return nrt * 32 * (K // 2) + nrt * 32 * (K // 16)
+
+
+def nv_pack_operand(codes: np.ndarray, scales: np.ndarray, rows: int, K: int) -> np.ndarray:
+    """Row-major NVFP4 operand (codes [rows, K/2], E4M3 scales [rows, K/16])
+    to the packed NVFP4 layout, byte by byte in the order the layout lists."""
+    nrt, nks = (rows + 31) // 32, K // 64
+    c = np.zeros((nrt * 32, K // 2), np.uint8)
+    c[:rows] = np.asarray(codes, np.uint8).reshape(rows, K // 2)
+    s = np.zeros((nrt * 32, K // 16), np.uint8)
+    s[:rows] = np.asarray(scales, np.uint8).reshape(rows, K // 16)
+    out_c = np.zeros((nrt, nks, 64, 16), np.uint8)
+    out_s = np.zeros((nrt, nks // 8, 64, 16), np.uint8)
+    for l in range(64):
+        row = np.arange(nrt)[:, None] * 32 + l % 32
+        blk = 2 * np.arange(nks)[None, :] + l // 32           # 32-value block of this lane
+        for b in range(16):
+            out_c[:, :, l, b] = c[row, 16 * blk + b]
+        for i in range(8):
+            step = 8 * np.arange(nks // 8)[None, :] + i
+            for b in range(2):
+                out_s[:, :, l, 2 * i + b] = s[row, 4 * step + 2 * (l // 32) + b]
+    return np.concatenate([out_c.reshape(-1), out_s.reshape(-1)])
+
+
+def nv_gemm_from_packed(a_packed: np.ndarray, sg_a, bt_packed: np.ndarray, sg_b, M: int,
+                        N: int, K: int) -> np.ndarray:
+    """C = A @ B in binary64 from two packed NVFP4 operands, read the way the
+    fp16 MFMA (v_mfma_f32_32x32x16_f16) consumes them: in sub-step u (0..3)
+    of a 64-value step, lane l supplies row l % 32 and the eight values in
+    bytes 4 u .. 4 u + 3 of its 16, times the E4M3 byte 2 i + (u >= 2) of
+    its scale word, into K slots 8 (l // 32) .. + 7; both operands use the
+    same slots, so the step adds all 64 products.  Written from the consumer's
+    side, independently of nv_pack_operand."""
+    ev = np.array([e2m1_value(c) for c in range(16)])
+    mag = np.array([e4m3_value(c) if c < 127 else np.nan for c in range(128)])
+    sv = np.concatenate([mag, -mag])
+
+    def tiles(packed, rows):
+        nrt, nks = (rows + 31) // 32, K // 64
+        codes = np.asarray(packed[:nrt * nks * 1024], np.uint8).reshape(nrt, nks, 64, 16)
+        scl = np.asarray(packed[nrt * nks * 1024:], np.uint8).reshape(nrt, nks // 8, 64, 16)
+        vals = np.zeros((nrt, nks, 4, 32, 16))                  # [tile, step, u, row, slot]
+        for l in range(64):
+            sc = scl[:, :, l, :].reshape(nrt, nks, 2)            # [tile, step, b]
+            for u in range(4):
+                w = codes[:, :, l, 4 * u:4 * u + 4]
+                v = np.stack([ev[w & 15], ev[w >> 4]], axis=-1).reshape(nrt, nks, 8)
+                slot = 8 * (l // 32)
+                vals[:, :, u, l % 32, slot:slot + 8] = v * sv[sc[:, :, u // 2]][:, :, None]
+        return vals
+
+    A, B = tiles(a_packed, M), tiles(bt_packed, N)
+    C = np.zeros((A.shape[0] * 32, B.shape[0] * 32))
+    for ks in range(K // 64):
+        for u in range(4):
+            C += np.einsum("irk,jck->irjc", A[:, ks, u], B[:, ks, u]).reshape(C.shape)
+    return C[:M, :N] * float(np.float32(sg_a)) * float(np.float32(sg_b))

@@ -295,6 +295,35 @@ def test_packed_sizes_and_validation():
     assert g(c=ctypes.c_void_p(0x10002)) == E_ALIGN
 
 
+def test_nv_packed_sizes_and_validation():
+    L = fp4.lib()
+    assert fp4.nv_packed_operand_bytes(1, 512) == 32 * 256 + 32 * 32
+    assert fp4.nv_packed_operand_bytes(33, 1024) == 64 * 512 + 64 * 64
+    assert fp4.nv_packed_operand_bytes(8192, 8192) == 8192 * 4096 + 8192 * 512
+    assert fp4.nv_packed_operand_bytes(1, 256) == 0
+    assert fp4.nv_packed_operand_bytes(0, 512) == 0
+
+    def p(c=A16, s=A16, rows=64, K=1024, out=A16, nb=1 << 20):
+        return L.fp4_pack_nvfp4_operand(c, s, rows, K, out, nb, NULL)
+    assert p(s=NULL) == E_ARG
+    assert p(K=1000) == E_SHAPE
+    assert p(nb=fp4.nv_packed_operand_bytes(64, 1024) - 1) == E_WORKSPACE
+    assert p(out=A1) == E_ALIGN
+
+    def g(a=A16, sa=A16, b=A16, sb=A16, M=128, N=256, K=2048, c=A16, ct=fp4.BF16):
+        return L.fp4_gemm_nvfp4_packed(a, sa, b, sb, M, N, K, c, ct, NULL)
+    assert g(sa=NULL) == E_ARG
+    assert g(sb=NULL) == E_ARG
+    assert g(ct=7) == E_DTYPE
+    assert g(K=1024) == E_SHAPE
+    assert g(K=6144 + 512) == E_SHAPE
+    assert g(K=18432) == E_SHAPE
+    assert g(N=0) == E_SHAPE
+    assert g(N=1 << 20, K=16384) == E_SHAPE   # packed Bt above 1 GiB
+    assert g(b=A1) == E_ALIGN
+    assert g(sa=ctypes.c_void_p(0x10002)) == E_ALIGN
+
+
 def test_packed_quantize_and_linear_validation():
     L = fp4.lib()
 

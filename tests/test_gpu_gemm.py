@@ -354,6 +354,74 @@ def test_gemm_packed_integer_valued_is_exact_and_deterministic():
     assert torch.equal(c1, c2)
 
 
+# ---- NVFP4 on packed operands ---------------------------------------------------
+
+def _nv_pack_dev(p, sc, rows, K, what):
+    packed = fp4.pack_nvfp4_operand(dev(torch.from_numpy(p.reshape(rows, K // 2))),
+                                    dev(torch.from_numpy(sc.reshape(rows, K // 16))))
+    torch.cuda.synchronize()
+    if rows * K <= 2048 * 8192:
+        assert_bytes_equal(host_u8(packed), og.nv_pack_operand(p, sc, rows, K), what)
+    return packed
+
+
+def _check_nv_packed(ops, M, N, K, what):
+    ap, asc, sga, bp, bsc, sgb = ops
+    announce(f"pack nvfp4 operands {M}x{K} and {N}x{K} ({what})")
+    pa = _nv_pack_dev(ap, asc, M, K, f"nv packed A {M}x{K}")
+    pb = _nv_pack_dev(bp, bsc, N, K, f"nv packed Bt {N}x{K}")
+    t = lambda v: dev(torch.tensor([float(v)], dtype=torch.float32))
+    announce(f"gemm nvfp4 packed {what} {M}x{N}x{K} fp32 and bf16 out")
+    c32 = fp4.gemm_nvfp4_packed(pa, t(sga), pb, t(sgb), M, N, K, torch.float32)
+    c16 = fp4.gemm_nvfp4_packed(pa, t(sga), pb, t(sgb), M, N, K, torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = og.nv_gemm_f64(ap, asc, sga, bp, bsc, sgb, M, N, K)
+    got = c32.cpu().numpy().astype(np.float64)
+    err = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert err <= REL_FROB, f"nvfp4 packed {what} {M}x{N}x{K}: relative Frobenius error {err:.3e}"
+    assert torch.equal(c16.cpu().view(torch.int16), c32.cpu().to(torch.bfloat16).view(torch.int16))
+    return c32, err
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 256, 2048), (1, 32, 2048), (70, 100, 2048),
+                                   (130, 64, 6144), (256, 96, 8192), (33, 40, 16384)])
+def test_gemm_nvfp4_packed_small_and_ragged(M, N, K):
+    _check_nv_packed(_nv_operands(M, N, K), M, N, K, "random")
+
+
+def test_gemm_nvfp4_packed_full_size_128x8192x8192():
+    _, err = _check_nv_packed(_nv_operands(128, 8192, 8192), 128, 8192, 8192, "full size")
+    print(f"relative Frobenius error {err:.3e}")
+
+
+def test_gemm_nvfp4_packed_every_code_under_every_scale_of_both_signs():
+    # A: row r takes E4M3 byte (r % 126) + 1, with the sign bit on odd rows,
+    # on every block and the sixteen FP4 codes in each block
+    M, N, K = 252, 64, 2048
+    ap = oracle.pack(np.tile(np.arange(16, dtype=np.uint8), M * K // 16))
+    r = np.arange(M)
+    asc = np.repeat(((r % 126 + 1) | ((r % 2) << 7)).astype(np.uint8), K // 16)
+    _, _, _, bp, bsc, sgb = _nv_operands(8, N, K, seed=7)
+    for sga in (1.0, 2.0 ** -20):
+        _check_nv_packed((ap, asc, np.float32(sga), bp, bsc, sgb), M, N, K,
+                         f"every code, s_gA={sga}")
+
+
+def test_gemm_nvfp4_packed_integer_case_is_exact_and_deterministic():
+    M, N, K = 64, 48, 2048
+    ap = oracle.pack(np.full(M * K, 4, np.uint8))          # 2.0
+    bp = oracle.pack(np.full(N * K, 5, np.uint8))          # 3.0
+    asc = np.full(M * K // 16, 0x38, np.uint8)             # scale 1
+    bsc = np.full(N * K // 16, 0x40, np.uint8)             # scale 2
+    c1, _ = _check_nv_packed((ap, asc, np.float32(1.0), bp, bsc, np.float32(0.5)), M, N, K,
+                             "integer")
+    assert np.all(c1.cpu().numpy() == K * 6.0)
+    ops = _nv_operands(128, 1024, 4096, seed=4)
+    ca, _ = _check_nv_packed(ops, 128, 1024, 4096, "repeat 1")
+    cb, _ = _check_nv_packed(ops, 128, 1024, 4096, "repeat 2")
+    assert torch.equal(ca, cb)
+
+
 # ---- quantize straight into the packed layout, and the packed W4A4 linear ------
 
 @pytest.mark.parametrize("rows,cols,dt", [(1, 512, torch.float32), (70, 2048, torch.bfloat16),
