@@ -1,7 +1,8 @@
 """Seeded sweep over the GEMM family on generated shapes, each path with the
 shapes it takes: fp4_gemm_mxfp4 (whichever of its kernels the shape and the
-alignment select), split over K, on packed operands, NVFP4 x NVFP4, and the
-W4A4 linear in one launch, two launches and on a packed weight.  Each result
+alignment select), split over K, on packed operands, NVFP4 x NVFP4 (row-major
+and packed), and the W4A4 linear in one launch, two launches and on a packed
+weight.  Each result
 is within the relative Frobenius bound of the oracle's binary64 product, and
 its bf16 output equals the RNE of its fp32 output."""
 import numpy as np
@@ -92,6 +93,28 @@ def test_nvfp4_gemm(i):
     what = f"sweep {i}: gemm_nvfp4 {M}x{N}x{K}"
     announce(what)
     _close(fp4.gemm_nvfp4(*ops, torch.float32), fp4.gemm_nvfp4(*ops, torch.bfloat16), ref, what)
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_nvfp4_gemm_packed(i):
+    M, N, K = _shape(250 + i, 2048, 16384)
+    a, bt = workloads.gemm_operands(M, N, K, seed_a=70 + i, seed_b=71 + i)
+    ap, asc, sga, f1 = oracle.nv_quantize(a.numpy().reshape(-1))
+    bp, bsc, sgb, f2 = oracle.nv_quantize(bt.numpy().reshape(-1))
+    assert f1 == 0 and f2 == 0
+    ref = og.nv_gemm_f64(ap, asc, sga, bp, bsc, sgb, M, N, K)
+    what = f"sweep {i}: pack_nvfp4_operand {M}x{K}, {N}x{K}"
+    announce(what)
+    pa = fp4.pack_nvfp4_operand(_t(ap, M, K // 2), _t(asc, M, K // 16))
+    pb = fp4.pack_nvfp4_operand(_t(bp, N, K // 2), _t(bsc, N, K // 16))
+    torch.cuda.synchronize()
+    assert np.array_equal(pa.cpu().numpy(), og.nv_pack_operand(ap, asc, M, K)), what
+    assert np.array_equal(pb.cpu().numpy(), og.nv_pack_operand(bp, bsc, N, K)), what
+    sa, sb = dev(torch.tensor([float(sga)])), dev(torch.tensor([float(sgb)]))
+    what = f"sweep {i}: gemm_nvfp4_packed {M}x{N}x{K}"
+    announce(what)
+    _close(fp4.gemm_nvfp4_packed(pa, sa, pb, sb, M, N, K, torch.float32),
+           fp4.gemm_nvfp4_packed(pa, sa, pb, sb, M, N, K, torch.bfloat16), ref, what)
 
 
 @pytest.mark.parametrize("i", range(6))
