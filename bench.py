@@ -460,6 +460,17 @@ def extra_workloads():
     ms2 = time_rotating([lambda: fp4.pack_nvfp4_operand(an[0], an[1], out=anp)])
     d["pack_a_us"] = round(ms2 * 1e3, 2)
     out["nvfp4_gemm_packed_128x8192x8192_bf16out"] = d
+    # NVFP4 W4A4 linear on a packed weight: bf16 activations quantized
+    # straight into the packed layout (amax pass, encode), then the packed GEMM
+    wsn = fp4.new_workspace(M, K, "cuda")
+    apn = (torch.empty(fp4.nv_packed_operand_bytes(M, K), dtype=torch.uint8, device="cuda"),
+           torch.empty(1, dtype=torch.float32, device="cuda"))
+    ms = time_rotating([lambda b=b, bb=bb: fp4.linear_nvfp4_packed(xa, bb, b[2], N, out=c, a_out=apn,
+                                                                   status=st, workspace=wsn,
+                                                                   check=False)
+                        for b, bb in zip(bn, bnp)])
+    nv_lin_bytes = (M * K * 2 + M * K // 2 + M * K // 16 + N * K // 2 + N * K // 16 + M * N * 2)
+    out["nvfp4_linear_w4a4_packed_128x8192x8192_bf16"] = _rate(nv_lin_bytes, ms)
     del bnp
     if int(st.item()) != 0:
         raise RuntimeError(f"a timed call raised status flags {int(st.item())}")

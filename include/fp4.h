@@ -386,6 +386,43 @@ fp4_status fp4_gemm_nvfp4_packed(const uint8_t *a_packed, const float *a_global_
                                  void *stream);
 
 /*
+ * NVFP4 quantize of x [rows, cols] (fp32 or bf16), as fp4_quantize_nvfp4
+ * (same codes, E4M3 scale bytes and tensor scale, "NVFP4 / MXFP4 format"
+ * page, section 3), written directly in the packed layout of
+ * fp4_pack_nvfp4_operand (padding rows come out as zero codes and zero scale
+ * bytes).  Two launches on `stream`: the tensor amax, then the encode.
+ * cols must be a multiple of 512; packed must hold
+ * fp4_nv_packed_operand_bytes(rows, cols) bytes, 16-byte aligned; x 16-byte
+ * aligned; global_scale receives s_g; workspace as for fp4_quantize_nvfp4.
+ * status as for fp4_quantize_nvfp4 (FP4_FLAG_NONFINITE,
+ * FP4_FLAG_SCALE_UNDERFLOW; with either, the outputs are unspecified).
+ * Errors: FP4_E_SHAPE, FP4_E_WORKSPACE (packed or workspace too small),
+ * FP4_E_ALIGN.
+ */
+fp4_status fp4_quantize_nvfp4_packed(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
+                                     uint8_t *packed, size_t packed_bytes, float *global_scale,
+                                     void *workspace, size_t workspace_bytes, int32_t *status,
+                                     void *stream);
+
+/*
+ * NVFP4 W4A4 linear on a packed weight: x [M, K] (fp32 or bf16) quantized
+ * to NVFP4 into a_packed with its tensor scale in a_global_scale
+ * (fp4_quantize_nvfp4_packed), then fp4_gemm_nvfp4_packed with bt_packed =
+ * Bt [N, K] packed once and its tensor scale bt_global_scale (the W4A4
+ * linear of the "FP4, FP8 and INT8/INT4" page, section 5.1, in the NVFP4
+ * format).  Three launches on one stream.  K a multiple of 2048, at most
+ * 16384; a_packed at least fp4_nv_packed_operand_bytes(M, K) bytes;
+ * workspace as for fp4_quantize_nvfp4; alignment as for the two calls.
+ * status receives the quantize's flags.
+ */
+fp4_status fp4_linear_nvfp4_packed(const void *x, fp4_dtype xt, int64_t M, int64_t K,
+                                   const uint8_t *bt_packed, const float *bt_global_scale,
+                                   int64_t N, uint8_t *a_packed, size_t a_packed_bytes,
+                                   float *a_global_scale, void *c, fp4_dtype ct,
+                                   void *workspace, size_t workspace_bytes, int32_t *status,
+                                   void *stream);
+
+/*
  * W4A4 linear layer: the activations quantized to MXFP4, then the MXFP4 GEMM
  * ("FP4, FP8 and INT8/INT4" page, tom-jerr.github.io, section 5: the cost of
  * a low-bit linear layer is the activation quantize plus the block-scaled

@@ -48,6 +48,7 @@ EXPORTS = ("fp4_quantize_mxfp4", "fp4_quantize_mxfp4_rule", "fp4_quantize_nvfp4"
            "fp4_debug_barrier_spin_limit", "fp4_packed_operand_bytes", "fp4_pack_mxfp4_operand",
            "fp4_gemm_mxfp4_packed", "fp4_quantize_mxfp4_packed", "fp4_linear_mxfp4_packed",
            "fp4_nv_packed_operand_bytes", "fp4_pack_nvfp4_operand", "fp4_gemm_nvfp4_packed",
+           "fp4_quantize_nvfp4_packed", "fp4_linear_nvfp4_packed",
            "fp4_workspace_bytes", "fp4_status_str")
 
 # fp4_mx_rule: the MXFP4 block-exponent rules
@@ -96,6 +97,8 @@ def lib() -> ctypes.CDLL:
     L.fp4_nv_packed_operand_bytes.restype = I64
     L.fp4_pack_nvfp4_operand.argtypes = [P, P, I64, I64, P, S, P]
     L.fp4_gemm_nvfp4_packed.argtypes = [P, P, P, P, I64, I64, I64, P, I, P]
+    L.fp4_quantize_nvfp4_packed.argtypes = [P, I, I64, I64, P, S, P, P, S, P, P]
+    L.fp4_linear_nvfp4_packed.argtypes = [P, I, I64, I64, P, P, I64, P, S, P, P, I, P, S, P, P]
     L.fp4_quantize_mxfp4_packed.argtypes = [P, I, I64, I64, P, S, P, P]
     L.fp4_linear_mxfp4_packed.argtypes = [P, I, I64, I64, P, I64, P, S, P, I, P, P]
     L.fp4_debug_barrier_spin_limit.argtypes = [ctypes.c_uint32]
@@ -463,6 +466,56 @@ def gemm_nvfp4_packed(a_packed: torch.Tensor, a_global_scale: torch.Tensor,
                                     _ptr(bt_global_scale), int(M), int(N), int(K), _ptr(c),
                                     _dtype_code(c.dtype), _stream(a_packed)))
     return c
+
+
+def quantize_nvfp4_packed(x: torch.Tensor, check: bool = True, out=None, status=None,
+                          workspace=None):
+    """NVFP4 quantize of x [rows, cols] written in the packed NVFP4 layout:
+    returns (packed, s_g), the bytes pack_nvfp4_operand(*quantize_nvfp4(x)[:2])
+    would give and the tensor scale."""
+    rows, cols = _rows_cols(x)
+    n = nv_packed_operand_bytes(rows, cols)
+    if n == 0:
+        raise ValueError("the packed layout needs cols a positive multiple of 512")
+    if out is None:
+        packed = torch.empty(n, dtype=torch.uint8, device=x.device)
+        s_g = torch.empty(1, dtype=torch.float32, device=x.device)
+    else:
+        packed, s_g = out
+    if workspace is None:
+        workspace = new_workspace(rows, cols, x.device)
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _ok(lib().fp4_quantize_nvfp4_packed(_ptr(x), _dtype_code(x.dtype), rows, cols, _ptr(packed),
+                                        packed.numel(), _ptr(s_g), _ptr(workspace),
+                                        workspace.numel(), _ptr(status), _stream(x)))
+    _finish(status, check)
+    return packed, s_g
+
+
+def linear_nvfp4_packed(x: torch.Tensor, bt_packed: torch.Tensor, bt_global_scale: torch.Tensor,
+                        N: int, out_dtype=torch.bfloat16, out=None, a_out=None, status=None,
+                        workspace=None, check: bool = True):
+    """NVFP4 W4A4 linear on a packed weight: x [M, K] quantized to NVFP4 in
+    the packed layout, times Bt [N, K] (packed, with its tensor scale).
+    Returns (C [M, N], (a_packed, a_s_g))."""
+    M, K = _rows_cols(x)
+    if a_out is None:
+        a_out = (torch.empty(nv_packed_operand_bytes(M, K), dtype=torch.uint8, device=x.device),
+                 torch.empty(1, dtype=torch.float32, device=x.device))
+    a_packed, a_sg = a_out
+    c = out if out is not None else torch.empty(M, int(N), dtype=out_dtype, device=x.device)
+    if workspace is None:
+        workspace = new_workspace(M, K, x.device)
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _ok(lib().fp4_linear_nvfp4_packed(_ptr(x), _dtype_code(x.dtype), M, K, _ptr(bt_packed),
+                                      _ptr(bt_global_scale), int(N), _ptr(a_packed),
+                                      a_packed.numel(), _ptr(a_sg), _ptr(c), _dtype_code(c.dtype),
+                                      _ptr(workspace), workspace.numel(), _ptr(status),
+                                      _stream(x)))
+    _finish(status, check)
+    return c, a_out
 
 
 def linear_mxfp4(x: torch.Tensor, bt_codes: torch.Tensor, bt_scales: torch.Tensor,

@@ -230,6 +230,53 @@ fp4_status fp4_gemm_nvfp4_packed(const uint8_t *a_packed, const float *a_global_
                                                      (hipStream_t)stream));
 }
 
+fp4_status fp4_quantize_nvfp4_packed(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
+                                     uint8_t *packed, size_t packed_bytes, float *global_scale,
+                                     void *workspace, size_t workspace_bytes, int32_t *status,
+                                     void *stream) {
+    if (!x || !packed || !global_scale) return FP4_E_ARG;
+    if (!valid_dtype(xt)) return FP4_E_DTYPE;
+    const int64_t need = fp4_nv_packed_operand_bytes(rows, cols);
+    if (need == 0 || rows > kMaxElems / cols) return FP4_E_SHAPE;
+    if (packed_bytes < (size_t)need) return FP4_E_WORKSPACE;
+    if (!workspace || workspace_bytes < nv_workspace()) return FP4_E_WORKSPACE;
+    if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(global_scale, 4) ||
+        !aligned(workspace, 16) || !aligned(status, 4))
+        return FP4_E_ALIGN;
+    return from_hip(fp4dev::launch_nv_quantize_packed(x, xt == FP4_BF16, rows, cols, packed,
+                                                      global_scale, workspace, status,
+                                                      (hipStream_t)stream));
+}
+
+fp4_status fp4_linear_nvfp4_packed(const void *x, fp4_dtype xt, int64_t M, int64_t K,
+                                   const uint8_t *bt_packed, const float *bt_global_scale,
+                                   int64_t N, uint8_t *a_packed, size_t a_packed_bytes,
+                                   float *a_global_scale, void *c, fp4_dtype ct,
+                                   void *workspace, size_t workspace_bytes, int32_t *status,
+                                   void *stream) {
+    if (!x || !bt_packed || !bt_global_scale || !a_packed || !a_global_scale || !c)
+        return FP4_E_ARG;
+    if (!valid_dtype(xt) || !valid_dtype(ct)) return FP4_E_DTYPE;
+    if (M < 1 || N < 1 || K < 2048 || K % 2048 != 0 || K > 16384) return FP4_E_SHAPE;
+    if (M > INT32_MAX / 2 || N > INT32_MAX / 2 || M > kMaxElems / K) return FP4_E_SHAPE;
+    if (fp4_nv_packed_operand_bytes(M, K) > (1 << 30) ||
+        fp4_nv_packed_operand_bytes(N, K) > (1 << 30))
+        return FP4_E_SHAPE;
+    if (a_packed_bytes < (size_t)fp4_nv_packed_operand_bytes(M, K)) return FP4_E_WORKSPACE;
+    if (!workspace || workspace_bytes < nv_workspace()) return FP4_E_WORKSPACE;
+    if (!aligned(x, 16) || !aligned(bt_packed, 16) || !aligned(a_packed, 16) || !aligned(c, 4) ||
+        !aligned(bt_global_scale, 4) || !aligned(a_global_scale, 4) ||
+        !aligned(workspace, 16) || !aligned(status, 4))
+        return FP4_E_ALIGN;
+    hipError_t e = fp4dev::launch_nv_quantize_packed(x, xt == FP4_BF16, M, K, a_packed,
+                                                     a_global_scale, workspace, status,
+                                                     (hipStream_t)stream);
+    if (e != hipSuccess) return from_hip(e);
+    return from_hip(fp4dev::launch_gemm_nvfp4_packed(a_packed, a_global_scale, bt_packed,
+                                                     bt_global_scale, M, N, K, c,
+                                                     ct == FP4_BF16, (hipStream_t)stream));
+}
+
 fp4_status fp4_quantize_mxfp4_packed(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
                                      uint8_t *packed, size_t packed_bytes, int32_t *status,
                                      void *stream) {

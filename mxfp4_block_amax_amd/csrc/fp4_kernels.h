@@ -74,6 +74,11 @@ hipError_t launch_pack_nvfp4(const uint8_t *codes, const uint8_t *scales, int64_
 hipError_t launch_gemm_nvfp4_packed(const uint8_t *a_packed, const float *sg_a,
                                     const uint8_t *bt_packed, const float *sg_b, int64_t M,
                                     int64_t N, int64_t K, void *c, bool out_bf16, hipStream_t s);
+// NVFP4 quantize of x [rows, cols] (tensor amax pass, then the encode)
+// written in the packed NVFP4 layout; workspace holds the amax partials.
+hipError_t launch_nv_quantize_packed(const void *x, bool bf16, int64_t rows, int64_t cols,
+                                     uint8_t *packed, float *global_scale, void *workspace,
+                                     int32_t *status, hipStream_t s);
 // MXFP4 quantize (floor rule) of x [rows, cols] written in the packed layout.
 hipError_t launch_mx_quantize_packed(const void *x, bool bf16, int64_t rows, int64_t cols,
                                      uint8_t *packed, int32_t *status, hipStream_t s);

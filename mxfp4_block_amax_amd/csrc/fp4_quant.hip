@@ -671,6 +671,65 @@ typedef __attribute__((address_space(3))) void *lds_ptr;
 
 // EXACT: the grid covers the tensor exactly (nchunks = gridDim.x * 512 * CPL),
 // so no load is clamped and no store predicated.
+// ---------------------------------------------------------------------------
+// NVFP4 quantize, pass 2, written in the packed NVFP4 operand layout: one
+// wave per (row tile rt, K step ks) writes the tile's contiguous kilobyte of
+// codes; lane l takes row 32 rt + l % 32, values 32 (2 ks + l / 32) .. + 31,
+// which are two 16-blocks, and derives both block scales itself (the same
+// per-block scale and divide as the row-major kernel, so the same codes and
+// scale bytes).  The two E4M3 bytes go to bytes 16 l + 2 (ks % 8) + {0, 1}
+// of the tile's scale group ks / 8.  Rows past the tensor are written as
+// the layout's padding (codes 0, scale bytes 0).
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(WG) void nv_quantize_packed_kernel(
+    const uint4 *__restrict__ x, int64_t rows, int64_t K, int64_t ntiles,
+    const uint32_t *__restrict__ partials, int npart, uint4 *__restrict__ codes,
+    uint16_t *__restrict__ scales, float *__restrict__ global_scale, int32_t *status) {
+    __shared__ NvScaleTable T;
+    TensorScale ts = tensor_scale<BF16>(partials, npart);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *global_scale = ts.s_g;
+    if (ts.flags) {  // uniform over the grid: outputs unspecified
+        if (blockIdx.x == 0 && threadIdx.x == 0 && status) atomicOr(status, (int32_t)ts.flags);
+        return;
+    }
+    nv_table_build(T, ts.s_g);
+    __syncthreads();
+    const CodeGuess G = make_code_guess(ts.s_g);
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int64_t wave = (int64_t)blockIdx.x * WAVES_PER_WG + (threadIdx.x / WAVE);
+    const int64_t nwaves = (int64_t)gridDim.x * WAVES_PER_WG;
+    const int64_t nks = K / 64;
+    uint32_t flags = 0;
+    for (int64_t t = wave; t < ntiles; t += nwaves) {
+        const int64_t rt = t / nks, ks = t % nks;
+        const int64_t row = rt * 32 + (lane & 31);
+        const bool ok = row < rows;
+        const int64_t c0 = (row * K + (2 * ks + (lane >> 5)) * 32) / 8;
+        Chunk<BF16> k[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) k[i] = load_chunk<BF16>(x, c0 + i, ok);
+        const uint32_t ma = max(chunk_amax<BF16>(k[0]), chunk_amax<BF16>(k[1]));
+        const uint32_t mb = max(chunk_amax<BF16>(k[2]), chunk_amax<BF16>(k[3]));
+        uint32_t fa = 0;
+        const BlockScale sa = nv_block_scale(T, amax_as_f32_bits<BF16>(ma), G, fa);
+        const BlockScale sb = nv_block_scale(T, amax_as_f32_bits<BF16>(mb), G, fa);
+        if (ok) flags |= fa;
+        uint32_t q[4];
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const BlockScale &b = i < 2 ? sa : sb;
+            chunk_values<BF16>(k[i], v);
+            q[i] = nv_quant8<BF16>(v, b.ad, b.y, b.sc);
+        }
+        codes[t * 64 + lane] = ok ? make_uint4(q[0], q[1], q[2], q[3]) : make_uint4(0u, 0u, 0u, 0u);
+        const uint16_t sc = ok ? (uint16_t)(sa.code | (sb.code << 8)) : (uint16_t)0;
+        scales[((rt * (nks / 8) + ks / 8) * 64 + lane) * 8 + ks % 8] = sc;
+    }
+    report_flags(status, flags);
+}
+
 template <int CPL, bool EXACT>
 __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
     const uint4 *__restrict__ x, int nchunks, uint32_t *__restrict__ codes,
@@ -1314,6 +1373,23 @@ static ResidentInfo resident_info() {
         info[dev].cus = cus > kResidentSlots ? 0 : cus;
     });
     return info[dev];
+}
+
+hipError_t launch_nv_quantize_packed(const void *x, bool bf16, int64_t rows, int64_t cols,
+                                     uint8_t *packed, float *global_scale, void *workspace,
+                                     int32_t *status, hipStream_t s) {
+    const int64_t nrt = (rows + 31) / 32, ntiles = nrt * (cols / 64);
+    uint32_t *partials = (uint32_t *)workspace;
+    const int g1 = amax_grid(rows * cols / 8);
+    hipError_t e = launch_amax(x, bf16, rows * cols / 8, partials, g1, s);
+    if (e != hipSuccess) return e;
+    int64_t g = (ntiles + WAVES_PER_WG - 1) / WAVES_PER_WG;
+    if (g > kMaxGrid) g = kMaxGrid;
+    uint16_t *scales = (uint16_t *)(packed + nrt * 32 * (cols / 2));
+    auto k = bf16 ? nv_quantize_packed_kernel<true> : nv_quantize_packed_kernel<false>;
+    hipLaunchKernelGGL(k, dim3((unsigned)g), dim3(WG), 0, s, (const uint4 *)x, rows, cols, ntiles,
+                       partials, g1, (uint4 *)packed, scales, global_scale, status);
+    return hipGetLastError();
 }
 
 template <int CPL>

@@ -323,6 +323,28 @@ def test_nv_packed_sizes_and_validation():
     assert g(b=A1) == E_ALIGN
     assert g(sa=ctypes.c_void_p(0x10002)) == E_ALIGN
 
+    ws = fp4.workspace_bytes(fp4.NVFP4, 64, 1024)
+
+    def q(x=A16, xt=fp4.F32, rows=64, cols=1024, out=A16, nb=1 << 20, sg=A16, w=A16, wb=ws, st=A16):
+        return L.fp4_quantize_nvfp4_packed(x, xt, rows, cols, out, nb, sg, w, wb, st, NULL)
+    assert q(sg=NULL) == E_ARG
+    assert q(xt=9) == E_DTYPE
+    assert q(cols=1000) == E_SHAPE
+    assert q(nb=fp4.nv_packed_operand_bytes(64, 1024) - 1) == E_WORKSPACE
+    assert q(w=NULL) == E_WORKSPACE
+    assert q(wb=ws - 1) == E_WORKSPACE
+    assert q(x=A1) == E_ALIGN
+
+    def lin(M=128, K=2048, N=256, nb=1 << 20, w=A16, wb=ws, c=A16, sb=A16):
+        return L.fp4_linear_nvfp4_packed(A16, fp4.F32, M, K, A16, sb, N, A16, nb, A16, c,
+                                         fp4.BF16, w, wb, NULL, NULL)
+    assert lin(sb=NULL) == E_ARG
+    assert lin(K=1024) == E_SHAPE
+    assert lin(N=0) == E_SHAPE
+    assert lin(nb=fp4.nv_packed_operand_bytes(128, 2048) - 1) == E_WORKSPACE
+    assert lin(w=NULL) == E_WORKSPACE
+    assert lin(c=A1) == E_ALIGN
+
 
 def test_packed_quantize_and_linear_validation():
     L = fp4.lib()

@@ -422,6 +422,54 @@ def test_gemm_nvfp4_packed_integer_case_is_exact_and_deterministic():
     assert torch.equal(ca, cb)
 
 
+# ---- NVFP4 quantize into the packed layout, and the packed NVFP4 linear ---------
+
+@pytest.mark.parametrize("rows,cols,dt", [(1, 512, torch.float32), (70, 2048, torch.bfloat16),
+                                          (128, 8192, torch.bfloat16), (33, 1536, torch.float32)])
+def test_quantize_nvfp4_packed_matches_oracle(rows, cols, dt):
+    g = torch.Generator().manual_seed(3 * rows + cols)
+    x = (torch.randn(rows, cols, generator=g) * torch.rand(rows, cols, generator=g) ** 3).to(dt)
+    announce(f"quantize nvfp4 packed {rows}x{cols} {dt}")
+    got, sg = fp4.quantize_nvfp4_packed(dev(x))
+    torch.cuda.synchronize()
+    p, sc, sg_ref, flags = oracle.nv_quantize(oracle_view(x).reshape(-1))
+    assert flags == 0
+    assert np.float32(sg.item()) == np.float32(sg_ref)
+    assert_bytes_equal(host_u8(got), og.nv_pack_operand(p, sc, rows, cols),
+                       f"nv packed quantize {rows}x{cols}")
+
+
+def test_quantize_nvfp4_packed_flags_nonfinite():
+    x = torch.zeros(32, 512)
+    x[5, 100] = float("inf")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    announce("quantize nvfp4 packed, one inf")
+    fp4.quantize_nvfp4_packed(dev(x), check=False, status=st)
+    assert int(st.item()) & fp4.FLAG_NONFINITE
+
+
+@pytest.mark.parametrize("M,N,K,dt", [(128, 8192, 8192, torch.bfloat16), (70, 100, 2048, torch.float32),
+                                      (33, 40, 16384, torch.bfloat16)])
+def test_linear_nvfp4_packed_matches_oracle(M, N, K, dt):
+    a, bt = workloads.gemm_operands(M, N, K, seed_a=11, seed_b=12)
+    x = a.to(dt)
+    xp, xs, xg, f1 = oracle.nv_quantize(oracle_view(x).reshape(-1))
+    bp, bsc, bg, f2 = oracle.nv_quantize(bt.numpy().reshape(-1))
+    assert f1 == 0 and f2 == 0
+    pb = _nv_pack_dev(bp, bsc, N, K, f"nv packed Bt {N}x{K}")
+    t = lambda v: dev(torch.tensor([float(v)], dtype=torch.float32))
+    announce(f"linear nvfp4 packed {M}x{N}x{K} {dt}")
+    c32, (apk, ag) = fp4.linear_nvfp4_packed(dev(x), pb, t(bg), N, torch.float32)
+    c16, _ = fp4.linear_nvfp4_packed(dev(x), pb, t(bg), N, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert np.float32(ag.item()) == np.float32(xg)
+    assert_bytes_equal(host_u8(apk), og.nv_pack_operand(xp, xs, M, K), f"linear nv packed A {M}x{K}")
+    ref = og.nv_gemm_f64(xp, xs, xg, bp, bsc, bg, M, N, K)
+    err = np.linalg.norm(c32.cpu().numpy().astype(np.float64) - ref) / np.linalg.norm(ref)
+    assert err <= REL_FROB, f"linear nvfp4 packed {M}x{N}x{K}: relative Frobenius error {err:.3e}"
+    assert torch.equal(c16.cpu().view(torch.int16), c32.cpu().to(torch.bfloat16).view(torch.int16))
+
+
 # ---- quantize straight into the packed layout, and the packed W4A4 linear ------
 
 @pytest.mark.parametrize("rows,cols,dt", [(1, 512, torch.float32), (70, 2048, torch.bfloat16),
