@@ -93,6 +93,13 @@ def test_sweep(i):
         assert_bytes_equal(host_u8(scales), s, f"{what}: NV scales")
         assert_bytes_equal(host_u8(codes), p, f"{what}: NV codes")
         _dequant_check(fp4.NVFP4, p, s, float(sg), rows, f"{what} NV")
+    if cols % 512 == 0:
+        st = _status()
+        got, s_g = fp4.quantize_nvfp4_packed(xd, check=False, status=st)
+        assert int(st.item()) == f, f"{what}: NV packed flags {int(st.item())} vs oracle {f}"
+        if f == 0:
+            assert f32_bits(s_g.cpu().numpy())[0] == f32_bits([sg])[0], f"{what}: packed s_g"
+            assert_bytes_equal(host_u8(got), og.nv_pack_operand(p, s, rows, cols), f"{what}: NV packed")
     p, s, sg, f = oracle.scale_search(xo)
     st = _status()
     codes, scales, s_g = fp4.scale_search(xd, check=False, status=st)
@@ -145,3 +152,28 @@ def test_sweep_padded(i):
             want = oracle.dequantize_padded(fmt, p, s, rows, cols, sg, out_bf16=bf)
             got = workloads.bf16_bits(y.cpu()).reshape(-1) if bf else y.cpu().numpy().reshape(-1)
             assert_float_bits_equal(got, want, f"{what}: padded decode fmt={fmt} -> {out_dtype}")
+
+
+@pytest.mark.parametrize("i", range(10))
+def test_sweep_packed_layouts(i):
+    """The generated tensors, their rows repeated out to a multiple of 512
+    columns, through both quantizers that write the packed layouts."""
+    x, what = _case(i)
+    rows, cols = x.shape
+    k = max(1, cols // 512)
+    x = x.repeat(1, -(-512 * k // cols))[:, :512 * k].contiguous()
+    cols = x.shape[1]
+    what = f"{what}, repeated to {rows}x{cols}"
+    xd, xo = dev(x), oracle_view(x)
+    announce(f"{what}: quantize into the packed layouts")
+    p, s, f = oracle.mx_quantize(xo)
+    assert f == 0
+    got = fp4.quantize_mxfp4_packed(xd)
+    assert_bytes_equal(host_u8(got), og.pack_operand(p, s, rows, cols), f"{what}: MX packed")
+    p, s, sg, f = oracle.nv_quantize(xo)
+    st = _status()
+    got, s_g = fp4.quantize_nvfp4_packed(xd, check=False, status=st)
+    assert int(st.item()) == f, f"{what}: NV packed flags {int(st.item())} vs oracle {f}"
+    if f == 0:
+        assert f32_bits(s_g.cpu().numpy())[0] == f32_bits([sg])[0], f"{what}: packed s_g"
+        assert_bytes_equal(host_u8(got), og.nv_pack_operand(p, s, rows, cols), f"{what}: NV packed")
