@@ -35,7 +35,7 @@
  * Because every row holds whole blocks, the flat order of elements, codes and
  * scales is the row-major order; the library treats the tensor as flat.  The
  * *_packed entry points use the MFMA operand order instead, described at
- * fp4_pack_mxfp4_operand.
+ * fp4_pack_mxfp4_operand (MXFP4) and fp4_pack_nvfp4_operand (NVFP4).
  *
  * Errors.  Argument errors are returned synchronously, before any HIP call
  * (so they are testable without a GPU).  Data-dependent conditions are found
