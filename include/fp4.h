@@ -135,6 +135,33 @@ fp4_status fp4_quantize_nvfp4(const void *x, fp4_dtype xt, int64_t rows, int64_t
                               int32_t *status, void *stream);
 
 /*
+ * NVFP4 quantize without allocation, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, results, errors and status as
+ * fp4_quantize_nvfp4, minus the workspace: the library uses its own fixed
+ * scratch instead, FP4_NOALLOC_SCRATCH_BYTES bytes per GPU in a static device
+ * array, which stays allocated until the process ends.
+ *   - The scratch need does not grow with the tensor: every shape
+ *     fp4_quantize_nvfp4 accepts fits (a shape that did not would be rejected
+ *     with FP4_E_WORKSPACE).
+ *   - The first call on a device sets the scratch up: it looks up the array's
+ *     device address and zero-fills it with a synchronous hipMemset waited on
+ *     the null stream (FP4_E_HIP if that fails, e.g. when the first call is
+ *     made while a stream is being captured; make one call outside capture
+ *     first).  Later calls make no allocating or synchronising HIP call.
+ *   - Every call on one GPU shares that GPU's scratch and keeps the last
+ *     call's contents there (the grid barrier's epoch).  Calls that overlap
+ *     in time on one GPU (different streams, or different host threads
+ *     without ordering) RACE on it: their results are then unspecified.
+ *     Order them on one stream, or use fp4_quantize_nvfp4 with a workspace
+ *     per stream.
+ */
+#define FP4_NOALLOC_SCRATCH_BYTES 20480u
+fp4_status fp4_quantize_nvfp4_noalloc(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
+                                      int32_t block, uint8_t *codes, uint8_t *scales,
+                                      float *global_scale, int32_t *status, void *stream);
+
+/*
  * Quantize with stochastic element rounding (Ultralytics glossary "FP4",
  * section "Inferenza e addestramento FP4": NVFP4 pretraining rounds
  * gradients stochastically; the pages name the technique, not a rule).

@@ -49,7 +49,7 @@ EXPORTS = ("fp4_quantize_mxfp4", "fp4_quantize_mxfp4_rule", "fp4_quantize_nvfp4"
            "fp4_gemm_mxfp4_packed", "fp4_quantize_mxfp4_packed", "fp4_linear_mxfp4_packed",
            "fp4_nv_packed_operand_bytes", "fp4_pack_nvfp4_operand", "fp4_gemm_nvfp4_packed",
            "fp4_quantize_nvfp4_packed", "fp4_linear_nvfp4_packed",
-           "fp4_workspace_bytes", "fp4_status_str")
+           "fp4_quantize_nvfp4_noalloc", "fp4_workspace_bytes", "fp4_status_str")
 
 # fp4_mx_rule: the MXFP4 block-exponent rules
 MX_RULES = {"ocp": 0, "ceil": 1, "mse": 2}
@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
     L.fp4_quantize_mxfp4_rule.argtypes = [P, I, I64, I64, I32, I, P, P, P, P]
     L.fp4_scale_search_exhaustive.argtypes = [P, I, I64, I64, I32, P, P, P, P, S, P, P]
     L.fp4_quantize_nvfp4.argtypes = [P, I, I64, I64, I32, P, P, P, P, S, P, P]
+    L.fp4_quantize_nvfp4_noalloc.argtypes = [P, I, I64, I64, I32, P, P, P, P, P]
     L.fp4_dequantize.argtypes = [I, P, P, P, I64, I64, I32, P, I, P]
     L.fp4_scale_search.argtypes = [P, I, I64, I64, I32, I32, F, F, P, P, P, P, S, P, P]
     L.fp4_gemm_mxfp4.argtypes = [P, P, P, P, I64, I64, I64, P, I, P]
@@ -108,6 +109,7 @@ def lib() -> ctypes.CDLL:
     L.fp4_status_str.argtypes = [I]
     L.fp4_status_str.restype = ctypes.c_char_p
     for name in ("fp4_quantize_mxfp4", "fp4_quantize_mxfp4_rule", "fp4_quantize_nvfp4",
+                 "fp4_quantize_nvfp4_noalloc",
                  "fp4_dequantize", "fp4_scale_search", "fp4_scale_search_exhaustive",
                  "fp4_gemm_mxfp4", "fp4_gemm_mxfp4_splitk", "fp4_gemm_nvfp4",
                  "fp4_linear_mxfp4", "fp4_quantize_padded", "fp4_dequantize_padded",
@@ -238,6 +240,30 @@ def quantize_nvfp4(x: torch.Tensor, check: bool = True, out=None, status=None, w
     _ok(lib().fp4_quantize_nvfp4(_ptr(x), _dtype_code(x.dtype), rows, cols, 16, _ptr(codes),
                                  _ptr(scales), _ptr(s_g), _ptr(workspace), workspace.numel(),
                                  _ptr(status), _stream(x)))
+    _finish(status, check)
+    return codes, scales, s_g
+
+
+NOALLOC_SCRATCH_BYTES = 20480
+
+
+def quantize_nvfp4_noalloc(x: torch.Tensor, check: bool = True, out=None, status=None):
+    """NVFP4 quantize through the entry point that allocates nothing (its
+    workspace is the library's fixed per-GPU scratch).  Same results as
+    quantize_nvfp4.  Calls that overlap in time on one GPU race on the
+    scratch; keep them on one stream."""
+    rows, cols = _rows_cols(x)
+    if out is None:
+        codes = torch.empty(*x.shape[:-1], cols // 2, dtype=torch.uint8, device=x.device)
+        scales = torch.empty(*x.shape[:-1], max(cols // 16, 1), dtype=torch.uint8, device=x.device)
+        s_g = torch.empty(1, dtype=torch.float32, device=x.device)
+    else:
+        codes, scales, s_g = out
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _ok(lib().fp4_quantize_nvfp4_noalloc(_ptr(x), _dtype_code(x.dtype), rows, cols, 16,
+                                         _ptr(codes), _ptr(scales), _ptr(s_g), _ptr(status),
+                                         _stream(x)))
     _finish(status, check)
     return codes, scales, s_g
 

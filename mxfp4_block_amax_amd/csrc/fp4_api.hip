@@ -3,8 +3,22 @@
 // the caller's stream.  Every argument error is returned before any HIP call.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/fp4.h"
 #include "fp4_kernels.h"
+
+// Device scratch of fp4_quantize_nvfp4_noalloc, for callers that cannot
+// allocate: the same workspace fp4_quantize_nvfp4 takes from its caller
+// (tensor-amax partials, then the grid barrier's epoch word and slots), one
+// copy per GPU, held until the process ends.  Its size does not depend on
+// the tensor.  In host code the name stands for a host-side shadow, never a
+// device address: host code uses the address hipGetSymbolAddress returns.
+static __device__ __align__(256) uint8_t scratch[fp4dev::kNoAllocScratchBytes];
+static_assert(FP4_NOALLOC_SCRATCH_BYTES == fp4dev::kNoAllocScratchBytes,
+              "the header states the scratch size");
+static_assert(fp4dev::kNvWorkspaceBytes <= fp4dev::kNoAllocScratchBytes,
+              "the scratch holds one NVFP4 workspace");
 
 namespace {
 
@@ -25,6 +39,35 @@ fp4_status from_hip(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_E_HIP;
 
 // The NVFP4 and scale-search tensor-amax pass needs this many bytes.
 size_t nv_workspace() { return fp4dev::kNvWorkspaceBytes; }
+
+// Per-device address of `scratch`, looked up and zero-filled once per device
+// (with that device current) on the first no-allocation call there.  The
+// fill is synchronous and waited for on the null stream, so it is complete
+// before any kernel on any stream can use the scratch.
+struct ScratchSlot {
+    std::once_flag once;
+    void *ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[fp4dev::kMaxDevices];
+
+hipError_t device_scratch(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= fp4dev::kMaxDevices) return hipErrorInvalidDevice;
+    ScratchSlot &s = g_scratch[dev];
+    std::call_once(s.once, [&s] {
+        void *p = nullptr;
+        hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (r == hipSuccess) r = hipMemset(p, 0, fp4dev::kNoAllocScratchBytes);
+        if (r == hipSuccess) r = hipStreamSynchronize(nullptr);
+        s.ptr = r == hipSuccess ? p : nullptr;
+        s.err = r;
+    });
+    *out = s.ptr;
+    return s.err;
+}
 
 }  // namespace
 
@@ -74,6 +117,27 @@ fp4_status fp4_quantize_nvfp4(const void *x, fp4_dtype xt, int64_t rows, int64_t
     return from_hip(fp4dev::launch_nv_quantize(x, xt == FP4_BF16, rows * cols, codes, scales,
                                                global_scale, workspace, status,
                                                (hipStream_t)stream));
+}
+
+fp4_status fp4_quantize_nvfp4_noalloc(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
+                                      int32_t block, uint8_t *codes, uint8_t *scales,
+                                      float *global_scale, int32_t *status, void *stream) {
+    if (!x || !codes || !scales || !global_scale) return FP4_E_ARG;
+    if (block != 16) return FP4_E_ARG;
+    if (!valid_dtype(xt)) return FP4_E_DTYPE;
+    fp4_status st = check_shape(rows, cols, block);
+    if (st != FP4_OK) return st;
+    // the scratch holds the whole workspace of any accepted shape; the check
+    // keeps that true if the workspace ever grows with the shape
+    if (fp4_workspace_bytes(FP4_NVFP4, rows, cols) > fp4dev::kNoAllocScratchBytes)
+        return FP4_E_WORKSPACE;
+    if (!aligned(x, 16) || !aligned(codes, 4) || !aligned(global_scale, 4) || !aligned(status, 4))
+        return FP4_E_ALIGN;
+    void *ws = nullptr;
+    hipError_t e = device_scratch(&ws);
+    if (e != hipSuccess) return FP4_E_HIP;
+    return from_hip(fp4dev::launch_nv_quantize(x, xt == FP4_BF16, rows * cols, codes, scales,
+                                               global_scale, ws, status, (hipStream_t)stream));
 }
 
 fp4_status fp4_quantize_sr(fp4_format fmt, const void *x, fp4_dtype xt, int64_t rows,

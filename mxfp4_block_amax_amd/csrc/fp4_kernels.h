@@ -20,6 +20,9 @@ constexpr size_t kResidentEpochOffset = kAmaxPartials * sizeof(uint32_t);
 constexpr size_t kResidentSlotsOffset = kResidentEpochOffset + 256;
 constexpr int kResidentSlots = 1024;
 constexpr size_t kNvWorkspaceBytes = kResidentSlotsOffset + kResidentSlots * sizeof(uint64_t);
+// Size of the fixed device scratch of the no-allocation NVFP4 entry point:
+// one NVFP4 workspace, rounded up to 4 KiB.
+constexpr size_t kNoAllocScratchBytes = (kNvWorkspaceBytes + 4095) / 4096 * 4096;
 // Polls of the one-pass grid barrier before it gives up (about a second).
 constexpr uint32_t kResidentSpinLimit = 1u << 19;
 // The limit launches use: kResidentSpinLimit unless a test of the timeout

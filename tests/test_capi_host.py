@@ -370,3 +370,28 @@ def test_packed_quantize_and_linear_validation():
     assert lin(K=20480) == E_SHAPE
     assert lin(nb=fp4.packed_operand_bytes(128, 2048) - 1) == E_WORKSPACE
     assert lin(a=ctypes.c_void_p(0x10008)) == E_ALIGN
+
+
+def nv_noalloc(x=A16, dt=fp4.BF16, rows=4, cols=64, block=16, codes=A16, scales=A16, sg=A16,
+               status=NULL):
+    return fp4.lib().fp4_quantize_nvfp4_noalloc(x, dt, rows, cols, block, codes, scales, sg,
+                                                status, NULL)
+
+
+def test_nv_noalloc_validation():
+    # every argument error comes back before the scratch is set up (no HIP call)
+    assert nv_noalloc(x=NULL) == E_ARG
+    assert nv_noalloc(sg=NULL) == E_ARG
+    assert nv_noalloc(block=32) == E_ARG
+    assert nv_noalloc(dt=7) == E_DTYPE
+    assert nv_noalloc(cols=17) == E_SHAPE
+    assert nv_noalloc(rows=0) == E_SHAPE
+    assert nv_noalloc(x=A1) == E_ALIGN
+    assert nv_noalloc(sg=ctypes.c_void_p(0x10002)) == E_ALIGN
+
+
+def test_noalloc_scratch_holds_a_workspace():
+    # the fixed scratch is at least the workspace of the largest accepted shape
+    assert fp4.workspace_bytes(fp4.NVFP4, 1 << 20, 1 << 20) <= fp4.NOALLOC_SCRATCH_BYTES
+    src = open(HEADER).read()
+    assert f"#define FP4_NOALLOC_SCRATCH_BYTES {fp4.NOALLOC_SCRATCH_BYTES}u" in src
