@@ -9,7 +9,11 @@
  * and the grid barrier's poll limit, a process-wide setting that only
  * fp4_debug_barrier_spin_limit changes.
  * Calls on different streams may run concurrently unless they share a
- * workspace.  All work is
+ * workspace (or, for fp4_quantize_nvfp4_noalloc, a GPU).  The one-pass NVFP4
+ * quantize and the one-launch W4A4 linear meet at a grid barrier that does
+ * not need their workgroups to be resident together: a workgroup that waits
+ * too long (another kernel holding CUs) finishes by a fallback with the same
+ * result, so concurrent calls give the same outputs, only slower.  All work is
  * enqueued asynchronously on `stream` (a hipStream_t passed as void*; NULL is
  * the null stream).
  *
@@ -40,8 +44,9 @@
  * Errors.  Argument errors are returned synchronously, before any HIP call
  * (so they are testable without a GPU).  Data-dependent conditions are found
  * on the device and OR-ed into *status (a device int32 the caller zeroes
- * beforehand; may be NULL to ignore them) as FP4_FLAG_* bits; when a flag is
- * set the outputs are unspecified.
+ * beforehand; may be NULL to ignore them) as FP4_FLAG_* bits; when
+ * FP4_FLAG_NONFINITE or FP4_FLAG_SCALE_UNDERFLOW is set the outputs are
+ * unspecified (FP4_FLAG_BARRIER_TIMEOUT is information only).
  */
 #ifndef FP4_H
 #define FP4_H
@@ -67,7 +72,9 @@ typedef enum {
 /* Device-side condition flags OR-ed into *status. */
 #define FP4_FLAG_NONFINITE 1       /* an input element is NaN or +-Inf          */
 #define FP4_FLAG_SCALE_UNDERFLOW 2 /* tensor scale, block scale or alpha is 0   */
-#define FP4_FLAG_BARRIER_TIMEOUT 4 /* one-pass NVFP4: the grid barrier gave up   */
+#define FP4_FLAG_BARRIER_TIMEOUT 4 /* information, not an error: a grid-barrier
+                                      wait timed out and some workgroup took the
+                                      fallback; the outputs are exact            */
 
 typedef enum { FP4_F32 = 0, FP4_BF16 = 1 } fp4_dtype;
 typedef enum { FP4_MXFP4 = 0, FP4_NVFP4 = 1 } fp4_format;
@@ -121,7 +128,7 @@ fp4_status fp4_quantize_mxfp4_rule(const void *x, fp4_dtype xt, int64_t rows, in
  *                 (one stream, or synchronised); the same workspace may serve
  *                 fp4_scale_search too.
  *   status        FP4_FLAG_NONFINITE, FP4_FLAG_SCALE_UNDERFLOW,
- *                 FP4_FLAG_BARRIER_TIMEOUT (then zero the workspace again)
+ *                 FP4_FLAG_BARRIER_TIMEOUT (information only: outputs exact)
  * s_g needs the amax of the whole tensor.  A bf16 tensor that fits on chip
  * (one 512 KiB slice per CU: 8192 x 8192 on 256 CUs) is read from HBM once
  * by a single kernel whose workgroups, one per CU, meet at a grid barrier
@@ -462,8 +469,8 @@ fp4_status fp4_linear_nvfp4_packed(const void *x, fp4_dtype xt, int64_t M, int64
  *   workspace  as for fp4_quantize_nvfp4 (fp4_workspace_bytes(FP4_NVFP4, M, K)
  *              bytes, zero-filled before its first use, then left to the
  *              library; calls sharing it must be stream-ordered)
- *   status     FP4_FLAG_NONFINITE (x), FP4_FLAG_BARRIER_TIMEOUT (then zero
- *              the workspace again)
+ *   status     FP4_FLAG_NONFINITE (x), FP4_FLAG_BARRIER_TIMEOUT (information
+ *              only: the outputs are exact)
  *   mode       FP4_LINEAR_ONE_LAUNCH: when the GEMM's grid (ceil(N/32) *
  *              ceil(M/128) workgroups) fits on the device at once and K is a
  *              multiple of 512 up to 8192, one kernel quantizes x (each
@@ -511,16 +518,16 @@ fp4_status fp4_dequantize_padded(fp4_format fmt, const uint8_t *codes, const uin
 int64_t fp4_padded_storage_bytes(fp4_format fmt, int64_t rows, int64_t cols);
 
 /*
- * For tests of the failure path of the grid barrier (the one-pass NVFP4
- * quantize and the one-launch W4A4 linear): sets how many times a workgroup
- * polls the other workgroups' slots before it gives up and raises
- * FP4_FLAG_BARRIER_TIMEOUT (0 = after the first poll), for launches enqueued
- * from then on, process-wide; returns the previous value.  The default is
- * FP4_BARRIER_SPIN_LIMIT_DEFAULT polls (about a second).  Every kernel exits
- * normally whatever the value; after a timeout the workspace must be zeroed
- * again.
+ * For tests of the grid barrier's fallback (the one-pass NVFP4 quantize and
+ * the one-launch W4A4 linear): sets how many times a workgroup polls the
+ * other workgroups' slots before it stops waiting, takes the fallback and
+ * raises FP4_FLAG_BARRIER_TIMEOUT (0 = after the first poll), for launches
+ * enqueued from then on, process-wide; returns the previous value.  The
+ * default is FP4_BARRIER_SPIN_LIMIT_DEFAULT polls (a few milliseconds, far
+ * above the barrier's usual microseconds).  Results are exact whatever the
+ * value; only the time changes.
  */
-#define FP4_BARRIER_SPIN_LIMIT_DEFAULT 524288u
+#define FP4_BARRIER_SPIN_LIMIT_DEFAULT 2048u
 uint32_t fp4_debug_barrier_spin_limit(uint32_t polls);
 
 /* Bytes of device workspace fp4_quantize_nvfp4 / fp4_scale_search need for a

@@ -160,9 +160,8 @@ def _raise_flags(flags: int):
         raise ValueError("finite input required (NaN or Inf found)")
     if flags & FLAG_SCALE_UNDERFLOW:
         raise ValueError("a nonzero scale rounded to zero (tensor, block scale or alpha underflow)")
-    if flags & FLAG_BARRIER_TIMEOUT:
-        raise Fp4Error("a grid barrier timed out (one-pass NVFP4 quantize or one-launch linear); "
-                       "re-zero the workspace")
+    # FLAG_BARRIER_TIMEOUT is information only: a workgroup took the grid
+    # barrier's fallback and the outputs are exact
 
 
 def _finish(status: torch.Tensor, check: bool):
@@ -170,7 +169,7 @@ def _finish(status: torch.Tensor, check: bool):
         _raise_flags(int(status.item()))
 
 
-BARRIER_SPIN_LIMIT_DEFAULT = 524288
+BARRIER_SPIN_LIMIT_DEFAULT = 2048
 
 
 def debug_barrier_spin_limit(polls: int) -> int:

@@ -423,51 +423,80 @@ __device__ __forceinline__ void report_flags(int32_t *status, uint32_t flags) {
 }
 
 // ---- grid barrier ----------------------------------------------------------
-// For kernels whose whole grid is resident at once (at most one workgroup
-// per CU, no more workgroups than CUs).  The workspace keeps an epoch word
-// and one 64-bit slot per workgroup, zeroed before the first call and left
-// alone between calls.  Each call tags its slots with epoch + 1 (never 0),
-// read by every workgroup before any can pass the barrier; workgroup 0
-// stores the new epoch once it has passed, for the next call in stream order.
+// For kernels whose workgroups are normally all resident at once (at most one
+// workgroup per CU, no more workgroups than CUs), but correct when they are
+// not (another kernel holding CUs, e.g. a concurrent call on another stream):
+// a workgroup that does not see the barrier complete within a bounded wait
+// goes on without it, by a fallback that gives the same result (reading the
+// missing workgroups' inputs itself), so nothing ever waits on a workgroup
+// that cannot start.
+//
+// The workspace keeps an epoch word and one 64-bit slot (tag << 32 | value)
+// per workgroup, zeroed before the first call and left alone between calls.
+// A call's workgroups read the epoch when they start and tag their slots with
+// epoch + 1 (never 0).  Rules:
+//   complete  (every slot carried the tag) workgroup 0 stores epoch = tag;
+//   timed out the workgroup stores epoch = tag, takes the fallback, and at
+//             its end retracts its slot (stores 0).
+// Invariant at the start of every call: no slot carries epoch + 1.  If some
+// workgroup saw the barrier complete, every workgroup had read the same epoch
+// E before any store to it, all tags were E + 1 and every store writes E + 1,
+// so the surviving slots carry the epoch itself.  If none did, every
+// workgroup timed out and retracted its slot.  So a slot only ever matches a
+// tag when it was written in the same call, with that call's value; a
+// workgroup that starts after a timed-out one advanced the epoch takes a tag
+// nobody else has, times out too and takes the fallback.
 __device__ __forceinline__ uint32_t barrier_tag(const uint32_t *epoch) {
     const uint32_t e = __hip_atomic_load(epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return e + 1u == 0u ? 1u : e + 1u;
 }
 
-// Called by one whole wave of every workgroup: publishes (tag, value) in
-// this workgroup's slot and polls until every slot of the grid carries the
-// tag; returns the largest value.  A bounded wait: after spin_limit polls it
-// sets FLAG_BARRIER_TIMEOUT in flags and returns what it has, never less than
-// its own value (so a workgroup's own amax stays within the scale it uses).
-__device__ __forceinline__ uint32_t grid_barrier_max(uint64_t *slots, uint32_t *epoch, uint32_t tag,
-                                                     uint32_t value, uint32_t spin_limit,
-                                                     uint32_t &flags) {
+__device__ __forceinline__ void barrier_store_epoch(uint32_t *epoch, uint32_t tag) {
+    __hip_atomic_store(epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void barrier_retract(uint64_t *slots) {
+    __hip_atomic_store(&slots[blockIdx.y * gridDim.x + blockIdx.x], (uint64_t)0, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool barrier_slot_tagged(const uint64_t *slots, int i, uint32_t tag,
+                                                    uint32_t &value) {
+    const uint64_t sl = __hip_atomic_load(&slots[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    value = (uint32_t)sl;
+    return (uint32_t)(sl >> 32) == tag;
+}
+
+// Called by one whole wave of every workgroup: publishes (tag, value) in this
+// workgroup's slot and polls, at most spin_limit + 1 times, until every slot
+// of the grid carries the tag.  Returns whether it did; A is the largest
+// value among the tagged slots (and this workgroup's own), which is every
+// workgroup's when it returns true.  Stores no epoch: the caller follows the
+// rules above.
+__device__ __forceinline__ bool grid_barrier_max(uint64_t *slots, uint32_t tag, uint32_t value,
+                                                 uint32_t spin_limit, uint32_t &A) {
     const int lane = threadIdx.x & (WAVE - 1);
     const int G = gridDim.x * gridDim.y;
     const int wg = blockIdx.y * gridDim.x + blockIdx.x;
     if (lane == 0)
         __hip_atomic_store(&slots[wg], ((uint64_t)tag << 32) | value, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-    uint32_t A = 0;
     for (uint32_t it = 0;; ++it) {
         bool ok = true;
         uint32_t mm = 0;
         for (int i = lane; i < G; i += WAVE) {
-            const uint64_t sl = __hip_atomic_load(&slots[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            ok = ok && (uint32_t)(sl >> 32) == tag;
-            mm = max(mm, (uint32_t)sl);
+            uint32_t v;
+            const bool t = barrier_slot_tagged(slots, i, tag, v);
+            ok = ok && t;
+            mm = t ? max(mm, v) : mm;
         }
         const bool all = __ballot(!ok) == 0;
         if (all || it >= spin_limit) {
-            if (!all) flags |= FLAG_BARRIER_TIMEOUT;
             A = max(wave_max_u32(mm), value);
-            break;
+            return all;
         }
         __builtin_amdgcn_s_sleep(2);
     }
-    if (lane == 0 && wg == 0)
-        __hip_atomic_store(epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return A;
 }
 
 }  // namespace fp4dev

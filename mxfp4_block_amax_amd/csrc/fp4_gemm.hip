@@ -1157,14 +1157,14 @@ __global__ __launch_bounds__(GEMM_WG) void nvfp4_gemm_simple_kernel(
 // a_scales are outputs too), the grid meets at a barrier, and the tiles then
 // read A as the plain GEMM does.  The grid must be resident at once.
 // ---------------------------------------------------------------------------
+// MXFP4 quantize of the wave tiles wave, wave + nwaves, ... of A: a share of
+// the grid's (the fused path) or all of A by one workgroup (its fallback).
 template <bool XBF16>
 __device__ __forceinline__ uint32_t quantize_share(const uint4 *__restrict__ x, int64_t nchunks,
                                                    uint32_t *__restrict__ a_codes,
-                                                   uint8_t *__restrict__ a_scales) {
+                                                   uint8_t *__restrict__ a_scales, int64_t wave,
+                                                   int64_t nwaves) {
     const int lane = threadIdx.x & (WAVE - 1);
-    constexpr int WPG = GEMM_WG / WAVE;
-    const int64_t wave = (int64_t)(blockIdx.y * gridDim.x + blockIdx.x) * WPG + threadIdx.x / WAVE;
-    const int64_t nwaves = (int64_t)gridDim.x * gridDim.y * WPG;
     uint32_t flags = 0;
     // a wave takes 64 consecutive chunks of 8 values; four lanes hold a block
     for (int64_t t = wave; t * WAVE < nchunks; t += nwaves) {
@@ -1202,8 +1202,12 @@ __global__ __launch_bounds__(GEMM_WG) void mxfp4_linear_kernel(
     void *__restrict__ C, uint64_t *slots, uint32_t *epoch, uint32_t spin_limit,
     int32_t *status) {
     const int wv = threadIdx.x / WAVE;
+    constexpr int WPG = GEMM_WG / WAVE;
+    const int64_t nchunks = (int64_t)M * K / 8;
     const uint32_t tag = wv == 0 ? barrier_tag(epoch) : 0u;
-    uint32_t flags = quantize_share<XBF16>(x, (int64_t)M * K / 8, a_codes, a_scales);
+    uint32_t flags = quantize_share<XBF16>(x, nchunks, a_codes, a_scales,
+                                           (int64_t)(blockIdx.y * gridDim.x + blockIdx.x) * WPG + wv,
+                                           (int64_t)gridDim.x * gridDim.y * WPG);
     // Every wave's stores of its share have completed at the workgroup
     // barrier; then one wave makes them visible to the device (the release
     // writes back this XCD's L2) before it publishes its slot, and after the
@@ -1211,14 +1215,36 @@ __global__ __launch_bounds__(GEMM_WG) void mxfp4_linear_kernel(
     // invalidates the caches) before any wave reads A.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    __shared__ uint32_t late_tag;
     if (wv == 0) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        grid_barrier_max(slots, epoch, tag, 0u, spin_limit, flags);
+        uint32_t A;
+        const bool done = grid_barrier_max(slots, tag, 0u, spin_limit, A);
+        if ((threadIdx.x & (WAVE - 1)) == 0) {
+            late_tag = done ? 0u : tag;
+            if (!done || (blockIdx.x == 0 && blockIdx.y == 0)) barrier_store_epoch(epoch, tag);
+        }
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
+    const bool late = late_tag != 0u;
+    if (late) {
+        // Fallback: the wait timed out, so other shares of A may not be
+        // written yet.  This workgroup quantizes all of A itself; where
+        // another workgroup writes the same bytes it writes the same values.
+        flags |= quantize_share<XBF16>(x, nchunks, a_codes, a_scales, wv, WPG);
+        flags |= FLAG_BARRIER_TIMEOUT;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (wv == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
+        __syncthreads();
+    }
     report_flags(status, flags);
     gemm_lds_tile<OUT_BF16>((const uint4 *)a_codes, a_scales, Bt, Bs, M, N, K, C);
+    if (late && threadIdx.x == 0) barrier_retract(slots);
 }
 
 // Workgroups one CU holds of the linear kernel's largest instance (its LDS

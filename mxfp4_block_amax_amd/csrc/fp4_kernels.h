@@ -23,8 +23,9 @@ constexpr size_t kNvWorkspaceBytes = kResidentSlotsOffset + kResidentSlots * siz
 // Size of the fixed device scratch of the no-allocation NVFP4 entry point:
 // one NVFP4 workspace, rounded up to 4 KiB.
 constexpr size_t kNoAllocScratchBytes = (kNvWorkspaceBytes + 4095) / 4096 * 4096;
-// Polls of the one-pass grid barrier before it gives up (about a second).
-constexpr uint32_t kResidentSpinLimit = 1u << 19;
+// Polls of the grid barrier before a workgroup takes the fallback (a few
+// milliseconds; a poll takes a microsecond or two).
+constexpr uint32_t kResidentSpinLimit = 2048;
 // The limit launches use: kResidentSpinLimit unless a test of the timeout
 // path has set another (fp4_debug_barrier_spin_limit).
 uint32_t barrier_spin_limit();

@@ -591,16 +591,15 @@ __global__ __launch_bounds__(WG) void nv_quantize_kernel(const uint4 *__restrict
 // Loads past the end of the tensor re-read its last chunk (a duplicate
 // cannot change the amax); stores past it are skipped.
 //
-// Grid barrier.  Each workgroup publishes (tag << 32 | partial amax) in its
-// own 64-bit slot with one device-coherent store, then polls every slot with
-// device-coherent loads until all carry the tag.  The tag is one more than
-// the epoch word in the workspace; every workgroup reads the epoch before it
-// publishes, and workgroup 0 advances it only after the barrier, so the next
-// call (stream-ordered) uses a new tag and stale slots never match.  The
+// Grid barrier (grid_barrier_max).  Each workgroup publishes (tag << 32 |
+// partial amax) in its own 64-bit slot with one device-coherent store, then
+// polls every slot with device-coherent loads until all carry the tag.  The
 // launcher starts this kernel only when one workgroup per CU fits and the
-// grid is at most the CU count, so all workgroups are resident together; the
-// wait is still bounded: past spin_limit polls a workgroup raises
-// FLAG_BARRIER_TIMEOUT and goes on.
+// grid is at most the CU count, so the workgroups are normally resident
+// together.  When they are not (a concurrent kernel holds CUs), a workgroup
+// stops waiting after spin_limit polls and takes the tensor amax itself: the
+// tagged slots' values plus the amax of every other slice, read from x.  The
+// result is the same; FLAG_BARRIER_TIMEOUT records that it happened.
 // ---------------------------------------------------------------------------
 // Block scales of a tile of two chunk rows held by a lane pair: the even
 // lane derives row 0's scale, the odd lane row 1's (one table read each),
@@ -743,6 +742,7 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
         NvGuessTable R;
         uint32_t red[RES_WAVES];
         uint32_t tensor_amax;
+        uint32_t late_tag;
         uint4 data[LC * RES_WG];
     };
     __shared__ Shared sh;
@@ -787,14 +787,50 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
     if (wv == 0) {
         uint32_t wm = lane < RES_WAVES ? red[lane] : 0u;
         wm = wave_max_u32(wm);
-        const uint32_t A = grid_barrier_max(slots, epoch, tag, wm, spin_limit, flags);
-        if (lane == 0) tensor_amax = A;
+        uint32_t A;
+        const bool done = grid_barrier_max(slots, tag, wm, spin_limit, A);
+        if (lane == 0) {
+            tensor_amax = A;
+            sh.late_tag = done ? 0u : tag;
+            if (!done || blockIdx.x == 0) barrier_store_epoch(epoch, tag);
+        }
     }
     __syncthreads();
+    const uint32_t late = sh.late_tag;  // uniform: the tag, when the wait timed out
+    if (late) {
+        // Fallback: the tensor amax without the barrier.  A slot carrying the
+        // tag holds its slice's amax from this call; every other slice is read
+        // here from x (the same chunks its workgroup loads).
+        uint32_t mf = 0;
+        for (int w = wv; w < (int)gridDim.x; w += RES_WAVES) {
+            uint32_t sv;
+            const bool tagged = barrier_slot_tagged(slots, w, late, sv);
+            if (__builtin_amdgcn_readfirstlane((int)tagged)) {
+                mf = max(mf, (uint32_t)__builtin_amdgcn_readfirstlane((int)sv));
+                continue;
+            }
+            for (int j = 0; j < CPL; ++j)
+                for (int t = lane; t < RES_WG; t += WAVE) {
+                    const int c = j * stride + w * RES_WG + t;
+                    if (c < nchunks) mf = max(mf, amax_bf16x8(ld_stream(x + c)));
+                }
+        }
+        mf = wave_max_u32(mf);
+        if (lane == 0) red[wv] = mf;  // wave 0 read red before the barrier above
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t a = tensor_amax;
+            for (int i = 0; i < RES_WAVES; ++i) a = max(a, red[i]);
+            tensor_amax = a;
+        }
+        __syncthreads();
+        flags |= FLAG_BARRIER_TIMEOUT;
+    }
     const TensorScale ts = scale_from_amax(tensor_amax << 16);
     if (blockIdx.x == 0 && tid == 0) *global_scale = ts.s_g;
     if (ts.flags) {  // uniform over the grid: outputs unspecified
         if (blockIdx.x == 0 && tid == 0 && status) atomicOr(status, (int32_t)ts.flags);
+        if (late && tid == 0) barrier_retract(slots);
         report_flags(status, flags);
         return;
     }
@@ -892,6 +928,7 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
         }
     }
     flags |= ymin == 0.0f ? FLAG_SCALE_UNDERFLOW : 0u;
+    if (late && tid == 0) barrier_retract(slots);
     report_flags(status, flags);
 }
 
