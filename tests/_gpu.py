@@ -1,6 +1,8 @@
 """Helpers for the GPU parity tests: move seeded inputs to the device, hand
 the same bytes to the oracle, and announce each case before its GPU step."""
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -57,3 +59,22 @@ def assert_float_bits_equal(got: np.ndarray, want: np.ndarray, what: str):
         g, w = f32_bits(g), f32_bits(w)
     assert np.array_equal(gn, wn), f"{what}: NaN positions differ"
     assert_bytes_equal(np.where(gn, 0, g), np.where(wn, 0, w), what)
+
+
+def oracle_threads() -> int:
+    """Host threads for splitting an oracle call (at most 16: the GPU host's
+    CPU share)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def oracle_split(fn, x: np.ndarray, unit: int, nparts: int = None):
+    """fn over contiguous slices of the flat array x, each a multiple of
+    `unit` elements (whole blocks), run on host threads (the oracle's C calls
+    release the GIL); returns the per-slice results in order."""
+    n = x.size
+    assert n % unit == 0
+    nparts = nparts or 4 * oracle_threads()
+    per = max(1, (n // unit + nparts - 1) // nparts) * unit
+    parts = [x[i:i + per] for i in range(0, n, per)]
+    with ThreadPoolExecutor(oracle_threads()) as pool:
+        return list(pool.map(fn, parts))

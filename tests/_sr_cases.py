@@ -69,20 +69,36 @@ def threshold_blocks(block: int, nblocks: int, seed: int, offset: int = 0):
     return x, want
 
 
+# Failure probability allowed to each statistical check below.
+STAT_DELTA = 1e-9
+
+
+def bernstein_halfwidth(var: np.ndarray, bound: np.ndarray, delta: float = STAT_DELTA):
+    """Half-width t of Bernstein's inequality for a sum of independent,
+    zero-mean terms each bounded by `bound` in magnitude, with total variance
+    `var`: P(|sum| >= t) <= 2 exp(-t^2 / (2 (var + bound t / 3))) = delta.
+    Unlike a k-sigma rule it holds for every distribution of the terms, in
+    particular for the skewed two-point draws of a rounding probability near 0
+    or 1."""
+    L = np.log(2.0 / delta)
+    a = bound * L / 3.0
+    return a + np.sqrt(a * a + 2.0 * L * var)
+
+
 def mean_within_bounds(x: np.ndarray, lo: np.ndarray, hi: np.ndarray, mean: np.ndarray, n: int):
-    """Whether the mean of n two-point draws (lo or hi, up with probability
-    (x - lo) / (hi - lo)) is consistent with its expectation: x, clamped to
-    the saturation value where lo = hi; every element within 6 standard
-    errors plus 2 (hi - lo) / n (the draws are discrete), and the summed
-    deviation within 6 of its standard error."""
+    """Whether the mean of n independent two-point draws (lo or hi, up with
+    probability p = (x - lo) / (hi - lo)) is consistent with its expectation
+    x (x clamped to the saturation value where lo = hi): every element, and
+    the sum over elements, within Bernstein's bound at failure probability
+    STAT_DELTA.  Per element the mean is a sum of n terms bounded by
+    (hi - lo) / n with variance (hi - lo)^2 p (1 - p) / n."""
     x = np.where(lo == hi, lo, x)  # saturated: the draw is always +-6 scale
     gap = np.abs(hi - lo)
     p = np.where(gap > 0, np.abs(x - lo) / np.where(gap > 0, gap, 1), 0.0)
-    se = gap * np.sqrt(p * (1 - p) / n)
+    var = gap * gap * p * (1 - p) / n
     dev = mean - x
-    ok_each = bool(np.all(np.abs(dev) <= 6 * se + 2 * gap / n + 1e-12))
-    tot = np.sqrt(np.sum(se * se))
-    ok_sum = bool(abs(dev.sum()) <= 6 * tot + 1e-12)
+    ok_each = bool(np.all(np.abs(dev) <= bernstein_halfwidth(var, gap / n) + 1e-12))
+    ok_sum = bool(abs(dev.sum()) <= bernstein_halfwidth(var.sum(), gap.max() / n) + 1e-12)
     return ok_each and ok_sum
 
 

@@ -8,7 +8,7 @@ import mxfp4_block_amax_amd as fp4
 import oracle
 import workloads
 from tests._gpu import (announce, assert_bytes_equal, assert_float_bits_equal, dev, f32_bits,
-                        host_u8, oracle_view)
+                        host_u8, oracle_split, oracle_view)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,6 +37,9 @@ def test_dequant_roundtrips_of_the_workloads():
     w = workloads.nvfp4_weight()
     p, s, sg, f = oracle.nv_quantize(oracle_view(w))
     _dq_check(fp4.NVFP4, p, s, float(sg), 8192, "weight 8192x8192 NV")
+    p, s, f = oracle.mx_quantize(oracle_view(w))
+    assert f == 0
+    _dq_check(fp4.MXFP4, p, s, 1.0, 8192, "weight 8192x8192 MX")
 
 
 def test_dequant_every_code_and_scale_byte():
@@ -53,7 +56,7 @@ def test_dequant_every_code_and_scale_byte():
         _dq_check(fp4.NVFP4, codes, s_nv, sg, 64, f"all codes x E4M3, s_g={sg}")
 
 
-def _search_check(x: torch.Tensor, what: str, ncand=64, c_lo=0.5, c_hi=1.0, sample=None):
+def _search_check(x: torch.Tensor, what: str, ncand=64, c_lo=0.5, c_hi=1.0):
     announce(f"scale search {what} {tuple(x.shape)} n={ncand} c=[{c_lo},{c_hi}]")
     codes, scales, sg = fp4.scale_search(dev(x), ncand, c_lo, c_hi)
     torch.cuda.synchronize()
@@ -61,19 +64,11 @@ def _search_check(x: torch.Tensor, what: str, ncand=64, c_lo=0.5, c_hi=1.0, samp
     s_g, f1 = oracle.nv_global_scale(xo)
     assert f1 == 0
     assert f32_bits(sg.cpu().numpy())[0] == f32_bits([s_g])[0]
-    gc, gs = host_u8(codes), host_u8(scales)
-    if sample is None:
-        p, s, f2 = oracle.scale_search_with_scale(xo, s_g, ncand, c_lo, c_hi)
-        assert f2 == 0
-        assert_bytes_equal(gs, s, f"{what}: scales")
-        assert_bytes_equal(gc, p, f"{what}: codes")
-    else:
-        blocks = np.asarray(sample)
-        xb = xo.reshape(-1, 16)[blocks].reshape(-1)
-        p, s, f2 = oracle.scale_search_with_scale(xb, s_g, ncand, c_lo, c_hi)
-        assert f2 == 0
-        assert_bytes_equal(gs[blocks], s, f"{what}: sampled scales")
-        assert_bytes_equal(gc.reshape(-1, 8)[blocks].reshape(-1), p, f"{what}: sampled codes")
+    res = oracle_split(lambda part: oracle.scale_search_with_scale(part, s_g, ncand, c_lo, c_hi),
+                       xo, 16)
+    assert all(r[2] == 0 for r in res)
+    assert_bytes_equal(host_u8(scales), np.concatenate([r[1] for r in res]), f"{what}: scales")
+    assert_bytes_equal(host_u8(codes), np.concatenate([r[0] for r in res]), f"{what}: codes")
 
 
 def test_search_counterexample_and_wide_range():
@@ -93,11 +88,8 @@ def test_search_small_laplace_full_compare():
     _search_check((y * 2.0 ** -120).to(torch.float32), "tiny magnitudes 2^-120")
 
 
-def test_search_full_size_sampled():
-    x = workloads.scale_search_input()
-    nblocks = x.numel() // 16
-    rng = np.random.default_rng(0)
-    sample = np.unique(np.concatenate([np.arange(0, 1792),                       # first two rows
-                                       rng.integers(0, nblocks, 20000),
-                                       np.arange(nblocks - 896, nblocks)]))     # last row
-    _search_check(x, "laplace 4096x14336 (sampled blocks)", sample=sample)
+def test_search_full_size_every_block():
+    # the 4096 x 14336 Laplace(0, 0.01) search input, 64 candidates in
+    # [0.5, 1]: every one of its 3.67M blocks against the oracle (the oracle
+    # split over host threads)
+    _search_check(workloads.scale_search_input(), "laplace 4096x14336 (every block)")

@@ -10,7 +10,8 @@ import torch
 import mxfp4_block_amax_amd as fp4
 import oracle
 import workloads
-from tests._gpu import announce, assert_bytes_equal, dev, f32_bits, host_u8, oracle_view
+from tests._gpu import (announce, assert_bytes_equal, dev, f32_bits, host_u8, oracle_split,
+                        oracle_view)
 from tests.test_gpu_dequant_search import _search_check
 from tests.test_gpu_quantize import _mx_fp32_midpoint_tensor, _mx_sweep_tensor
 
@@ -82,18 +83,14 @@ def test_search_range_to_1_5_small_full_compare():
     assert float(sg) == 1.0 and int(scales[0, 0]) == 0x38   # the max maps to 4
 
 
-def test_search_range_to_1_5_full_size_sampled():
-    x = workloads.scale_search_input()
-    nblocks = x.numel() // 16
-    rng = np.random.default_rng(1)
-    sample = np.unique(np.concatenate([np.arange(0, 1792), rng.integers(0, nblocks, 20000),
-                                       np.arange(nblocks - 896, nblocks)]))
-    _search_check(x, "laplace 4096x14336 c=[0.5,1.5] (sampled blocks)", c_hi=1.5, sample=sample)
+def test_search_range_to_1_5_full_size_every_block():
+    _search_check(workloads.scale_search_input(), "laplace 4096x14336 c=[0.5,1.5] (every block)",
+                  c_hi=1.5)
 
 
 # ---- brute force over every E4M3 code -----------------------------------------
 
-def check_search_all(x: torch.Tensor, what: str, sample=None):
+def check_search_all(x: torch.Tensor, what: str):
     announce(f"exhaustive scale search {what} {tuple(x.shape)} {x.dtype}")
     codes, scales, sg = fp4.scale_search_exhaustive(dev(x))
     torch.cuda.synchronize()
@@ -101,18 +98,10 @@ def check_search_all(x: torch.Tensor, what: str, sample=None):
     s_g, f1 = oracle.nv_global_scale(xo)
     assert f1 == 0
     assert f32_bits(sg.cpu().numpy())[0] == f32_bits([s_g])[0]
-    gc, gs = host_u8(codes), host_u8(scales)
-    if sample is None:
-        p, s, f2 = oracle.scale_search_all_with_scale(xo, s_g)
-        assert f2 == 0
-        assert_bytes_equal(gs, s, f"{what}: scales")
-        assert_bytes_equal(gc, p, f"{what}: codes")
-    else:
-        blocks = np.asarray(sample)
-        p, s, f2 = oracle.scale_search_all_with_scale(xo.reshape(-1, 16)[blocks].reshape(-1), s_g)
-        assert f2 == 0
-        assert_bytes_equal(gs[blocks], s, f"{what}: sampled scales")
-        assert_bytes_equal(gc.reshape(-1, 8)[blocks].reshape(-1), p, f"{what}: sampled codes")
+    res = oracle_split(lambda part: oracle.scale_search_all_with_scale(part, s_g), xo, 16)
+    assert all(r[2] == 0 for r in res)
+    assert_bytes_equal(host_u8(scales), np.concatenate([r[1] for r in res]), f"{what}: scales")
+    assert_bytes_equal(host_u8(codes), np.concatenate([r[0] for r in res]), f"{what}: codes")
 
 
 def test_exhaustive_search_page_block():
@@ -135,13 +124,8 @@ def test_exhaustive_search_laplace_and_heavy_tails():
     check_search_all(z.to(torch.bfloat16), "zero blocks bf16")
 
 
-def test_exhaustive_search_full_size_sampled():
-    x = workloads.scale_search_input()
-    nblocks = x.numel() // 16
-    rng = np.random.default_rng(2)
-    sample = np.unique(np.concatenate([np.arange(0, 896), rng.integers(0, nblocks, 4000),
-                                       np.arange(nblocks - 896, nblocks)]))
-    check_search_all(x, "laplace 4096x14336 (sampled blocks)", sample=sample)
+def test_exhaustive_search_full_size_every_block():
+    check_search_all(workloads.scale_search_input(), "laplace 4096x14336 (every block)")
 
 
 def test_search_exact_loss_ties_go_to_the_smaller_code():
