@@ -3,36 +3,36 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--no-extra] [--calibrate-copy]
 
-A step is one pass of the whole quantize/dequantize path over the
-8192 x 8192 bf16 tensor ~ N(0, 0.02^2) (seed 0):
-    NVFP4 quantize (tensor-amax kernel + quantize kernel),
-    NVFP4 dequantize -> bf16,
-    MXFP4 quantize, MXFP4 dequantize -> bf16.
-The step is captured once as a HIP graph and replayed K times between two
-HIP events (the timed region).  NVFP4 works on one copy of the input and
-MXFP4 on another, so between two reads of the same input ~500 MB of other
-traffic passes through the 256 MB MALL; nothing is flushed.  Inputs are
-resident in HBM before timing.
+Headline (`value`): NVFP4 quantize of the 8192 x 8192 bf16 tensor
+~ N(0, 0.02^2) (seed 0), the binding format of the metric.  A step is one
+call of fp4_quantize_nvfp4 on that tensor (one-pass kernel: tensor amax,
+grid barrier, block scales, divide, E2M1 rounding, packing).  W warmup
+steps, then EXACTLY K steps captured as one HIP graph of K launches and
+replayed once between two HIP events; the launches cycle through three
+copies of input and outputs (each evicted from the 256 MB MALL before it is
+reused), and inputs are resident in HBM before timing.
+value = algorithmic bytes per step / time per step, in GB/s.
 
-Per-op rows (`breakdown`) time each entry point over a graph of 24
-back-to-back launches cycling through three buffer sets (each set is evicted
-from the MALL before it is reused), so they match the profiler's kernel
-durations.
-
-value = algorithmic bytes of the four ops per step / step time (GB/s).
 Algorithmic bytes count every input byte once and every output byte once:
-  quantize: 2 B per bf16 element in, 1/2 B codes + 1 B per block scale out
-            (+ 4 B tensor scale for NVFP4); dequantize: the mirror.
-The NVFP4 tensor-amax pass re-reads the input; that is implementation cost,
-not algorithmic bytes.
+  quantize: 2 B per bf16 element in (4 B fp32), 1/2 B codes + 1 B per block
+            scale out (+ 4 B tensor scale for NVFP4); dequantize: the mirror.
 
-One JSON line on stdout.  `roofline` is for the op with the largest launch
-time in the breakdown, timed with HIP events on the stream it runs on (for
-NVFP4 quantize that launch is the entry point's two kernels).
-`cpu_baseline` is the CPU oracle (single thread) on one full step of the same
-input.  `extra` reports the other workloads measured in the same run: MXFP4
-quantize of the 16384 x 7168 activation, the 4096 x 14336 NVFP4 scale
-search, and the 128 x 8192 x 8192 MXFP4 GEMM.
+`formats` puts MXFP4 quantize of the same tensor beside NVFP4, timed the same
+way.  `breakdown` has the per-op rows of the quantize/dequantize round trip
+(both formats) and the round-trip step as a whole.  Before any timing, the
+timed buffers' codes, scale bytes and s_g are checked against the oracle's
+SHA-256 digests (tests/golden/workload_digests.json, written by a script
+that runs the CPU oracle on the same seeded inputs).
+
+`roofline` is for the headline kernel (NVFP4 quantize): achieved = its
+algorithmic bytes / its average launch duration from the HIP events of the
+timed region (the launches run on the stream the events are recorded on).
+`cpu_baseline` is the CPU oracle's NVFP4 quantize of the same tensor, rows
+split over up to 16 host threads, repeated until ~10 s of thread time.
+`extra` reports the other workloads measured in the same run: the
+4096-element fp32 round trip (codes, scales, MAE, latency), MXFP4 quantize of
+the 16384 x 7168 activation, the 4096 x 14336 NVFP4 scale search, fp32
+inputs, the 128 x 8192 x 8192 MXFP4 GEMM and the NEXT-row variants.
 """
 import argparse
 import glob
@@ -77,6 +77,53 @@ def gemm_bytes(M: int, N: int, K: int, out_bytes: int = 2) -> int:
 
 def gemm_flops(M: int, N: int, K: int) -> int:
     return 2 * M * N * K
+
+
+# ---------------------------------------------------------------------------
+# the oracle's outputs on the seeded inputs, as digests (written by
+# tests/golden/make_workload_digests.py from the CPU oracle)
+# ---------------------------------------------------------------------------
+DIGESTS = os.path.join(ROOT, "tests", "golden", "workload_digests.json")
+
+
+def digests() -> dict:
+    with open(DIGESTS) as f:
+        return json.load(f)
+
+
+def _sha(t: torch.Tensor) -> str:
+    return hashlib.sha256(t.detach().contiguous().cpu().numpy().tobytes()).hexdigest()
+
+
+def _f32_hex(t: torch.Tensor) -> str:
+    return "0x%08x" % int(t.detach().cpu().view(torch.int32).item() & 0xFFFFFFFF)
+
+
+# Per workload: whether the gate compared its outputs with the oracle's.
+GATE = {}
+
+
+def input_matches(x: torch.Tensor, want_sha: str, what: str) -> bool:
+    """Whether the seeded input generated here has the bytes the digests were
+    taken on.  The generators use only operations that give the same bits on
+    every host tried, but if a host's CPU kernels differ the outputs cannot be
+    compared with the stored digests: the gate then records that it skipped
+    this workload rather than failing on a different input."""
+    ok = _sha(x.contiguous().view(torch.uint8)) == want_sha
+    GATE[what] = ("outputs equal the oracle's digests" if ok else
+                  "skipped: this host generated different input bytes than the digests' host")
+    return ok
+
+
+def check_digest(got: dict, want: dict, what: str):
+    """Compare output tensors (codes, scales[, s_g]) with the oracle's digests."""
+    mine = {"codes_sha256": _sha(got["codes"]), "scales_sha256": _sha(got["scales"])}
+    if "s_g" in got:
+        mine["s_g_bits"] = _f32_hex(got["s_g"])
+    bad = [k for k in mine if mine[k] != want.get(k)]
+    if bad:
+        raise RuntimeError(f"{what}: the GPU output differs from the oracle's ({', '.join(bad)})")
+    return True
 
 
 # ---------------------------------------------------------------------------
@@ -243,31 +290,22 @@ def _cpu_model() -> str:
 
 
 def cpu_baseline(x_cpu: torch.Tensor, step_bytes: int):
-    """The oracle (plain C) on one full step of the same input, its rows split
-    over the host's threads (at most 16); the C calls release the GIL.  The
-    NVFP4 tensor scale is the largest of the slices' (it is monotone in the
-    amax)."""
+    """The oracle (plain C) doing the headline step, NVFP4 quantize of the same
+    input: its rows split over the host's threads (at most 16; the C calls
+    release the GIL), the tensor scale the largest of the slices' (it is
+    monotone in the amax).  Whole steps are repeated until the threads have
+    done ~10 s of CPU work."""
     import oracle
     from concurrent.futures import ThreadPoolExecutor
     xo = workloads.bf16_bits(x_cpu).reshape(x_cpu.shape[0], -1)
     nt = max(1, min(16, len(os.sched_getaffinity(0))))
     parts = [p.reshape(-1) for p in np.array_split(xo, nt) if p.size]
+
     def one_step(pool):
         sgs = list(pool.map(oracle.nv_global_scale, parts))
         sg = max(v for v, _ in sgs)
+        list(pool.map(lambda part: oracle.nv_quantize_with_scale(part, sg), parts))
 
-        def nv(part):
-            p, s, _ = oracle.nv_quantize_with_scale(part, sg)
-            oracle.dequantize(oracle.NV, p, s, sg, out_bf16=True)
-
-        def mx(part):
-            p, s, _ = oracle.mx_quantize(part)
-            oracle.dequantize(oracle.MX, p, s, out_bf16=True)
-        list(pool.map(nv, parts))
-        list(pool.map(mx, parts))
-
-    # whole steps until the threads have done at least ~10 s of CPU work (at
-    # most 8 steps)
     steps = 0
     t0 = time.perf_counter()
     with ThreadPoolExecutor(nt) as pool:
@@ -275,13 +313,12 @@ def cpu_baseline(x_cpu: torch.Tensor, step_bytes: int):
             one_step(pool)
             steps += 1
             dt = time.perf_counter() - t0
-            if dt * len(parts) >= 10.0 or steps >= 8:
+            if dt * len(parts) >= 10.0 or steps >= 64:
                 break
     return {"value": round(steps * step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": len(parts),
             "kind": "oracle", "cpu": _cpu_model(),
-            "sample": f"{steps} full step(s) (NVFP4 + MXFP4 quantize and dequantize) of the "
-                      f"{x_cpu.shape[0]}x{x_cpu.shape[1]} bf16 input, rows split over "
-                      f"{len(parts)} threads; {dt:.2f} s wall"}
+            "sample": f"{steps} full NVFP4 quantize step(s) of the {x_cpu.shape[0]}x{x_cpu.shape[1]} "
+                      f"bf16 input, rows split over {len(parts)} threads; {dt:.2f} s wall"}
 
 
 def _rate(b: int, ms: float, elements: int = None):
@@ -292,7 +329,9 @@ def _rate(b: int, ms: float, elements: int = None):
     return d
 
 
-def extra_workloads():
+def extra_workloads(dg: dict):
+    """The other workloads; each output is checked against the oracle's
+    digests where the digests file holds it."""
     out = {}
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
     # NVFP4 quantize of the same-shape weight with seed 1: amax 235 * 2^-11,
@@ -301,6 +340,9 @@ def extra_workloads():
     xw_cpu = workloads.nvfp4_weight(8192, 8192, seed=1)
     xs = [xw_cpu.cuda() for _ in range(3)]
     outs = [fp4.quantize_nvfp4(x) for x in xs]
+    d1 = dg["nvfp4_weight_8192x8192_bf16_seed1"]
+    if input_matches(xw_cpu, d1["input_sha256"], "nvfp4_weight_8192x8192_bf16_seed1"):
+        check_digest(dict(zip(("codes", "scales", "s_g"), outs[0])), d1["nv"], "NVFP4 8192x8192 seed 1")
     wss = [fp4.new_workspace(8192, 8192, "cuda") for _ in range(3)]
     ms = time_rotating([lambda x=x, o=o, w=w: fp4.quantize_nvfp4(x, check=False, out=o, status=st,
                                                                  workspace=w)
@@ -312,6 +354,9 @@ def extra_workloads():
     xa_cpu = workloads.mxfp4_activation()
     xs = [xa_cpu.cuda() for _ in range(2)]
     outs = [fp4.quantize_mxfp4(x) for x in xs]
+    d2 = dg["mxfp4_activation_16384x7168_bf16"]
+    if input_matches(xa_cpu, d2["input_sha256"], "mxfp4_activation_16384x7168_bf16"):
+        check_digest(dict(zip(("codes", "scales"), outs[0])), d2["mx"], "MXFP4 activation 16384x7168")
     ms = time_rotating([lambda x=x, o=o: fp4.quantize_mxfp4(x, check=False, out=o, status=st)
                         for x, o in zip(xs, outs)])
     out["mxfp4_activation_quantize_16384x7168_bf16"] = _rate(quantize_bytes(xa_cpu.numel(), 2, "mx"),
@@ -321,6 +366,10 @@ def extra_workloads():
     xs_cpu = workloads.scale_search_input()
     xs = [xs_cpu.cuda() for _ in range(3)]
     res = [fp4.scale_search(x) for x in xs]
+    d3 = dg["scale_search_4096x14336_bf16"]
+    if input_matches(xs_cpu, d3["input_sha256"], "scale_search_4096x14336_bf16"):
+        check_digest(dict(zip(("codes", "scales", "s_g"), res[0])), d3["search_64_c0.5_1.0"],
+                     "NVFP4 scale search 4096x14336")
     ws = fp4.new_workspace(*xs_cpu.shape, "cuda")
     ms = time_rotating([lambda x=x, r=r: fp4.scale_search(x, check=False, out=r, status=st, workspace=ws)
                         for x, r in zip(xs, res)], launches=6)
@@ -373,6 +422,11 @@ def extra_workloads():
     a, bt = workloads.gemm_operands(M, N, K)
     ac, asc = fp4.quantize_mxfp4(a.cuda())
     bq = [fp4.quantize_mxfp4(bt.cuda()) for _ in range(8)]
+    d4 = dg["gemm_operands_128x8192x8192"]
+    if input_matches(a, d4["a_input_sha256"], "gemm_operand_a_128x8192_f32"):
+        check_digest({"codes": ac, "scales": asc}, d4["a_mx"], "GEMM A")
+    if input_matches(bt, d4["bt_input_sha256"], "gemm_operand_bt_8192x8192_f32"):
+        check_digest({"codes": bq[0][0], "scales": bq[0][1]}, d4["bt_mx"], "GEMM Bt")
     c = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
     ms = time_rotating([lambda b=b: fp4.gemm_mxfp4(ac, asc, b[0], b[1], out=c) for b in bq])
     d = _rate(gemm_bytes(M, N, K), ms)
@@ -517,6 +571,118 @@ def copy_ceiling(iters: int = 20):
                       "bytes read + written"}
 
 
+def timed_steps(fns, steps: int, warmup: int):
+    """`warmup` untimed launches, then EXACTLY `steps` launches captured as one
+    HIP graph and replayed once between two HIP events recorded on the replay
+    stream; the launches cycle through fns (one per buffer set).  Returns
+    (ms per launch from the events, wall-clock ms per launch)."""
+    g = capture(lambda: [fns[i % len(fns)]() for i in range(steps)])
+    if warmup:
+        capture(lambda: [fns[i % len(fns)]() for i in range(warmup)]).replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    s.record()
+    g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return s.elapsed_time(e) / steps, wall * 1e3 / steps
+
+
+def tiny_roundtrip_entry(dg: dict):
+    """The 4096-element fp32 round trip (N(0, 1), seed 0, every 512th value
+    x20) in both formats: digests of the codes and scales against the
+    oracle's, the codes and scales themselves (hex), the mean absolute error
+    of the library's own encoders (fp64 accumulation), and the round-trip
+    latency (quantize + dequantize) back to back in a graph and as eager
+    calls with a synchronisation."""
+    x = workloads.tiny_roundtrip()
+    xd = x.cuda()
+    xv = x.numpy().reshape(-1).astype(np.float64)
+    want = dg["tiny_roundtrip_4096_f32"]
+    gated = input_matches(x, want["input_sha256"], "tiny_roundtrip_4096_f32")
+    out = {"input": "fp32 [1, 4096] ~ N(0, 1), seed 0, every 512th element x20; one tensor "
+                    "(NVFP4 s_g over all 4096 values; 128 MXFP4 / 256 NVFP4 blocks)"}
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for name in ("mx", "nv"):
+        if name == "mx":
+            codes, scales = fp4.quantize_mxfp4(xd)
+            y = torch.empty(1, 4096, dtype=torch.float32, device="cuda")
+
+            def rt(codes=codes, scales=scales, y=y):
+                fp4.quantize_mxfp4(xd, check=False, out=(codes, scales), status=st)
+                fp4.dequantize(fp4.MXFP4, codes, scales, None, out=y)
+            got = {"codes": codes, "scales": scales}
+        else:
+            ws = fp4.new_workspace(1, 4096, "cuda")
+            codes, scales, sg = fp4.quantize_nvfp4(xd, workspace=ws)
+            y = torch.empty(1, 4096, dtype=torch.float32, device="cuda")
+
+            def rt(codes=codes, scales=scales, sg=sg, y=y, ws=ws):
+                fp4.quantize_nvfp4(xd, check=False, out=(codes, scales, sg), status=st, workspace=ws)
+                fp4.dequantize(fp4.NVFP4, codes, scales, sg, out=y)
+            got = {"codes": codes, "scales": scales, "s_g": sg}
+        rt()
+        torch.cuda.synchronize()
+        if gated:
+            check_digest(got, want[name], f"4096 fp32 round trip, {name}")
+        mae = float(np.abs(y.cpu().numpy().reshape(-1).astype(np.float64) - xv).mean())
+        ms_graph = time_rotating([rt], launches=32, reps=5)
+        t0 = time.perf_counter()
+        for _ in range(20):
+            rt()
+            torch.cuda.synchronize()
+        eager_us = (time.perf_counter() - t0) / 20 * 1e6
+        e = {"codes_sha256": _sha(codes), "codes_hex": codes.cpu().numpy().tobytes().hex(),
+             "scales_hex": scales.cpu().numpy().tobytes().hex(), "matches_oracle": gated or None,
+             "mae": round(mae, 6), "roundtrip_us_graph": round(ms_graph * 1e3, 2),
+             "roundtrip_us_eager_with_sync": round(eager_us, 1)}
+        if name == "nv":
+            e["s_g_bits"] = _f32_hex(sg)
+        out["mxfp4" if name == "mx" else "nvfp4"] = e
+    if int(st.item()) != 0:
+        raise RuntimeError(f"a timed call raised status flags {int(st.item())}")
+    out["context"] = ("the glossary page's MAE with the ideal, unencoded scale amax/6: 0.7238 "
+                      "(one 4096-block) / 0.0901 (32-blocks) / 0.0747 (16-blocks); the library's "
+                      "encoders store an E8M0 or E4M3 scale, so theirs differ")
+    return out
+
+
+def fp32_workloads(dg: dict, st: torch.Tensor):
+    """fp32 inputs: the GEMM's A operand (128 x 8192 ~ N(0, 1)) and the
+    8192 x 8192 weight widened to fp32 (its values are bf16, so its codes,
+    scales and s_g are the bf16 tensor's), both formats; NVFP4 of fp32 takes
+    the two-pass path (tensor-amax pass, then quantize)."""
+    out = {}
+    a, _ = workloads.gemm_operands()
+    ga = dg["gemm_operands_128x8192x8192"]
+    w = workloads.nvfp4_weight().float()
+    gw = dg["nvfp4_weight_8192x8192_bf16_seed0"]
+    for tag, xc, g, nsets in (("128x8192_f32", a, ga, 3), ("8192x8192_f32", w, gw, 3)):
+        xs = [xc.cuda() for _ in range(nsets)]
+        mxo = [fp4.quantize_mxfp4(x) for x in xs]
+        wss = [fp4.new_workspace(*xc.shape, "cuda") for _ in range(nsets)]
+        nvo = [fp4.quantize_nvfp4(x, workspace=ws) for x, ws in zip(xs, wss)]
+        src = (a, g["a_input_sha256"]) if g is ga else (workloads.nvfp4_weight(), g["input_sha256"])
+        if input_matches(src[0], src[1], f"quantize_{tag}"):
+            check_digest({"codes": mxo[0][0], "scales": mxo[0][1]}, g["a_mx" if g is ga else "mx"],
+                         f"MXFP4 {tag}")
+            check_digest({"codes": nvo[0][0], "scales": nvo[0][1], "s_g": nvo[0][2]},
+                         g["a_nv" if g is ga else "nv"], f"NVFP4 {tag}")
+        n = xc.numel()
+        ms = time_rotating([lambda x=x, o=o: fp4.quantize_mxfp4(x, check=False, out=o, status=st)
+                            for x, o in zip(xs, mxo)])
+        out[f"mxfp4_quantize_{tag}"] = _rate(quantize_bytes(n, 4, "mx"), ms, n)
+        ms = time_rotating([lambda x=x, o=o, ws=ws: fp4.quantize_nvfp4(x, check=False, out=o,
+                                                                       status=st, workspace=ws)
+                            for x, o, ws in zip(xs, nvo, wss)])
+        out[f"nvfp4_quantize_{tag}"] = _rate(quantize_bytes(n, 4, "nv"), ms, n)
+        del xs, mxo, nvo, wss
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -533,85 +699,112 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
     torch.cuda.set_device(0)
 
     x_cpu = workloads.nvfp4_weight()
     rt = RoundTrip(x_cpu)
-    step_bytes = sum(rt.bytes.values())
+    dg = digests()
+    want = dg["nvfp4_weight_8192x8192_bf16_seed0"]
+    gated = input_matches(x_cpu, want["input_sha256"], "nvfp4_weight_8192x8192_bf16_seed0")
 
-    # correctness gate on the benchmark's own buffers before timing
-    for i in range(NSETS):
-        b = rt.sets[i]
+    def gate(when: str):
+        """Every buffer set's NVFP4 and MXFP4 outputs equal the oracle's."""
+        for i, b in enumerate(rt.sets):
+            if gated:
+                check_digest({"codes": b["nv"][0], "scales": b["nv"][1], "s_g": b["nv"][2]},
+                             want["nv"], f"NVFP4 8192x8192, buffer set {i}, {when}")
+                check_digest({"codes": b["mx"][0], "scales": b["mx"][1]}, want["mx"],
+                             f"MXFP4 8192x8192, buffer set {i}, {when}")
+            if int(b["status"].item()) != 0:
+                raise RuntimeError(f"buffer set {i}: status flags {int(b['status'].item())} ({when})")
+
+    for b in rt.sets:
         fp4.quantize_nvfp4(b["x"], out=b["nv"], workspace=b["ws"])
         fp4.quantize_mxfp4(b["x"], out=b["mx"])
-
-    # the timed region: K replays of the graph-captured step
-    step_graph = capture(rt.step)
-    for _ in range(args.warmup):
-        step_graph.replay()
     torch.cuda.synchronize()
-    s_ev = torch.cuda.Event(enable_timing=True)
-    e_ev = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    s_ev.record()
-    for _ in range(args.steps):
-        step_graph.replay()
-    e_ev.record()
-    torch.cuda.synchronize()
-    wall_s = time.perf_counter() - t0
-    ms_per_step = max(wall_s * 1e3, s_ev.elapsed_time(e_ev)) / args.steps
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    gate("before timing")
 
-    # per-op launch durations: back-to-back launches rotating NSETS buffer sets
+    # the timed region: K NVFP4 quantize steps (one graph of K launches)
+    nv_bytes = rt.bytes["nvfp4_quantize"]
+    ms_nv, wall_nv = timed_steps([rt.op("nvfp4_quantize", i) for i in range(NSETS)], args.steps,
+                                 args.warmup)
+    value = nv_bytes / (ms_nv * 1e-3) / 1e9
+    # MXFP4 quantize of the same tensor, the same way
+    ms_mx, wall_mx = timed_steps([rt.op("mxfp4_quantize", i) for i in range(NSETS)], args.steps,
+                                 args.warmup)
+    torch.cuda.synchronize()
+    gate("after timing")
+
+    formats = {"nvfp4_quantize": _rate(nv_bytes, ms_nv, rt.elements),
+               "mxfp4_quantize": _rate(rt.bytes["mxfp4_quantize"], ms_mx, rt.elements)}
+    formats["nvfp4_quantize"]["wall_us"] = round(wall_nv * 1e3, 2)
+    formats["mxfp4_quantize"]["wall_us"] = round(wall_mx * 1e3, 2)
+
+    # the round trip: per-op launch durations (back-to-back launches rotating
+    # NSETS buffer sets) and the four-op step as a whole
     breakdown = {}
     for tag in rt.bytes:
         ms = time_rotating([rt.op(tag, i) for i in range(NSETS)])
         breakdown[tag] = _rate(rt.bytes[tag], ms, rt.elements)
         breakdown[tag]["bytes"] = rt.bytes[tag]
-
-    # every call of the timed region reported its conditions here
+    step_bytes = sum(rt.bytes.values())
+    ms_rt = time_graph(capture(rt.step), 20)
+    breakdown["roundtrip_step"] = _rate(step_bytes, ms_rt)
+    breakdown["roundtrip_step"].update({"bytes": step_bytes, "ops": list(rt.bytes)})
     for b in rt.sets:
         if int(b["status"].item()) != 0:
             raise RuntimeError(f"a timed call raised status flags {int(b['status'].item())}")
 
-    dom = max(breakdown, key=lambda t: breakdown[t]["us"])
-    kernel_names = {"nvfp4_quantize": "nv_resident_kernel<64, exact> (one pass, tensor held on chip; "
-                                      "this tensor's s_g = 11 * 2^-18 takes the two-operation divide)",
-                    "nvfp4_dequantize": "dequant_kernel<1, bf16 out>",
-                    "mxfp4_quantize": "mx_quantize_kernel<bf16 in>",
-                    "mxfp4_dequantize": "dequant_kernel<0, bf16 out>"}
     traffic = measured_traffic()
-    roofline = {"bound": "hbm", "kernel": kernel_names[dom],
-                "achieved": breakdown[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(breakdown[dom]["GB/s"] / HBM_PEAK_GBS, 4),
-                "traffic": traffic[dom] if traffic else None,
-                "algorithmic_bytes_per_launch": rt.bytes[dom],
-                "avg_launch_us": breakdown[dom]["us"]}
+    roofline = {"bound": "hbm",
+                "kernel": "nv_resident_kernel<64, exact> (NVFP4 quantize in one pass, the tensor "
+                          "held on chip; this tensor's s_g = 11 * 2^-18 takes the two-operation divide)",
+                "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(value / HBM_PEAK_GBS, 4),
+                "traffic": traffic["nvfp4_quantize"] if traffic else None,
+                "algorithmic_bytes_per_launch": nv_bytes,
+                "avg_launch_us": round(ms_nv * 1e3, 2)}
     if traffic:
-        roofline["traffic_GB/s"] = round(traffic[dom] / (breakdown[dom]["us"] * 1e3), 1)
+        roofline["traffic_GB/s"] = round(traffic["nvfp4_quantize"] / (ms_nv * 1e6), 1)
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_nv, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "nvfp4_mxfp4_roundtrip_8192x8192_bf16",
+        "config": {"workload": "nvfp4_quantize_8192x8192_bf16",
                    "shape": [8192, 8192], "input": "bf16 N(0, 0.02^2), seed 0",
-                   "ops": list(rt.bytes), "step_bytes": step_bytes,
+                   "step": "one fp4_quantize_nvfp4 call (16-blocks, E4M3 block scales, fp32 tensor "
+                           "scale, packed codes)",
+                   "step_bytes": nv_bytes,
                    "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
-                   "Gelem/s_per_op": round(4 * rt.elements / (ms_per_step * 1e-3) / 1e9, 1),
-                   "timing": "HIP graph of one step replayed K times; per-op rows from graphs "
-                             "of back-to-back launches over 3 rotating buffer sets"},
+                   "Gelem/s": round(rt.elements / (ms_nv * 1e-3) / 1e9, 1),
+                   "timing": "HIP graph of K launches over 3 rotating buffer sets, replayed once "
+                             "between HIP events; inputs resident in HBM",
+                   "parity_gate": ("codes, scale bytes and s_g of every timed buffer equal the CPU "
+                                   "oracle's (SHA-256 digests) before and after timing" if gated else
+                                   GATE["nvfp4_weight_8192x8192_bf16_seed0"])},
+        "formats": formats,
         "breakdown": breakdown,
         "roofline": roofline,
         "copy_ceiling": copy_ceiling(),
     }
     if not args.no_extra:
-        line["extra"] = extra_workloads()
+        st = torch.zeros(1, dtype=torch.int32, device="cuda")
+        extra = {"tiny_roundtrip_4096_f32": tiny_roundtrip_entry(dg)}
+        extra.update(fp32_workloads(dg, st))
+        extra.update(extra_workloads(dg))
+        if int(st.item()) != 0:
+            raise RuntimeError(f"a timed call raised status flags {int(st.item())}")
+        line["extra"] = extra
+        line["parity_gate_extra"] = dict(GATE)
     if args.calibrate_copy:
         line["copy_calibration"] = calibrate_copy()
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(x_cpu, step_bytes)
+        line["cpu_baseline"] = cpu_baseline(x_cpu, nv_bytes)
     print(json.dumps(line), flush=True)
 
 

@@ -57,13 +57,17 @@ def nvfp4_weight(rows: int = 8192, cols: int = 8192, seed: int = 0, std: float =
 
 def _student_t3(shape, g: torch.Generator) -> torch.Tensor:
     # Student-t with 3 degrees of freedom: Z / sqrt(V / 3), V ~ chi^2(3),
-    # the chi-square drawn as a sum of three squared standard normals.
-    z = torch.randn(shape, generator=g)
-    v = torch.zeros(shape)
+    # the chi-square drawn as a sum of three squared standard normals.  The
+    # quotient is taken in float64 with numpy's IEEE divide and square root
+    # and rounded once to float32: torch's float32 CPU kernels for it give
+    # different last bits on different host CPUs, and the input must be the
+    # same bytes wherever it is generated.
+    z = torch.randn(shape, generator=g).numpy().astype(np.float64)
+    v = np.zeros(shape)
     for _ in range(3):
-        w = torch.randn(shape, generator=g)
+        w = torch.randn(shape, generator=g).numpy().astype(np.float64)
         v += w * w
-    return z / torch.sqrt(v / 3.0)
+    return torch.from_numpy((z / np.sqrt(v / 3.0)).astype(np.float32))
 
 
 def outlier_columns(cols: int, frac: float = 0.01, seed: int = 1) -> torch.Tensor:
