@@ -250,77 +250,6 @@ __device__ __forceinline__ void nv_table_build(NvScaleTable &T, float s_g) {
     }
 }
 
-// Compact table for the one-pass bf16 kernel.  A block scale takes two
-// dependent LDS reads: the guess g's thresholds, then the final code's entry:
-//   lohi[g]  = {lo[g], lo[g+1]} as fp32 bit patterns (integer order equals
-//              value order for these non-negative numbers), except that
-//              lo[0] is 1: a zero amax then resolves to "code" -1; and
-//              lohi[127] = {~0, ~0}, which resolves the converter's NaN code
-//              (a guess past 448) to 126;
-//   ent[c+1] = {Y_c, D_c, c, 0} for codes c = 0..126, and ent[0] = the
-//              entry of code 0x38 (scale 1), which a zero block takes;
-// where, for code c,
-//   in general        Y = RN32(1/alpha'_c) (0 for alpha_c = 0) and
-//                     D = alpha'_c, for the reciprocal-correction divide;
-//   for a short s_g   Y = RD32(1/alpha_c) and D = RN32(1/alpha_c - Y) >= 0, a
-//   (<= 12 bits)      two-float reciprocal for the two-operation divide;
-//   sa[c] = {alpha'_c, sc_c}, always, for the compact full-divide pass.
-// lo is staged in the last array.
-struct NvGuessTable {
-    uint2 lohi[128];
-    float4 ent[128];
-    float2 sa[127];
-    float lo[127];
-};
-
-// An s_g with at most 12 significant bits: every alpha_c = s_g E4M3(c) then
-// has at most 16, which the two-operation divide needs.
-__device__ __forceinline__ bool short_tensor_scale(float s_g) {
-    return s_g >= 0x1p-126f && (f2u(s_g) & 0xFFFu) == 0;
-}
-
-__device__ __forceinline__ float nv_signed_recip(int c, float s_g) {
-    const float4 q = nv_divisor(c, s_g);
-    return q.w != 1.0f ? -__builtin_fabsf(q.z) : q.z;
-}
-
-// Builds the table in two steps over the workgroup (per code, then per
-// guess); returns to every thread whether some code needs operand scaling.
-// Ends with a barrier.
-__device__ __forceinline__ bool nv_guess_table_build(NvGuessTable &R, float s_g) {
-    int scaled = 0;
-    const int t = threadIdx.x;
-    const bool shrt = short_tensor_scale(s_g);
-    // step 1: per code c, sa[c] and ent[c + 1]; lo[k]
-    if (t < 127) {
-        const float a = s_g * e4m3_pos_value((uint32_t)t);
-        const float sc = a > 0.0f && a < kDivScaleBelow ? kDivScale : 1.0f;  // code 0: alpha = 0
-        const float ad = a * sc;  // exact
-        float Y = a > 0.0f ? 1.0f / ad : 0.0f, D = ad;
-        if (shrt && a > 0.0f) {
-            // RD32 and the (non-negative) remainder of 1 / alpha
-            const double r = 1.0 / (double)a;
-            float yh = (float)r;
-            if ((double)yh > r) yh = u2f(f2u(yh) - 1u);
-            Y = yh;
-            D = (float)(r - (double)yh);
-        }
-        R.sa[t] = make_float2(ad, sc);
-        R.ent[t + 1] = make_float4(Y, D, u2f((uint32_t)t), 0.0f);
-        if (t == 0x38) R.ent[0] = make_float4(Y, D, u2f(0x38u), 0.0f);
-        scaled = sc != 1.0f;
-    } else if (t >= 128 && t < 128 + 127) {
-        R.lo[t - 128] = nv_lo(t - 128, s_g);
-    }
-    __syncthreads();
-    // step 2: threshold pairs per guess g
-    if (t < 127)
-        R.lohi[t] = make_uint2(t == 0 ? 1u : f2u(R.lo[t]), t < 126 ? f2u(R.lo[t + 1]) : 0x7F800000u);
-    else if (t == 127)
-        R.lohi[t] = make_uint2(~0u, ~0u);
-    return __syncthreads_or(scaled) != 0;
-}
-
 // Truncated E4M3 code of an approximate quotient t >= 0 (saturating);
 // branch-free: the subnormal-range form reads t clamped below 2^-6.
 __device__ __forceinline__ uint32_t e4m3_trunc_code(float t) {
@@ -351,19 +280,6 @@ __device__ __forceinline__ CodeGuess make_code_guess(float s_g) {
     G.bias = tiny ? 960u - 512u : 960u;
     G.cs = tiny ? 0x1p-64f : 1.0f;
     return G;
-}
-
-// The same guess from the FP8 converter: the E4M3 code of t 2^k rounded to
-// nearest even (it divides t by its scale's power of two and keeps
-// subnormals; past 464 it gives the NaN code 127, which a table must map to
-// 126).  Within one code of the exact one, like the truncated guess.  The
-// converter writes the low two bytes (t's code, then 0.0's) over t's own bits.
-__device__ __forceinline__ uint32_t code_guess_cvt(float ag, const CodeGuess &G) {
-    typedef short v2i16 __attribute__((ext_vector_type(2)));
-    const float t = ag * G.r;
-    const v2i16 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(v2i16, t), t, 0.0f,
-                                                             G.cs, false);
-    return __builtin_bit_cast(uint32_t, r) & 0xFFu;
 }
 
 // E4M3 code of a nonzero finite block amax ag: nearest to the exact
@@ -403,6 +319,192 @@ __device__ __forceinline__ float div_rn(float x, float alpha, float y) {
     float q0 = x * y;
     float rn = __builtin_fmaf(alpha, q0, -x);
     return __builtin_fmaf(-rn, y, q0);
+}
+
+// ---- direct block-scale table of the one-pass bf16 kernel ------------------
+// For a bf16 tensor every block amax is a bf16 magnitude, and under one s_g
+// every amax with a nonzero E4M3 code lies in a window of under 20 binades:
+// from 6 s_g 2^-10 (the threshold of code 1) to the tensor amax 2688 s_g.
+// The table maps each bf16 magnitude of a 20-binade window straight to its
+// block's E4M3 code and divisor term, so a block scale is one LDS lookup
+// indexed by the amax bits:
+//   index 0      a zero block: code 0x38 (scale 1);
+//   index 1      a nonzero amax below the window: code 0 (a scale underflow);
+//   index 2 + i  the bf16 magnitude whose bits are base + i.
+// The divisor term Y_c of code c is a reciprocal of alpha_c = RN32(s_g E4M3(c))
+// for which the one product RN32(x Y_c) gives every bf16 x the E2M1 code of
+// the correctly rounded quotient RN32(x / alpha_c):
+//  - Y_c is RN32(1 / alpha_c) or one of its two fp32 neighbours, so RN32(x Y_c)
+//    lies within 2^-21.4 (relative) of x / alpha_c, as does RN32(x / alpha_c);
+//    an E2M1 decision point m (0.25, 0.75, ..., 5) farther than 2^-20 from
+//    x / alpha_c cannot separate them;
+//  - at most one bf16 x lies within 2^-20 of m alpha_c for each m (bf16 values
+//    are 2^-8 apart or more, relatively); the build finds these "hazards" and
+//    takes the first candidate (RN32(1 / alpha), then the one below, then the
+//    one above) under which every hazard's product gets the code of its
+//    correctly rounded quotient (reciprocal-correction divide), both taken on
+//    the converter itself.
+// No candidate fits only at exact ties x = m alpha_c, where alpha_c has few
+// significant bits; such a code takes the two-operation quotient
+// fma(x, Y, x D) with Y = RD32(1 / alpha), D = RN32(1 / alpha - Y), exact for
+// an alpha of at most 16 significant bits.  A code that fits neither form
+// (none known), or an alpha below 2^-90 (operands would need scaling), sends
+// the whole call to the exact compact loop.
+constexpr int RES_NIDX = 2560;  // window entries: 20 binades of 128 bf16 magnitudes
+constexpr uint32_t NV_NEEDS_TWO_OP = 1;  // some code takes fma(x, Y, x D)
+constexpr uint32_t NV_NEEDS_EXACT = 2;   // some code needs the exact divide loop
+
+struct NvDirectTable {
+    // Y of each entry's code (0 for code 0).  The build's per-code scratch
+    // (alpha_c, RN32(1 / alpha_c), each decision point's failed candidates)
+    // lives in its first entries until the last step writes them.
+    union {
+        float y[RES_NIDX + 2];
+        struct {
+            float a[128];
+            float y0[128];
+            uint8_t fail[128 * 8];
+        } b;
+    };
+    float yc[128];               // per code: Y_c
+    float dc[128];               // per code: D_c (0 where the product alone is exact)
+    uint32_t lo[128];            // bf16 bits of the smallest magnitude with code >= c
+    uint8_t code[RES_NIDX + 4];  // each entry's E4M3 code
+    uint32_t need;               // NV_NEEDS_* of the call
+};
+
+// Bits of the largest bf16 magnitude at or below 6 s_g 2^-10, the threshold
+// of E4M3 code 1 (smaller amaxes all take code 0).
+__device__ __forceinline__ uint32_t nv_window_base(float s_g) {
+    const double t = 6.0 * (double)s_g * 0x1p-10;  // exact
+    float f = (float)t;
+    if ((double)f > t) f = u2f(f2u(f) - 1u);
+    return f2u(f) >> 16;
+}
+
+// Bits of the smallest bf16 magnitude whose E4M3 code under s_g is at least
+// c (1 <= c <= 126): above the exact threshold 6 s_g midpoint(c - 1, c) (at
+// most 31 significant bits, so exact in binary64), or on it when c is even.
+__device__ __forceinline__ uint32_t nv_lo_bf16(uint32_t c, float s_g) {
+    const double th = (double)e4m3_mid6(c - 1u) * (double)s_g;
+    const uint32_t f = f2u((float)th);
+    uint32_t b = f >> 16;
+    b = b > 0u ? b - 1u : 0u;
+    for (int k = 0; k < 4 && b < 0x7F80u; ++k) {
+        const double v = (double)u2f(b << 16);
+        if (v > th || (v == th && (c & 1u) == 0)) break;
+        ++b;
+    }
+    return b;
+}
+
+// E2M1 code (sign and magnitude) the converter gives one fp32 value.
+__device__ __forceinline__ uint32_t e2m1_code1(float q) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q, 0.0f, e8m0_operand(E8M0_ONE), 0) & 0xFu;
+}
+
+// Builds the table over the workgroup in three steps (per code and decision
+// point; per code; per window entry).  Ends with a barrier; T.need then holds
+// the call's NV_NEEDS_* for every thread.
+__device__ __forceinline__ void nv_direct_table_build(NvDirectTable &T, float s_g, uint32_t base) {
+    const int t = threadIdx.x;
+    // step 1, per (code c, decision point m): the bf16 value nearest m alpha_c
+    // if it lies within 2^-20 of it (a hazard), and which of the candidates
+    // RN32(1 / alpha), its lower and its upper neighbour give it a wrong code
+    // (bits 0, 1, 2 of the point's fail byte)
+    constexpr int ITEMS = 126 * 7;
+#pragma unroll
+    for (int r = 0; r < (ITEMS + 511) / 512; ++r) {
+        const int it = t + r * (int)blockDim.x;
+        if (it >= ITEMS) break;
+        const int c = 1 + it / 7, i = it % 7;
+        const float a = s_g * e4m3_pos_value((uint32_t)c);
+        const float y0 = a > 0.0f ? 1.0f / a : 0.0f;  // correctly rounded
+        if (i == 0) {
+            T.b.a[c] = a;
+            T.b.y0[c] = y0;
+        }
+        uint32_t mask = 0;
+        if (a >= kDivScaleBelow) {  // else: code 0 alpha, or operands needing scaling
+            const float m = i < 4 ? 0.25f + 0.5f * (float)i : (i == 4 ? 2.5f : (i == 5 ? 3.5f : 5.0f));
+            const double tt = (double)m * (double)a;  // exact
+            const uint32_t tb = f2u((float)tt);
+            // nearest bf16 of tt (a double rounding picks the far neighbour
+            // only when tt is near a bf16 midpoint, and then neither is a hazard)
+            const float xh = u2f(((tb + 0x7FFFu + ((tb >> 16) & 1u)) >> 16) << 16);
+            if (__builtin_fabs((double)xh - tt) <= tt * 0x1p-20) {
+                const uint32_t want = e2m1_code1(div_rn(xh, a, y0));
+                mask |= e2m1_code1(xh * y0) != want ? 1u : 0u;
+                mask |= e2m1_code1(xh * u2f(f2u(y0) - 1u)) != want ? 2u : 0u;
+                mask |= e2m1_code1(xh * u2f(f2u(y0) + 1u)) != want ? 4u : 0u;
+            }
+        }
+        T.b.fail[c * 8 + i] = (uint8_t)mask;
+    }
+    if (t == 0) {
+        T.b.a[0] = 0.0f;
+        T.b.y0[0] = 0.0f;
+        T.need = 0u;
+    }
+    __syncthreads();
+    // step 2, per code: Y_c, D_c and the code's lower bound
+    if (t < 128) {
+        float Y = 0.0f, D = 0.0f;
+        uint32_t need = 0;
+        if (t > 0 && t < 127) {
+            const float a = T.b.a[t], y0 = T.b.y0[t];
+            const uint2 f2 = *(const uint2 *)&T.b.fail[t * 8];
+            const uint32_t fo = f2.x | (f2.y & 0x00FFFFFFu);
+            const uint32_t fail = (fo | (fo >> 8) | (fo >> 16) | (fo >> 24)) & 7u;
+            if (a > 0.0f && a < kDivScaleBelow) {  // operands would need scaling: exact loop
+                Y = 1.0f;
+                need = NV_NEEDS_EXACT;
+            } else if (a > 0.0f) {
+                if (!(fail & 1u)) {
+                    Y = y0;
+                } else if (!(fail & 2u)) {
+                    Y = u2f(f2u(y0) - 1u);
+                } else if (!(fail & 4u)) {
+                    Y = u2f(f2u(y0) + 1u);
+                } else if ((f2u(a) & 0xFFu) == 0u && a >= 0x1p-126f) {  // <= 16 significant bits
+                    const double r = 1.0 / (double)a;
+                    float yh = (float)r;
+                    if ((double)yh > r) yh = u2f(f2u(yh) - 1u);
+                    Y = yh;
+                    D = (float)(r - (double)yh);
+                    need = NV_NEEDS_TWO_OP;
+                } else {
+                    Y = y0;
+                    need = NV_NEEDS_EXACT;
+                }
+            }
+        }
+        T.yc[t] = Y;
+        T.dc[t] = D;
+        T.lo[t] = t == 0 ? 0u : (t == 127 ? 0xFFFFu : nv_lo_bf16((uint32_t)t, s_g));
+        if (need) atomicOr(&T.need, need);
+    }
+    __syncthreads();
+    // step 3, per window entry: the code of a bf16 magnitude, from a guess
+    // within one code of it settled by the two bounds around it
+    const CodeGuess G = make_code_guess(s_g);
+#pragma unroll
+    for (int r = 0; r < (RES_NIDX + 2 + 511) / 512; ++r) {
+        const int i = t + r * (int)blockDim.x;
+        if (i < RES_NIDX + 2) {
+            uint32_t c;
+            if (i < 2) {
+                c = i == 0 ? 0x38u : 0u;
+            } else {
+                const uint32_t bits = min(base + (uint32_t)(i - 2), 0x7F7Fu);  // finite
+                const uint32_t g = code_guess(u2f(bits << 16), G);
+                c = g + (bits >= T.lo[g + 1] ? 1u : 0u) - (bits < T.lo[g] ? 1u : 0u);
+            }
+            T.code[i] = (uint8_t)c;
+            T.y[i] = T.yc[c];
+        }
+    }
+    __syncthreads();
 }
 
 // ---- wave-level helpers ---------------------------------------------------

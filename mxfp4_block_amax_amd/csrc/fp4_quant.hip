@@ -601,26 +601,6 @@ __global__ __launch_bounds__(WG) void nv_quantize_kernel(const uint4 *__restrict
 // tagged slots' values plus the amax of every other slice, read from x.  The
 // result is the same; FLAG_BARRIER_TIMEOUT records that it happened.
 // ---------------------------------------------------------------------------
-// Block scales of a tile of two chunk rows held by a lane pair: the even
-// lane derives row 0's scale, the odd lane row 1's (one table read each),
-// and they swap the table's reciprocal term Y and divisor term D.
-struct PairScales {
-    uint32_t c;     // this lane's E4M3 code
-    float ys[2];    // each row's Y: RN32(1/alpha'), or RD32(1/alpha) for a short s_g
-    float ad[2];    // each row's D: alpha', or the reciprocal's remainder for a short s_g
-};
-
-// Largest magnitude of 8 finite fp32 values (three-input max with |.|
-// operand modifiers; finite inputs need no NaN handling).
-__device__ __forceinline__ float absmax8(const float (&f)[8]) {
-    float a, b, c;
-    asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(a) : "v"(f[0]), "v"(f[1]), "v"(f[2]));
-    asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(b) : "v"(f[3]), "v"(f[4]), "v"(f[5]));
-    asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(c) : "v"(a), "v"(f[6]), "v"(f[7]));
-    asm("v_max_f32 %0, %1, %2" : "=v"(a) : "v"(b), "v"(c));
-    return a;
-}
-
 // Amax bits (bf16 magnitude) of the block this lane derives the scale of,
 // given its chunk amaxes m0 (row 0) and m1 (row 1): the even lane takes row
 // 0's block and the odd lane row 1's; each lane also hands its partner its
@@ -630,46 +610,21 @@ __device__ __forceinline__ uint32_t pair_amax(uint32_t m0, uint32_t m1, bool odd
     return max(own, dpp<QP_XOR1>(other));
 }
 
-// The block scales of a chunk pair from this lane's block amax (fp32 bit
-// pattern): the code byte for this lane's row, and both rows' divide
-// operands.  A zero block resolves to the table's first entry (code 0x38,
-// scale 1).  ymin collects min Y (Y >= 0): 0 marks a scale that underflowed.
-__device__ __forceinline__ PairScales pair_scales(uint32_t ag, const NvGuessTable &R,
-                                                  const CodeGuess &G, float &ymin) {
-    const uint32_t g = code_guess_cvt(u2f(ag), G);
-    const uint2 e = R.lohi[g];
-    // c = g + [ag >= lo[g+1]] - [ag < lo[g]] with carry arithmetic; -1 for a
-    // zero block
-    int c;
-    asm("v_cmp_le_u32 vcc, %3, %1\n\t"
-        "v_addc_co_u32 %0, vcc, %2, 0, vcc\n\t"
-        "v_cmp_gt_u32 vcc, %4, %1\n\t"
-        "v_subb_co_u32 %0, vcc, %0, 0, vcc"
-        : "=&v"(c)
-        : "v"(ag), "v"(g), "v"(e.y), "v"(e.x)
-        : "vcc");
-    const float4 en = R.ent[c + 1];
-    PairScales p;
-    p.c = f2u(en.z);
-    asm("v_min_f32 %0, %1, %2" : "=v"(ymin) : "v"(ymin), "v"(en.x));
-    // row 0 takes the even lane's values, row 1 the odd lane's
-    p.ys[0] = dppf<0xA0>(en.x);  // quad_perm [0,0,2,2]
-    p.ys[1] = dppf<0xF5>(en.x);  // quad_perm [1,1,3,3]
-    p.ad[0] = dppf<0xA0>(en.y);
-    p.ad[1] = dppf<0xF5>(en.y);
-    return p;
+// Row 0's and row 1's Y for a tile of two chunk rows held by a lane pair
+// (the even lane looked up row 0's block, the odd lane row 1's).
+__device__ __forceinline__ void pair_rows(float v, float (&rows)[2]) {
+    rows[0] = dppf<0xA0>(v);  // quad_perm [0,0,2,2]
+    rows[1] = dppf<0xF5>(v);  // quad_perm [1,1,3,3]
 }
 
 constexpr int RES_WG = 512;
 constexpr int RES_WAVES = RES_WG / WAVE;
-constexpr int RES_LDS_CHUNKS = 19;
+constexpr int RES_LDS_CHUNKS = 18;
 constexpr int RES_MAX_CHUNKS = 64;
 
 typedef __attribute__((address_space(1))) const void *global_cptr;
 typedef __attribute__((address_space(3))) void *lds_ptr;
 
-// EXACT: the grid covers the tensor exactly (nchunks = gridDim.x * 512 * CPL),
-// so no load is clamped and no store predicated.
 // ---------------------------------------------------------------------------
 // NVFP4 quantize, pass 2, written in the packed NVFP4 operand layout: one
 // wave per (row tile rt, K step ks) writes the tile's contiguous kilobyte of
@@ -729,6 +684,8 @@ __global__ __launch_bounds__(WG) void nv_quantize_packed_kernel(
     report_flags(status, flags);
 }
 
+// EXACT: the grid covers the tensor exactly (nchunks = gridDim.x * 512 * CPL),
+// so no load is clamped and no store predicated.
 template <int CPL, bool EXACT>
 __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
     const uint4 *__restrict__ x, int nchunks, uint32_t *__restrict__ codes,
@@ -739,14 +696,14 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
     // one LDS block, table first: its addresses then fit the 16-bit
     // immediate offset of an LDS read, so no base is rebuilt per lookup
     struct Shared {
-        NvGuessTable R;
+        NvDirectTable T;
         uint32_t red[RES_WAVES];
         uint32_t tensor_amax;
         uint32_t late_tag;
         uint4 data[LC * RES_WG];
     };
     __shared__ Shared sh;
-    NvGuessTable &R = sh.R;
+    NvDirectTable &T = sh.T;
     uint32_t(&red)[RES_WAVES] = sh.red;
     uint32_t &tensor_amax = sh.tensor_amax;
     uint4(&lds)[LC * RES_WG] = sh.data;
@@ -772,12 +729,30 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
         v[r] = ld_stream(x + j * stride + (EXACT ? c00 : min(c00, last - j * stride)));
     }
     const uint32_t tag = wv == 0 ? barrier_tag(epoch) : 0u;
-    uint32_t m = 0;
+    // The amaxes of the blocks this lane will derive scales for, while the
+    // loads stream in: chunk rows 2p and 2p + 1 form pair p, whose block amax
+    // (bf16 magnitude bits) is kept, two pairs per register, for phase 2.
+    constexpr int NP = CPL / 2;
+    const bool odd = lane & 1;
+    uint32_t am[(NP + 1) / 2];
 #pragma unroll
-    for (int r = 0; r < RC; ++r) m = max(m, amax_bf16x8(v[r]));
+    for (int i = 0; i < (NP + 1) / 2; ++i) am[i] = 0;
+    uint32_t m = 0;
+    auto keep_pair = [&](int p, uint32_t m0, uint32_t m1) {
+        m = max(m, max(m0, m1));
+        const uint32_t ag = pair_amax(m0, m1, odd);
+        am[p >> 1] |= (p & 1) ? ag << 16 : ag;  // pairs are kept in no particular order
+    };
+#pragma unroll
+    for (int r = 0; r < RC; r += 2) keep_pair((LC + r) / 2, amax_bf16x8(v[r]), amax_bf16x8(v[r + 1]));
     __builtin_amdgcn_s_waitcnt(0);  // the global->LDS loads of this wave have landed
 #pragma unroll
-    for (int j = 0; j < LC; ++j) m = max(m, amax_bf16x8(lds[j * RES_WG + tid]));
+    for (int j = 0; j < LC; j += 2)
+        keep_pair(j / 2, amax_bf16x8(lds[j * RES_WG + tid]), amax_bf16x8(lds[(j + 1) * RES_WG + tid]));
+    // opaque to the optimiser: the packed amaxes are final here (it would
+    // otherwise carry the per-chunk maxima across the barrier instead)
+#pragma unroll
+    for (int i = 0; i < (NP + 1) / 2; ++i) asm volatile("" : "+v"(am[i]));
     m = wave_max_u32(m);
     if (lane == 0) red[wv] = m;
     __syncthreads();
@@ -834,93 +809,107 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
         report_flags(status, flags);
         return;
     }
-    // ends with a barrier; true when some code needs operand scaling
-    const bool any_scaled = nv_guess_table_build(R, ts.s_g);
+    const uint32_t base = nv_window_base(ts.s_g);
+    nv_direct_table_build(T, ts.s_g, base);  // ends with a barrier
+    const uint32_t need = T.need;            // uniform
 
     // ---- phase 2: quantize from LDS and registers -----------------------
-    // Four chunk rows per iteration: the even lane of a pair derives the block
-    // scales of rows 0 and 2, the odd lane those of rows 1 and 3 (two
-    // independent chains per lane), and they swap them.
+    // Two chunk rows per iteration: a lane pair holds one 16-element block of
+    // each; the even lane looks up row 0's block scale, the odd lane row 1's,
+    // and they swap the divisor terms.
     // Opaque to the optimiser: phase 1's per-chunk results are not kept alive
     // across the barrier for reuse (there are no registers for them).
 #pragma unroll
     for (int r = 0; r < RC; ++r) asm volatile("" : "+v"(v[r].x), "+v"(v[r].y), "+v"(v[r].z), "+v"(v[r].w));
-    const CodeGuess G = make_code_guess(ts.s_g);
-    const bool shrt = short_tensor_scale(ts.s_g);
     float ymin = __builtin_inff();
-    const bool odd = lane & 1;
     // code dwords go out as buffer stores: one resource, the lane's byte
     // offset in a VGPR and the uniform part of the address in an SGPR
     const uint32_t coff = (uint32_t)c00 * 4u;
     const __amdgpu_buffer_rsrc_t crs =
         __builtin_amdgcn_make_buffer_rsrc(codes, (short)0, nchunks * 4, kBufferRsrcWord3);
     const int cs = odd ? c00 + stride : c00;  // this lane's scale chunk, relative to row 0
-    // The quotient x / alpha, chosen once per call (uniformly: it depends on
-    // s_g alone):
-    //  - s_g with at most 12 significant bits: fma(x, Y, x D), the two-float
-    //    reciprocal, exact there;
-    //  - otherwise the reciprocal-correction divide.  (For bf16 the plain
-    //    product x / alpha ~ x * RN(1/alpha) is wrong too often to pay: s_g is
-    //    a bf16 amax over 2688 = 21 * 2^7, whose period-6 binary expansion puts
-    //    m alpha within 2^-24 of a bf16 value for many codes.)
-    //  - some code needs operand scaling (tensors below ~1e-21): every tile
-    //    goes through a compact loop that re-reads it from HBM.
+    // pair p's block amax (bf16 bits) -> its table entry
+    auto entry = [&](int p) {
+        const uint32_t ag = (p & 1) ? (am[p >> 1] >> 16) : (am[p >> 1] & 0xFFFFu);
+        return ag == 0 ? 0 : min(max((int)ag - (int)base + 2, 1), RES_NIDX + 1);
+    };
+    // The quotient x / alpha, chosen once per call (uniformly, from the table):
+    //  - the product x * Y_c (every code's Y_c makes it exact for bf16 input);
+    //  - fma(x, Y_c, x * D_c) when some code needs the two-operation form (D_c
+    //    is 0 for the others, where it is the product again);
+    //  - the exact compact loop otherwise (tiny tensors whose small codes need
+    //    operand scaling; a code no form fits), re-reading the tiles from HBM.
     // Only the chosen loop is ever fetched: the unrolled loop's size, not its
-    // arithmetic, is what limits it otherwise.
-    auto full_loop = [&](auto short_tag) {
-        constexpr bool SHORT = decltype(short_tag)::value;
+    // arithmetic, is what limits it otherwise.  The table lookups of pair
+    // p + 1 are issued before pair p's arithmetic.
+    auto full_loop = [&](auto two_op_tag) {
+        constexpr bool TWO = decltype(two_op_tag)::value;
+        int idx = entry(0);
+        float y = T.y[idx];
+        uint32_t c = T.code[idx];
 #pragma unroll
-        for (int j0 = 0; j0 < CPL; j0 += 2) {
+        for (int p = 0; p < NP; ++p) {
             __builtin_amdgcn_sched_barrier(0);  // keep iterations apart: registers are scarce
-            const int j1 = j0 + 1;
+            float yn = 0.0f;
+            uint32_t cn = 0;
+            if (p + 1 < NP) {
+                const int in = entry(p + 1);
+                yn = T.y[in];
+                cn = T.code[in];
+            }
+            const int j0 = 2 * p, j1 = j0 + 1;
             const uint4 w0 = j0 < LC ? lds[j0 * RES_WG + tid] : v[j0 - LC];
             const uint4 w1 = j1 < LC ? lds[j1 * RES_WG + tid] : v[j1 - LC];
-            // widened first: the block amax comes from the fp32 values (finite
-            // here: a non-finite tensor returned before the barrier)
-            float fw[2][8];
-            widen_bf16x8(w0, fw[0]);
-            widen_bf16x8(w1, fw[1]);
-            const uint32_t ag = pair_amax(f2u(absmax8(fw[0])), f2u(absmax8(fw[1])), odd);
-            const PairScales t = pair_scales(ag, R, G, ymin);
+            asm("v_min_f32 %0, %1, %2" : "=v"(ymin) : "v"(ymin), "v"(y));
+            float ys[2], ds[2];
+            pair_rows(y, ys);
+            if (TWO) pair_rows(T.dc[c], ds);
             const int b0 = j0 * stride;
-            if (EXACT || cs <= last - b0) (scales + (b0 >> 1))[(uint32_t)cs >> 1] = (uint8_t)t.c;
+            if (EXACT || cs <= last - b0) (scales + (b0 >> 1))[(uint32_t)cs >> 1] = (uint8_t)c;
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
-                float(&f)[8] = fw[k];
-                const float y = t.ys[k];
+                float f[8];
+                widen_bf16x8(k == 0 ? w0 : w1, f);
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    f[i] = SHORT ? __builtin_fmaf(f[i], y, f[i] * t.ad[k]) : div_rn(f[i], t.ad[k], y);
+                for (int i = 0; i < 8; ++i) f[i] = TWO ? __builtin_fmaf(f[i], ys[k], f[i] * ds[k]) : f[i] * ys[k];
                 const uint32_t q = cvt_fp4x8_f32(f, e8m0_operand(E8M0_ONE));
                 const int bk = (j0 + k) * stride;  // uniform
                 if (EXACT || c00 <= last - bk) __builtin_amdgcn_raw_buffer_store_b32(q, crs, (int)coff, bk * 4, 0);
             }
+            y = yn;
+            c = cn;
         }
     };
-    if (!any_scaled) {
-        if (shrt) full_loop(std::true_type{});
+    if (!(need & NV_NEEDS_EXACT)) {
+        if (need & NV_NEEDS_TWO_OP) full_loop(std::true_type{});
         else full_loop(std::false_type{});
     } else {
-        // the compact loop: (x sc) / alpha' with alpha' = alpha sc from sa
+        // the compact loop: (x sc) / (alpha sc), sc = 2^64 for alpha < 2^-90,
+        // with the reciprocal-correction divide
         for (int j0 = 0; j0 < CPL; j0 += 2) {
             uint4 w[2];
             for (int k = 0; k < 2; ++k) {
                 const int bk = (j0 + k) * stride;
                 w[k] = ld_stream(x + bk + (EXACT ? c00 : min(c00, last - bk)));
             }
-            const uint32_t ag = pair_amax(amax_bf16x8(w[0]), amax_bf16x8(w[1]), odd) << 16;
-            const PairScales t = pair_scales(ag, R, G, ymin);
+            // the block amax again from the tiles (a rolled loop cannot index am)
+            const uint32_t ag = pair_amax(amax_bf16x8(w[0]), amax_bf16x8(w[1]), odd);
+            const int idx = ag == 0 ? 0 : min(max((int)ag - (int)base + 2, 1), RES_NIDX + 1);
+            const uint32_t c = T.code[idx];
+            ymin = __builtin_fminf(ymin, T.y[idx]);
             const int b0 = j0 * stride;
-            if (EXACT || cs <= last - b0) (scales + (b0 >> 1))[(uint32_t)cs >> 1] = (uint8_t)t.c;
-            const float2 sa = R.sa[t.c];
-            const float ad[2] = {dppf<0xA0>(sa.x), dppf<0xF5>(sa.x)};  // rows 0, 1
-            const float sc[2] = {dppf<0xA0>(sa.y), dppf<0xF5>(sa.y)};
+            if (EXACT || cs <= last - b0) (scales + (b0 >> 1))[(uint32_t)cs >> 1] = (uint8_t)c;
+            const float a = ts.s_g * e4m3_pos_value(c);
+            const float sc = a < kDivScaleBelow ? kDivScale : 1.0f;
+            float ad[2], scr[2];
+            pair_rows(a * sc, ad);  // exact
+            pair_rows(sc, scr);
             for (int k = 0; k < 2; ++k) {
                 float f[8];
                 widen_bf16x8(w[k], f);
                 const float y = ad[k] > 0.0f ? 1.0f / ad[k] : 0.0f;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) f[i] = div_rn(f[i] * sc[k], ad[k], y);
+                for (int i = 0; i < 8; ++i) f[i] = div_rn(f[i] * scr[k], ad[k], y);
                 const uint32_t q = cvt_fp4x8_f32(f, e8m0_operand(E8M0_ONE));
                 const int bk = (j0 + k) * stride;
                 if (EXACT || c00 <= last - bk) __builtin_amdgcn_raw_buffer_store_b32(q, crs, (int)coff, bk * 4, 0);

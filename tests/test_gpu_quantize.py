@@ -401,3 +401,41 @@ def test_nv_every_block_amax_under_one_tensor_scale(M, exp):
     for rows, cols in [(2048, 4096), (333, 1040)]:   # exact cover, and ragged
         x = _amax_sweep_tensor(A, M + exp + rows, rows, cols)
         check_nv(x, f"every block amax under amax {A!r} ({_one_pass_form(A)}) {rows}x{cols}")
+
+
+# ---- hazard values of the one-pass kernel's per-code reciprocal --------------------
+
+def _hazard_tensor(A: float) -> torch.Tensor:
+    """One bf16 row: a block holding the tensor amax A (it fixes s_g), then,
+    for every E4M3 code c whose block amax a bf16 value can reach, a block with
+    that amax and, over two blocks, the bf16 values nearest to m alpha_c and
+    their bf16 neighbours for the seven E2M1 decision points m (alpha_c =
+    RN32(s_g E4M3(c))), both signs: the inputs whose product with an inexact
+    reciprocal may round to the wrong side of a decision point."""
+    s_g = np.float32(np.float64(np.float32(A)) / 2688.0)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    blocks = [np.concatenate([[A], np.zeros(15)])]
+    for c in range(1, 127):
+        alpha = np.float64(np.float32(s_g * np.float32(oracle.e4m3_value(c))))
+        ag = _bf16([6.0 * np.float64(s_g) * oracle.e4m3_value(c)])[0]
+        if not (0 < ag <= A):
+            continue
+        near = _bf16(mids * alpha).view(np.uint32)
+        vals = np.concatenate([near - 0x10000, near, near + 0x10000]).view(np.float32)
+        vals = vals[(vals > 0) & (vals < ag)]
+        vals = np.concatenate([vals, -vals])[:30]
+        pad = np.zeros(31 - vals.size, np.float32)
+        two = np.concatenate([[ag], vals, pad]).astype(np.float64)
+        blocks.append(two[:16])
+        blocks.append(np.concatenate([[ag], two[16:31]]))
+    row = np.concatenate(blocks).astype(np.float32)
+    return torch.from_numpy(row).reshape(1, -1).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("exp", [-6, -20, 3])
+def test_nv_hazard_values_every_code_every_bf16_significand(exp):
+    # every one of the 128 bf16 significands of the tensor amax, so every
+    # distinct s_g significand a bf16 tensor can have, at three exponents
+    for j in range(128):
+        A = float(np.float32((128 + j) / 128.0 * 2.0 ** exp))
+        check_nv(_hazard_tensor(A), f"hazards, amax {A!r}")
