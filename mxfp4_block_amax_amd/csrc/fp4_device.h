@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fp4_recip_table.h"
+
 namespace fp4dev {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -333,39 +335,24 @@ __device__ __forceinline__ float div_rn(float x, float alpha, float y) {
 //   index 2 + i  the bf16 magnitude whose bits are base + i.
 // The divisor term Y_c of code c is a reciprocal of alpha_c = RN32(s_g E4M3(c))
 // for which the one product RN32(x Y_c) gives every bf16 x the E2M1 code of
-// the correctly rounded quotient RN32(x / alpha_c):
-//  - Y_c is RN32(1 / alpha_c) or one of its two fp32 neighbours, so RN32(x Y_c)
-//    lies within 2^-21.4 (relative) of x / alpha_c, as does RN32(x / alpha_c);
-//    an E2M1 decision point m (0.25, 0.75, ..., 5) farther than 2^-20 from
-//    x / alpha_c cannot separate them;
-//  - at most one bf16 x lies within 2^-20 of m alpha_c for each m (bf16 values
-//    are 2^-8 apart or more, relatively); the build finds these "hazards" and
-//    takes the first candidate (RN32(1 / alpha), then the one below, then the
-//    one above) under which every hazard's product gets the code of its
-//    correctly rounded quotient (reciprocal-correction divide), both taken on
-//    the converter itself.
-// No candidate fits only at exact ties x = m alpha_c, where alpha_c has few
-// significant bits; such a code takes the two-operation quotient
-// fma(x, Y, x D) with Y = RD32(1 / alpha), D = RN32(1 / alpha - Y), exact for
-// an alpha of at most 16 significant bits.  A code that fits neither form
-// (none known), or an alpha below 2^-90 (operands would need scaling), sends
-// the whole call to the exact compact loop.
+// the correctly rounded quotient RN32(x / alpha_c): RN32(1 / alpha_c) or one
+// of its two fp32 neighbours, as kRecipCorrection (fp4_recip_table.h, with the
+// rule that chose it) gives for the amax significand M and alpha_c's
+// significand 1 + k/8.  Any of the three is within 2^-21.4 of 1 / alpha_c, so
+// it decides every x farther than 2^-20 from a decision point m alpha_c (m =
+// 0.25, 0.75, ..., 5) as the correctly rounded quotient does; the table's
+// choice also decides the bf16 values nearer to one.  Where none fits (exact
+// ties x = m alpha_c, with alpha_c of few significant bits), the code takes
+// the two-operation quotient fma(x, Y, x D) with Y = RD32(1 / alpha),
+// D = RN32(1 / alpha - Y), exact for an alpha of at most 16 significant bits.
+// A tensor whose s_g is not a normal number, or with an alpha below 2^-90
+// (operands would need scaling), takes the exact compact loop instead.
 constexpr int RES_NIDX = 2560;  // window entries: 20 binades of 128 bf16 magnitudes
 constexpr uint32_t NV_NEEDS_TWO_OP = 1;  // some code takes fma(x, Y, x D)
 constexpr uint32_t NV_NEEDS_EXACT = 2;   // some code needs the exact divide loop
 
 struct NvDirectTable {
-    // Y of each entry's code (0 for code 0).  The build's per-code scratch
-    // (alpha_c, RN32(1 / alpha_c), each decision point's failed candidates)
-    // lives in its first entries until the last step writes them.
-    union {
-        float y[RES_NIDX + 2];
-        struct {
-            float a[128];
-            float y0[128];
-            uint8_t fail[128 * 8];
-        } b;
-    };
+    float y[RES_NIDX + 2];       // Y of each entry's code (0 for code 0)
     float yc[128];               // per code: Y_c
     float dc[128];               // per code: D_c (0 where the product alone is exact)
     uint32_t lo[128];            // bf16 bits of the smallest magnitude with code >= c
@@ -398,85 +385,43 @@ __device__ __forceinline__ uint32_t nv_lo_bf16(uint32_t c, float s_g) {
     return b;
 }
 
-// E2M1 code (sign and magnitude) the converter gives one fp32 value.
-__device__ __forceinline__ uint32_t e2m1_code1(float q) {
-    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q, 0.0f, e8m0_operand(E8M0_ONE), 0) & 0xFu;
+// Significand index k (E4M3(c) = (1 + k/8) 2^e) of a nonzero code c.
+__device__ __forceinline__ uint32_t e4m3_frac_index(uint32_t c) {
+    // subnormal codes c 2^-9: 1, 2, 4 -> 1; 3, 6 -> 1.5; 5 -> 1.25; 7 -> 1.75
+    return c >= 8u ? (c & 7u) : ((0x64204000u >> (4u * c)) & 0xFu);
 }
 
-// Builds the table over the workgroup in three steps (per code and decision
-// point; per code; per window entry).  Ends with a barrier; T.need then holds
-// the call's NV_NEEDS_* for every thread.
-__device__ __forceinline__ void nv_direct_table_build(NvDirectTable &T, float s_g, uint32_t base) {
+// Builds the table in two steps (per code; per window entry) for the tensor
+// scale s_g of a bf16 tensor amax with significand index M (its low 7 bits).
+// Ends with a barrier; T.need then holds the call's NV_NEEDS_*.
+__device__ __forceinline__ void nv_direct_table_build(NvDirectTable &T, float s_g, uint32_t M,
+                                                      uint32_t base) {
     const int t = threadIdx.x;
-    // step 1, per (code c, decision point m): the bf16 value nearest m alpha_c
-    // if it lies within 2^-20 of it (a hazard), and which of the candidates
-    // RN32(1 / alpha), its lower and its upper neighbour give it a wrong code
-    // (bits 0, 1, 2 of the point's fail byte)
-    constexpr int ITEMS = 126 * 7;
-#pragma unroll
-    for (int r = 0; r < (ITEMS + 511) / 512; ++r) {
-        const int it = t + r * (int)blockDim.x;
-        if (it >= ITEMS) break;
-        const int c = 1 + it / 7, i = it % 7;
-        const float a = s_g * e4m3_pos_value((uint32_t)c);
-        const float y0 = a > 0.0f ? 1.0f / a : 0.0f;  // correctly rounded
-        if (i == 0) {
-            T.b.a[c] = a;
-            T.b.y0[c] = y0;
-        }
-        uint32_t mask = 0;
-        if (a >= kDivScaleBelow) {  // else: code 0 alpha, or operands needing scaling
-            const float m = i < 4 ? 0.25f + 0.5f * (float)i : (i == 4 ? 2.5f : (i == 5 ? 3.5f : 5.0f));
-            const double tt = (double)m * (double)a;  // exact
-            const uint32_t tb = f2u((float)tt);
-            // nearest bf16 of tt (a double rounding picks the far neighbour
-            // only when tt is near a bf16 midpoint, and then neither is a hazard)
-            const float xh = u2f(((tb + 0x7FFFu + ((tb >> 16) & 1u)) >> 16) << 16);
-            if (__builtin_fabs((double)xh - tt) <= tt * 0x1p-20) {
-                const uint32_t want = e2m1_code1(div_rn(xh, a, y0));
-                mask |= e2m1_code1(xh * y0) != want ? 1u : 0u;
-                mask |= e2m1_code1(xh * u2f(f2u(y0) - 1u)) != want ? 2u : 0u;
-                mask |= e2m1_code1(xh * u2f(f2u(y0) + 1u)) != want ? 4u : 0u;
-            }
-        }
-        T.b.fail[c * 8 + i] = (uint8_t)mask;
-    }
-    if (t == 0) {
-        T.b.a[0] = 0.0f;
-        T.b.y0[0] = 0.0f;
-        T.need = 0u;
-    }
+    if (t == 0) T.need = 0u;
     __syncthreads();
-    // step 2, per code: Y_c, D_c and the code's lower bound
+    // step 1, per code: Y_c, D_c and the code's lower bound
     if (t < 128) {
         float Y = 0.0f, D = 0.0f;
         uint32_t need = 0;
-        if (t > 0 && t < 127) {
-            const float a = T.b.a[t], y0 = T.b.y0[t];
-            const uint2 f2 = *(const uint2 *)&T.b.fail[t * 8];
-            const uint32_t fo = f2.x | (f2.y & 0x00FFFFFFu);
-            const uint32_t fail = (fo | (fo >> 8) | (fo >> 16) | (fo >> 24)) & 7u;
-            if (a > 0.0f && a < kDivScaleBelow) {  // operands would need scaling: exact loop
-                Y = 1.0f;
+        const float a = t > 0 && t < 127 ? s_g * e4m3_pos_value((uint32_t)t) : 0.0f;
+        if (a > 0.0f) {
+            const uint32_t sel = (kRecipCorrection[M & 127u] >> (2u * e4m3_frac_index((uint32_t)t))) & 3u;
+            const float y0 = 1.0f / a;  // correctly rounded
+            if (a < kDivScaleBelow || s_g < 0x1p-126f) {  // outside the table's rule: exact loop
+                Y = y0;
                 need = NV_NEEDS_EXACT;
-            } else if (a > 0.0f) {
-                if (!(fail & 1u)) {
-                    Y = y0;
-                } else if (!(fail & 2u)) {
-                    Y = u2f(f2u(y0) - 1u);
-                } else if (!(fail & 4u)) {
-                    Y = u2f(f2u(y0) + 1u);
-                } else if ((f2u(a) & 0xFFu) == 0u && a >= 0x1p-126f) {  // <= 16 significant bits
-                    const double r = 1.0 / (double)a;
-                    float yh = (float)r;
-                    if ((double)yh > r) yh = u2f(f2u(yh) - 1u);
-                    Y = yh;
-                    D = (float)(r - (double)yh);
-                    need = NV_NEEDS_TWO_OP;
-                } else {
-                    Y = y0;
-                    need = NV_NEEDS_EXACT;
-                }
+            } else if (sel < 3u) {
+                Y = sel == 0u ? y0 : u2f(f2u(y0) + (sel == 1u ? ~0u : 1u));
+            } else if ((f2u(a) & 0xFFu) == 0u) {  // at most 16 significant bits
+                const double r = 1.0 / (double)a;
+                float yh = (float)r;
+                if ((double)yh > r) yh = u2f(f2u(yh) - 1u);
+                Y = yh;
+                D = (float)(r - (double)yh);
+                need = NV_NEEDS_TWO_OP;
+            } else {
+                Y = y0;
+                need = NV_NEEDS_EXACT;
             }
         }
         T.yc[t] = Y;
@@ -485,7 +430,7 @@ __device__ __forceinline__ void nv_direct_table_build(NvDirectTable &T, float s_
         if (need) atomicOr(&T.need, need);
     }
     __syncthreads();
-    // step 3, per window entry: the code of a bf16 magnitude, from a guess
+    // step 2, per window entry: the code of a bf16 magnitude, from a guess
     // within one code of it settled by the two bounds around it
     const CodeGuess G = make_code_guess(s_g);
 #pragma unroll

@@ -810,7 +810,7 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
         return;
     }
     const uint32_t base = nv_window_base(ts.s_g);
-    nv_direct_table_build(T, ts.s_g, base);  // ends with a barrier
+    nv_direct_table_build(T, ts.s_g, tensor_amax, base);  // ends with a barrier
     const uint32_t need = T.need;            // uniform
 
     // ---- phase 2: quantize from LDS and registers -----------------------
