@@ -159,6 +159,12 @@ __device__ __forceinline__ float e4m3_pos_value(uint32_t c) {
                    : (float)c * 0x1p-9f;
 }
 
+// Significand index k (E4M3(c) = (1 + k/8) 2^e) of a nonzero code c.
+__device__ __forceinline__ uint32_t e4m3_frac_index(uint32_t c) {
+    // subnormal codes c 2^-9: 1, 2, 4 -> 1; 3, 6 -> 1.5; 5 -> 1.25; 7 -> 1.75
+    return c >= 8u ? (c & 7u) : ((0x64204000u >> (4u * c)) & 0xFu);
+}
+
 // 6 times the midpoint between codes c and c+1, c in [0, 125]; exact in fp32.
 // Subnormal side: (2c+1) * 2^-10; normal side: 2^(E-7) (17 + 2f) / 16.
 __device__ __forceinline__ float e4m3_mid6(uint32_t c) {
@@ -196,6 +202,7 @@ constexpr float kDivScaleBelow = 0x1p-90f;
 struct NvScaleTable {
     float lo[128];
     float4 q[127];
+    float yc[127];  // the reciprocal the one-product quotient uses (when q.z > 0)
     double th[128];
 };
 
@@ -244,11 +251,29 @@ __device__ __forceinline__ float4 nv_divisor(int c, float s_g) {
     return make_float4(a, ad, y, sc);
 }
 
-__device__ __forceinline__ void nv_table_build(NvScaleTable &T, float s_g) {
+// recipM: for a bf16 tensor whose s_g is a normal number, the significand
+// index M of its amax (low 7 bits of its bf16 pattern), else -1.  With it,
+// a code's one-product quotient uses the corrected reciprocal of
+// kRecipCorrection (fp4_recip_table.h: exact for every bf16 input, see the
+// direct table below) and is marked only where no reciprocal fits; without
+// it, the plain RN32(1/alpha') is used where no 8-significant-bit value
+// comes near a decision point (near_bf16_midpoint), and the rest is marked.
+__device__ __forceinline__ void nv_table_build(NvScaleTable &T, float s_g, int recipM) {
     for (int k = threadIdx.x; k < 128; k += blockDim.x) {
         T.lo[k] = nv_lo(k, s_g);
         T.th[k] = k == 0 ? -1.0 : (k == 127 ? __builtin_inf() : nv_threshold(k, s_g));
-        if (k < 127) T.q[k] = nv_divisor(k, s_g);
+        if (k < 127) {
+            float4 q = nv_divisor(k, s_g);
+            float yc = __builtin_fabsf(q.z);
+            if (recipM >= 0 && q.x > 0.0f && q.w == 1.0f) {
+                const uint32_t sel = (kRecipCorrection[recipM & 127] >> (2u * e4m3_frac_index((uint32_t)k))) & 3u;
+                q.z = sel < 3u ? yc : -yc;
+                if (sel == 1u) yc = u2f(f2u(yc) - 1u);
+                if (sel == 2u) yc = u2f(f2u(yc) + 1u);
+            }
+            T.q[k] = q;
+            T.yc[k] = yc;
+        }
     }
 }
 
@@ -383,12 +408,6 @@ __device__ __forceinline__ uint32_t nv_lo_bf16(uint32_t c, float s_g) {
         ++b;
     }
     return b;
-}
-
-// Significand index k (E4M3(c) = (1 + k/8) 2^e) of a nonzero code c.
-__device__ __forceinline__ uint32_t e4m3_frac_index(uint32_t c) {
-    // subnormal codes c 2^-9: 1, 2, 4 -> 1; 3, 6 -> 1.5; 5 -> 1.25; 7 -> 1.75
-    return c >= 8u ? (c & 7u) : ((0x64204000u >> (4u * c)) & 0xFu);
 }
 
 // Builds the table in two steps (per code; per window entry) for the tensor

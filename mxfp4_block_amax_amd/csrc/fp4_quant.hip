@@ -385,12 +385,20 @@ __global__ __launch_bounds__(WG) void tensor_amax_kernel(const uint4 *__restrict
 struct TensorScale {
     float s_g;
     uint32_t flags;
+    uint32_t amax;  // fp32 bits of the tensor amax
 };
+
+// kRecipCorrection's row for a tensor (see nv_table_build), or -1.
+template <bool BF16>
+__device__ __forceinline__ int recip_row(const TensorScale &ts) {
+    return BF16 && ts.s_g >= 0x1p-126f ? (int)((ts.amax >> 16) & 127u) : -1;
+}
 
 // s_g from the fp32 bit pattern of the tensor amax.
 __device__ __forceinline__ TensorScale scale_from_amax(uint32_t A) {
     TensorScale ts;
     ts.flags = 0;
+    ts.amax = A;
     if (A >= 0x7F800000u) {
         ts.flags = FLAG_NONFINITE;
         ts.s_g = 1.0f;
@@ -417,10 +425,11 @@ __device__ TensorScale tensor_scale(const uint32_t *__restrict__ partials, int n
 // Per-block NVFP4 scale from the workgroup's table: the E4M3 code and the
 // divide operands alpha', +-1/alpha', sc (x / alpha is done as
 // (x sc) / alpha'; a negative reciprocal marks a scale whose one-multiply
-// quotient may differ for some bf16 input).  A zero block takes scale 1
-// (code 0x38).
+// quotient may differ for some bf16 input), and yc, the reciprocal of the
+// one-multiply quotient.  A zero block takes scale 1 (code 0x38).
 struct BlockScale {
     float a, ad, y, sc;  // a: alpha itself
+    float yc;
     uint32_t code;
 };
 
@@ -434,6 +443,7 @@ __device__ __forceinline__ BlockScale nv_block_scale(const NvScaleTable &T, uint
     b.ad = q.y;
     b.y = q.z;
     b.sc = q.w;
+    b.yc = T.yc[b.code];
     const bool under = (ag_bits != 0 && c == 0) || q.z == 0.0f;
     flags |= under ? FLAG_SCALE_UNDERFLOW : 0u;
     return b;
@@ -449,17 +459,18 @@ __device__ __forceinline__ void scale_values(float (&v)[8], float sc) {
 }
 
 // E2M1 codes of 8 values divided by alpha, the fp32 correctly rounded
-// quotient, given alpha' = alpha sc, ys = +-RN32(1 / alpha') and sc.  BF16:
-// the inputs have at most 8 significant bits, so unless some lane's scale is
-// marked (ys < 0) the product with the reciprocal decides the same codes.
+// quotient, given alpha' = alpha sc, ys = +-RN32(1 / alpha'), sc and yc.
+// BF16: the inputs have at most 8 significant bits, so unless some lane's
+// scale is marked (ys < 0) the product with yc decides the same codes.
 template <bool BF16>
-__device__ __forceinline__ uint32_t nv_quant8(float (&v)[8], float ad, float ys, float sc) {
+__device__ __forceinline__ uint32_t nv_quant8(float (&v)[8], float ad, float ys, float sc,
+                                              float yc) {
     scale_values(v, sc);
     const float y = __builtin_fabsf(ys);
     float q[8];
     if (BF16 && !__ballot(ys < 0.0f)) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = v[i] * y;
+        for (int i = 0; i < 8; ++i) q[i] = v[i] * yc;
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) q[i] = div_rn(v[i], ad, y);
@@ -528,7 +539,7 @@ __global__ __launch_bounds__(WG) void nv_quantize_kernel(const uint4 *__restrict
         if (blockIdx.x == 0 && threadIdx.x == 0 && status) atomicOr(status, (int32_t)ts.flags);
         return;
     }
-    nv_table_build(T, ts.s_g);
+    nv_table_build(T, ts.s_g, recip_row<BF16>(ts));
     __syncthreads();
     const CodeGuess G = make_code_guess(ts.s_g);
     const int lane = threadIdx.x & (WAVE - 1);
@@ -546,10 +557,11 @@ __global__ __launch_bounds__(WG) void nv_quantize_kernel(const uint4 *__restrict
         m1 = max(m1, dpp<QP_XOR1>(m1));
         BlockScale mine = nv_block_scale(T, amax_as_f32_bits<BF16>(odd ? m1 : m0), G, flags);
         const float pa = dppf<QP_XOR1>(mine.ad), py = dppf<QP_XOR1>(mine.y),
-                    ps = dppf<QP_XOR1>(mine.sc);
+                    ps = dppf<QP_XOR1>(mine.sc), pc = dppf<QP_XOR1>(mine.yc);
         // row 0 uses the even lane's scale, row 1 the odd lane's
         const float a0 = odd ? pa : mine.ad, y0 = odd ? py : mine.y, s0 = odd ? ps : mine.sc;
         const float a1 = odd ? mine.ad : pa, y1 = odd ? mine.y : py, s1 = odd ? mine.sc : ps;
+        const float c0y = odd ? pc : mine.yc, c1y = odd ? mine.yc : pc;
         float v[8];
         uint32_t q0, q1;
         if (SR) {
@@ -560,9 +572,9 @@ __global__ __launch_bounds__(WG) void nv_quantize_kernel(const uint4 *__restrict
             q1 = nv_sr8(v, odd ? mine.a : pal, seed, c1);
         } else {
             chunk_values<BF16>(k0, v);
-            q0 = nv_quant8<BF16>(v, a0, y0, s0);
+            q0 = nv_quant8<BF16>(v, a0, y0, s0, c0y);
             chunk_values<BF16>(k1, v);
-            q1 = nv_quant8<BF16>(v, a1, y1, s1);
+            q1 = nv_quant8<BF16>(v, a1, y1, s1, c1y);
         }
         if (c0 < nchunks) codes[c0] = q0;
         if (c1 < nchunks) codes[c1] = q1;
@@ -647,7 +659,7 @@ __global__ __launch_bounds__(WG) void nv_quantize_packed_kernel(
         if (blockIdx.x == 0 && threadIdx.x == 0 && status) atomicOr(status, (int32_t)ts.flags);
         return;
     }
-    nv_table_build(T, ts.s_g);
+    nv_table_build(T, ts.s_g, recip_row<BF16>(ts));
     __syncthreads();
     const CodeGuess G = make_code_guess(ts.s_g);
     const int lane = threadIdx.x & (WAVE - 1);
@@ -675,7 +687,7 @@ __global__ __launch_bounds__(WG) void nv_quantize_packed_kernel(
         for (int i = 0; i < 4; ++i) {
             const BlockScale &b = i < 2 ? sa : sb;
             chunk_values<BF16>(k[i], v);
-            q[i] = nv_quant8<BF16>(v, b.ad, b.y, b.sc);
+            q[i] = nv_quant8<BF16>(v, b.ad, b.y, b.sc, b.yc);
         }
         codes[t * 64 + lane] = ok ? make_uint4(q[0], q[1], q[2], q[3]) : make_uint4(0u, 0u, 0u, 0u);
         const uint16_t sc = ok ? (uint16_t)(sa.code | (sb.code << 8)) : (uint16_t)0;
@@ -1032,11 +1044,11 @@ __global__ __launch_bounds__(WG) void dequant_kernel(const uint32_t *__restrict_
 // error as the signed values.
 // ---------------------------------------------------------------------------
 template <bool BF16>
-__device__ __forceinline__ float half_block_loss(const float (&a)[8], float4 sq) {
+__device__ __forceinline__ float half_block_loss(const float (&a)[8], float4 sq, float yc) {
     // sq = {alpha, alpha', +-1/alpha', sc}: divide as (a sc) / alpha' (one
-    // multiply for bf16 input when no lane's scale is marked), rebuild with alpha
-    // Both choices are wave-uniform; operands are scaled (x sc, exact) only
-    // when some lane of the wave needs it (tensors with a tiny s_g).
+    // multiply by yc for bf16 input when no lane's scale is marked), rebuild
+    // with alpha.  Both choices are wave-uniform; operands are scaled (x sc,
+    // exact) only when some lane of the wave needs it (tensors with a tiny s_g).
     const float alpha = sq.x;
     const float y = __builtin_fabsf(sq.z);
     const bool scaled = __ballot(sq.w != 1.0f) != 0;
@@ -1044,10 +1056,10 @@ __device__ __forceinline__ float half_block_loss(const float (&a)[8], float4 sq)
     if (BF16 && !__ballot(sq.z < 0.0f)) {
         if (!scaled) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) q[i] = a[i] * y;
+            for (int i = 0; i < 8; ++i) q[i] = a[i] * yc;
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) q[i] = (a[i] * sq.w) * y;
+            for (int i = 0; i < 8; ++i) q[i] = (a[i] * sq.w) * yc;
         }
     } else {
         if (!scaled) {
@@ -1092,7 +1104,7 @@ __global__ __launch_bounds__(WG) void scale_search_kernel(
         if (blockIdx.x == 0 && threadIdx.x == 0 && status) atomicOr(status, (int32_t)ts.flags);
         return;
     }
-    nv_table_build(T, ts.s_g);
+    nv_table_build(T, ts.s_g, recip_row<BF16>(ts));
     __syncthreads();
     const double inv6sg = 1.0 / (6.0 * (double)ts.s_g);
     const int lane = threadIdx.x & (WAVE - 1);
@@ -1136,7 +1148,7 @@ __global__ __launch_bounds__(WG) void scale_search_kernel(
                 if (bound > bestL) break;
                 // a code whose alpha underflowed to 0 is evaluated (its loss
                 // is finite) but never taken
-                float part = half_block_loss<BF16>(a, sq);
+                float part = half_block_loss<BF16>(a, sq, T.yc[code]);
                 float L = part + dppf<QP_XOR1>(part);
                 if (sq.x != 0.0f && L <= bestL) {
                     best = code;
@@ -1151,7 +1163,7 @@ __global__ __launch_bounds__(WG) void scale_search_kernel(
         }
         const float4 sq = T.q[best];
         chunk_values<BF16>(k, a);
-        uint32_t q = nv_quant8<BF16>(a, sq.y, sq.z, sq.w);
+        uint32_t q = nv_quant8<BF16>(a, sq.y, sq.z, sq.w, T.yc[best]);
         if (c < nchunks) {
             codes[c] = q;
             if ((lane & 1) == 0) scales[c >> 1] = (uint8_t)best;
@@ -1253,7 +1265,7 @@ __global__ __launch_bounds__(WG) void nv_quantize_padded_kernel(
         if (blockIdx.x == 0 && threadIdx.x == 0 && status) atomicOr(status, (int32_t)ts.flags);
         return;
     }
-    nv_table_build(T, ts.s_g);
+    nv_table_build(T, ts.s_g, -1);
     __syncthreads();
     const CodeGuess G = make_code_guess(ts.s_g);
     const int lane = threadIdx.x & (WAVE - 1);
@@ -1266,7 +1278,7 @@ __global__ __launch_bounds__(WG) void nv_quantize_padded_kernel(
         uint32_t m = padded_values<BF16>(x, cols, cpr, c, c < nchunks, v);
         m = max(m, dpp<QP_XOR1>(m));
         const BlockScale b = nv_block_scale(T, m, G, flags);
-        const uint32_t q = nv_quant8<false>(v, b.ad, b.y, b.sc);
+        const uint32_t q = nv_quant8<false>(v, b.ad, b.y, b.sc, b.yc);
         if (c < nchunks) {
             codes[c] = q;
             if ((lane & 1) == 0) scales[c >> 1] = (uint8_t)b.code;

@@ -439,3 +439,28 @@ def test_nv_hazard_values_every_code_every_bf16_significand(exp):
     for j in range(128):
         A = float(np.float32((128 + j) / 128.0 * 2.0 ** exp))
         check_nv(_hazard_tensor(A), f"hazards, amax {A!r}")
+
+
+def test_nv_hazard_values_two_pass_quantize_and_scale_search():
+    # the same hazard tensors through the two-pass encoder (here its packed
+    # form, which shares the block-scale table and quotient) and through the
+    # scale search, whose candidates use the same corrected reciprocals
+    import oracle.gemm as og
+    for j in range(128):
+        A = float(np.float32((128 + j) / 128.0 * 2.0 ** -6))
+        t = _hazard_tensor(A)
+        x = torch.zeros(1, 4096, dtype=torch.bfloat16)
+        x[:, : t.shape[1]] = t
+        announce(f"hazards two-pass packed quantize + search, amax {A!r}")
+        got, sg = fp4.quantize_nvfp4_packed(dev(x))
+        codes, scales, sgs = fp4.scale_search(dev(x))
+        torch.cuda.synchronize()
+        xo = oracle_view(x)
+        p, sc, sg_ref, flags = oracle.nv_quantize(xo)
+        assert flags == 0
+        assert np.float32(sg.item()) == np.float32(sg_ref)
+        assert_bytes_equal(host_u8(got), og.nv_pack_operand(p, sc, 1, 4096), f"packed, amax {A!r}")
+        p, s, f2 = oracle.scale_search_with_scale(xo, sg_ref, 64, 0.5, 1.0)
+        assert f2 == 0
+        assert_bytes_equal(host_u8(scales), s, f"search scales, amax {A!r}")
+        assert_bytes_equal(host_u8(codes), p, f"search codes, amax {A!r}")
