@@ -1090,6 +1090,273 @@ __device__ __forceinline__ float half_block_loss(const float (&a)[8], float4 sq,
     return ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
 }
 
+// ---- the bf16 search with per-code tables and a work queue -----------------
+// For a bf16 tensor whose s_g is a normal number (and every divisor alpha_c,
+// c >= 1, at least 2^-90) a workgroup tabulates per code c:
+//   {alpha_c, Y_c, D_c, RN32(6 alpha_c)}: the block quotient of code c is
+//   RN32(x Y_c) (D_c = 0) or fma(x, Y_c, x D_c), chosen per code as in the
+//   one-pass quantize (kRecipCorrection): the E2M1 code of the correctly
+//   rounded quotient for every bf16 x;
+//   thi[c], tlo[c]: bf16 bits of the smallest block amax whose upper / lower
+//   candidate code, the RN-even E4M3 code of c_hi amax / (6 s_g) (c_lo ...),
+//   is at least c.  A block's candidate code is then its fp32 guess g (the
+//   truncated code of amax RN32(c / (6 s_g)), within one code below the
+//   exact one) plus whether its amax reaches thi[g + 1].
+// The loss is that of half_block_loss on the signed values (the quotient,
+// the E2M1 code and the error are odd in x, and the squared error is even),
+// so the code word of the best candidate is the block's output as it stands.
+//
+// A lane pair walks its block's first two candidates in place; a block that
+// still has one to evaluate then goes to its wave's queue in LDS (its 16
+// values, its best code word and its walk state), and once 32 blocks wait
+// the wave evaluates the next candidate of 32 of them at once, putting back
+// those that go on.  Every block visits the same codes in the same order as
+// a plain walk, so the result is the same; only the lanes' idle time changes
+// (a wave no longer waits for its slowest block).
+struct SearchTable {
+    float4 e[128];      // per code: {alpha, Y, D, RN32(6 alpha)}; code 0 and 127: zeros
+    uint16_t thi[128];  // thi[0] = 0, thi[127] = 0xFFFF (no amax reaches code 127)
+    uint16_t tlo[128];
+};
+constexpr int SQ_CAP = 64;  // a wave's queue holds < 32 blocks between passes, plus 32
+struct SearchQueue {
+    uint4 data[SQ_CAP][2];     // lane h of the pair: its 8 bf16 values
+    uint4 st[SQ_CAP];          // {block index, code | lo << 8 | best << 16, best loss, amax}
+    uint32_t bq[SQ_CAP][2];    // lane h: its code word at the best candidate so far
+};
+struct SearchShared {
+    SearchTable tab;
+    SearchQueue q[WAVES_PER_WG];
+};
+
+// bits of the smallest positive bf16 magnitude v with candidate code >= c
+// (1 <= c <= 126): c_mul v (exact in binary64) above the exact threshold
+// 6 s_g midpoint(c - 1, c), or on it when c is even.  0x7F80: no finite v.
+__device__ __forceinline__ uint32_t search_bound_bf16(uint32_t c, float s_g, float cmul) {
+    const double th = nv_threshold((int)c, s_g);
+    uint32_t b = f2u((float)(th / (double)cmul)) >> 16;  // within a unit of the answer
+    b = b > 1u ? b - 1u : 0u;
+    for (int k = 0; k < 4 && b < 0x7F80u; ++k) {
+        const double z = (double)cmul * (double)u2f(b << 16);
+        if (z > th || (z == th && (c & 1u) == 0)) break;
+        ++b;
+    }
+    return min(b, 0x7F80u);
+}
+
+// Builds the table; returns (to every thread, after a barrier) whether the
+// table's rule covers the call (else the generic walk runs).
+template <bool ALL>
+__device__ __forceinline__ bool search_table_build(SearchTable &S, const TensorScale &ts, float c_lo,
+                                                   float c_hi) {
+    const int t = threadIdx.x;
+    int slow = 0;
+    if (t < 128) {
+        const float s_g = ts.s_g;
+        const uint32_t M = (ts.amax >> 16) & 127u;
+        float a = 0.0f, Y = 0.0f, D = 0.0f;
+        if (t >= 1 && t <= 126) {
+            a = s_g * e4m3_pos_value((uint32_t)t);
+            const uint32_t sel = (kRecipCorrection[M] >> (2u * e4m3_frac_index((uint32_t)t))) & 3u;
+            const float y0 = 1.0f / a;  // correctly rounded
+            if (!(a >= kDivScaleBelow) || !(s_g >= 0x1p-126f)) {
+                slow = 1;
+            } else if (sel < 3u) {
+                Y = sel == 0u ? y0 : u2f(f2u(y0) + (sel == 1u ? ~0u : 1u));
+            } else if ((f2u(a) & 0xFFu) == 0u) {  // at most 16 significant bits
+                const double r = 1.0 / (double)a;
+                float yh = (float)r;
+                if ((double)yh > r) yh = u2f(f2u(yh) - 1u);
+                Y = yh;
+                D = (float)(r - (double)yh);
+            } else {
+                slow = 1;
+            }
+        }
+        S.e[t] = make_float4(a, Y, D, 6.0f * a);
+        if (!ALL) {
+            const uint32_t c = (uint32_t)t;
+            S.thi[t] = (uint16_t)(c == 0 ? 0u : (c == 127 ? 0xFFFFu : search_bound_bf16(c, s_g, c_hi)));
+            S.tlo[t] = (uint16_t)(c == 0 ? 0u : (c == 127 ? 0xFFFFu : search_bound_bf16(c, s_g, c_lo)));
+        }
+    }
+    return __syncthreads_or(slow) == 0;
+}
+
+// Loss of one candidate on the lane's 8 signed values (see half_block_loss),
+// and the lane's code word.  TWO: the two-operation quotient.
+template <bool TWO>
+__device__ __forceinline__ float cand_half_loss(const float (&a)[8], float4 e, uint32_t &code) {
+    float q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = TWO ? __builtin_fmaf(a[i], e.y, a[i] * e.z) : a[i] * e.y;
+    const float one = e8m0_operand(E8M0_ONE);
+    code = cvt_fp4x8_f32(q, one);
+    float t[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f32x2_t p;
+        switch (j) {  // the byte selector must be a constant
+            case 0: p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, one, 0); break;
+            case 1: p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, one, 1); break;
+            case 2: p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, one, 2); break;
+            default: p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, one, 3); break;
+        }
+        float e0 = a[2 * j] - p.x * e.x;
+        float e1 = a[2 * j + 1] - p.y * e.x;
+        t[2 * j] = e0 * e0;
+        t[2 * j + 1] = e1 * e1;
+    }
+    return ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+}
+
+// The walk state of the lane pair's block.
+struct Walk {
+    int code;       // next candidate; < lo when the walk has ended
+    int lo;
+    int best;
+    float bestL;
+    uint32_t bq;    // this lane's code word at the best candidate
+    float agf;      // block amax
+};
+
+// Evaluates the pair's next candidate where `go` (uniform over the pair),
+// then steps the walk.  Every lane of the wave takes part (the pair sum is a
+// lane exchange).
+__device__ __forceinline__ void walk_step(const SearchTable &S, const float (&a)[8], Walk &w, bool go) {
+    const float4 e = S.e[max(w.code, 0)];
+    uint32_t q;
+    float part = __ballot(go && e.z != 0.0f) ? cand_half_loss<true>(a, e, q)
+                                              : cand_half_loss<false>(a, e, q);
+    const float L = part + dppf<QP_XOR1>(part);
+    if (go && L <= w.bestL) {
+        w.best = w.code;
+        w.bestL = L;
+        w.bq = q;
+    }
+    if (go) --w.code;
+}
+
+// Whether the walk goes on: a next code in range that the early-stop bound
+// (see scale_search_kernel) does not rule out.
+__device__ __forceinline__ bool walk_goes_on(const SearchTable &S, const Walk &w) {
+    const float x6 = S.e[max(w.code, 0)].w;
+    const float e6 = w.agf - x6;
+    const float bound = w.agf >= x6 ? e6 * e6 : 0.0f;
+    return w.code >= w.lo && !(bound > w.bestL);
+}
+
+__device__ __forceinline__ void walk_finish(const Walk &w, int64_t c, uint32_t *__restrict__ codes,
+                                            uint8_t *__restrict__ scales, uint32_t &flags) {
+    codes[c] = w.bq;
+    if ((c & 1) == 0) scales[c >> 1] = (uint8_t)w.best;
+    if (w.best == 0 && w.agf != 0.0f) flags |= FLAG_SCALE_UNDERFLOW;
+}
+
+// Pushes the pairs with `more` onto the wave's queue; n: the queue's length
+// (wave-uniform).
+__device__ __forceinline__ void queue_push(SearchQueue &Q, int &n, bool more, uint4 k, const Walk &w,
+                                           int64_t c) {
+    const int lane = __lane_id();
+    const uint64_t even = __ballot(more && (lane & 1) == 0);
+    const int slot = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(even >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)even, 0u)) -
+                     (lane & 1);  // the odd lane counts its partner, which is below it
+    if (more) {
+        Q.data[slot][lane & 1] = k;
+        Q.bq[slot][lane & 1] = w.bq;
+        if ((lane & 1) == 0)
+            Q.st[slot] = make_uint4((uint32_t)(c >> 1),
+                                    (uint32_t)w.code | ((uint32_t)w.lo << 8) | ((uint32_t)w.best << 16),
+                                    f2u(w.bestL), f2u(w.agf));
+    }
+    n += __builtin_popcountll(even);
+}
+
+// One pass over the top m (<= 32) blocks of the queue: each evaluates its
+// next candidate; those whose walk goes on are pushed back, the rest written.
+__device__ __forceinline__ void queue_pass(const SearchTable &S, SearchQueue &Q, int &n, int m,
+                                           uint32_t *__restrict__ codes, uint8_t *__restrict__ scales,
+                                           uint32_t &flags) {
+    const int lane = __lane_id();
+    const int p = lane >> 1;
+    const bool act = p < m;
+    const int j = n - m + (act ? p : 0);
+    const uint4 k = Q.data[j][lane & 1];
+    const uint4 st = Q.st[j];
+    Walk w;
+    w.bq = Q.bq[j][lane & 1];
+    w.code = (int)(st.y & 0xFFu);
+    w.lo = (int)((st.y >> 8) & 0xFFu);
+    w.best = (int)(st.y >> 16);
+    w.bestL = u2f(st.z);
+    w.agf = u2f(st.w);
+    const int64_t c = (int64_t)st.x * 2 + (lane & 1);
+    float a[8];
+    widen_bf16x8(k, a);
+    walk_step(S, a, w, act);
+    const bool more = act && walk_goes_on(S, w);
+    if (act && !more) walk_finish(w, c, codes, scales, flags);
+    n -= m;
+    queue_push(Q, n, more, k, w, c);
+}
+
+template <bool ALL>
+__device__ __forceinline__ void search_bf16_tiles(const SearchShared &SS, SearchQueue &Q,
+                                                  const uint4 *__restrict__ x, int64_t nchunks,
+                                                  float r_lo, float r_hi, uint32_t *__restrict__ codes,
+                                                  uint8_t *__restrict__ scales, uint32_t &flags) {
+    const SearchTable &S = SS.tab;
+    const int lane = __lane_id();
+    const int64_t wave = (int64_t)blockIdx.x * WAVES_PER_WG + (threadIdx.x / WAVE);
+    const int64_t nwaves = (int64_t)gridDim.x * WAVES_PER_WG;
+    const int64_t ntiles = (nchunks + WAVE - 1) / WAVE;
+    int n = 0;  // blocks waiting in the queue
+    for (int64_t t = wave; t < ntiles; t += nwaves) {
+        const int64_t c = t * WAVE + lane;
+        const bool ok = c < nchunks;
+        const uint4 k = ok ? ld_stream(x + c) : make_uint4(0, 0, 0, 0);
+        uint32_t m = amax_bf16x8(k);
+        m = max(m, dpp<QP_XOR1>(m));  // block amax (bf16 bits)
+        Walk w;
+        w.agf = u2f(m << 16);
+        if (m == 0) {
+            w.code = w.lo = 0x38;  // a zero block: scale 1, all codes zero
+        } else if (ALL) {
+            w.code = 126;
+            w.lo = 1;
+        } else {
+            const uint32_t gh = e4m3_trunc_code(w.agf * r_hi), gl = e4m3_trunc_code(w.agf * r_lo);
+            const int hi = (int)(gh + (m >= S.thi[gh + 1] ? 1u : 0u));
+            const int lo = max((int)(gl + (m >= S.tlo[gl + 1] ? 1u : 0u)), 1);
+            w.code = hi >= lo ? hi : 0;  // none in range: code 0, a scale underflow
+            w.lo = hi >= lo ? lo : 0;
+        }
+        w.best = 0;
+        w.bestL = __builtin_inff();
+        w.bq = 0;
+        float a[8];
+        widen_bf16x8(k, a);
+        walk_step(S, a, w, true);  // the first candidate always exists
+        bool more = walk_goes_on(S, w);
+        if (__ballot(more)) {
+            walk_step(S, a, w, more);
+            more = more && walk_goes_on(S, w);
+        }
+        if (ok && !more) walk_finish(w, c, codes, scales, flags);
+        queue_push(Q, n, ok && more, k, w, c);
+        n = __builtin_amdgcn_readfirstlane(n);
+        while (n >= 32) {
+            queue_pass(S, Q, n, 32, codes, scales, flags);
+            n = __builtin_amdgcn_readfirstlane(n);
+        }
+    }
+    while (n > 0) {
+        queue_pass(S, Q, n, min(n, 32), codes, scales, flags);
+        n = __builtin_amdgcn_readfirstlane(n);
+    }
+}
+
 // ALL: every E4M3 code 1..126 is a candidate (the format page's brute force,
 // section 4), instead of the codes the candidate range c_lo..c_hi reaches.
 template <bool BF16, bool ALL>
@@ -1097,13 +1364,29 @@ __global__ __launch_bounds__(WG) void scale_search_kernel(
     const uint4 *__restrict__ x, int64_t nchunks, const uint32_t *__restrict__ partials,
     int npart, float c_lo, float c_hi, uint32_t *__restrict__ codes,
     uint8_t *__restrict__ scales, float *__restrict__ global_scale, int32_t *status) {
-    __shared__ NvScaleTable T;
+    constexpr size_t kShared = BF16 && sizeof(SearchShared) > sizeof(NvScaleTable) ? sizeof(SearchShared)
+                                                                                    : sizeof(NvScaleTable);
+    __shared__ __align__(16) uint8_t smem[kShared];
     TensorScale ts = tensor_scale<BF16>(partials, npart);
     if (blockIdx.x == 0 && threadIdx.x == 0) *global_scale = ts.s_g;
     if (ts.flags) {
         if (blockIdx.x == 0 && threadIdx.x == 0 && status) atomicOr(status, (int32_t)ts.flags);
         return;
     }
+    uint32_t flags = 0;
+    if constexpr (BF16) {
+        SearchShared &S = *reinterpret_cast<SearchShared *>(smem);
+        // the queue stores block indices in 32 bits
+        if (search_table_build<ALL>(S.tab, ts, c_lo, c_hi) && (nchunks >> 33) == 0) {
+            const double d6 = 6.0 * (double)ts.s_g;
+            search_bf16_tiles<ALL>(S, S.q[threadIdx.x / WAVE], x, nchunks, (float)((double)c_lo / d6),
+                                   (float)((double)c_hi / d6), codes, scales, flags);
+            report_flags(status, flags);
+            return;
+        }
+        // (uniform: no thread reads the search table again)
+    }
+    NvScaleTable &T = *reinterpret_cast<NvScaleTable *>(smem);
     nv_table_build(T, ts.s_g, recip_row<BF16>(ts));
     __syncthreads();
     const double inv6sg = 1.0 / (6.0 * (double)ts.s_g);
@@ -1111,7 +1394,6 @@ __global__ __launch_bounds__(WG) void scale_search_kernel(
     const int64_t wave = (int64_t)blockIdx.x * WAVES_PER_WG + (threadIdx.x / WAVE);
     const int64_t nwaves = (int64_t)gridDim.x * WAVES_PER_WG;
     const int64_t ntiles = (nchunks + WAVE - 1) / WAVE;
-    uint32_t flags = 0;
     for (int64_t t = wave; t < ntiles; t += nwaves) {
         const int64_t c = t * WAVE + lane;
         Chunk<BF16> k = load_chunk<BF16>(x, c, c < nchunks);

@@ -86,6 +86,29 @@ def test_search_small_laplace_full_compare():
     y = torch.randn(32, 512, generator=g) * torch.rand(32, 512, generator=g) ** 3 * 1e-3
     _search_check(y, "heavy-tailed fp32 32x512")
     _search_check((y * 2.0 ** -120).to(torch.float32), "tiny magnitudes 2^-120")
+    # bf16 with s_g below the normal range: the generic walk (exact divides)
+    _search_check((y * 2.0 ** -120).to(torch.bfloat16), "tiny magnitudes bf16 2^-120")
+    # bf16, a ragged last tile (222 chunks): blocks still queued when a
+    # wave's tiles run out are drained in partial passes
+    _search_check(workloads.scale_search_input(3, 592, seed=4), "laplace bf16 3x592")
+    _search_check(workloads.scale_search_input(3, 592, seed=4), "laplace bf16 3x592 wide", c_hi=1.5)
+
+
+def test_search_scale_underflow_flag_bf16():
+    # a block whose amax is far below the tensor amax has no candidate code
+    # (every one rounds to code 0): the oracle and the kernel both flag it
+    x = torch.tensor([1.0] * 16 + [2.0 ** -24] * 16 + [0.5, -0.25] * 8).reshape(1, 48)
+    x = x.to(torch.bfloat16)
+    p, s, sg, f = oracle.scale_search(oracle_view(x))
+    assert f == fp4.FLAG_SCALE_UNDERFLOW
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    announce("scale search bf16 with a scale underflow")
+    codes, scales, s_g = fp4.scale_search(dev(x), check=False, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == f
+    # the underflowing block gets code 0 and zero codes, the others their search
+    assert_bytes_equal(host_u8(scales), s, "search scales with an underflow")
+    assert_bytes_equal(host_u8(codes), p, "search codes with an underflow")
 
 
 def test_search_full_size_every_block():
