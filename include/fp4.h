@@ -226,7 +226,8 @@ fp4_status fp4_dequantize(fp4_format fmt, const uint8_t *codes, const uint8_t *s
  *   1/15 of their value wide, so the distinct candidate scales of a block
  *   are exactly the consecutive E4M3 codes between the two ends).
  *   Other arguments as for fp4_quantize_nvfp4 (two kernels: tensor amax, then
- *   search and quantize).  Deterministic.
+ *   search and quantize); codes must be at least 8-byte aligned (FP4_E_ALIGN).
+ *   Deterministic.
  */
 fp4_status fp4_scale_search(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
                             int32_t block, int32_t n_candidates, float c_lo, float c_hi,

@@ -195,7 +195,8 @@ fp4_status fp4_scale_search(const void *x, fp4_dtype xt, int64_t rows, int64_t c
     fp4_status st = check_shape(rows, cols, block);
     if (st != FP4_OK) return st;
     if (!workspace || workspace_bytes < nv_workspace()) return FP4_E_WORKSPACE;
-    if (!aligned(x, 16) || !aligned(codes, 4) || !aligned(global_scale, 4) ||
+    // a block's 16 codes are stored as one 8-byte word
+    if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(global_scale, 4) ||
         !aligned(workspace, 16) || !aligned(status, 4))
         return FP4_E_ALIGN;
     return from_hip(fp4dev::launch_scale_search(x, xt == FP4_BF16, rows * cols, false, c_lo,
@@ -213,7 +214,8 @@ fp4_status fp4_scale_search_exhaustive(const void *x, fp4_dtype xt, int64_t rows
     fp4_status st = check_shape(rows, cols, block);
     if (st != FP4_OK) return st;
     if (!workspace || workspace_bytes < nv_workspace()) return FP4_E_WORKSPACE;
-    if (!aligned(x, 16) || !aligned(codes, 4) || !aligned(global_scale, 4) ||
+    // a block's 16 codes are stored as one 8-byte word
+    if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(global_scale, 4) ||
         !aligned(workspace, 16) || !aligned(status, 4))
         return FP4_E_ALIGN;
     return from_hip(fp4dev::launch_scale_search(x, xt == FP4_BF16, rows * cols, true, 0.0f, 0.0f,

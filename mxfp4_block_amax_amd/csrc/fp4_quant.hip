@@ -1093,36 +1093,39 @@ __device__ __forceinline__ float half_block_loss(const float (&a)[8], float4 sq,
 // ---- the bf16 search with per-code tables and a work queue -----------------
 // For a bf16 tensor whose s_g is a normal number (and every divisor alpha_c,
 // c >= 1, at least 2^-90) a workgroup tabulates per code c:
-//   {alpha_c, Y_c, D_c, RN32(6 alpha_c)}: the block quotient of code c is
+//   {alpha_c, tlo[c + 1], Y_c, D_c}: the block quotient of code c is
 //   RN32(x Y_c) (D_c = 0) or fma(x, Y_c, x D_c), chosen per code as in the
 //   one-pass quantize (kRecipCorrection): the E2M1 code of the correctly
 //   rounded quotient for every bf16 x;
 //   thi[c], tlo[c]: bf16 bits of the smallest block amax whose upper / lower
 //   candidate code, the RN-even E4M3 code of c_hi amax / (6 s_g) (c_lo ...),
-//   is at least c.  A block's candidate code is then its fp32 guess g (the
-//   truncated code of amax RN32(c / (6 s_g)), within one code below the
-//   exact one) plus whether its amax reaches thi[g + 1].
+//   is at least c.  A block's upper code is its fp32 guess g (the truncated
+//   code of amax RN32(c_hi / (6 s_g)), within one code below the exact one)
+//   plus whether its amax reaches thi[g + 1]; code c is at or above the
+//   lower code when the amax stays below tlo[c + 1].
 // The loss is that of half_block_loss on the signed values (the quotient,
 // the E2M1 code and the error are odd in x, and the squared error is even),
-// so the code word of the best candidate is the block's output as it stands.
+// so the code words of the best candidate are the block's output as they
+// stand.
 //
-// A lane pair walks its block's first two candidates in place; a block that
-// still has one to evaluate then goes to its wave's queue in LDS (its 16
-// values, its best code word and its walk state), and once 32 blocks wait
-// the wave evaluates the next candidate of 32 of them at once, putting back
+// Each lane holds one block (16 values).  It walks its first two candidates
+// in place; a block that still has one to evaluate then goes to its wave's
+// queue in LDS (its 16 values and its walk state), and once 64 blocks wait
+// the wave evaluates the next candidate of 64 of them at once, putting back
 // those that go on.  Every block visits the same codes in the same order as
 // a plain walk, so the result is the same; only the lanes' idle time changes
 // (a wave no longer waits for its slowest block).
 struct SearchTable {
-    float4 e[128];      // per code: {alpha, Y, D, RN32(6 alpha)}; code 0 and 127: zeros
+    float4 e[128];      // per code: {alpha, tlo[c + 1] bits, Y, D}; code 0 and 127: alpha = 0
     uint16_t thi[128];  // thi[0] = 0, thi[127] = 0xFFFF (no amax reaches code 127)
-    uint16_t tlo[128];
 };
-constexpr int SQ_CAP = 64;  // a wave's queue holds < 32 blocks between passes, plus 32
+// Between passes a queue holds < 64 blocks; a tile adds at most 32 (a tile
+// with more steps its blocks in place until at most 32 remain).
+constexpr int SQ_CAP = 96;
 struct SearchQueue {
-    uint4 data[SQ_CAP][2];     // lane h of the pair: its 8 bf16 values
-    uint4 st[SQ_CAP];          // {block index, code | lo << 8 | best << 16, best loss, amax}
-    uint32_t bq[SQ_CAP][2];    // lane h: its code word at the best candidate so far
+    uint4 data[SQ_CAP][2];  // the block's 16 bf16 values
+    uint2 st[SQ_CAP];       // {block index, next code | best code << 8 | amax bits << 16}
+    float bestL[SQ_CAP];    // the best loss so far
 };
 struct SearchShared {
     SearchTable tab;
@@ -1173,25 +1176,32 @@ __device__ __forceinline__ bool search_table_build(SearchTable &S, const TensorS
                 slow = 1;
             }
         }
-        S.e[t] = make_float4(a, Y, D, 6.0f * a);
+        // every code is at or above the lower code 1 of the exhaustive search
+        const uint32_t c1 = (uint32_t)t + 1u;
+        const uint32_t tlo = ALL || c1 >= 127u ? 0xFFFFu : search_bound_bf16(c1, s_g, c_lo);
+        S.e[t] = make_float4(a, u2f(tlo), Y, D);
         if (!ALL) {
             const uint32_t c = (uint32_t)t;
             S.thi[t] = (uint16_t)(c == 0 ? 0u : (c == 127 ? 0xFFFFu : search_bound_bf16(c, s_g, c_hi)));
-            S.tlo[t] = (uint16_t)(c == 0 ? 0u : (c == 127 ? 0xFFFFu : search_bound_bf16(c, s_g, c_lo)));
         }
     }
     return __syncthreads_or(slow) == 0;
 }
 
-// Loss of one candidate on the lane's 8 signed values (see half_block_loss),
-// and the lane's code word.  TWO: the two-operation quotient.
+// The code word of 8 values a[0..7] under a code's quotient (TWO: the
+// two-operation one).
 template <bool TWO>
-__device__ __forceinline__ float cand_half_loss(const float (&a)[8], float4 e, uint32_t &code) {
+__device__ __forceinline__ uint32_t cand_codes8(const float *a, float4 e) {
     float q[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = TWO ? __builtin_fmaf(a[i], e.y, a[i] * e.z) : a[i] * e.y;
+    for (int i = 0; i < 8; ++i) q[i] = TWO ? __builtin_fmaf(a[i], e.z, a[i] * e.w) : a[i] * e.z;
+    return cvt_fp4x8_f32(q, e8m0_operand(E8M0_ONE));
+}
+
+// Sum of the squared errors of a[0..7] with code word `code` under alpha:
+// ((t0+t1)+(t2+t3))+((t4+t5)+(t6+t7)), one half of the block's pairwise tree.
+__device__ __forceinline__ float half_sq_error(const float *a, uint32_t code, float alpha) {
     const float one = e8m0_operand(E8M0_ONE);
-    code = cvt_fp4x8_f32(q, one);
     float t[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -1202,33 +1212,35 @@ __device__ __forceinline__ float cand_half_loss(const float (&a)[8], float4 e, u
             case 2: p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, one, 2); break;
             default: p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, one, 3); break;
         }
-        float e0 = a[2 * j] - p.x * e.x;
-        float e1 = a[2 * j + 1] - p.y * e.x;
+        float e0 = a[2 * j] - p.x * alpha;
+        float e1 = a[2 * j + 1] - p.y * alpha;
         t[2 * j] = e0 * e0;
         t[2 * j + 1] = e1 * e1;
     }
     return ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
 }
 
-// The walk state of the lane pair's block.
+// The block's code words under a code (wave-uniform choice of quotient).
+__device__ __forceinline__ uint2 cand_codes16(const float (&a)[16], float4 e, bool two) {
+    if (two) return make_uint2(cand_codes8<true>(a, e), cand_codes8<true>(a + 8, e));
+    return make_uint2(cand_codes8<false>(a, e), cand_codes8<false>(a + 8, e));
+}
+
+// The walk state of the lane's block.
 struct Walk {
-    int code;       // next candidate; < lo when the walk has ended
-    int lo;
+    int code;       // next candidate
     int best;
     float bestL;
-    uint32_t bq;    // this lane's code word at the best candidate
+    uint2 bq;       // code words at the best candidate (when known)
     float agf;      // block amax
+    uint32_t agb;   // its bf16 bits
 };
 
-// Evaluates the pair's next candidate where `go` (uniform over the pair),
-// then steps the walk.  Every lane of the wave takes part (the pair sum is a
-// lane exchange).
-__device__ __forceinline__ void walk_step(const SearchTable &S, const float (&a)[8], Walk &w, bool go) {
+// Evaluates the lane's next candidate where `go`, then steps the walk.
+__device__ __forceinline__ void walk_step(const SearchTable &S, const float (&a)[16], Walk &w, bool go) {
     const float4 e = S.e[max(w.code, 0)];
-    uint32_t q;
-    float part = __ballot(go && e.z != 0.0f) ? cand_half_loss<true>(a, e, q)
-                                              : cand_half_loss<false>(a, e, q);
-    const float L = part + dppf<QP_XOR1>(part);
+    const uint2 q = cand_codes16(a, e, __ballot(go && e.w != 0.0f) != 0);
+    const float L = half_sq_error(a, q.x, e.x) + half_sq_error(a + 8, q.y, e.x);
     if (go && L <= w.bestL) {
         w.best = w.code;
         w.bestL = L;
@@ -1237,122 +1249,155 @@ __device__ __forceinline__ void walk_step(const SearchTable &S, const float (&a)
     if (go) --w.code;
 }
 
+// Whether code w.code is a candidate: at least 1 and at or above the lower
+// code (a zero block has its one code only).
+__device__ __forceinline__ bool walk_in_range(float2 g, const Walk &w) {
+    return w.code >= 1 && w.agb != 0u && w.agb < f2u(g.y);
+}
+
 // Whether the walk goes on: a next code in range that the early-stop bound
 // (see scale_search_kernel) does not rule out.
 __device__ __forceinline__ bool walk_goes_on(const SearchTable &S, const Walk &w) {
-    const float x6 = S.e[max(w.code, 0)].w;
+    const float2 g = *reinterpret_cast<const float2 *>(&S.e[max(w.code, 0)]);
+    const float x6 = 6.0f * g.x;
     const float e6 = w.agf - x6;
     const float bound = w.agf >= x6 ? e6 * e6 : 0.0f;
-    return w.code >= w.lo && !(bound > w.bestL);
+    return walk_in_range(g, w) && !(bound > w.bestL);
 }
 
-__device__ __forceinline__ void walk_finish(const Walk &w, int64_t c, uint32_t *__restrict__ codes,
+__device__ __forceinline__ void walk_finish(const Walk &w, int64_t b, uint32_t *__restrict__ codes,
                                             uint8_t *__restrict__ scales, uint32_t &flags) {
-    codes[c] = w.bq;
-    if ((c & 1) == 0) scales[c >> 1] = (uint8_t)w.best;
-    if (w.best == 0 && w.agf != 0.0f) flags |= FLAG_SCALE_UNDERFLOW;
+    reinterpret_cast<uint2 *>(codes)[b] = w.bq;
+    scales[b] = (uint8_t)w.best;
+    if (w.best == 0 && w.agb != 0u) flags |= FLAG_SCALE_UNDERFLOW;
 }
 
-// Pushes the pairs with `more` onto the wave's queue; n: the queue's length
-// (wave-uniform).
-__device__ __forceinline__ void queue_push(SearchQueue &Q, int &n, bool more, uint4 k, const Walk &w,
-                                           int64_t c) {
-    const int lane = __lane_id();
-    const uint64_t even = __ballot(more && (lane & 1) == 0);
-    const int slot = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(even >> 32),
-                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)even, 0u)) -
-                     (lane & 1);  // the odd lane counts its partner, which is below it
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (f2u(hi) & 0xFFFF0000u) | (f2u(lo) >> 16);
+}
+
+// Pushes the lanes with `more` onto the wave's queue; n: its length (uniform).
+__device__ __forceinline__ void queue_push(SearchQueue &Q, int &n, bool more, const float (&a)[16],
+                                           const Walk &w, int64_t b) {
+    const uint64_t bal = __ballot(more);
+    const int slot = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
     if (more) {
-        Q.data[slot][lane & 1] = k;
-        Q.bq[slot][lane & 1] = w.bq;
-        if ((lane & 1) == 0)
-            Q.st[slot] = make_uint4((uint32_t)(c >> 1),
-                                    (uint32_t)w.code | ((uint32_t)w.lo << 8) | ((uint32_t)w.best << 16),
-                                    f2u(w.bestL), f2u(w.agf));
+        Q.data[slot][0] = make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                     pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7]));
+        Q.data[slot][1] = make_uint4(pack_bf16x2(a[8], a[9]), pack_bf16x2(a[10], a[11]),
+                                     pack_bf16x2(a[12], a[13]), pack_bf16x2(a[14], a[15]));
+        Q.st[slot] = make_uint2((uint32_t)b, (uint32_t)w.code | ((uint32_t)w.best << 8) | (w.agb << 16));
+        Q.bestL[slot] = w.bestL;
     }
-    n += __builtin_popcountll(even);
+    n += __builtin_popcountll(bal);
 }
 
-// One pass over the top m (<= 32) blocks of the queue: each evaluates its
-// next candidate; those whose walk goes on are pushed back, the rest written.
+__device__ __forceinline__ void widen_block(uint4 k0, uint4 k1, float (&a)[16]) {
+    float (&lo)[8] = *reinterpret_cast<float (*)[8]>(&a[0]);
+    float (&hi)[8] = *reinterpret_cast<float (*)[8]>(&a[8]);
+    widen_bf16x8(k0, lo);
+    widen_bf16x8(k1, hi);
+}
+
+// One pass over the top m (<= 64) blocks of the queue: each evaluates its
+// next candidate; those whose walk goes on are pushed back, the rest written
+// (their code words recomputed where the best candidate is an earlier one).
 __device__ __forceinline__ void queue_pass(const SearchTable &S, SearchQueue &Q, int &n, int m,
                                            uint32_t *__restrict__ codes, uint8_t *__restrict__ scales,
                                            uint32_t &flags) {
     const int lane = __lane_id();
-    const int p = lane >> 1;
-    const bool act = p < m;
-    const int j = n - m + (act ? p : 0);
-    const uint4 k = Q.data[j][lane & 1];
-    const uint4 st = Q.st[j];
+    const bool act = lane < m;
+    const int j = n - m + (act ? lane : 0);
+    const uint2 st = Q.st[j];
     Walk w;
-    w.bq = Q.bq[j][lane & 1];
+    w.bestL = Q.bestL[j];
     w.code = (int)(st.y & 0xFFu);
-    w.lo = (int)((st.y >> 8) & 0xFFu);
-    w.best = (int)(st.y >> 16);
-    w.bestL = u2f(st.z);
-    w.agf = u2f(st.w);
-    const int64_t c = (int64_t)st.x * 2 + (lane & 1);
-    float a[8];
-    widen_bf16x8(k, a);
+    w.best = (int)((st.y >> 8) & 0xFFu);
+    w.agb = st.y >> 16;
+    w.agf = u2f(w.agb << 16);
+    w.bq = make_uint2(0, 0);
+    float a[16];
+    widen_block(Q.data[j][0], Q.data[j][1], a);
+    const int evaluated = w.code;
     walk_step(S, a, w, act);
     const bool more = act && walk_goes_on(S, w);
-    if (act && !more) walk_finish(w, c, codes, scales, flags);
+    const bool fin = act && !more;
+    if (__ballot(fin && w.best != evaluated)) {
+        const float4 e = S.e[w.best];
+        const uint2 q = cand_codes16(a, e, __ballot(fin && w.best != evaluated && e.w != 0.0f) != 0);
+        if (w.best != evaluated) w.bq = q;
+    }
+    if (fin) walk_finish(w, st.x, codes, scales, flags);
     n -= m;
-    queue_push(Q, n, more, k, w, c);
+    queue_push(Q, n, more, a, w, st.x);
 }
 
+// k0, k1: the wave's first tile, loaded by the caller before the table build.
 template <bool ALL>
 __device__ __forceinline__ void search_bf16_tiles(const SearchShared &SS, SearchQueue &Q,
-                                                  const uint4 *__restrict__ x, int64_t nchunks,
-                                                  float r_lo, float r_hi, uint32_t *__restrict__ codes,
+                                                  const uint4 *__restrict__ x, int64_t nblocks,
+                                                  uint4 k0, uint4 k1, float r_hi,
+                                                  uint32_t *__restrict__ codes,
                                                   uint8_t *__restrict__ scales, uint32_t &flags) {
     const SearchTable &S = SS.tab;
     const int lane = __lane_id();
     const int64_t wave = (int64_t)blockIdx.x * WAVES_PER_WG + (threadIdx.x / WAVE);
     const int64_t nwaves = (int64_t)gridDim.x * WAVES_PER_WG;
-    const int64_t ntiles = (nchunks + WAVE - 1) / WAVE;
+    const int64_t ntiles = (nblocks + WAVE - 1) / WAVE;
     int n = 0;  // blocks waiting in the queue
     for (int64_t t = wave; t < ntiles; t += nwaves) {
-        const int64_t c = t * WAVE + lane;
-        const bool ok = c < nchunks;
-        const uint4 k = ok ? ld_stream(x + c) : make_uint4(0, 0, 0, 0);
-        uint32_t m = amax_bf16x8(k);
-        m = max(m, dpp<QP_XOR1>(m));  // block amax (bf16 bits)
+        const int64_t b = t * WAVE + lane;
+        const bool ok = b < nblocks;
+        const int64_t bn = b + nwaves * WAVE;  // the next tile's, loaded while this one is searched
+        uint4 n0 = make_uint4(0, 0, 0, 0), n1 = n0;
+        if (bn < nblocks) {
+            n0 = ld_stream(x + 2 * bn);
+            n1 = ld_stream(x + 2 * bn + 1);
+        }
         Walk w;
-        w.agf = u2f(m << 16);
-        if (m == 0) {
-            w.code = w.lo = 0x38;  // a zero block: scale 1, all codes zero
+        w.agb = max(amax_bf16x8(k0), amax_bf16x8(k1));
+        w.agf = u2f(w.agb << 16);
+        if (w.agb == 0) {
+            w.code = 0x38;  // a zero block: scale 1, all codes zero
         } else if (ALL) {
             w.code = 126;
-            w.lo = 1;
         } else {
-            const uint32_t gh = e4m3_trunc_code(w.agf * r_hi), gl = e4m3_trunc_code(w.agf * r_lo);
-            const int hi = (int)(gh + (m >= S.thi[gh + 1] ? 1u : 0u));
-            const int lo = max((int)(gl + (m >= S.tlo[gl + 1] ? 1u : 0u)), 1);
-            w.code = hi >= lo ? hi : 0;  // none in range: code 0, a scale underflow
-            w.lo = hi >= lo ? lo : 0;
+            const uint32_t gh = e4m3_trunc_code(w.agf * r_hi);
+            const uint32_t hi = gh + (w.agb >= S.thi[gh + 1] ? 1u : 0u);
+            // none in range (hi is 0 or below the lower code): code 0, a scale underflow
+            w.code = hi >= 1u && w.agb < f2u(S.e[hi].y) ? (int)hi : 0;
         }
         w.best = 0;
         w.bestL = __builtin_inff();
-        w.bq = 0;
-        float a[8];
-        widen_bf16x8(k, a);
+        w.bq = make_uint2(0, 0);
+        float a[16];
+        widen_block(k0, k1, a);
         walk_step(S, a, w, true);  // the first candidate always exists
-        bool more = walk_goes_on(S, w);
+        // the second without the early-stop test: a code the bound rules out
+        // has a loss above the best and is not taken, and the test after it
+        // stops the walk
+        bool more = walk_in_range(*reinterpret_cast<const float2 *>(&S.e[max(w.code, 0)]), w);
         if (__ballot(more)) {
             walk_step(S, a, w, more);
             more = more && walk_goes_on(S, w);
         }
-        if (ok && !more) walk_finish(w, c, codes, scales, flags);
-        queue_push(Q, n, ok && more, k, w, c);
+        while (n + __builtin_popcountll(__ballot(more)) > SQ_CAP) {
+            walk_step(S, a, w, more);
+            more = more && walk_goes_on(S, w);
+        }
+        if (ok && !more) walk_finish(w, b, codes, scales, flags);
+        queue_push(Q, n, ok && more, a, w, b);
         n = __builtin_amdgcn_readfirstlane(n);
-        while (n >= 32) {
-            queue_pass(S, Q, n, 32, codes, scales, flags);
+        while (n >= WAVE) {
+            queue_pass(S, Q, n, WAVE, codes, scales, flags);
             n = __builtin_amdgcn_readfirstlane(n);
         }
+        k0 = n0;
+        k1 = n1;
     }
     while (n > 0) {
-        queue_pass(S, Q, n, min(n, 32), codes, scales, flags);
+        queue_pass(S, Q, n, min(n, WAVE), codes, scales, flags);
         n = __builtin_amdgcn_readfirstlane(n);
     }
 }
@@ -1367,6 +1412,16 @@ __global__ __launch_bounds__(WG) void scale_search_kernel(
     constexpr size_t kShared = BF16 && sizeof(SearchShared) > sizeof(NvScaleTable) ? sizeof(SearchShared)
                                                                                     : sizeof(NvScaleTable);
     __shared__ __align__(16) uint8_t smem[kShared];
+    // bf16: the wave's first tile (a block per lane), in flight during the set-up
+    uint4 k0 = make_uint4(0, 0, 0, 0), k1 = k0;
+    if (BF16) {
+        const int64_t b0 = ((int64_t)blockIdx.x * WAVES_PER_WG + threadIdx.x / WAVE) * WAVE +
+                           (threadIdx.x & (WAVE - 1));
+        if (b0 < nchunks / 2) {
+            k0 = ld_stream(x + 2 * b0);
+            k1 = ld_stream(x + 2 * b0 + 1);
+        }
+    }
     TensorScale ts = tensor_scale<BF16>(partials, npart);
     if (blockIdx.x == 0 && threadIdx.x == 0) *global_scale = ts.s_g;
     if (ts.flags) {
@@ -1378,9 +1433,8 @@ __global__ __launch_bounds__(WG) void scale_search_kernel(
         SearchShared &S = *reinterpret_cast<SearchShared *>(smem);
         // the queue stores block indices in 32 bits
         if (search_table_build<ALL>(S.tab, ts, c_lo, c_hi) && (nchunks >> 33) == 0) {
-            const double d6 = 6.0 * (double)ts.s_g;
-            search_bf16_tiles<ALL>(S, S.q[threadIdx.x / WAVE], x, nchunks, (float)((double)c_lo / d6),
-                                   (float)((double)c_hi / d6), codes, scales, flags);
+            search_bf16_tiles<ALL>(S, S.q[threadIdx.x / WAVE], x, nchunks / 2, k0, k1,
+                                   (float)((double)c_hi / (6.0 * (double)ts.s_g)), codes, scales, flags);
             report_flags(status, flags);
             return;
         }
@@ -1779,6 +1833,25 @@ hipError_t launch_quantize_sr(int fmt, const void *x, bool bf16, int64_t n, uint
     return hipGetLastError();
 }
 
+// Workgroups of the bf16 search resident at once on the current device
+// (kMaxGrid if the device cannot be queried).  Probed once per device.
+static int search_grid_cap() {
+    static int cap[kMaxDevices];
+    static std::once_flag once[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return kMaxGrid;
+    std::call_once(once[dev], [dev] {
+        int cus = 0, per_cu = 0;
+        cap[dev] = kMaxGrid;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scale_search_kernel<true, false>, WG,
+                                                         0) == hipSuccess &&
+            cus > 0 && per_cu > 0)
+            cap[dev] = cus * per_cu < kMaxGrid ? cus * per_cu : kMaxGrid;
+    });
+    return cap[dev];
+}
+
 hipError_t launch_scale_search(const void *x, bool bf16, int64_t n, bool all, float c_lo,
                                float c_hi, uint8_t *codes, uint8_t *scales, float *global_scale,
                                void *workspace, int32_t *status, hipStream_t s) {
@@ -1787,12 +1860,14 @@ hipError_t launch_scale_search(const void *x, bool bf16, int64_t n, bool all, fl
     const int g1 = amax_grid(nchunks);
     hipError_t e = launch_amax(x, bf16, nchunks, partials, g1, s);
     if (e != hipSuccess) return e;
-    const int g = grid_for((nchunks + WAVE - 1) / WAVE, kMaxGrid);
     using K = void (*)(const uint4 *, int64_t, const uint32_t *, int, float, float, uint32_t *,
                        uint8_t *, float *, int32_t *);
     static const K kernels[2][2] = {
         {scale_search_kernel<false, false>, scale_search_kernel<false, true>},
         {scale_search_kernel<true, false>, scale_search_kernel<true, true>}};
+    // bf16: at most the workgroups the device holds at once (each sets up its
+    // tables once and its waves drain their queues once)
+    const int g = grid_for((nchunks + WAVE - 1) / WAVE, bf16 ? search_grid_cap() : kMaxGrid);
     hipLaunchKernelGGL(kernels[bf16 ? 1 : 0][all ? 1 : 0], dim3(g), dim3(WG), 0, s,
                        (const uint4 *)x, nchunks, partials, g1, c_lo, c_hi, (uint32_t *)codes,
                        scales, global_scale, status);

@@ -100,6 +100,9 @@ def test_search_validation():
     assert s(hi=5.0, n=4096) == E_ARG
     assert s(block=32) == E_ARG
     assert s(cols=24) == E_SHAPE
+    # a block's codes are one 8-byte store
+    assert L.fp4_scale_search(A16, fp4.BF16, 4, 64, 16, 64, 0.5, 1.0, ctypes.c_void_p(0x10004), A16,
+                              A16, A16, 1 << 20, NULL, NULL) == E_ALIGN
 
 
 def test_mx_rule_validation():
@@ -127,6 +130,8 @@ def test_exhaustive_search_validation():
     assert s(cols=24) == E_SHAPE
     assert s(ws=NULL) == E_WORKSPACE
     assert s(wsb=8) == E_WORKSPACE
+    assert L.fp4_scale_search_exhaustive(A16, fp4.BF16, 4, 64, 16, ctypes.c_void_p(0x10004), A16, A16,
+                                         A16, 1 << 20, NULL, NULL) == E_ALIGN
 
 
 def test_linear_validation():
