@@ -1130,6 +1130,25 @@ struct SearchQueue {
 struct SearchShared {
     SearchTable tab;
     SearchQueue q[WAVES_PER_WG];
+    int left[WAVES_PER_WG];  // blocks left in each wave's queue after its tiles
+};
+
+// The blocks waiting: pool index p lives in queue k at entry p - start_k.
+// MULTI = false: one queue.  MULTI: the workgroup's queues back to back
+// (queue k from s[k - 1]), drained together at the end.
+template <bool MULTI>
+struct QueuePool {
+    SearchQueue *q;
+    int s1, s2, s3;
+    __device__ __forceinline__ SearchQueue &at(int p, int &j) const {
+        if (!MULTI) {
+            j = p;
+            return q[0];
+        }
+        const int k = (p >= s1 ? 1 : 0) + (p >= s2 ? 1 : 0) + (p >= s3 ? 1 : 0);
+        j = p - (k == 0 ? 0 : (k == 1 ? s1 : (k == 2 ? s2 : s3)));
+        return q[k];
+    }
 };
 
 // bits of the smallest positive bf16 magnitude v with candidate code >= c
@@ -1276,13 +1295,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (f2u(hi) & 0xFFFF0000u) | (f2u(lo) >> 16);
 }
 
-// Pushes the lanes with `more` onto the wave's queue; n: its length (uniform).
-__device__ __forceinline__ void queue_push(SearchQueue &Q, int &n, bool more, const float (&a)[16],
-                                           const Walk &w, int64_t b) {
+// Pushes the lanes with `more` onto the pool; n: its length (uniform).
+template <bool MULTI>
+__device__ __forceinline__ void queue_push(const QueuePool<MULTI> &P, int &n, bool more,
+                                           const float (&a)[16], const Walk &w, int64_t b) {
     const uint64_t bal = __ballot(more);
-    const int slot = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    const int p = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
     if (more) {
+        int slot;
+        SearchQueue &Q = P.at(p, slot);
         Q.data[slot][0] = make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
                                      pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7]));
         Q.data[slot][1] = make_uint4(pack_bf16x2(a[8], a[9]), pack_bf16x2(a[10], a[11]),
@@ -1300,15 +1322,17 @@ __device__ __forceinline__ void widen_block(uint4 k0, uint4 k1, float (&a)[16]) 
     widen_bf16x8(k1, hi);
 }
 
-// One pass over the top m (<= 64) blocks of the queue: each evaluates its
+// One pass over the top m (<= 64) blocks of the pool: each evaluates its
 // next candidate; those whose walk goes on are pushed back, the rest written
 // (their code words recomputed where the best candidate is an earlier one).
-__device__ __forceinline__ void queue_pass(const SearchTable &S, SearchQueue &Q, int &n, int m,
-                                           uint32_t *__restrict__ codes, uint8_t *__restrict__ scales,
-                                           uint32_t &flags) {
+template <bool MULTI>
+__device__ __forceinline__ void queue_pass(const SearchTable &S, const QueuePool<MULTI> &P, int &n,
+                                           int m, uint32_t *__restrict__ codes,
+                                           uint8_t *__restrict__ scales, uint32_t &flags) {
     const int lane = __lane_id();
     const bool act = lane < m;
-    const int j = n - m + (act ? lane : 0);
+    int j;
+    SearchQueue &Q = P.at(n - m + (act ? lane : 0), j);
     const uint2 st = Q.st[j];
     Walk w;
     w.bestL = Q.bestL[j];
@@ -1330,31 +1354,30 @@ __device__ __forceinline__ void queue_pass(const SearchTable &S, SearchQueue &Q,
     }
     if (fin) walk_finish(w, st.x, codes, scales, flags);
     n -= m;
-    queue_push(Q, n, more, a, w, st.x);
+    queue_push(P, n, more, a, w, st.x);
 }
 
 // k0, k1: the wave's first tile, loaded by the caller before the table build.
 template <bool ALL>
-__device__ __forceinline__ void search_bf16_tiles(const SearchShared &SS, SearchQueue &Q,
+__device__ __forceinline__ void search_bf16_tiles(SearchShared &SS,
                                                   const uint4 *__restrict__ x, int64_t nblocks,
                                                   uint4 k0, uint4 k1, float r_hi,
                                                   uint32_t *__restrict__ codes,
                                                   uint8_t *__restrict__ scales, uint32_t &flags) {
     const SearchTable &S = SS.tab;
-    const int lane = __lane_id();
-    const int64_t wave = (int64_t)blockIdx.x * WAVES_PER_WG + (threadIdx.x / WAVE);
+    const int lane = __lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+    const QueuePool<false> P{&SS.q[wv], 0, 0, 0};
+    const int64_t wave = (int64_t)blockIdx.x * WAVES_PER_WG + wv;
     const int64_t nwaves = (int64_t)gridDim.x * WAVES_PER_WG;
     const int64_t ntiles = (nblocks + WAVE - 1) / WAVE;
     int n = 0;  // blocks waiting in the queue
     for (int64_t t = wave; t < ntiles; t += nwaves) {
         const int64_t b = t * WAVE + lane;
         const bool ok = b < nblocks;
-        const int64_t bn = b + nwaves * WAVE;  // the next tile's, loaded while this one is searched
-        uint4 n0 = make_uint4(0, 0, 0, 0), n1 = n0;
-        if (bn < nblocks) {
-            n0 = ld_stream(x + 2 * bn);
-            n1 = ld_stream(x + 2 * bn + 1);
-        }
+        // the next tile's block, loaded while this one is searched (past the
+        // end: the last block again, never used)
+        const int64_t bn = min(b + nwaves * WAVE, nblocks - 1);
+        const uint4 n0 = ld_stream(x + 2 * bn), n1 = ld_stream(x + 2 * bn + 1);
         Walk w;
         w.agb = max(amax_bf16x8(k0), amax_bf16x8(k1));
         w.agf = u2f(w.agb << 16);
@@ -1387,25 +1410,33 @@ __device__ __forceinline__ void search_bf16_tiles(const SearchShared &SS, Search
             more = more && walk_goes_on(S, w);
         }
         if (ok && !more) walk_finish(w, b, codes, scales, flags);
-        queue_push(Q, n, ok && more, a, w, b);
+        queue_push(P, n, ok && more, a, w, b);
         n = __builtin_amdgcn_readfirstlane(n);
         while (n >= WAVE) {
-            queue_pass(S, Q, n, WAVE, codes, scales, flags);
+            queue_pass(S, P, n, WAVE, codes, scales, flags);
             n = __builtin_amdgcn_readfirstlane(n);
         }
         k0 = n0;
         k1 = n1;
     }
-    while (n > 0) {
-        queue_pass(S, Q, n, min(n, WAVE), codes, scales, flags);
-        n = __builtin_amdgcn_readfirstlane(n);
+    // the blocks left in the four queues (< 64 each) are drained by one wave,
+    // in passes over all of them
+    if (lane == 0) SS.left[wv] = n;
+    __syncthreads();
+    if (wv != 0) return;
+    const int s1 = SS.left[0], s2 = s1 + SS.left[1], s3 = s2 + SS.left[2];
+    const QueuePool<true> all{&SS.q[0], s1, s2, s3};
+    int left = s3 + SS.left[3];
+    while (left > 0) {
+        queue_pass(S, all, left, min(left, WAVE), codes, scales, flags);
+        left = __builtin_amdgcn_readfirstlane(left);
     }
 }
 
 // ALL: every E4M3 code 1..126 is a candidate (the format page's brute force,
 // section 4), instead of the codes the candidate range c_lo..c_hi reaches.
 template <bool BF16, bool ALL>
-__global__ __launch_bounds__(WG) void scale_search_kernel(
+__global__ __launch_bounds__(WG, 8) void scale_search_kernel(
     const uint4 *__restrict__ x, int64_t nchunks, const uint32_t *__restrict__ partials,
     int npart, float c_lo, float c_hi, uint32_t *__restrict__ codes,
     uint8_t *__restrict__ scales, float *__restrict__ global_scale, int32_t *status) {
@@ -1415,12 +1446,11 @@ __global__ __launch_bounds__(WG) void scale_search_kernel(
     // bf16: the wave's first tile (a block per lane), in flight during the set-up
     uint4 k0 = make_uint4(0, 0, 0, 0), k1 = k0;
     if (BF16) {
-        const int64_t b0 = ((int64_t)blockIdx.x * WAVES_PER_WG + threadIdx.x / WAVE) * WAVE +
-                           (threadIdx.x & (WAVE - 1));
-        if (b0 < nchunks / 2) {
-            k0 = ld_stream(x + 2 * b0);
-            k1 = ld_stream(x + 2 * b0 + 1);
-        }
+        const int64_t b0 = min(((int64_t)blockIdx.x * WAVES_PER_WG + threadIdx.x / WAVE) * WAVE +
+                                   (threadIdx.x & (WAVE - 1)),
+                               nchunks / 2 - 1);  // past the end: the last block, never used
+        k0 = ld_stream(x + 2 * b0);
+        k1 = ld_stream(x + 2 * b0 + 1);
     }
     TensorScale ts = tensor_scale<BF16>(partials, npart);
     if (blockIdx.x == 0 && threadIdx.x == 0) *global_scale = ts.s_g;
@@ -1433,7 +1463,7 @@ __global__ __launch_bounds__(WG) void scale_search_kernel(
         SearchShared &S = *reinterpret_cast<SearchShared *>(smem);
         // the queue stores block indices in 32 bits
         if (search_table_build<ALL>(S.tab, ts, c_lo, c_hi) && (nchunks >> 33) == 0) {
-            search_bf16_tiles<ALL>(S, S.q[threadIdx.x / WAVE], x, nchunks / 2, k0, k1,
+            search_bf16_tiles<ALL>(S, x, nchunks / 2, k0, k1,
                                    (float)((double)c_hi / (6.0 * (double)ts.s_g)), codes, scales, flags);
             report_flags(status, flags);
             return;
