@@ -398,8 +398,8 @@ __global__ __launch_bounds__(GEMM_WG) void mxfp4_gemm_packed_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// LDS-staged kernel (K a multiple of 256; code rows 16-byte and scale rows
-// 8-byte aligned).  The operand layout of the scaled MFMA wants, per load
+// LDS-staged kernel (K a multiple of 512; code and scale rows 16-byte
+// aligned).  The operand layout of the scaled MFMA wants, per load
 // instruction, 32 rows x 32 bytes at the row stride, which keeps the address
 // unit busy most of the time.  Here every load instruction instead reads
 // eight full 128-byte row segments, straight into LDS (global->LDS loads, no
@@ -415,7 +415,11 @@ __global__ __launch_bounds__(GEMM_WG) void mxfp4_gemm_packed_kernel(
 // LDS row: a ds_read_b128 serves 16 lanes per pass, rows r and r + 1 fall in
 // different halves of the 64 banks, so the 16 rows of a pass of the
 // MFMA-layout reads (one chunk each) hit 16 distinct 4-bank groups.
-// Scale bytes go to registers: one 8-byte load per operand row per stage.
+// The scale bytes of a K segment of up to GEMM_MAX_K are preloaded into LDS
+// in whole 16-byte row chunks (a per-stage scale load would cost the L2 a
+// request per row for 8 bytes, and the kernel is bound by its per-CU fetch
+// requests); a longer K runs its segments one after another into the same
+// accumulators.
 // ---------------------------------------------------------------------------
 constexpr int GEMM_S = 5;                   // stages in flight
 constexpr int GEMM_STAGE_K = 256;           // K values per stage (4 MFMA steps)
@@ -423,7 +427,7 @@ constexpr int GEMM_A_CHUNKS = GEMM_TM * 8;  // 16-byte chunks of A codes per sta
 constexpr int GEMM_B_CHUNKS = GEMM_TN * 8;
 constexpr int GEMM_STAGE_CHUNKS = GEMM_A_CHUNKS + GEMM_B_CHUNKS;
 constexpr int GEMM_LOADS = 5;               // code loads per wave per stage
-constexpr int GEMM_MAX_K = 8192;            // scales of the whole K range held in LDS
+constexpr int GEMM_MAX_K = 8192;            // K of one segment (its scales held in LDS)
 constexpr int GEMM_SCALE_COLS = GEMM_MAX_K / 32 / 16;  // 16-byte scale chunks per row
 
 typedef __attribute__((address_space(1))) const void *gemm_gptr;
@@ -431,15 +435,17 @@ typedef __attribute__((address_space(3))) void *gemm_lptr;
 
 __device__ __forceinline__ int gemm_swizzle(int row) { return (row >> 1) & 7; }
 
-// One workgroup's 128 x 32 tile of C (blockIdx.y, blockIdx.x), all of K.
-template <bool OUT_BF16>
-__device__ __forceinline__ void gemm_lds_tile(const uint4 *__restrict__ A,
-                                              const uint8_t *__restrict__ As,
-                                              const uint4 *__restrict__ Bt,
-                                              const uint8_t *__restrict__ Bs, int M, int N,
-                                              int K, void *__restrict__ C) {
+// One K segment (at most GEMM_MAX_K, a multiple of 512, starting at block
+// kb0 of the rows) of one workgroup's 128 x 32 tile of C (blockIdx.y,
+// blockIdx.x), added to the accumulators.
+__device__ __forceinline__ void gemm_lds_segment(const uint4 *__restrict__ A,
+                                                 const uint8_t *__restrict__ As,
+                                                 const uint4 *__restrict__ Bt,
+                                                 const uint8_t *__restrict__ Bs, int M, int N,
+                                                 int nblk, int kb0, int Kseg, f32x16_t &acc0,
+                                                 f32x16_t &acc1) {
     // ring of code stages: A [128 rows][8 chunks], B [32][8];
-    // the scales of all K, transposed: A [16-byte chunk][128 rows], B [chunk][32 rows]
+    // the segment's scales, transposed: A [16-byte chunk][128 rows], B [chunk][32 rows]
     __shared__ uint4 ring[GEMM_S][GEMM_STAGE_CHUNKS];
     __shared__ uint4 a_scales[GEMM_SCALE_COLS][GEMM_TM];
     __shared__ uint4 b_scales[GEMM_SCALE_COLS][GEMM_TN];
@@ -447,21 +453,20 @@ __device__ __forceinline__ void gemm_lds_tile(const uint4 *__restrict__ A,
     const int w = threadIdx.x >> 6;
     const int r32 = lane & 31;
     const int kh = lane >> 5;
-    const int nblk = K / 32;
-    const int nst = K / GEMM_STAGE_K;
-    const int ncols = nblk / 16;  // 16-byte scale chunks per row (2 stages each)
+    const int nst = Kseg / GEMM_STAGE_K;
+    const int ncols = Kseg / 32 / 16;  // 16-byte scale chunks per row (2 stages each)
     const int m0 = blockIdx.y * GEMM_TM, n0 = blockIdx.x * GEMM_TN;
 
     // ---- the scales, once: lane l of a load moves 16 bytes (2 stages) of one
     // row; A: chunk column c, rows 64h + l; B: columns 2j + l / 32, rows l % 32
     for (int i = w; i < 2 * ncols; i += 4) {
         const int c = i >> 1, row = 64 * (i & 1) + lane;
-        const uint8_t *src = As + (int64_t)min(m0 + row, M - 1) * nblk + 16 * c;
+        const uint8_t *src = As + (int64_t)min(m0 + row, M - 1) * nblk + kb0 + 16 * c;
         __builtin_amdgcn_global_load_lds((gemm_gptr)src, (gemm_lptr)&a_scales[c][64 * (i & 1)], 16, 0, 0);
     }
     for (int j = w; 2 * j < ncols; j += 4) {
         const int c = 2 * j + kh;
-        const uint8_t *src = Bs + (int64_t)min(n0 + r32, N - 1) * nblk + 16 * min(c, ncols - 1);
+        const uint8_t *src = Bs + (int64_t)min(n0 + r32, N - 1) * nblk + kb0 + 16 * min(c, ncols - 1);
         __builtin_amdgcn_global_load_lds((gemm_gptr)src, (gemm_lptr)&b_scales[2 * j][0], 16, 0, 0);
     }
 
@@ -473,10 +478,10 @@ __device__ __forceinline__ void gemm_lds_tile(const uint4 *__restrict__ A,
     for (int i = 0; i < 4; ++i) {
         const int row = 32 * w + 8 * i + lrow;  // row within the A tile
         const int am = min(m0 + row, M - 1);
-        ga[i] = A + (int64_t)am * nblk + (lpc ^ gemm_swizzle(row));
+        ga[i] = A + (int64_t)am * nblk + kb0 + (lpc ^ gemm_swizzle(row));
     }
     const int brow = 8 * w + lrow;
-    const uint4 *gb = Bt + (int64_t)min(n0 + brow, N - 1) * nblk + (lpc ^ gemm_swizzle(brow));
+    const uint4 *gb = Bt + (int64_t)min(n0 + brow, N - 1) * nblk + kb0 + (lpc ^ gemm_swizzle(brow));
 
     // Five code loads per wave per stage: its 32 rows of A and 8 of the 32
     // rows of B, global -> LDS.  Stages past the end re-read the last one
@@ -493,9 +498,6 @@ __device__ __forceinline__ void gemm_lds_tile(const uint4 *__restrict__ A,
                                          (gemm_lptr)&sb[GEMM_A_CHUNKS + 8 * w * 8], 16, 0, 0);
     };
 
-    // two accumulators (alternate MFMA steps) so that consecutive MFMAs do
-    // not wait for each other; summed once at the end, in a fixed order
-    f32x16_t acc0 = {}, acc1 = {};
     const int arow = 32 * w + r32;  // this lane's A operand row in the tile
     const int sw = gemm_swizzle(r32);  // its swizzle (= that of arow and of the B row r32)
     // LDS byte addresses of this lane's operands in slot 0: chunk
@@ -567,8 +569,32 @@ __device__ __forceinline__ void gemm_lds_tile(const uint4 *__restrict__ A,
                                                                       0, (int)eb);
         }
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // the trailing re-reads land before the workgroup ends
+    // the trailing re-reads land, and every wave is done with the segment's
+    // LDS, before the next segment or the end of the workgroup
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_s_barrier();
+}
+
+// One workgroup's 128 x 32 tile of C (blockIdx.y, blockIdx.x), all of K: the
+// K segments in order, each with its scales preloaded.
+template <bool OUT_BF16>
+__device__ __forceinline__ void gemm_lds_tile(const uint4 *__restrict__ A,
+                                              const uint8_t *__restrict__ As,
+                                              const uint4 *__restrict__ Bt,
+                                              const uint8_t *__restrict__ Bs, int M, int N,
+                                              int K, void *__restrict__ C) {
+    // two accumulators (alternate MFMA steps) so that consecutive MFMAs do
+    // not wait for each other; summed once at the end, in a fixed order
+    f32x16_t acc0 = {}, acc1 = {};
+    const int nblk = K / 32;
+    for (int k0 = 0; k0 < K; k0 += GEMM_MAX_K)
+        gemm_lds_segment(A, As, Bt, Bs, M, N, nblk, k0 / 32, min(K - k0, GEMM_MAX_K), acc0, acc1);
     const f32x16_t acc = acc0 + acc1;
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int r32 = lane & 31;
+    const int kh = lane >> 5;
+    const int m0 = blockIdx.y * GEMM_TM, n0 = blockIdx.x * GEMM_TN;
 
     // accumulator layout of the 32x32 MFMA: lane l holds column l % 32 and
     // rows 8 (j / 4) + 4 (l / 32) + (j % 4), j = 0..15
@@ -1271,7 +1297,7 @@ static int linear_capacity() {
 static bool gemm_lds_ok(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *bt_codes,
                         const uint8_t *bt_scales, int64_t K) {
     auto al = [](const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; };
-    return K % (2 * GEMM_STAGE_K) == 0 && K <= GEMM_MAX_K && al(a_codes, 16) && al(bt_codes, 16) &&
+    return K % (2 * GEMM_STAGE_K) == 0 && al(a_codes, 16) && al(bt_codes, 16) &&
            al(a_scales, 16) && al(bt_scales, 16);
 }
 

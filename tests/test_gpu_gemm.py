@@ -56,7 +56,7 @@ def _check(M, N, K, seed=0):
 
 @pytest.mark.parametrize("M,N,K", [(128, 256, 512), (32, 32, 64), (70, 50, 96), (128, 96, 32),
                                    (256, 64, 8192), (1, 33, 4128), (200, 72, 1536), (130, 96, 768),
-                                   (96, 40, 8704)])
+                                   (96, 40, 8704), (64, 96, 256), (33, 64, 20736)])
 def test_gemm_small_and_ragged(M, N, K):
     _check(M, N, K)
 
@@ -76,6 +76,13 @@ def test_gemm_integer_valued_is_exact():
 
 def test_gemm_full_size_128x8192x8192():
     err = _check(128, 8192, 8192)
+    print(f"relative Frobenius error {err:.3e}")
+
+
+def test_gemm_full_size_128x8192x16384():
+    # K past 8192 takes the same LDS-staged kernel (the scales stream with
+    # the codes, so K has no upper limit)
+    err = _check(128, 8192, 16384)
     print(f"relative Frobenius error {err:.3e}")
 
 
