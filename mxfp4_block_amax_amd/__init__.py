@@ -363,6 +363,25 @@ def packed_operand_bytes(rows: int, K: int) -> int:
     return int(lib().fp4_packed_operand_bytes(int(rows), int(K)))
 
 
+def _check_u8(t: torch.Tensor, numel: int, what: str, device):
+    """t must be a contiguous uint8 tensor on `device` with `numel` elements
+    (checked here because the C call takes no size for it)."""
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.uint8:
+        raise TypeError(f"{what} must be a uint8 tensor")
+    if t.device != torch.device(device) or not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous on {device}")
+    if t.numel() != numel:
+        raise ValueError(f"{what} has {t.numel()} elements, needs {numel}")
+
+
+def _check_global_scale(t: torch.Tensor, what: str, device):
+    """A tensor scale: a float32 tensor on `device` with at least one element."""
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32:
+        raise TypeError(f"{what} must be a float32 tensor")
+    if t.device != torch.device(device) or t.numel() < 1:
+        raise ValueError(f"{what} must hold at least one element on {device}")
+
+
 def pack_mxfp4_operand(codes: torch.Tensor, scales: torch.Tensor, out=None) -> torch.Tensor:
     """An MXFP4 operand [rows, K] (codes [rows, K/2], scales [rows, K/32]) in
     MFMA operand order, one uint8 buffer, for gemm_mxfp4_packed."""
@@ -370,6 +389,7 @@ def pack_mxfp4_operand(codes: torch.Tensor, scales: torch.Tensor, out=None) -> t
     n = packed_operand_bytes(rows, 2 * kh)
     if n == 0:
         raise ValueError("packing needs K a positive multiple of 512")
+    _check_u8(scales, rows * (2 * kh) // 32, "scales", codes.device)
     packed = out if out is not None else torch.empty(n, dtype=torch.uint8, device=codes.device)
     _ok(lib().fp4_pack_mxfp4_operand(_ptr(codes), _ptr(scales), rows, 2 * kh, _ptr(packed),
                                      packed.numel(), _stream(codes)))
@@ -472,6 +492,7 @@ def pack_nvfp4_operand(codes: torch.Tensor, scales: torch.Tensor, out=None) -> t
     n = nv_packed_operand_bytes(rows, 2 * kh)
     if n == 0:
         raise ValueError("packing needs K a positive multiple of 512")
+    _check_u8(scales, rows * (2 * kh) // 16, "scales", codes.device)
     packed = out if out is not None else torch.empty(n, dtype=torch.uint8, device=codes.device)
     _ok(lib().fp4_pack_nvfp4_operand(_ptr(codes), _ptr(scales), rows, 2 * kh, _ptr(packed),
                                      packed.numel(), _stream(codes)))
@@ -486,6 +507,8 @@ def gemm_nvfp4_packed(a_packed: torch.Tensor, a_global_scale: torch.Tensor,
     if (a_packed.numel() < nv_packed_operand_bytes(M, K)
             or bt_packed.numel() < nv_packed_operand_bytes(N, K)):
         raise ValueError("packed operand smaller than its shape")
+    _check_global_scale(a_global_scale, "a_global_scale", a_packed.device)
+    _check_global_scale(bt_global_scale, "bt_global_scale", a_packed.device)
     c = out if out is not None else torch.empty(M, N, dtype=out_dtype, device=a_packed.device)
     _ok(lib().fp4_gemm_nvfp4_packed(_ptr(a_packed), _ptr(a_global_scale), _ptr(bt_packed),
                                     _ptr(bt_global_scale), int(M), int(N), int(K), _ptr(c),
@@ -525,10 +548,12 @@ def linear_nvfp4_packed(x: torch.Tensor, bt_packed: torch.Tensor, bt_global_scal
     the packed layout, times Bt [N, K] (packed, with its tensor scale).
     Returns (C [M, N], (a_packed, a_s_g))."""
     M, K = _rows_cols(x)
+    _check_global_scale(bt_global_scale, "bt_global_scale", x.device)
     if a_out is None:
         a_out = (torch.empty(nv_packed_operand_bytes(M, K), dtype=torch.uint8, device=x.device),
                  torch.empty(1, dtype=torch.float32, device=x.device))
     a_packed, a_sg = a_out
+    _check_global_scale(a_sg, "a_out[1]", x.device)
     c = out if out is not None else torch.empty(M, int(N), dtype=out_dtype, device=x.device)
     if workspace is None:
         workspace = new_workspace(M, K, x.device)

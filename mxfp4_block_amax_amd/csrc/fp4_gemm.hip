@@ -886,7 +886,7 @@ constexpr int NVPK_RING = 8;  // K steps in flight per wave
 
 // The NVFP4 GEMM on packed operands: a workgroup owns a 128 x 32 tile of C,
 // its four waves take the four quarters of the K steps (SW each, unrolled,
-// step st's loads in ring slot st % 6, issued six steps ahead); each wave
+// step st's loads in ring slot st % NVPK_RING, issued NVPK_RING steps ahead); each wave
 // decodes its own operands once (FP4 -> fp16 times the E4M3 scale, exact),
 // 16 fp16 MFMAs per step; the partial tiles are added through LDS in a fixed
 // order and C = RN32(sum * RN32(s_gA s_gB)).

@@ -521,3 +521,31 @@ def test_linear_packed_matches_oracle(M, N, K, dt):
     # the same bits as the packed GEMM on the same packed operands
     c2 = fp4.gemm_mxfp4_packed(a_packed, bt_packed, M, N, K, torch.float32)
     assert torch.equal(c2, c32)
+
+
+def test_packed_binding_rejects_bad_scales_and_global_scales():
+    # checked in Python before any launch: the C calls take no size for the
+    # scale buffers, and the tensor scales are read on the device
+    rows, K = 64, 512
+    codes = torch.zeros(rows, K // 2, dtype=torch.uint8, device="cuda")
+    good_nv = torch.zeros(rows, K // 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        fp4.pack_nvfp4_operand(codes, good_nv[:, :-1].contiguous())      # short
+    with pytest.raises(TypeError):
+        fp4.pack_nvfp4_operand(codes, good_nv.float())                    # dtype
+    with pytest.raises(ValueError):
+        fp4.pack_nvfp4_operand(codes, good_nv.cpu())                      # host memory
+    with pytest.raises(ValueError):
+        fp4.pack_mxfp4_operand(codes, torch.zeros(rows, K // 16, dtype=torch.uint8, device="cuda"))
+    ap = fp4.pack_nvfp4_operand(codes, good_nv)
+    sg = torch.ones(1, dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        fp4.gemm_nvfp4_packed(ap, sg.cpu(), ap, sg, rows, rows, K)
+    with pytest.raises(TypeError):
+        fp4.gemm_nvfp4_packed(ap, sg, ap, sg.double(), rows, rows, K)
+    with pytest.raises(ValueError):
+        fp4.gemm_nvfp4_packed(ap, sg[:0], ap, sg, rows, rows, K)
+    x = torch.zeros(rows, K, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(TypeError):
+        fp4.linear_nvfp4_packed(x, ap, sg.half(), rows)
+    torch.cuda.synchronize()
