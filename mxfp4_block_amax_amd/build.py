@@ -1,6 +1,10 @@
 """Build libfp4.so (the C-ABI library) in-tree with hipcc for gfx950.
 
-Usage: python -m mxfp4_block_amax_amd.build [-v]
+Usage: python -m mxfp4_block_amax_amd.build [-v] [--phase-clock]
+
+--phase-clock builds libfp4_phase.so instead: the same library with the
+one-pass NVFP4 kernel's phase clock compiled in (include/fp4_phase_clock.h),
+a profiling aid read by mxfp4_block_amax_amd/phase_timeline.py.
 """
 import concurrent.futures as cf
 import os
@@ -11,6 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfp4.so")
+PHASE_LIB = os.path.join(HERE, "libfp4_phase.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["fp4_api.hip", "fp4_quant.hip", "fp4_gemm.hip"]
 
@@ -23,9 +28,9 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=o
          "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, verbose: bool, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -39,18 +44,20 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, phase_clock: bool = False) -> str:
+    build_dir = os.path.join(BUILD, "phase") if phase_clock else BUILD
+    lib = PHASE_LIB if phase_clock else LIB
+    extra = ("-DFP4_PHASE_CLOCK",) if phase_clock else ()
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"]
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, extra), SOURCES))
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", lib + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv)
-    print(LIB)
+    print(build(verbose="-v" in sys.argv, phase_clock="--phase-clock" in sys.argv))

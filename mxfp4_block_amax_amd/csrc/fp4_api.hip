@@ -6,6 +6,9 @@
 #include <mutex>
 
 #include "../../include/fp4.h"
+#ifdef FP4_PHASE_CLOCK
+#include "../../include/fp4_phase_clock.h"
+#endif
 #include "fp4_kernels.h"
 
 // Device scratch of fp4_quantize_nvfp4_noalloc, for callers that cannot
@@ -483,6 +486,13 @@ int64_t fp4_padded_storage_bytes(fp4_format fmt, int64_t rows, int64_t cols) {
     const int64_t blocks = rows * ((cols + block - 1) / block);
     return blocks * (block / 2 + 1) + (fmt == FP4_NVFP4 ? 4 : 0);
 }
+
+#ifdef FP4_PHASE_CLOCK
+fp4_status fp4_debug_phase_clock(uint64_t *host, size_t n) {
+    if (!host) return FP4_E_ARG;
+    return from_hip(fp4dev::read_phase_clock(host, n));
+}
+#endif
 
 uint32_t fp4_debug_barrier_spin_limit(uint32_t polls) {
     return fp4dev::set_barrier_spin_limit(polls);

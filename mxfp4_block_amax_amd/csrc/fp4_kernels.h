@@ -35,6 +35,9 @@ constexpr int kMaxDevices = 64;
 // rule: 0 the OCP floor rule, 1 the ceil rule, 2 the three-exponent search
 hipError_t launch_mx_quantize(const void *x, bool bf16, int64_t n, int rule, uint8_t *codes,
                               uint8_t *scales, int32_t *status, hipStream_t s);
+#ifdef FP4_PHASE_CLOCK
+hipError_t read_phase_clock(uint64_t *host, size_t n);
+#endif
 hipError_t launch_nv_quantize(const void *x, bool bf16, int64_t n, uint8_t *codes,
                               uint8_t *scales, float *global_scale, void *workspace,
                               int32_t *status, hipStream_t s);

@@ -696,6 +696,27 @@ __global__ __launch_bounds__(WG) void nv_quantize_packed_kernel(
     report_flags(status, flags);
 }
 
+// Phase clock (a separate profiling build, -DFP4_PHASE_CLOCK): thread 0 of
+// each workgroup of the one-pass kernel stamps the device's constant 100 MHz
+// clock at its start, after its loads and partial amax, after the grid
+// barrier, after the table build and at its end (slots 0..4 of 8).
+#ifdef FP4_PHASE_CLOCK
+__device__ uint64_t g_phase_clock[kResidentSlots * 8];
+#define FP4_PHASE(k)                                                                     \
+    do {                                                                                 \
+        if (threadIdx.x == 0) g_phase_clock[blockIdx.x * 8 + (k)] = __builtin_amdgcn_s_memrealtime(); \
+    } while (0)
+hipError_t read_phase_clock(uint64_t *host, size_t n) {
+    if (n > (size_t)kResidentSlots * 8) n = (size_t)kResidentSlots * 8;
+    return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_phase_clock), n * sizeof(uint64_t), 0,
+                               hipMemcpyDeviceToHost);
+}
+#else
+#define FP4_PHASE(k) \
+    do {             \
+    } while (0)
+#endif
+
 // EXACT: the grid covers the tensor exactly (nchunks = gridDim.x * 512 * CPL),
 // so no load is clamped and no store predicated.
 template <int CPL, bool EXACT>
@@ -720,6 +741,7 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
     uint32_t &tensor_amax = sh.tensor_amax;
     uint4(&lds)[LC * RES_WG] = sh.data;
 
+    FP4_PHASE(0);
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), wv = tid / WAVE;
     const int stride = gridDim.x * RES_WG;       // chunks covered by one step j of the grid
     const int c00 = blockIdx.x * RES_WG + tid;   // this lane's chunk at step 0
@@ -768,6 +790,7 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
     m = wave_max_u32(m);
     if (lane == 0) red[wv] = m;
     __syncthreads();
+    FP4_PHASE(1);
 
     // ---- grid barrier: wave 0 publishes the partial amax and polls --------
     uint32_t flags = 0;
@@ -813,6 +836,7 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
         __syncthreads();
         flags |= FLAG_BARRIER_TIMEOUT;
     }
+    FP4_PHASE(2);
     const TensorScale ts = scale_from_amax(tensor_amax << 16);
     if (blockIdx.x == 0 && tid == 0) *global_scale = ts.s_g;
     if (ts.flags) {  // uniform over the grid: outputs unspecified
@@ -824,6 +848,7 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
     const uint32_t base = nv_window_base(ts.s_g);
     nv_direct_table_build(T, ts.s_g, tensor_amax, base);  // ends with a barrier
     const uint32_t need = T.need;            // uniform
+    FP4_PHASE(3);
 
     // ---- phase 2: quantize from LDS and registers -----------------------
     // Two chunk rows per iteration: a lane pair holds one 16-element block of
@@ -931,6 +956,11 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
     flags |= ymin == 0.0f ? FLAG_SCALE_UNDERFLOW : 0u;
     if (late && tid == 0) barrier_retract(slots);
     report_flags(status, flags);
+#ifdef FP4_PHASE_CLOCK
+    __builtin_amdgcn_s_waitcnt(0);  // this workgroup's stores have left
+    __syncthreads();
+    FP4_PHASE(4);
+#endif
 }
 
 // ---------------------------------------------------------------------------
