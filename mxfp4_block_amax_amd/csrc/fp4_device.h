@@ -411,20 +411,20 @@ __device__ __forceinline__ uint32_t nv_lo_bf16(uint32_t c, float s_g) {
 }
 
 // Builds the table in two steps (per code; per window entry) for the tensor
-// scale s_g of a bf16 tensor amax with significand index M (its low 7 bits).
-// Ends with a barrier; T.need then holds the call's NV_NEEDS_*.
-__device__ __forceinline__ void nv_direct_table_build(NvDirectTable &T, float s_g, uint32_t M,
+// scale s_g of a bf16 tensor; rcrow is kRecipCorrection's row for the tensor
+// amax's significand index M (its low 7 bits).  T.need must be zero, and a
+// barrier passed since it was zeroed, on entry (512 threads).  Ends with a
+// barrier; T.need then holds the call's NV_NEEDS_*.
+__device__ __forceinline__ void nv_direct_table_build(NvDirectTable &T, float s_g, uint32_t rcrow,
                                                       uint32_t base) {
     const int t = threadIdx.x;
-    if (t == 0) T.need = 0u;
-    __syncthreads();
     // step 1, per code: Y_c, D_c and the code's lower bound
     if (t < 128) {
         float Y = 0.0f, D = 0.0f;
         uint32_t need = 0;
         const float a = t > 0 && t < 127 ? s_g * e4m3_pos_value((uint32_t)t) : 0.0f;
         if (a > 0.0f) {
-            const uint32_t sel = (kRecipCorrection[M & 127u] >> (2u * e4m3_frac_index((uint32_t)t))) & 3u;
+            const uint32_t sel = (rcrow >> (2u * e4m3_frac_index((uint32_t)t))) & 3u;
             const float y0 = 1.0f / a;  // correctly rounded
             if (a < kDivScaleBelow || s_g < 0x1p-126f) {  // outside the table's rule: exact loop
                 Y = y0;
@@ -450,22 +450,29 @@ __device__ __forceinline__ void nv_direct_table_build(NvDirectTable &T, float s_
     }
     __syncthreads();
     // step 2, per window entry: the code of a bf16 magnitude, from a guess
-    // within one code of it settled by the two bounds around it
+    // within one code of it settled by the two bounds around it.  All of a
+    // thread's reads come before its stores, so its entries' LDS round trips
+    // overlap (a store between them would order every later read after it).
+    constexpr int NR = (RES_NIDX + 2 + 511) / 512;
     const CodeGuess G = make_code_guess(s_g);
+    uint32_t code[NR];
 #pragma unroll
-    for (int r = 0; r < (RES_NIDX + 2 + 511) / 512; ++r) {
-        const int i = t + r * (int)blockDim.x;
+    for (int r = 0; r < NR; ++r) {
+        const int i = t + r * 512;
+        const uint32_t bits = min(base + (uint32_t)max(i - 2, 0), 0x7F7Fu);  // finite
+        const uint32_t g = code_guess(u2f(bits << 16), G);
+        const uint32_t c = g + (bits >= T.lo[g + 1] ? 1u : 0u) - (bits < T.lo[g] ? 1u : 0u);
+        code[r] = i < 2 ? (i == 0 ? 0x38u : 0u) : c;
+    }
+    float y[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) y[r] = T.yc[code[r]];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const int i = t + r * 512;
         if (i < RES_NIDX + 2) {
-            uint32_t c;
-            if (i < 2) {
-                c = i == 0 ? 0x38u : 0u;
-            } else {
-                const uint32_t bits = min(base + (uint32_t)(i - 2), 0x7F7Fu);  // finite
-                const uint32_t g = code_guess(u2f(bits << 16), G);
-                c = g + (bits >= T.lo[g + 1] ? 1u : 0u) - (bits < T.lo[g] ? 1u : 0u);
-            }
-            T.code[i] = (uint8_t)c;
-            T.y[i] = T.yc[c];
+            T.code[i] = (uint8_t)code[r];
+            T.y[i] = y[r];
         }
     }
     __syncthreads();

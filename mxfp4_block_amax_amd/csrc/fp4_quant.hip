@@ -717,6 +717,10 @@ hipError_t read_phase_clock(uint64_t *host, size_t n) {
     } while (0)
 #endif
 
+// Cache policy of the code stores: non-temporal (the 33.6 MB of codes are
+// not read again by this kernel; measured ~1 us faster per call at 8192^2).
+constexpr int kStoreNT = 2;
+
 // EXACT: the grid covers the tensor exactly (nchunks = gridDim.x * 512 * CPL),
 // so no load is clamped and no store predicated.
 template <int CPL, bool EXACT>
@@ -733,6 +737,7 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
         uint32_t red[RES_WAVES];
         uint32_t tensor_amax;
         uint32_t late_tag;
+        uint16_t rc[128];  // kRecipCorrection, staged during phase 1
         uint4 data[LC * RES_WG];
     };
     __shared__ Shared sh;
@@ -746,6 +751,10 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
     const int stride = gridDim.x * RES_WG;       // chunks covered by one step j of the grid
     const int c00 = blockIdx.x * RES_WG + tid;   // this lane's chunk at step 0
     const int last = nchunks - 1;
+    // the table build's inputs that do not depend on s_g, ready before the
+    // grid barrier (barriers below order these stores before their reads)
+    if (tid < 128) sh.rc[tid] = kRecipCorrection[tid];
+    if (tid == 0) T.need = 0u;
 
     // ---- phase 1: load the slice once, partial amax ----------------------
     // step j reads x[j*stride + c00]: a uniform base plus this lane's offset,
@@ -846,7 +855,7 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
         return;
     }
     const uint32_t base = nv_window_base(ts.s_g);
-    nv_direct_table_build(T, ts.s_g, tensor_amax, base);  // ends with a barrier
+    nv_direct_table_build(T, ts.s_g, sh.rc[tensor_amax & 127u], base);  // ends with a barrier
     const uint32_t need = T.need;            // uniform
     FP4_PHASE(3);
 
@@ -911,7 +920,7 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
                 for (int i = 0; i < 8; ++i) f[i] = TWO ? __builtin_fmaf(f[i], ys[k], f[i] * ds[k]) : f[i] * ys[k];
                 const uint32_t q = cvt_fp4x8_f32(f, e8m0_operand(E8M0_ONE));
                 const int bk = (j0 + k) * stride;  // uniform
-                if (EXACT || c00 <= last - bk) __builtin_amdgcn_raw_buffer_store_b32(q, crs, (int)coff, bk * 4, 0);
+                if (EXACT || c00 <= last - bk) __builtin_amdgcn_raw_buffer_store_b32(q, crs, (int)coff, bk * 4, kStoreNT);
             }
             y = yn;
             c = cn;
@@ -949,7 +958,7 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
                 for (int i = 0; i < 8; ++i) f[i] = div_rn(f[i] * scr[k], ad[k], y);
                 const uint32_t q = cvt_fp4x8_f32(f, e8m0_operand(E8M0_ONE));
                 const int bk = (j0 + k) * stride;
-                if (EXACT || c00 <= last - bk) __builtin_amdgcn_raw_buffer_store_b32(q, crs, (int)coff, bk * 4, 0);
+                if (EXACT || c00 <= last - bk) __builtin_amdgcn_raw_buffer_store_b32(q, crs, (int)coff, bk * 4, kStoreNT);
             }
         }
     }
@@ -1138,11 +1147,12 @@ __device__ __forceinline__ float half_block_loss(const float (&a)[8], float4 sq,
 // so the code words of the best candidate are the block's output as they
 // stand.
 //
-// Each lane holds one block (16 values).  It walks its first two candidates
-// in place; a block that still has one to evaluate then goes to its wave's
-// queue in LDS (its 16 values and its walk state), and once 64 blocks wait
-// the wave evaluates the next candidate of 64 of them at once, putting back
-// those that go on.  Every block visits the same codes in the same order as
+// Each lane holds one block (16 values).  The wave steps its tile's walks in
+// place while many lanes still walk (at least the first two candidates);
+// a block that still has one to evaluate then goes to its wave's queue in
+// LDS (its 16 values and its walk state), and once 64 blocks wait the wave
+// evaluates the next candidate of 64 of them at once, putting back those
+// that go on.  Every block visits the same codes in the same order as
 // a plain walk, so the result is the same; only the lanes' idle time changes
 // (a wave no longer waits for its slowest block).
 struct SearchTable {
@@ -1152,6 +1162,10 @@ struct SearchTable {
 // Between passes a queue holds < 64 blocks; a tile adds at most 32 (a tile
 // with more steps its blocks in place until at most 32 remain).
 constexpr int SQ_CAP = 96;
+// A tile's blocks step in place while more than this many lanes walk: an
+// in-place step is ~105 VALU instructions for the wave, a queue pass ~150
+// for 64 blocks, so in place wins above ~45 walking lanes.
+constexpr int SQ_INLINE = 40;
 struct SearchQueue {
     uint4 data[SQ_CAP][2];  // the block's 16 bf16 values
     uint2 st[SQ_CAP];       // {block index, next code | best code << 8 | amax bits << 16}
@@ -1431,13 +1445,13 @@ __device__ __forceinline__ void search_bf16_tiles(SearchShared &SS,
         // has a loss above the best and is not taken, and the test after it
         // stops the walk
         bool more = walk_in_range(*reinterpret_cast<const float2 *>(&S.e[max(w.code, 0)]), w);
-        if (__ballot(more)) {
+        // In place while many lanes still walk (a step then costs less than
+        // a queue pass per block), and while the queue has no room.
+        int k = __builtin_popcountll(__ballot(more));
+        while (k > 0 && (k > SQ_INLINE || n + k > SQ_CAP)) {
             walk_step(S, a, w, more);
             more = more && walk_goes_on(S, w);
-        }
-        while (n + __builtin_popcountll(__ballot(more)) > SQ_CAP) {
-            walk_step(S, a, w, more);
-            more = more && walk_goes_on(S, w);
+            k = __builtin_popcountll(__ballot(more));
         }
         if (ok && !more) walk_finish(w, b, codes, scales, flags);
         queue_push(P, n, ok && more, a, w, b);
