@@ -554,14 +554,26 @@ __device__ __forceinline__ bool grid_barrier_max(uint64_t *slots, uint32_t tag, 
     if (lane == 0)
         __hip_atomic_store(&slots[wg], ((uint64_t)tag << 32) | value, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
+    // A poll issues a lane's slot loads four at a time before it looks at
+    // any: one device-coherent round trip per poll for up to 256 workgroups,
+    // not one per slot.
     for (uint32_t it = 0;; ++it) {
         bool ok = true;
         uint32_t mm = 0;
-        for (int i = lane; i < G; i += WAVE) {
-            uint32_t v;
-            const bool t = barrier_slot_tagged(slots, i, tag, v);
-            ok = ok && t;
-            mm = t ? max(mm, v) : mm;
+        for (int i0 = 0; i0 < G; i0 += 4 * WAVE) {
+            uint64_t sl[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int i = i0 + lane + k * WAVE;
+                sl[k] = i < G ? __hip_atomic_load(&slots[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                              : (uint64_t)tag << 32;
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const bool t = (uint32_t)(sl[k] >> 32) == tag;
+                ok = ok && t;
+                mm = t ? max(mm, (uint32_t)sl[k]) : mm;
+            }
         }
         const bool all = __ballot(!ok) == 0;
         if (all || it >= spin_limit) {
