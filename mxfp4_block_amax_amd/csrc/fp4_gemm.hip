@@ -1197,8 +1197,10 @@ __device__ __forceinline__ uint32_t quantize_share(const uint4 *__restrict__ x, 
         const int64_t c = t * WAVE + lane;
         const bool ok = c < nchunks;
         const uint4 z = make_uint4(0, 0, 0, 0);
-        const uint4 lo = ok ? ld_stream(x + (XBF16 ? c : 2 * c)) : z;
-        const uint4 hi = (!XBF16 && ok) ? ld_stream(x + 2 * c + 1) : z;
+        // fp32: two loads 32 bytes apart per lane, ordinary (cached) so the
+        // second finds the line the first brought in
+        const uint4 lo = ok ? (XBF16 ? ld_stream(x + c) : x[2 * c]) : z;
+        const uint4 hi = (!XBF16 && ok) ? x[2 * c + 1] : z;
         uint32_t m = XBF16 ? amax_bf16x8(lo) : amax_f32x8(lo, hi);
         m = max(m, dpp<QP_XOR1>(m));
         m = max(m, dpp<QP_XOR2>(m));
