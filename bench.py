@@ -329,14 +329,22 @@ def _rate(b: int, ms: float, elements: int = None):
     return d
 
 
+class _Progress(dict):
+    """A dict that reports each workload as it is stored (stderr), so a long
+    profiled run shows progress."""
+
+    def __setitem__(self, key, value):
+        print(f"[bench] {key} done", file=sys.stderr, flush=True)
+        super().__setitem__(key, value)
+
+
 def extra_workloads(dg: dict):
     """The other workloads; each output is checked against the oracle's
     digests where the digests file holds it."""
-    out = {}
+    out = _Progress()
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
     # NVFP4 quantize of the same-shape weight with seed 1: amax 235 * 2^-11,
-    # a generic tensor scale, so the one-pass kernel takes the
-    # reciprocal-correction divide (seed 0's amax is 21 * 11 * 2^-11)
+    # a generic tensor scale (seed 0's amax is 21 * 11 * 2^-11)
     xw_cpu = workloads.nvfp4_weight(8192, 8192, seed=1)
     xs = [xw_cpu.cuda() for _ in range(3)]
     outs = [fp4.quantize_nvfp4(x) for x in xs]
@@ -451,8 +459,8 @@ def extra_workloads(dg: dict):
     d["pack_a_us"] = round(ms2 * 1e3, 2)
     out["mxfp4_gemm_packed_128x8192x8192_bf16out"] = d
     del bps
-    # K = 16384, beyond the staged kernel's scale capacity: the split-K path
-    # against the entry point's register-fed fallback
+    # K = 16384: the split-K path against the default entry point (the
+    # LDS-staged kernel in two K segments of 8192)
     K2 = 16384
     a2, bt2 = workloads.gemm_operands(M, N, K2)
     ac2, asc2 = fp4.quantize_mxfp4(a2.cuda())
@@ -761,7 +769,9 @@ def main():
     traffic = measured_traffic()
     roofline = {"bound": "hbm",
                 "kernel": "nv_resident_kernel<64, exact> (NVFP4 quantize in one pass, the tensor "
-                          "held on chip; this tensor's s_g = 11 * 2^-18 takes the two-operation divide)",
+                          "held on chip; block scales from a per-call table indexed by the block "
+                          "amax's bf16 bits; quotient one product with a per-code corrected "
+                          "reciprocal)",
                 "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(value / HBM_PEAK_GBS, 4),
                 "traffic": traffic["nvfp4_quantize"] if traffic else None,
