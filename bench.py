@@ -135,7 +135,8 @@ TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "roundtrip_8192x8192_bf16_hbm_t
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "mxfp4_block_amax_amd", "csrc", "*"))):
+    csrc = os.path.join(ROOT, "mxfp4_block_amax_amd", "csrc")
+    for p in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -156,12 +157,29 @@ def measured_traffic():
 
 
 VALU_PROFILE = os.path.join(ROOT, "profiles", "valu_issue_arithmetic_kernels.md")
+GEMM_PROFILE = os.path.join(ROOT, "profiles", "gemm_counters_128x8192.md")
+
+
+def _profile_record(path: str, tag: str, field: str):
+    """The `tag:` JSON record of a committed profile summary, if it was taken
+    on the current kernel sources."""
+    try:
+        with open(path) as f:
+            for line in f:
+                if line.startswith(tag + ":"):
+                    rec = json.loads(line.split(":", 1)[1])
+                    if rec.get("source_sha256_16") == kernel_source_hash():
+                        return rec[field]
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
 
 
 def measured_valu_issue():
     """VALU issue of the arithmetic-bound kernels (percent of one wave64
-    instruction per SIMD every two cycles at 2.4 GHz), by extra-workload
-    name, from the committed SQ-counter profile; None if the kernels changed."""
+    instruction per SIMD every four cycles at 2.4 GHz, the non-packed rate),
+    by extra-workload name, from the committed SQ-counter profile; None if
+    the kernels changed."""
     try:
         with open(VALU_PROFILE) as f:
             for line in f:
@@ -536,12 +554,19 @@ def extra_workloads(dg: dict):
     del bnp
     if int(st.item()) != 0:
         raise RuntimeError(f"a timed call raised status flags {int(st.item())}")
-    # arithmetic-bound workloads: their profiled VALU issue (SQ counters)
+    # arithmetic-bound workloads: their profiled VALU issue (SQ counters, % of
+    # the non-packed issue rate); GEMMs: profiled MFMA busy, address-unit busy,
+    # L2 read requests and hit rate
     valu = measured_valu_issue()
     if valu:
         for k, pct in valu.items():
             if k in out:
                 out[k]["valu_issue_pct_of_peak_profiled"] = pct
+    gemm = _profile_record(GEMM_PROFILE, "gemm_record", "counters")
+    if gemm:
+        for k, c in gemm.items():
+            if k in out:
+                out[k]["counters_profiled"] = c
     return out
 
 
