@@ -58,7 +58,17 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* The enumerations are 32-bit integers on both sides of the ABI.  In C++ the
+ * underlying type is fixed to int32_t, so that a value outside the named
+ * constants (which a C or ctypes caller may pass) is still a value of the
+ * type and is rejected by the checks below rather than being undefined. */
+#ifdef __cplusplus
+#define FP4_ENUM enum : int32_t
+#else
+#define FP4_ENUM enum
+#endif
+
+typedef FP4_ENUM {
     FP4_OK = 0,
     FP4_E_ARG = 1,       /* null pointer, wrong block size, bad candidate grid   */
     FP4_E_SHAPE = 2,     /* rows < 1, cols < 1, or cols not a multiple of block   */
@@ -76,10 +86,10 @@ typedef enum {
                                       wait timed out and some workgroup took the
                                       fallback; the outputs are exact            */
 
-typedef enum { FP4_F32 = 0, FP4_BF16 = 1 } fp4_dtype;
-typedef enum { FP4_MXFP4 = 0, FP4_NVFP4 = 1 } fp4_format;
-typedef enum { FP4_MX_RULE_OCP = 0, FP4_MX_RULE_CEIL = 1, FP4_MX_RULE_MSE = 2 } fp4_mx_rule;
-typedef enum { FP4_LINEAR_ONE_LAUNCH = 0, FP4_LINEAR_TWO_LAUNCHES = 1 } fp4_linear_mode;
+typedef FP4_ENUM { FP4_F32 = 0, FP4_BF16 = 1 } fp4_dtype;
+typedef FP4_ENUM { FP4_MXFP4 = 0, FP4_NVFP4 = 1 } fp4_format;
+typedef FP4_ENUM { FP4_MX_RULE_OCP = 0, FP4_MX_RULE_CEIL = 1, FP4_MX_RULE_MSE = 2 } fp4_mx_rule;
+typedef FP4_ENUM { FP4_LINEAR_ONE_LAUNCH = 0, FP4_LINEAR_TWO_LAUNCHES = 1 } fp4_linear_mode;
 
 /*
  * MXFP4 quantize ("NVFP4 / MXFP4 format" page, sections 1, 2 and 5).
@@ -505,7 +515,8 @@ fp4_status fp4_linear_mxfp4(const void *x, fp4_dtype xt, int64_t M, int64_t K,
  *   fp4_dequantize_padded: decodes the padded layout and writes only the
  *     logical [rows, cols] values of y (fp32 or bf16), as fp4_dequantize.
  *   fp4_padded_storage_bytes: rows * ceil(cols/block) * (block/2 + 1), plus
- *     4 for NVFP4's tensor scale (-1 for invalid arguments).
+ *     4 for NVFP4's tensor scale (-1 for invalid arguments, and for shapes
+ *     of more than 2^40 padded elements, which the entry points reject).
  * Values are moved one by one (rows need not be aligned): these are for
  * shapes the block-aligned entry points reject.  Deterministic.
  */

@@ -383,7 +383,13 @@ fp4_status fp4_linear_mxfp4_packed(const void *x, fp4_dtype xt, int64_t M, int64
 size_t fp4_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (M < 1 || N < 1 || M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return 0;
     const int S = fp4dev::gemm_splitk_parts(M, N, K);
-    return S < 1 ? 0 : (size_t)S * (size_t)M * (size_t)N * sizeof(float);
+    if (S < 1) return 0;
+    // S partial products of M x N fp32; a size past size_t is no shape at all
+    size_t bytes = 0;
+    if (__builtin_mul_overflow((size_t)S * sizeof(float), (size_t)M, &bytes) ||
+        __builtin_mul_overflow(bytes, (size_t)N, &bytes))
+        return 0;
+    return bytes;
 }
 
 fp4_status fp4_gemm_mxfp4_splitk(const uint8_t *a_codes, const uint8_t *a_scales,
@@ -483,6 +489,8 @@ fp4_status fp4_dequantize_padded(fp4_format fmt, const uint8_t *codes, const uin
 int64_t fp4_padded_storage_bytes(fp4_format fmt, int64_t rows, int64_t cols) {
     if ((fmt != FP4_MXFP4 && fmt != FP4_NVFP4) || rows < 1 || cols < 1) return -1;
     const int64_t block = fmt == FP4_MXFP4 ? 32 : 16;
+    // the shapes fp4_quantize_padded accepts; the products below then fit
+    if (cols > kMaxElems || rows > kMaxElems / ((cols + block - 1) / block * block)) return -1;
     const int64_t blocks = rows * ((cols + block - 1) / block);
     return blocks * (block / 2 + 1) + (fmt == FP4_NVFP4 ? 4 : 0);
 }
