@@ -412,13 +412,20 @@ __device__ __forceinline__ uint32_t nv_lo_bf16(uint32_t c, float s_g) {
 
 // Builds the table in two steps (per code; per window entry) for the tensor
 // scale s_g of a bf16 tensor; rcrow is kRecipCorrection's row for the tensor
-// amax's significand index M (its low 7 bits).  T.need must be zero, and a
-// barrier passed since it was zeroed, on entry (512 threads).  Ends with a
-// barrier; T.need then holds the call's NV_NEEDS_*.
+// amax's significand index M (its low 7 bits).  Entry i >= 2 is the bf16
+// magnitude base + i - 2; only entries 0, 1 and those in [i0, i1) are
+// written (a workgroup fills those its blocks can index).  T.need must be
+// zero, and a barrier passed since it was zeroed, on entry (512 threads).
+// Ends with a barrier; T.need then holds the call's NV_NEEDS_*.  between()
+// runs after the first step's barrier (a profiling hook; nothing otherwise).
+// The first step's two halves (threads 0-127: Y_c and D_c; threads 128-255:
+// the codes' lower bounds) run on different waves, side by side.
+template <typename Between>
 __device__ __forceinline__ void nv_direct_table_build(NvDirectTable &T, float s_g, uint32_t rcrow,
-                                                      uint32_t base) {
+                                                      uint32_t base, int i0, int i1,
+                                                      Between between) {
     const int t = threadIdx.x;
-    // step 1, per code: Y_c, D_c and the code's lower bound
+    // step 1, per code: Y_c and D_c, or the code's lower bound
     if (t < 128) {
         float Y = 0.0f, D = 0.0f;
         uint32_t need = 0;
@@ -445,35 +452,48 @@ __device__ __forceinline__ void nv_direct_table_build(NvDirectTable &T, float s_
         }
         T.yc[t] = Y;
         T.dc[t] = D;
-        T.lo[t] = t == 0 ? 0u : (t == 127 ? 0xFFFFu : nv_lo_bf16((uint32_t)t, s_g));
         if (need) atomicOr(&T.need, need);
+    } else if (t < 256) {
+        const uint32_t c = (uint32_t)t - 128u;
+        T.lo[c] = c == 0 ? 0u : (c == 127 ? 0xFFFFu : nv_lo_bf16(c, s_g));
     }
     __syncthreads();
+    between();
     // step 2, per window entry: the code of a bf16 magnitude, from a guess
     // within one code of it settled by the two bounds around it.  All of a
     // thread's reads come before its stores, so its entries' LDS round trips
     // overlap (a store between them would order every later read after it).
+    // Entries 0 and 1, then those in [i0, i1), 512 per round; rounds past
+    // the range are skipped (uniformly).
     constexpr int NR = (RES_NIDX + 2 + 511) / 512;
     const CodeGuess G = make_code_guess(s_g);
     uint32_t code[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-        const int i = t + r * 512;
-        const uint32_t bits = min(base + (uint32_t)max(i - 2, 0), 0x7F7Fu);  // finite
+        if (i0 + r * 512 >= i1) break;
+        const int i = i0 + t + r * 512;
+        const uint32_t bits = min(base + (uint32_t)(i - 2), 0x7F7Fu);  // finite
         const uint32_t g = code_guess(u2f(bits << 16), G);
-        const uint32_t c = g + (bits >= T.lo[g + 1] ? 1u : 0u) - (bits < T.lo[g] ? 1u : 0u);
-        code[r] = i < 2 ? (i == 0 ? 0x38u : 0u) : c;
+        code[r] = g + (bits >= T.lo[g + 1] ? 1u : 0u) - (bits < T.lo[g] ? 1u : 0u);
     }
     float y[NR];
 #pragma unroll
-    for (int r = 0; r < NR; ++r) y[r] = T.yc[code[r]];
+    for (int r = 0; r < NR; ++r) {
+        if (i0 + r * 512 >= i1) break;
+        y[r] = T.yc[code[r]];
+    }
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-        const int i = t + r * 512;
-        if (i < RES_NIDX + 2) {
+        if (i0 + r * 512 >= i1) break;
+        const int i = i0 + t + r * 512;
+        if (i < i1) {
             T.code[i] = (uint8_t)code[r];
             T.y[i] = y[r];
         }
+    }
+    if (t < 2) {
+        T.code[t] = t == 0 ? 0x38u : 0u;
+        T.y[t] = T.yc[t == 0 ? 0x38 : 0];
     }
     __syncthreads();
 }
@@ -481,6 +501,11 @@ __device__ __forceinline__ void nv_direct_table_build(NvDirectTable &T, float s_
 // ---- wave-level helpers ---------------------------------------------------
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, WAVE));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    for (int off = 32; off >= 1; off >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, off, WAVE));
     return v;
 }
 

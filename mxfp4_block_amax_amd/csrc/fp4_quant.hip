@@ -703,8 +703,10 @@ __global__ __launch_bounds__(WG) void nv_quantize_packed_kernel(
 
 // Phase clock (a separate profiling build, -DFP4_PHASE_CLOCK): thread 0 of
 // each workgroup of the one-pass kernel stamps the device's constant 100 MHz
-// clock at its start, after its loads and partial amax, after the grid
-// barrier, after the table build and at its end (slots 0..4 of 8).
+// clock in slots 0..7 of its row: 0 its start, 1 after its loads and partial
+// amax, 7 when its poll has seen every slot, 2 after the grid barrier, 5
+// once s_g and the table window are known, 6 after the table's per-code
+// step, 3 after the table, 4 at its end.
 #ifdef FP4_PHASE_CLOCK
 __device__ uint64_t g_phase_clock[kResidentSlots * 8];
 #define FP4_PHASE(k)                                                                     \
@@ -740,8 +742,10 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
     struct Shared {
         NvDirectTable T;
         uint32_t red[RES_WAVES];
+        uint32_t red_min[RES_WAVES];
         uint32_t tensor_amax;
         uint32_t late_tag;
+        uint32_t wg_lo, wg_hi;  // this workgroup's smallest nonzero and largest block amax
         uint16_t rc[128];  // kRecipCorrection, staged during phase 1
         uint4 data[LC * RES_WG];
     };
@@ -786,9 +790,13 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
 #pragma unroll
     for (int i = 0; i < (NP + 1) / 2; ++i) am[i] = 0;
     uint32_t m = 0;
+    // and the smallest nonzero block amax (0xFFFF: none), which with m bounds
+    // the table entries this workgroup's blocks index
+    uint32_t mn = 0xFFFFu;
     auto keep_pair = [&](int p, uint32_t m0, uint32_t m1) {
         m = max(m, max(m0, m1));
         const uint32_t ag = pair_amax(m0, m1, odd);
+        mn = min(mn, ag ? ag : 0xFFFFu);
         am[p >> 1] |= (p & 1) ? ag << 16 : ag;  // pairs are kept in no particular order
     };
 #pragma unroll
@@ -802,7 +810,11 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
 #pragma unroll
     for (int i = 0; i < (NP + 1) / 2; ++i) asm volatile("" : "+v"(am[i]));
     m = wave_max_u32(m);
-    if (lane == 0) red[wv] = m;
+    mn = wave_min_u32(mn);
+    if (lane == 0) {
+        red[wv] = m;
+        sh.red_min[wv] = mn;
+    }
     __syncthreads();
     FP4_PHASE(1);
 
@@ -810,9 +822,16 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
     uint32_t flags = 0;
     if (wv == 0) {
         uint32_t wm = lane < RES_WAVES ? red[lane] : 0u;
+        uint32_t wn = lane < RES_WAVES ? sh.red_min[lane] : 0xFFFFu;
         wm = wave_max_u32(wm);
+        wn = wave_min_u32(wn);
+        if (lane == 0) {
+            sh.wg_lo = wn;
+            sh.wg_hi = wm;
+        }
         uint32_t A;
         const bool done = grid_barrier_max(slots, tag, wm, spin_limit, A);
+        FP4_PHASE(7);
         if (lane == 0) {
             tensor_amax = A;
             sh.late_tag = done ? 0u : tag;
@@ -859,8 +878,18 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
         report_flags(status, flags);
         return;
     }
+    // The table's window starts at the smaller of the code-1 threshold and
+    // this workgroup's smallest nonzero block amax, and ends at its largest
+    // (entries past RES_NIDX + 1 all hold the saturated code).
+    // Entries this workgroup's blocks can index: 0 and 1, and those of its
+    // nonzero block amaxes in [wg_lo, wg_hi] (RES_NIDX + 1 for all at or
+    // past the window's last magnitude).
     const uint32_t base = nv_window_base(ts.s_g);
-    nv_direct_table_build(T, ts.s_g, sh.rc[tensor_amax & 127u], base);  // ends with a barrier
+    const int i0 = 2 + (int)min(max(sh.wg_lo, base) - base, (uint32_t)RES_NIDX - 1u);
+    const int i1 = 2 + (int)min(max(sh.wg_hi + 1u, base) - base, (uint32_t)RES_NIDX);
+    FP4_PHASE(5);
+    nv_direct_table_build(T, ts.s_g, sh.rc[tensor_amax & 127u], base, i0, i1,
+                          [] { FP4_PHASE(6); });  // ends with a barrier
     const uint32_t need = T.need;            // uniform
     FP4_PHASE(3);
 
