@@ -53,6 +53,21 @@ def test_mxfp4_activation_16384x7168_full():
     check_mx(workloads.mxfp4_activation(), "activation 16384x7168 bf16")
 
 
+def test_nv_one_pass_per_workgroup_ranges():
+    # The one-pass kernel at 8192 x 8192 holds, in workgroup w of 256, the
+    # 4096-element pieces p with p % 256 == w.  Each workgroup's pieces get
+    # their own scale 2^-(w % 13) (a different range of block amaxes, so a
+    # different part of the scale table) and every sixteenth workgroup's are
+    # all zero (no nonzero block at all); the tensor amax stays in workgroup 0.
+    x = workloads.nvfp4_weight().float().reshape(-1, 4096)
+    w = torch.arange(x.shape[0]) % 256
+    scale = torch.pow(2.0, -(w % 13).double()).float()
+    scale[w % 16 == 5] = 0.0
+    x = (x * scale[:, None]).reshape(8192, 8192)
+    x[0, 0] = 0.2  # above every other magnitude (N(0, 0.02^2) data)
+    check_nv(x.to(torch.bfloat16), "per-workgroup magnitude ranges 8192x8192 bf16")
+
+
 # ---- exhaustive conversion sweep --------------------------------------------
 
 def _mx_sweep_tensor() -> torch.Tensor:
