@@ -400,7 +400,9 @@ def extra_workloads(dg: dict):
     ms = time_rotating([lambda x=x, r=r: fp4.scale_search(x, check=False, out=r, status=st, workspace=ws)
                         for x, r in zip(xs, res)], launches=6)
     d = _rate(quantize_bytes(xs_cpu.numel(), 2, "nv"), ms, xs_cpu.numel())
-    d["candidate_element_evals_per_s"] = f"{xs_cpu.numel() * 64 / ms / 1e-3:.3e}"
+    # nominal: every one of the 64 candidates counted for every element; the
+    # kernel evaluates only the distinct encoded candidates its walk reaches
+    d["candidate_element_evals_per_s_nominal"] = f"{xs_cpu.numel() * 64 / ms / 1e-3:.3e}"
     out["nvfp4_scale_search_4096x14336_bf16"] = d
     # the same search over c in [0.5, 1.5] (amax may map to 4), and over every
     # E4M3 code
@@ -413,7 +415,7 @@ def extra_workloads(dg: dict):
                                                                      status=st, workspace=ws)
                         for x, r in zip(xs, res)], launches=3, reps=3)
     d = _rate(quantize_bytes(xs_cpu.numel(), 2, "nv"), ms, xs_cpu.numel())
-    d["candidate_element_evals_per_s"] = f"{xs_cpu.numel() * 126 / ms / 1e-3:.3e}"
+    d["candidate_element_evals_per_s_nominal"] = f"{xs_cpu.numel() * 126 / ms / 1e-3:.3e}"
     out["nvfp4_scale_search_all_codes_4096x14336_bf16"] = d
     del xs, res
     # MXFP4 quantize of the 8192 x 8192 weight under the ceil rule and the
