@@ -553,7 +553,12 @@ __global__ __launch_bounds__(WG) void nv_quantize_kernel(const uint4 *__restrict
     const int64_t nwaves = (int64_t)gridDim.x * WAVES_PER_WG;
     const int64_t ntiles = (nchunks + WAVE * U - 1) / (WAVE * U);
     uint32_t flags = 0;
-    for (int64_t t = wave; t < ntiles; t += nwaves) {
+    for (int64_t tt = wave; tt < ntiles; tt += nwaves) {
+        // fp32: back to front.  The amax pass read the input front to back,
+        // so its tail is what the memory-side cache still holds when the
+        // input is larger than that cache (8192 x 8192 fp32: 268 MB;
+        // 100.8 -> 96.5 us per call, paired timing).
+        const int64_t t = BF16 ? tt : ntiles - 1 - tt;
         const int64_t c0 = t * (WAVE * U) + lane, c1 = c0 + WAVE;
         Chunk<BF16> k0 = load_chunk<BF16>(x, c0, c0 < nchunks);
         Chunk<BF16> k1 = load_chunk<BF16>(x, c1, c1 < nchunks);
