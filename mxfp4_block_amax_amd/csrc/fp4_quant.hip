@@ -601,17 +601,18 @@ __global__ __launch_bounds__(WG) void nv_quantize_kernel(const uint4 *__restrict
 // so the two-pass path reads the input from HBM twice.  Here one workgroup
 // per CU (8 waves, two per SIMD) loads its slice once: up to 64 chunks of 16
 // bytes per lane, the first RES_LDS_CHUNKS of them straight into LDS (the
-// global->LDS load path; 152 KiB per workgroup) and the rest into VGPRs (180
-// registers).  It takes its partial amax, meets the other workgroups at a
-// grid barrier and quantizes from registers and LDS.  256 CUs hold 128 MiB of
-// bf16 this way, an 8192 x 8192 tensor.
+// global->LDS load path; 144 KiB per workgroup, beside the ~14 KiB scale
+// table) and the rest into VGPRs (184 registers).  It takes its partial
+// amax, meets the other workgroups at a grid barrier and quantizes from
+// registers and LDS.  256 CUs hold 128 MiB of bf16 this way, an 8192 x 8192
+// tensor.
 //
-// Chunk j of lane t in workgroup w is  w*cpl*512 + j*512 + t  (cpl chunks per
-// lane, even), so each wave load reads 1 KiB of consecutive bytes, a lane
-// pair holds one 16-element block, and rows j and j+1 pair up as in the
-// two-pass kernel (even lane: row j's block scale, odd lane: row j+1's).
-// Loads past the end of the tensor re-read its last chunk (a duplicate
-// cannot change the amax); stores past it are skipped.
+// Chunk j of lane t in workgroup w of G is  j*G*512 + w*512 + t  (rows j of
+// all workgroups side by side), so each wave load reads 1 KiB of consecutive
+// bytes, a lane pair holds one 16-element block, and rows j and j+1 pair up
+// as in the two-pass kernel (even lane: row j's block scale, odd lane: row
+// j+1's).  Loads past the end of the tensor re-read its last chunk (a
+// duplicate cannot change the amax); stores past it are skipped.
 //
 // Grid barrier (grid_barrier_max).  Each workgroup publishes (tag << 32 |
 // partial amax) in its own 64-bit slot with one device-coherent store, then
