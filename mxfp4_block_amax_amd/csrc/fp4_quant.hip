@@ -732,6 +732,7 @@ hipError_t read_phase_clock(uint64_t *host, size_t n) {
 
 // Cache policy of the code stores: non-temporal (the 33.6 MB of codes are
 // not read again by this kernel; measured ~1 us faster per call at 8192^2).
+// The scale bytes are stored non-temporally too (0.2 us).
 constexpr int kStoreNT = 2;
 
 // EXACT: the grid covers the tensor exactly (nchunks = gridDim.x * 512 * CPL),
@@ -951,7 +952,8 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
             pair_rows(y, ys);
             if (TWO) pair_rows(T.dc[c], ds);
             const int b0 = j0 * stride;
-            if (EXACT || cs <= last - b0) (scales + (b0 >> 1))[(uint32_t)cs >> 1] = (uint8_t)c;
+            if (EXACT || cs <= last - b0)
+                __builtin_nontemporal_store((uint8_t)c, &(scales + (b0 >> 1))[(uint32_t)cs >> 1]);
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
                 float f[8];
@@ -984,7 +986,8 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
             const uint32_t c = T.code[idx];
             ymin = __builtin_fminf(ymin, T.y[idx]);
             const int b0 = j0 * stride;
-            if (EXACT || cs <= last - b0) (scales + (b0 >> 1))[(uint32_t)cs >> 1] = (uint8_t)c;
+            if (EXACT || cs <= last - b0)
+                __builtin_nontemporal_store((uint8_t)c, &(scales + (b0 >> 1))[(uint32_t)cs >> 1]);
             const float a = ts.s_g * e4m3_pos_value(c);
             const float sc = a < kDivScaleBelow ? kDivScale : 1.0f;
             float ad[2], scr[2];
