@@ -90,6 +90,7 @@ typedef FP4_ENUM { FP4_F32 = 0, FP4_BF16 = 1 } fp4_dtype;
 typedef FP4_ENUM { FP4_MXFP4 = 0, FP4_NVFP4 = 1 } fp4_format;
 typedef FP4_ENUM { FP4_MX_RULE_OCP = 0, FP4_MX_RULE_CEIL = 1, FP4_MX_RULE_MSE = 2 } fp4_mx_rule;
 typedef FP4_ENUM { FP4_LINEAR_ONE_LAUNCH = 0, FP4_LINEAR_TWO_LAUNCHES = 1 } fp4_linear_mode;
+#undef FP4_ENUM
 
 /*
  * MXFP4 quantize ("NVFP4 / MXFP4 format" page, sections 1, 2 and 5).

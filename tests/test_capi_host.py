@@ -400,3 +400,24 @@ def test_noalloc_scratch_holds_a_workspace():
     assert fp4.workspace_bytes(fp4.NVFP4, 1 << 20, 1 << 20) <= fp4.NOALLOC_SCRATCH_BYTES
     src = open(HEADER).read()
     assert f"#define FP4_NOALLOC_SCRATCH_BYTES {fp4.NOALLOC_SCRATCH_BYTES}u" in src
+
+
+@pytest.mark.parametrize("lang,compiler,std", [("c", "gcc", "-std=c11"), ("c++", "g++", "-std=c++17")])
+def test_header_compiles_for_c_and_cpp_callers(tmp_path, lang, compiler, std):
+    # The header is the boundary for callers in either language: it must
+    # compile cleanly as both, with every enumeration 32 bits wide.
+    import shutil
+    import subprocess
+    if shutil.which(compiler) is None:
+        pytest.skip(f"{compiler} not found")
+    src = tmp_path / ("t.c" if lang == "c" else "t.cpp")
+    check = ("_Static_assert" if lang == "c" else "static_assert")
+    src.write_text(
+        '#include "fp4.h"\n'
+        f"{check}(sizeof(fp4_status) == 4, \"fp4_status is 32 bits\");\n"
+        f"{check}(sizeof(fp4_dtype) == 4 && sizeof(fp4_format) == 4, \"32-bit enums\");\n"
+        f"{check}(sizeof(fp4_mx_rule) == 4 && sizeof(fp4_linear_mode) == 4, \"32-bit enums\");\n"
+        "int f(void) { return (int)fp4_status_str(FP4_OK)[0]; }\n")
+    r = subprocess.run([compiler, std, "-Wall", "-Wextra", "-Werror", "-pedantic", "-fsyntax-only",
+                        "-I", os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
