@@ -908,17 +908,26 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
     // across the barrier for reuse (there are no registers for them).
 #pragma unroll
     for (int r = 0; r < RC; ++r) asm volatile("" : "+v"(v[r].x), "+v"(v[r].y), "+v"(v[r].z), "+v"(v[r].w));
-    float ymin = __builtin_inff();
+    float ymin = __builtin_inff();  // the compact loop's smallest Y (0: a scale underflow)
     // code dwords go out as buffer stores: one resource, the lane's byte
     // offset in a VGPR and the uniform part of the address in an SGPR
     const uint32_t coff = (uint32_t)c00 * 4u;
     const __amdgpu_buffer_rsrc_t crs =
         __builtin_amdgcn_make_buffer_rsrc(codes, (short)0, nchunks * 4, kBufferRsrcWord3);
     const int cs = odd ? c00 + stride : c00;  // this lane's scale chunk, relative to row 0
-    // pair p's block amax (bf16 bits) -> its table entry
+    // a block amax (bf16 bits) -> its table entry: 0 for a zero block, else
+    // base + i - 2 clamped to [1, RES_NIDX + 1] (one med3, whose lower bound
+    // min(ag, 1) is 0 for the zero block)
+    auto entry_of = [&](uint32_t ag) {
+        const int k = (int)ag - (int)base + 2, lo = (int)min(ag, 1u), hi = RES_NIDX + 1;
+        int e;
+        asm("v_med3_i32 %0, %1, %2, %3" : "=v"(e) : "v"(k), "v"(lo), "s"(hi));
+        return e;
+    };
+    // pair p's block amax -> its table entry
     auto entry = [&](int p) {
         const uint32_t ag = (p & 1) ? (am[p >> 1] >> 16) : (am[p >> 1] & 0xFFFFu);
-        return ag == 0 ? 0 : min(max((int)ag - (int)base + 2, 1), RES_NIDX + 1);
+        return entry_of(ag);
     };
     // The quotient x / alpha, chosen once per call (uniformly, from the table):
     //  - the product x * Y_c (every code's Y_c makes it exact for bf16 input);
@@ -947,7 +956,6 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
             const int j0 = 2 * p, j1 = j0 + 1;
             const uint4 w0 = j0 < LC ? lds[j0 * RES_WG + tid] : v[j0 - LC];
             const uint4 w1 = j1 < LC ? lds[j1 * RES_WG + tid] : v[j1 - LC];
-            asm("v_min_f32 %0, %1, %2" : "=v"(ymin) : "v"(ymin), "v"(y));
             float ys[2], ds[2];
             pair_rows(y, ys);
             if (TWO) pair_rows(T.dc[c], ds);
@@ -1006,6 +1014,11 @@ __global__ __launch_bounds__(RES_WG) void nv_resident_kernel(
         }
     }
     flags |= ymin == 0.0f ? FLAG_SCALE_UNDERFLOW : 0u;
+    // Some nonzero block took code 0 (its scale underflowed): codes never
+    // fall as the block amax grows, so the workgroup's smallest nonzero block
+    // amax has code 0 then.  (With s_g normal, as in the full loops, code 0 is
+    // the only code whose Y is 0.)
+    if (sh.wg_lo != 0xFFFFu && T.code[entry_of(sh.wg_lo)] == 0) flags |= FLAG_SCALE_UNDERFLOW;
     if (late && tid == 0) barrier_retract(slots);
     report_flags(status, flags);
 #ifdef FP4_PHASE_CLOCK
