@@ -3,11 +3,10 @@
  *
  * C ABI of libfp4.so.  Every tensor argument is a DEVICE pointer into memory
  * the caller owns (allocates and frees); the library allocates nothing.  Its
- * global state is two per-device records, each filled once (whether the
- * one-pass NVFP4 kernel fits, from the CU count and occupancy, and how many
- * workgroups of the one-launch W4A4 linear kernel the device holds at once),
- * and the grid barrier's poll limit, a process-wide setting that only
- * fp4_debug_barrier_spin_limit changes.
+ * only global state is two per-device records, each filled once and never
+ * changed (whether the one-pass NVFP4 kernel fits, from the CU count and
+ * occupancy, and how many workgroups of the one-launch W4A4 linear kernel the
+ * device holds at once).
  * Calls on different streams may run concurrently unless they share a
  * workspace (or, for fp4_quantize_nvfp4_noalloc, a GPU).  The one-pass NVFP4
  * quantize and the one-launch W4A4 linear meet at a grid barrier that does
@@ -532,16 +531,26 @@ int64_t fp4_padded_storage_bytes(fp4_format fmt, int64_t rows, int64_t cols);
 
 /*
  * For tests of the grid barrier's fallback (the one-pass NVFP4 quantize and
- * the one-launch W4A4 linear): sets how many times a workgroup polls the
- * other workgroups' slots before it stops waiting, takes the fallback and
- * raises FP4_FLAG_BARRIER_TIMEOUT (0 = after the first poll), for launches
- * enqueued from then on, process-wide; returns the previous value.  The
- * default is FP4_BARRIER_SPIN_LIMIT_DEFAULT polls (a few milliseconds, far
- * above the barrier's usual microseconds).  Results are exact whatever the
- * value; only the time changes.
+ * the one-launch W4A4 linear): fp4_quantize_nvfp4 and fp4_linear_mxfp4 with
+ * the number of times a workgroup polls the other workgroups' slots before
+ * it stops waiting, takes the fallback and raises FP4_FLAG_BARRIER_TIMEOUT
+ * (0 = after the first poll) as an argument.  The entry points above use
+ * FP4_BARRIER_SPIN_LIMIT_DEFAULT polls (a few milliseconds, far above the
+ * barrier's usual microseconds).  Results are exact whatever the value; only
+ * the time changes.  Other arguments, errors and outputs as for those two.
  */
 #define FP4_BARRIER_SPIN_LIMIT_DEFAULT 2048u
-uint32_t fp4_debug_barrier_spin_limit(uint32_t polls);
+fp4_status fp4_debug_quantize_nvfp4_spin(const void *x, fp4_dtype xt, int64_t rows,
+                                         int64_t cols, int32_t block, uint8_t *codes,
+                                         uint8_t *scales, float *global_scale, void *workspace,
+                                         size_t workspace_bytes, int32_t *status, void *stream,
+                                         uint32_t spin_limit);
+fp4_status fp4_debug_linear_mxfp4_spin(const void *x, fp4_dtype xt, int64_t M, int64_t K,
+                                       const uint8_t *bt_codes, const uint8_t *bt_scales,
+                                       int64_t N, uint8_t *a_codes, uint8_t *a_scales, void *c,
+                                       fp4_dtype ct, fp4_linear_mode mode, void *workspace,
+                                       size_t workspace_bytes, int32_t *status, void *stream,
+                                       uint32_t spin_limit);
 
 /* Bytes of device workspace fp4_quantize_nvfp4 / fp4_scale_search need for a
  * [rows, cols] input (0 for MXFP4). */

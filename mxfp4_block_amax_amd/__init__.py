@@ -45,7 +45,8 @@ EXPORTS = ("fp4_quantize_mxfp4", "fp4_quantize_mxfp4_rule", "fp4_quantize_nvfp4"
            "fp4_gemm_mxfp4", "fp4_gemm_mxfp4_splitk", "fp4_gemm_splitk_workspace_bytes",
            "fp4_gemm_nvfp4", "fp4_linear_mxfp4", "fp4_quantize_padded",
            "fp4_dequantize_padded", "fp4_padded_storage_bytes", "fp4_quantize_sr",
-           "fp4_debug_barrier_spin_limit", "fp4_packed_operand_bytes", "fp4_pack_mxfp4_operand",
+           "fp4_debug_quantize_nvfp4_spin", "fp4_debug_linear_mxfp4_spin",
+           "fp4_packed_operand_bytes", "fp4_pack_mxfp4_operand",
            "fp4_gemm_mxfp4_packed", "fp4_quantize_mxfp4_packed", "fp4_linear_mxfp4_packed",
            "fp4_nv_packed_operand_bytes", "fp4_pack_nvfp4_operand", "fp4_gemm_nvfp4_packed",
            "fp4_quantize_nvfp4_packed", "fp4_linear_nvfp4_packed",
@@ -102,8 +103,10 @@ def lib() -> ctypes.CDLL:
     L.fp4_linear_nvfp4_packed.argtypes = [P, I, I64, I64, P, P, I64, P, S, P, P, I, P, S, P, P]
     L.fp4_quantize_mxfp4_packed.argtypes = [P, I, I64, I64, P, S, P, P]
     L.fp4_linear_mxfp4_packed.argtypes = [P, I, I64, I64, P, I64, P, S, P, I, P, P]
-    L.fp4_debug_barrier_spin_limit.argtypes = [ctypes.c_uint32]
-    L.fp4_debug_barrier_spin_limit.restype = ctypes.c_uint32
+    L.fp4_debug_quantize_nvfp4_spin.argtypes = [P, I, I64, I64, I32, P, P, P, P, S, P, P,
+                                                ctypes.c_uint32]
+    L.fp4_debug_linear_mxfp4_spin.argtypes = [P, I, I64, I64, P, P, I64, P, P, P, I, I, P, S, P, P,
+                                              ctypes.c_uint32]
     L.fp4_workspace_bytes.argtypes = [I, I64, I64]
     L.fp4_workspace_bytes.restype = S
     L.fp4_status_str.argtypes = [I]
@@ -169,13 +172,15 @@ def _finish(status: torch.Tensor, check: bool):
         _raise_flags(int(status.item()))
 
 
-BARRIER_SPIN_LIMIT_DEFAULT = 2048
+BARRIER_SPIN_LIMIT_DEFAULT = 2048  # polls of the grid barrier before its fallback
 
 
-def debug_barrier_spin_limit(polls: int) -> int:
-    """Set the grid barrier's poll limit (tests of the timeout path); returns
-    the previous value.  BARRIER_SPIN_LIMIT_DEFAULT restores the default."""
-    return int(lib().fp4_debug_barrier_spin_limit(int(polls)))
+def _spin(spin_limit) -> int:
+    """A grid-barrier poll limit for the debug entry points (0 .. 2^32 - 1)."""
+    v = int(spin_limit)
+    if not 0 <= v < 2 ** 32:
+        raise ValueError("spin_limit must fit in 32 unsigned bits")
+    return v
 
 
 def workspace_bytes(fmt: int, rows: int, cols: int) -> int:
@@ -224,7 +229,11 @@ def quantize_mxfp4_rule(x: torch.Tensor, rule: str = "ocp", check: bool = True, 
     return codes, scales
 
 
-def quantize_nvfp4(x: torch.Tensor, check: bool = True, out=None, status=None, workspace=None):
+def quantize_nvfp4(x: torch.Tensor, check: bool = True, out=None, status=None, workspace=None,
+                   spin_limit=None):
+    """NVFP4 quantize; returns (codes, scales, s_g).  spin_limit (tests of the
+    grid barrier's fallback) calls fp4_debug_quantize_nvfp4_spin with that
+    poll limit instead of fp4_quantize_nvfp4."""
     rows, cols = _rows_cols(x)
     if out is None:
         codes = torch.empty(*x.shape[:-1], cols // 2, dtype=torch.uint8, device=x.device)
@@ -236,9 +245,12 @@ def quantize_nvfp4(x: torch.Tensor, check: bool = True, out=None, status=None, w
         workspace = new_workspace(rows, cols, x.device)
     if status is None:
         status = torch.zeros(1, dtype=torch.int32, device=x.device)
-    _ok(lib().fp4_quantize_nvfp4(_ptr(x), _dtype_code(x.dtype), rows, cols, 16, _ptr(codes),
-                                 _ptr(scales), _ptr(s_g), _ptr(workspace), workspace.numel(),
-                                 _ptr(status), _stream(x)))
+    args = (_ptr(x), _dtype_code(x.dtype), rows, cols, 16, _ptr(codes), _ptr(scales), _ptr(s_g),
+            _ptr(workspace), workspace.numel(), _ptr(status), _stream(x))
+    if spin_limit is None:
+        _ok(lib().fp4_quantize_nvfp4(*args))
+    else:
+        _ok(lib().fp4_debug_quantize_nvfp4_spin(*args, _spin(spin_limit)))
     _finish(status, check)
     return codes, scales, s_g
 
@@ -570,10 +582,12 @@ def linear_nvfp4_packed(x: torch.Tensor, bt_packed: torch.Tensor, bt_global_scal
 
 def linear_mxfp4(x: torch.Tensor, bt_codes: torch.Tensor, bt_scales: torch.Tensor,
                  out_dtype=torch.bfloat16, out=None, a_out=None, status=None, workspace=None,
-                 check: bool = True, one_launch: bool = True):
+                 check: bool = True, one_launch: bool = True, spin_limit=None):
     """W4A4 linear: x [M, K] (fp32/bf16) quantized to MXFP4, times B with
     Bt = B^T [N, K] in MXFP4.  Returns (C [M, N], (a_codes, a_scales)).
-    one_launch: quantize and multiply in one kernel when the grid fits."""
+    one_launch: quantize and multiply in one kernel when the grid fits.
+    spin_limit (tests of the grid barrier's fallback): through
+    fp4_debug_linear_mxfp4_spin with that poll limit."""
     M, K = _rows_cols(x)
     N, kh = _rows_cols(bt_codes)
     if 2 * kh != K:
@@ -588,10 +602,13 @@ def linear_mxfp4(x: torch.Tensor, bt_codes: torch.Tensor, bt_scales: torch.Tenso
         workspace = new_workspace(M, K, x.device)
     if status is None:
         status = torch.zeros(1, dtype=torch.int32, device=x.device)
-    _ok(lib().fp4_linear_mxfp4(_ptr(x), _dtype_code(x.dtype), M, K, _ptr(bt_codes),
-                               _ptr(bt_scales), N, _ptr(a_codes), _ptr(a_scales), _ptr(c),
-                               _dtype_code(c.dtype), 0 if one_launch else 1, _ptr(workspace),
-                               workspace.numel(), _ptr(status), _stream(x)))
+    args = (_ptr(x), _dtype_code(x.dtype), M, K, _ptr(bt_codes), _ptr(bt_scales), N,
+            _ptr(a_codes), _ptr(a_scales), _ptr(c), _dtype_code(c.dtype), 0 if one_launch else 1,
+            _ptr(workspace), workspace.numel(), _ptr(status), _stream(x))
+    if spin_limit is None:
+        _ok(lib().fp4_linear_mxfp4(*args))
+    else:
+        _ok(lib().fp4_debug_linear_mxfp4_spin(*args, _spin(spin_limit)))
     _finish(status, check)
     return c, (a_codes, a_scales)
 

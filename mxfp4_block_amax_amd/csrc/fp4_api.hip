@@ -22,6 +22,8 @@ static_assert(FP4_NOALLOC_SCRATCH_BYTES == fp4dev::kNoAllocScratchBytes,
               "the header states the scratch size");
 static_assert(fp4dev::kNvWorkspaceBytes <= fp4dev::kNoAllocScratchBytes,
               "the scratch holds one NVFP4 workspace");
+static_assert(FP4_BARRIER_SPIN_LIMIT_DEFAULT == fp4dev::kResidentSpinLimit,
+              "the header states the grid barrier's default poll limit");
 
 namespace {
 
@@ -104,10 +106,11 @@ fp4_status fp4_quantize_mxfp4_rule(const void *x, fp4_dtype xt, int64_t rows, in
                                                scales, status, (hipStream_t)stream));
 }
 
-fp4_status fp4_quantize_nvfp4(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
-                              int32_t block, uint8_t *codes, uint8_t *scales,
-                              float *global_scale, void *workspace, size_t workspace_bytes,
-                              int32_t *status, void *stream) {
+// fp4_quantize_nvfp4 with the grid barrier's poll limit as an argument
+static fp4_status quantize_nvfp4(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
+                                 int32_t block, uint8_t *codes, uint8_t *scales,
+                                 float *global_scale, void *workspace, size_t workspace_bytes,
+                                 int32_t *status, void *stream, uint32_t spin_limit) {
     if (!x || !codes || !scales || !global_scale) return FP4_E_ARG;
     if (block != 16) return FP4_E_ARG;
     if (!valid_dtype(xt)) return FP4_E_DTYPE;
@@ -119,7 +122,24 @@ fp4_status fp4_quantize_nvfp4(const void *x, fp4_dtype xt, int64_t rows, int64_t
         return FP4_E_ALIGN;
     return from_hip(fp4dev::launch_nv_quantize(x, xt == FP4_BF16, rows * cols, codes, scales,
                                                global_scale, workspace, status,
-                                               (hipStream_t)stream));
+                                               (hipStream_t)stream, spin_limit));
+}
+
+fp4_status fp4_quantize_nvfp4(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
+                              int32_t block, uint8_t *codes, uint8_t *scales,
+                              float *global_scale, void *workspace, size_t workspace_bytes,
+                              int32_t *status, void *stream) {
+    return quantize_nvfp4(x, xt, rows, cols, block, codes, scales, global_scale, workspace,
+                          workspace_bytes, status, stream, fp4dev::kResidentSpinLimit);
+}
+
+fp4_status fp4_debug_quantize_nvfp4_spin(const void *x, fp4_dtype xt, int64_t rows,
+                                         int64_t cols, int32_t block, uint8_t *codes,
+                                         uint8_t *scales, float *global_scale, void *workspace,
+                                         size_t workspace_bytes, int32_t *status, void *stream,
+                                         uint32_t spin_limit) {
+    return quantize_nvfp4(x, xt, rows, cols, block, codes, scales, global_scale, workspace,
+                          workspace_bytes, status, stream, spin_limit);
 }
 
 fp4_status fp4_quantize_nvfp4_noalloc(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
@@ -427,11 +447,12 @@ fp4_status fp4_gemm_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales,
                                               ct == FP4_BF16, (hipStream_t)stream));
 }
 
-fp4_status fp4_linear_mxfp4(const void *x, fp4_dtype xt, int64_t M, int64_t K,
-                            const uint8_t *bt_codes, const uint8_t *bt_scales, int64_t N,
-                            uint8_t *a_codes, uint8_t *a_scales, void *c, fp4_dtype ct,
-                            fp4_linear_mode mode, void *workspace, size_t workspace_bytes,
-                            int32_t *status, void *stream) {
+// fp4_linear_mxfp4 with the grid barrier's poll limit as an argument
+static fp4_status linear_mxfp4(const void *x, fp4_dtype xt, int64_t M, int64_t K,
+                               const uint8_t *bt_codes, const uint8_t *bt_scales, int64_t N,
+                               uint8_t *a_codes, uint8_t *a_scales, void *c, fp4_dtype ct,
+                               fp4_linear_mode mode, void *workspace, size_t workspace_bytes,
+                               int32_t *status, void *stream, uint32_t spin_limit) {
     if (!x || !bt_codes || !bt_scales || !a_codes || !a_scales || !c) return FP4_E_ARG;
     if (mode != FP4_LINEAR_ONE_LAUNCH && mode != FP4_LINEAR_TWO_LAUNCHES) return FP4_E_ARG;
     if (!valid_dtype(xt) || !valid_dtype(ct)) return FP4_E_DTYPE;
@@ -445,7 +466,26 @@ fp4_status fp4_linear_mxfp4(const void *x, fp4_dtype xt, int64_t M, int64_t K,
     return from_hip(fp4dev::launch_linear_mxfp4(x, xt == FP4_BF16, bt_codes, bt_scales, M, N, K,
                                                 a_codes, a_scales, c, ct == FP4_BF16,
                                                 mode == FP4_LINEAR_ONE_LAUNCH, workspace, status,
-                                                (hipStream_t)stream));
+                                                (hipStream_t)stream, spin_limit));
+}
+
+fp4_status fp4_linear_mxfp4(const void *x, fp4_dtype xt, int64_t M, int64_t K,
+                            const uint8_t *bt_codes, const uint8_t *bt_scales, int64_t N,
+                            uint8_t *a_codes, uint8_t *a_scales, void *c, fp4_dtype ct,
+                            fp4_linear_mode mode, void *workspace, size_t workspace_bytes,
+                            int32_t *status, void *stream) {
+    return linear_mxfp4(x, xt, M, K, bt_codes, bt_scales, N, a_codes, a_scales, c, ct, mode,
+                        workspace, workspace_bytes, status, stream, fp4dev::kResidentSpinLimit);
+}
+
+fp4_status fp4_debug_linear_mxfp4_spin(const void *x, fp4_dtype xt, int64_t M, int64_t K,
+                                       const uint8_t *bt_codes, const uint8_t *bt_scales,
+                                       int64_t N, uint8_t *a_codes, uint8_t *a_scales, void *c,
+                                       fp4_dtype ct, fp4_linear_mode mode, void *workspace,
+                                       size_t workspace_bytes, int32_t *status, void *stream,
+                                       uint32_t spin_limit) {
+    return linear_mxfp4(x, xt, M, K, bt_codes, bt_scales, N, a_codes, a_scales, c, ct, mode,
+                        workspace, workspace_bytes, status, stream, spin_limit);
 }
 
 fp4_status fp4_quantize_padded(fp4_format fmt, const void *x, fp4_dtype xt, int64_t rows,
@@ -501,10 +541,6 @@ fp4_status fp4_debug_phase_clock(uint64_t *host, size_t n) {
     return from_hip(fp4dev::read_phase_clock(host, n));
 }
 #endif
-
-uint32_t fp4_debug_barrier_spin_limit(uint32_t polls) {
-    return fp4dev::set_barrier_spin_limit(polls);
-}
 
 size_t fp4_workspace_bytes(fp4_format fmt, int64_t rows, int64_t cols) {
     (void)rows;

@@ -1477,7 +1477,8 @@ hipError_t launch_gemm_mxfp4_splitk(const uint8_t *a_codes, const uint8_t *a_sca
 hipError_t launch_linear_mxfp4(const void *x, bool x_bf16, const uint8_t *bt_codes,
                                const uint8_t *bt_scales, int64_t M, int64_t N, int64_t K,
                                uint8_t *a_codes, uint8_t *a_scales, void *c, bool out_bf16,
-                               bool one_launch, void *workspace, int32_t *status, hipStream_t s) {
+                               bool one_launch, void *workspace, int32_t *status, hipStream_t s,
+                               uint32_t spin_limit) {
     dim3 grid((unsigned)((N + GEMM_TN - 1) / GEMM_TN), (unsigned)((M + GEMM_TM - 1) / GEMM_TM));
     const int64_t G = (int64_t)grid.x * grid.y;
     if (one_launch && gemm_lds_ok(a_codes, a_scales, bt_codes, bt_scales, K) &&
@@ -1492,7 +1493,7 @@ hipError_t launch_linear_mxfp4(const void *x, bool x_bf16, const uint8_t *bt_cod
                            (const uint4 *)x, (uint32_t *)a_codes, a_scales,
                            (const uint4 *)bt_codes, bt_scales, (int)M, (int)N, (int)K, c,
                            (uint64_t *)(ws + kResidentSlotsOffset),
-                           (uint32_t *)(ws + kResidentEpochOffset), barrier_spin_limit(), status);
+                           (uint32_t *)(ws + kResidentEpochOffset), spin_limit, status);
         return hipGetLastError();
     }
     // the grid cannot be resident at once (or the shape takes another GEMM

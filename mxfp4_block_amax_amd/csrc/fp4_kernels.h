@@ -24,12 +24,10 @@ constexpr size_t kNvWorkspaceBytes = kResidentSlotsOffset + kResidentSlots * siz
 // one NVFP4 workspace, rounded up to 4 KiB.
 constexpr size_t kNoAllocScratchBytes = (kNvWorkspaceBytes + 4095) / 4096 * 4096;
 // Polls of the grid barrier before a workgroup takes the fallback (a few
-// milliseconds; a poll takes a microsecond or two).
+// milliseconds; a poll takes a microsecond or two).  The launchers of the
+// two grid-barrier kernels take the limit as an argument; only the debug
+// entry points pass another.
 constexpr uint32_t kResidentSpinLimit = 2048;
-// The limit launches use: kResidentSpinLimit unless a test of the timeout
-// path has set another (fp4_debug_barrier_spin_limit).
-uint32_t barrier_spin_limit();
-uint32_t set_barrier_spin_limit(uint32_t polls);  // returns the previous value
 constexpr int kMaxDevices = 64;
 
 // rule: 0 the OCP floor rule, 1 the ceil rule, 2 the three-exponent search
@@ -40,7 +38,8 @@ hipError_t read_phase_clock(uint64_t *host, size_t n);
 #endif
 hipError_t launch_nv_quantize(const void *x, bool bf16, int64_t n, uint8_t *codes,
                               uint8_t *scales, float *global_scale, void *workspace,
-                              int32_t *status, hipStream_t s);
+                              int32_t *status, hipStream_t s,
+                              uint32_t spin_limit = kResidentSpinLimit);
 // Stochastic element rounding (fmt 0 MXFP4, 1 NVFP4 in two passes); the
 // random bits of element i depend on seed and i only.
 hipError_t launch_quantize_sr(int fmt, const void *x, bool bf16, int64_t n, uint64_t seed,
@@ -109,6 +108,7 @@ hipError_t launch_gemm_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, co
 hipError_t launch_linear_mxfp4(const void *x, bool x_bf16, const uint8_t *bt_codes,
                                const uint8_t *bt_scales, int64_t M, int64_t N, int64_t K,
                                uint8_t *a_codes, uint8_t *a_scales, void *c, bool out_bf16,
-                               bool one_launch, void *workspace, int32_t *status, hipStream_t s);
+                               bool one_launch, void *workspace, int32_t *status, hipStream_t s,
+                               uint32_t spin_limit = kResidentSpinLimit);
 
 }  // namespace fp4dev

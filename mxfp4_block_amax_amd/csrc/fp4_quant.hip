@@ -20,7 +20,6 @@
 //     an s_g that underflows, raises FP4_FLAG_SCALE_UNDERFLOW.
 // Scale search ("FP4 / NVFP4 math summary" page, devpress.csdn.net, section 9):
 //   per block, the candidate E4M3 scale with the least fp32 squared error.
-#include <atomic>
 #include <mutex>
 #include <type_traits>
 
@@ -1790,18 +1789,6 @@ __global__ __launch_bounds__(WG) void dequant_padded_kernel(const uint32_t *__re
 }
 
 // ---------------------------------------------------------------------------
-// the grid barrier's poll limit (a process-wide setting for tests of the
-// timeout path; launches read it when they are enqueued)
-// ---------------------------------------------------------------------------
-static std::atomic<uint32_t> g_spin_limit{kResidentSpinLimit};
-
-uint32_t barrier_spin_limit() { return g_spin_limit.load(std::memory_order_relaxed); }
-
-uint32_t set_barrier_spin_limit(uint32_t polls) {
-    return g_spin_limit.exchange(polls, std::memory_order_relaxed);
-}
-
-// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 static inline int grid_for(int64_t waves_needed, int max_wg) {
@@ -1922,18 +1909,18 @@ hipError_t launch_nv_quantize_packed(const void *x, bool bf16, int64_t rows, int
 template <int CPL>
 static void launch_resident(int g, const void *x, int64_t nchunks, uint8_t *codes,
                             uint8_t *scales, float *global_scale, uint8_t *ws, int32_t *status,
-                            hipStream_t s) {
+                            hipStream_t s, uint32_t spin_limit) {
     const bool exact = nchunks == (int64_t)g * CPL * RES_WG;
     auto kernel = exact ? nv_resident_kernel<CPL, true> : nv_resident_kernel<CPL, false>;
     hipLaunchKernelGGL(kernel, dim3(g), dim3(RES_WG), 0, s, (const uint4 *)x,
                        (int)nchunks, (uint32_t *)codes, scales, global_scale,
                        (uint64_t *)(ws + kResidentSlotsOffset),
-                       (uint32_t *)(ws + kResidentEpochOffset), barrier_spin_limit(), status);
+                       (uint32_t *)(ws + kResidentEpochOffset), spin_limit, status);
 }
 
 hipError_t launch_nv_quantize(const void *x, bool bf16, int64_t n, uint8_t *codes,
                               uint8_t *scales, float *global_scale, void *workspace,
-                              int32_t *status, hipStream_t s) {
+                              int32_t *status, hipStream_t s, uint32_t spin_limit) {
     const int64_t nchunks = n / 8;
     if (bf16) {
         const ResidentInfo ri = resident_info();
@@ -1945,10 +1932,10 @@ hipError_t launch_nv_quantize(const void *x, bool bf16, int64_t n, uint8_t *code
             const int g = (int)((nchunks + (int64_t)cpl * RES_WG - 1) / ((int64_t)cpl * RES_WG));
             uint8_t *ws = (uint8_t *)workspace;
             switch (cpl) {
-                case 8: launch_resident<8>(g, x, nchunks, codes, scales, global_scale, ws, status, s); break;
-                case 16: launch_resident<16>(g, x, nchunks, codes, scales, global_scale, ws, status, s); break;
-                case 32: launch_resident<32>(g, x, nchunks, codes, scales, global_scale, ws, status, s); break;
-                default: launch_resident<64>(g, x, nchunks, codes, scales, global_scale, ws, status, s); break;
+                case 8: launch_resident<8>(g, x, nchunks, codes, scales, global_scale, ws, status, s, spin_limit); break;
+                case 16: launch_resident<16>(g, x, nchunks, codes, scales, global_scale, ws, status, s, spin_limit); break;
+                case 32: launch_resident<32>(g, x, nchunks, codes, scales, global_scale, ws, status, s, spin_limit); break;
+                default: launch_resident<64>(g, x, nchunks, codes, scales, global_scale, ws, status, s, spin_limit); break;
             }
             return hipGetLastError();
         }

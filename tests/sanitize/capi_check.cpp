@@ -287,9 +287,19 @@ void argument_checks() {
         const char *msg = fp4_status_str((fp4_status)s);
         if (!msg || !msg[0]) ++failures;
     }
-    // the poll limit: set, read back through the next call, restore
-    const uint32_t old = fp4_debug_barrier_spin_limit(1000);
-    EXPECT(fp4_debug_barrier_spin_limit(old), 1000);
+    // the debug entry points with a poll limit validate as the product ones
+    for (uint32_t spin : {0u, 1000u, 0xFFFFFFFFu}) {
+        EXPECT(fp4_debug_quantize_nvfp4_spin(A16, BF, 4, 64, 16, U16, U16, nullptr, A16, WS,
+                                             nullptr, nullptr, spin),
+               FP4_E_ARG);
+        EXPECT(fp4_debug_quantize_nvfp4_spin(A16, BF, 4, 17, 16, U16, U16, F16, A16, WS,
+                                             nullptr, nullptr, spin),
+               FP4_E_SHAPE);
+        EXPECT(fp4_debug_linear_mxfp4_spin(A16, BF, 128, 512, U16, U16, 64, U16, U16, A16, BF,
+                                           FP4_LINEAR_ONE_LAUNCH, nullptr, WS, nullptr, nullptr,
+                                           spin),
+               FP4_E_WORKSPACE);
+    }
 }
 
 }  // namespace

@@ -252,19 +252,37 @@ def test_gemm_validation():
     assert g(a=A1) == E_ALIGN
 
 
-def test_barrier_spin_limit_round_trip():
-    """The poll limit is a host-side setting: set, read back through the
-    previous value, restored; the header's default matches the binding's."""
+def test_debug_poll_limit_entry_points_validate_as_the_product_ones():
+    """The grid barrier's poll limit is an argument of two debug entry points
+    (no process-wide setting): they reject what fp4_quantize_nvfp4 and
+    fp4_linear_mxfp4 reject, with the same codes, whatever the limit; the
+    header's default matches the binding's; the binding checks the range."""
     m = re.search(r"#define FP4_BARRIER_SPIN_LIMIT_DEFAULT (\d+)u", open(HEADER).read())
     assert m and int(m.group(1)) == fp4.BARRIER_SPIN_LIMIT_DEFAULT
-    prev = fp4.debug_barrier_spin_limit(7)
-    try:
-        assert prev == fp4.BARRIER_SPIN_LIMIT_DEFAULT
-        assert fp4.debug_barrier_spin_limit(0) == 7
-        assert fp4.debug_barrier_spin_limit(2**32 - 1) == 0
-    finally:
-        fp4.debug_barrier_spin_limit(prev)
-    assert fp4.debug_barrier_spin_limit(prev) == fp4.BARRIER_SPIN_LIMIT_DEFAULT
+    L = fp4.lib()
+
+    def nv2(spin, x=A16, block=16, cols=64, sg=A16, ws=A16, wsb=1 << 20):
+        args = (x, fp4.BF16, 4, cols, block, A16, A16, sg, ws, wsb, NULL, NULL)
+        return L.fp4_quantize_nvfp4(*args), L.fp4_debug_quantize_nvfp4_spin(*args, spin)
+
+    def lin2(spin, x=A16, K=512, ws=A16, mode=0):
+        args = (x, fp4.BF16, 128, K, A16, A16, 64, A16, A16, A16, fp4.BF16, mode, ws, 1 << 20,
+                NULL, NULL)
+        return L.fp4_linear_mxfp4(*args), L.fp4_debug_linear_mxfp4_spin(*args, spin)
+
+    for spin in (0, 7, 2**32 - 1):
+        assert nv2(spin, sg=NULL) == (E_ARG, E_ARG)
+        assert nv2(spin, block=32) == (E_ARG, E_ARG)
+        assert nv2(spin, cols=17) == (E_SHAPE, E_SHAPE)
+        assert nv2(spin, ws=NULL) == (E_WORKSPACE, E_WORKSPACE)
+        assert nv2(spin, x=A1) == (E_ALIGN, E_ALIGN)
+        assert lin2(spin, mode=2) == (E_ARG, E_ARG)
+        assert lin2(spin, K=48) == (E_SHAPE, E_SHAPE)
+        assert lin2(spin, ws=NULL) == (E_WORKSPACE, E_WORKSPACE)
+        assert lin2(spin, x=A1) == (E_ALIGN, E_ALIGN)
+    for bad in (-1, 2**32):
+        with pytest.raises(ValueError):
+            fp4._spin(bad)
 
 
 def test_packed_sizes_and_validation():

@@ -4,10 +4,10 @@ meet at a grid barrier; a workgroup that stops waiting (poll limit reached,
 e.g. because another kernel holds CUs) finishes by a fallback that gives the
 same result: the NVFP4 kernel reads the missing slices' amax itself, the
 linear quantizes all of A itself.  FLAG_BARRIER_TIMEOUT only records that it
-happened.  Forced from the host (poll limit 0: every kernel still exits
-normally), and by two calls running at once on two streams, the results must
-be bit-exact; calls after a fallback must be too (the barrier's epoch rules
-keep stale slots from matching)."""
+happened.  Forced from the host (the debug entry points with poll limit 0:
+every kernel still exits normally), and by two calls running at once on two
+streams, the results must be bit-exact; calls after a fallback must be too
+(the barrier's epoch rules keep stale slots from matching)."""
 import numpy as np
 import pytest
 import torch
@@ -18,14 +18,6 @@ import workloads
 from tests._gpu import announce, assert_bytes_equal, dev, f32_bits, host_u8, oracle_view
 
 pytestmark = pytest.mark.gpu
-
-
-def _with_poll_limit(polls, fn):
-    prev = fp4.debug_barrier_spin_limit(polls)
-    try:
-        return fn()
-    finally:
-        fp4.debug_barrier_spin_limit(prev)
 
 
 def _status(device):
@@ -63,8 +55,7 @@ def test_nv_resident_quantize_fallback_is_exact():
     for i in range(3):
         st = _status(xd.device)
         announce(f"nvfp4 quantize 8192x8192 bf16, poll limit 0, call {i}")
-        got = _with_poll_limit(0, lambda: fp4.quantize_nvfp4(xd, check=False, status=st,
-                                                             workspace=ws))
+        got = fp4.quantize_nvfp4(xd, check=False, status=st, workspace=ws, spin_limit=0)
         torch.cuda.synchronize()
         timeouts += _flags_ok(st)
         _nv_exact(got, ref, f"poll limit 0, call {i}")
@@ -72,7 +63,6 @@ def test_nv_resident_quantize_fallback_is_exact():
     # the same workspace, not re-zeroed, with the default limit: the epoch
     # rules keep the slots left by the fallbacks from matching
     announce("nvfp4 quantize 8192x8192 bf16, default limit after fallbacks")
-    assert fp4.debug_barrier_spin_limit(fp4.BARRIER_SPIN_LIMIT_DEFAULT) == fp4.BARRIER_SPIN_LIMIT_DEFAULT
     for i in range(2):
         st = _status(xd.device)
         got = fp4.quantize_nvfp4(xd, check=False, status=st, workspace=ws)
@@ -84,7 +74,7 @@ def test_nv_resident_quantize_fallback_is_exact():
     ref2 = _nv_reference(x2)
     x2d = dev(x2)
     announce("nvfp4 quantize 8192x8192 bf16 seed 1, poll limit 0 then default, same workspace")
-    _nv_exact(_with_poll_limit(0, lambda: fp4.quantize_nvfp4(x2d, workspace=ws)), ref2, "seed 1, limit 0")
+    _nv_exact(fp4.quantize_nvfp4(x2d, workspace=ws, spin_limit=0), ref2, "seed 1, limit 0")
     _nv_exact(fp4.quantize_nvfp4(xd, workspace=ws), ref, "seed 0 after seed 1")
     _nv_exact(fp4.quantize_nvfp4(x2d, workspace=ws), ref2, "seed 1 after seed 0")
 
@@ -146,8 +136,8 @@ def test_one_launch_linear_fallback_is_exact():
     for i in range(2):
         st = _status(xd.device)
         announce(f"linear mxfp4 {M}x{N}x{K} one launch, poll limit 0, call {i}")
-        got = _with_poll_limit(0, lambda: fp4.linear_mxfp4(xd, bt_d, bs_d, torch.float32, status=st,
-                                                           workspace=ws, check=False))
+        got = fp4.linear_mxfp4(xd, bt_d, bs_d, torch.float32, status=st, workspace=ws,
+                               check=False, spin_limit=0)
         torch.cuda.synchronize()
         timeouts += _flags_ok(st)
         exact(got, f"poll limit 0, call {i}")
