@@ -644,8 +644,57 @@ constexpr int RES_WAVES = RES_WG / WAVE;
 constexpr int RES_LDS_CHUNKS = 18;
 constexpr int RES_MAX_CHUNKS = 64;
 
+
 typedef __attribute__((address_space(1))) const void *global_cptr;
 typedef __attribute__((address_space(3))) void *lds_ptr;
+
+// Tensor amax of a bf16 tensor by one large workgroup per CU (the grid of
+// the one-pass quantize, no barrier): each lane issues all of its CPL chunk
+// loads at once, the first RES_LDS_CHUNKS into LDS and the rest into VGPRs,
+// then reduces.  Row j of the grid is one contiguous span of G*512 chunks
+// dealt out in 512-byte pieces, piece (t / 32) G + w to lanes 32 (t / 32) ..
+// + 31 of workgroup w, so an XCD's pieces are 512 bytes of every 4 KiB (the
+// spread at which the XCDs' loads finish closest together).  Loads past the
+// end re-read the lane's chunk of row 0 (a duplicate cannot change the max;
+// the launcher keeps row 0 inside the tensor).  Writes one partial per
+// workgroup, as tensor_amax_kernel does.
+template <int CPL>
+__global__ __launch_bounds__(RES_WG) void tensor_amax_wide_kernel(const uint4 *__restrict__ x,
+                                                                  int64_t nchunks,
+                                                                  uint32_t *__restrict__ partials) {
+    constexpr int LC = CPL < RES_LDS_CHUNKS ? CPL : RES_LDS_CHUNKS;
+    constexpr int RC = CPL - LC;
+    __shared__ uint4 lds[LC * RES_WG];
+    __shared__ uint32_t red[RES_WAVES];
+    const int tid = threadIdx.x, wv = tid / WAVE;
+    const int64_t stride = (int64_t)gridDim.x * RES_WG;
+    const int64_t c00 = ((int64_t)(tid / 32) * gridDim.x + blockIdx.x) * 32 + tid % 32;
+    auto chunk = [&](int j) {
+        const int64_t c = j * stride + c00;
+        return x + (c < nchunks ? c : c00);
+    };
+#pragma unroll
+    for (int j = 0; j < LC; ++j)
+        __builtin_amdgcn_global_load_lds((global_cptr)chunk(j), (lds_ptr)&lds[j * RES_WG + wv * WAVE],
+                                         16, 0, 0);
+    uint4 v[RC > 0 ? RC : 1];
+#pragma unroll
+    for (int r = 0; r < RC; ++r) v[r] = ld_stream(chunk(LC + r));
+    uint32_t m = 0;
+#pragma unroll
+    for (int r = 0; r < RC; ++r) m = max(m, amax_bf16x8(v[r]));
+    __builtin_amdgcn_s_waitcnt(0);  // the global->LDS loads of this wave have landed
+#pragma unroll
+    for (int j = 0; j < LC; ++j) m = max(m, amax_bf16x8(lds[j * RES_WG + tid]));
+    m = wave_max_u32(m);
+    if ((tid & (WAVE - 1)) == 0) red[wv] = m;
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t r = red[0];
+        for (int i = 1; i < RES_WAVES; ++i) r = max(r, red[i]);
+        partials[blockIdx.x] = r;
+    }
+}
 
 // ---------------------------------------------------------------------------
 // NVFP4 quantize, pass 2, written in the packed NVFP4 operand layout: one
@@ -1851,16 +1900,6 @@ static int amax_grid(int64_t nchunks, bool two_per_cu) {
     return (int)(g < 1 ? 1 : g);
 }
 
-static hipError_t launch_amax(const void *x, bool bf16, int64_t nchunks, uint32_t *partials,
-                              int g, hipStream_t s) {
-    if (bf16)
-        hipLaunchKernelGGL(tensor_amax_kernel<true>, dim3(g), dim3(WG), 0, s, (const uint4 *)x,
-                           nchunks, partials);
-    else
-        hipLaunchKernelGGL(tensor_amax_kernel<false>, dim3(g), dim3(WG), 0, s, (const uint4 *)x,
-                           nchunks, partials);
-    return hipGetLastError();
-}
 
 // Whether the one-pass resident kernel can run on the current device, and on
 // how many CUs: one workgroup per CU must fit (so the whole grid is resident
@@ -1889,13 +1928,56 @@ static ResidentInfo resident_info() {
     return info[dev];
 }
 
+// The tensor-amax pass: the wide kernel (one workgroup per CU, every load
+// issued at once) for a bf16 tensor of 8 to 64 chunks per lane on the CUs
+// the one-pass quantize may use, else tensor_amax_kernel.  g is the number
+// of partials it writes.
+struct AmaxPlan {
+    int g;
+    int cpl;  // chunks per lane of the wide kernel, a multiple of 8; 0: the other kernel
+};
+
+static AmaxPlan amax_plan(int64_t nchunks, bool bf16, bool two_per_cu) {
+    if (bf16) {
+        const int cus = resident_info().cus;
+        const int64_t per = (int64_t)cus * RES_WG;  // chunks one row of the grid covers
+        if (cus > 0 && cus <= kAmaxPartials && nchunks >= per * 8 && nchunks <= per * RES_MAX_CHUNKS) {
+            const int cpl = (int)((nchunks + per * 8 - 1) / (per * 8)) * 8;
+            const int g = (int)((nchunks + (int64_t)cpl * RES_WG - 1) / ((int64_t)cpl * RES_WG));
+            return {g, cpl};
+        }
+    }
+    return {amax_grid(nchunks, two_per_cu), 0};
+}
+
+static hipError_t launch_amax(const void *x, bool bf16, int64_t nchunks, uint32_t *partials,
+                              const AmaxPlan &p, hipStream_t s) {
+    const dim3 g((unsigned)p.g);
+    const uint4 *xv = (const uint4 *)x;
+    switch (p.cpl) {
+        case 0:
+            if (bf16) hipLaunchKernelGGL(tensor_amax_kernel<true>, g, dim3(WG), 0, s, xv, nchunks, partials);
+            else hipLaunchKernelGGL(tensor_amax_kernel<false>, g, dim3(WG), 0, s, xv, nchunks, partials);
+            break;
+#define FP4_WIDE(C) \
+    case C: hipLaunchKernelGGL(tensor_amax_wide_kernel<C>, g, dim3(RES_WG), 0, s, xv, nchunks, partials); break
+        FP4_WIDE(8); FP4_WIDE(16); FP4_WIDE(24); FP4_WIDE(32);
+        FP4_WIDE(40); FP4_WIDE(48); FP4_WIDE(56); FP4_WIDE(64);
+#undef FP4_WIDE
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+
 hipError_t launch_nv_quantize_packed(const void *x, bool bf16, int64_t rows, int64_t cols,
                                      uint8_t *packed, float *global_scale, void *workspace,
                                      int32_t *status, hipStream_t s) {
     const int64_t nrt = (rows + 31) / 32, ntiles = nrt * (cols / 64);
     uint32_t *partials = (uint32_t *)workspace;
-    const int g1 = amax_grid(rows * cols / 8, false);
-    hipError_t e = launch_amax(x, bf16, rows * cols / 8, partials, g1, s);
+    const AmaxPlan ap = amax_plan(rows * cols / 8, bf16, false);
+    const int g1 = ap.g;
+    hipError_t e = launch_amax(x, bf16, rows * cols / 8, partials, ap, s);
     if (e != hipSuccess) return e;
     int64_t g = (ntiles + WAVES_PER_WG - 1) / WAVES_PER_WG;
     if (g > kMaxGrid) g = kMaxGrid;
@@ -1941,8 +2023,9 @@ hipError_t launch_nv_quantize(const void *x, bool bf16, int64_t n, uint8_t *code
         }
     }
     uint32_t *partials = (uint32_t *)workspace;
-    const int g1 = amax_grid(nchunks, !bf16);
-    hipError_t e = launch_amax(x, bf16, nchunks, partials, g1, s);
+    const AmaxPlan ap = amax_plan(nchunks, bf16, !bf16);
+    const int g1 = ap.g;
+    hipError_t e = launch_amax(x, bf16, nchunks, partials, ap, s);
     if (e != hipSuccess) return e;
     const int g = grid_for((nchunks + WAVE * 2 - 1) / (WAVE * 2), kMaxGrid);
     auto kernel = bf16 ? nv_quantize_kernel<true, false> : nv_quantize_kernel<false, false>;
@@ -1963,8 +2046,9 @@ hipError_t launch_quantize_sr(int fmt, const void *x, bool bf16, int64_t n, uint
         return hipGetLastError();
     }
     uint32_t *partials = (uint32_t *)workspace;
-    const int g1 = amax_grid(nchunks, false);
-    hipError_t e = launch_amax(x, bf16, nchunks, partials, g1, s);
+    const AmaxPlan ap = amax_plan(nchunks, bf16, false);
+    const int g1 = ap.g;
+    hipError_t e = launch_amax(x, bf16, nchunks, partials, ap, s);
     if (e != hipSuccess) return e;
     const int g = grid_for((nchunks + WAVE * 2 - 1) / (WAVE * 2), kMaxGrid);
     auto kernel = bf16 ? nv_quantize_kernel<true, true> : nv_quantize_kernel<false, true>;
@@ -1997,8 +2081,9 @@ hipError_t launch_scale_search(const void *x, bool bf16, int64_t n, bool all, fl
                                void *workspace, int32_t *status, hipStream_t s) {
     const int64_t nchunks = n / 8;
     uint32_t *partials = (uint32_t *)workspace;
-    const int g1 = amax_grid(nchunks, false);
-    hipError_t e = launch_amax(x, bf16, nchunks, partials, g1, s);
+    const AmaxPlan ap = amax_plan(nchunks, bf16, false);
+    const int g1 = ap.g;
+    hipError_t e = launch_amax(x, bf16, nchunks, partials, ap, s);
     if (e != hipSuccess) return e;
     using K = void (*)(const uint4 *, int64_t, const uint32_t *, int, float, float, uint32_t *,
                        uint8_t *, float *, int32_t *);
