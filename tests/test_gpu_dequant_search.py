@@ -111,6 +111,22 @@ def test_search_scale_underflow_flag_bf16():
     assert_bytes_equal(host_u8(codes), p, "search codes with an underflow")
 
 
+def test_search_ragged_shapes_of_the_one_wave_amax_pass():
+    # bf16 inputs of 8 to 64 chunks per lane on all CUs take the tensor-amax
+    # pass of one workgroup per CU; 2049 x 4112 (1,053,186 chunks: on 256
+    # CUs 129 workgroups of 16 chunks per lane, the last grid row partly past
+    # the end) with the largest magnitude planted in the tensor's last chunk,
+    # then in its first: s_g, codes and scale bytes every block against the
+    # oracle
+    x = workloads.scale_search_input(2049, 4112, seed=5)
+    y = x.clone()
+    y[-1, -3] = 0.75
+    _search_check(y, "laplace 2049x4112, amax in the last chunk")
+    y = x.clone()
+    y[0, 1] = -0.75
+    _search_check(y, "laplace 2049x4112, amax in the first chunk")
+
+
 def test_search_full_size_every_block():
     # the 4096 x 14336 Laplace(0, 0.01) search input, 64 candidates in
     # [0.5, 1]: every one of its 3.67M blocks against the oracle (the oracle
