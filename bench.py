@@ -606,6 +606,27 @@ def copy_ceiling(iters: int = 20):
                       "bytes read + written"}
 
 
+def fill_ceiling(iters: int = 20):
+    """Measured write-only rate of torch `fill_` over a 256 MiB buffer,
+    alternating two buffers so that the MALL cannot absorb the stores: the
+    practical ceiling of store-bound kernels such as dequantize."""
+    n = 256 << 20
+    bufs = [torch.empty(n, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    for i in range(2):
+        bufs[i].fill_(i + 1)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(iters):
+        bufs[i & 1].fill_(i & 0x7F)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / iters
+    gbs = n / (ms * 1e-3) / 1e9
+    return {"GB/s": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+            "method": "torch fill_ of 256 MiB, two buffers alternating, HIP events; bytes written"}
+
+
 def timed_steps(fns, steps: int, warmup: int):
     """`warmup` untimed launches, then EXACTLY `steps` launches captured as one
     HIP graph and replayed once between two HIP events recorded on the replay
@@ -828,6 +849,7 @@ def main():
         "breakdown": breakdown,
         "roofline": roofline,
         "copy_ceiling": copy_ceiling(),
+        "fill_ceiling": fill_ceiling(),
     }
     if not args.no_extra:
         st = torch.zeros(1, dtype=torch.int32, device="cuda")
